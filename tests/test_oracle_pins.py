@@ -1,0 +1,382 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle.
+
+Each test checks the token recurrence in ``oracle/lao.c`` against something
+fixed independently of it: a hand-worked example, a closed form evaluated with
+numpy's matmul / cumsum, brute-force finite differences, exact invariants of
+the mathematics (segment composition, streaming resume, Euler's identity for
+homogeneous functions) or degenerate inputs.  All of this runs on the CPU.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import lao
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(rng, *shape):
+    return rng.standard_normal(shape)
+
+
+def _rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    den = np.max(np.abs(b))
+    return float(np.max(np.abs(a - b)) / (den if den > 0 else 1.0))
+
+
+def quadratic_form(Q, K, V, lam, S0):
+    """Closed form for one (b, h) sequence, 1-indexed tokens t, s:
+         O = ((Q K^T) * D) V + diag(lam^t) Q S0,  D[t, s] = lam^(t-s) [s <= t]
+         S_end = lam^L S0 + K^T diag(lam^(L-s)) V
+    written with numpy matmul, independently of the recurrence."""
+    L = Q.shape[0]
+    t = np.arange(1, L + 1, dtype=np.float64)
+    diff = t[:, None] - t[None, :]
+    D = np.where(diff >= 0, lam ** np.maximum(diff, 0), 0.0)
+    O = ((Q @ K.T) * D) @ V
+    if S0 is not None:
+        O = O + (lam ** t)[:, None] * (Q @ S0)
+    w = lam ** (L - t)
+    S_end = K.T @ (w[:, None] * V)
+    if S0 is not None:
+        S_end = S_end + lam ** L * S0
+    return O, S_end
+
+
+# --------------------------------------------------------------------------
+# hand-worked examples
+
+
+def test_hand_example_forward():
+    g = json.load(open(os.path.join(GOLDEN, "hand_dk2_dv3.json")))
+    Q = np.array(g["q"], float)[None, None]
+    K = np.array(g["k"], float)[None, None]
+    V = np.array(g["v"], float)[None, None]
+    S0 = np.array(g["S0"], float)[None, None, None]
+    O, S_end = lao.fwd(Q, K, V, np.array([g["lam"]]), S0=S0)
+    # every value in the example is a dyadic rational: exact equality
+    np.testing.assert_array_equal(O[0, 0], np.array(g["O"], float))
+    np.testing.assert_array_equal(S_end[0, 0, 0], np.array(g["S_end"], float))
+
+
+def test_hand_example_rows():
+    g = json.load(open(os.path.join(GOLDEN, "hand_dk2_dv3.json")))
+    Q = np.array(g["q"], float)[None, None]
+    K = np.array(g["k"], float)[None, None]
+    V = np.array(g["v"], float)[None, None]
+    S0 = np.array(g["S0"], float)[None, None, None]
+    rows = lao.fwd_rows(Q, K, V, np.array([g["lam"]]), [0, 0, 0], [0, 1, 2], S0=S0)
+    np.testing.assert_array_equal(rows, np.array(g["O"], float))
+
+
+def test_hand_example_scan():
+    g = json.load(open(os.path.join(GOLDEN, "hand_scan.json")))
+    dS = np.array(g["dS"], float).reshape(1, 1, 3, 1, 1)
+    S0 = np.array([[[[g["S0"]]]]])
+    for key, rev in (("forward", False), ("reverse", True)):
+        st, en = lao.scan(dS, np.array([g["lam"]]), g["seg_len"], S0=S0, reverse=rev)
+        np.testing.assert_array_equal(st.reshape(-1), np.array(g[key]["S_start"]))
+        assert en.reshape(-1)[0] == g[key]["S_end"]
+
+
+# --------------------------------------------------------------------------
+# closed forms
+
+
+@pytest.mark.parametrize("L,dk,dv", [(1, 4, 4), (77, 16, 24), (300, 64, 64), (512, 16, 16)])
+def test_recurrence_equals_quadratic_form(L, dk, dv):
+    rng = np.random.default_rng(100 + L)
+    B, H = 2, 3
+    Q = _rand(rng, B, H, L, dk) / np.sqrt(dk)
+    K = _rand(rng, B, H, L, dk) / np.sqrt(dk)
+    V = _rand(rng, B, H, L, dv)
+    S0 = _rand(rng, B, H, 1, dk, dv)
+    lam = rng.uniform(0.5, 1.0, H)
+    lam[0] = 1.0
+    O, S_end = lao.fwd(Q, K, V, lam, S0=S0)
+    for b in range(B):
+        for h in range(H):
+            Oq, Sq = quadratic_form(Q[b, h], K[b, h], V[b, h], lam[h], S0[b, h, 0])
+            assert _rel(O[b, h], Oq) < 1e-12
+            assert _rel(S_end[b, h, 0], Sq) < 1e-12
+
+
+def test_lambda_one_cumsum_closed_form():
+    """lambda = 1: S_t = S0 + cumsum_s k_s v_s^T, O = tril(QK^T) V + Q S0."""
+    rng = np.random.default_rng(7)
+    L, dk, dv = 256, 8, 12
+    Q = _rand(rng, 1, 1, L, dk)
+    K = _rand(rng, 1, 1, L, dk)
+    V = _rand(rng, 1, 1, L, dv)
+    S0 = _rand(rng, 1, 1, 1, dk, dv)
+    O, S_end = lao.fwd(Q, K, V, np.array([1.0]), S0=S0)
+    outer = np.einsum("ti,tj->tij", K[0, 0], V[0, 0])
+    S_t = S0[0, 0, 0][None] + np.cumsum(outer, axis=0)
+    O_ref = np.einsum("ti,tij->tj", Q[0, 0], S_t)
+    assert _rel(O[0, 0], O_ref) < 1e-12
+    assert _rel(S_end[0, 0, 0], S_t[-1]) < 1e-12
+    O_ref2 = np.tril(Q[0, 0] @ K[0, 0].T) @ V[0, 0] + Q[0, 0] @ S0[0, 0, 0]
+    assert _rel(O[0, 0], O_ref2) < 1e-12
+
+
+def test_lambda_one_workload_shape_closed_form():
+    """The undecayed fp32 workload's shape (H=2, L=1024, d=64) at lambda = 1."""
+    rng = np.random.default_rng(11)
+    L, d = 1024, 64
+    Q = _rand(rng, 1, 2, L, d) / 8
+    K = _rand(rng, 1, 2, L, d) / 8
+    V = _rand(rng, 1, 2, L, d)
+    O, S_end = lao.fwd(Q, K, V, np.ones(2))
+    for h in range(2):
+        assert _rel(O[0, h], np.tril(Q[0, h] @ K[0, h].T) @ V[0, h]) < 1e-12
+        assert _rel(S_end[0, h, 0], K[0, h].T @ V[0, h]) < 1e-12
+
+
+def test_state_end_closed_form_long():
+    """S_end = lam^L S0 + K^T diag(lam^(L-s)) V at a longer length."""
+    rng = np.random.default_rng(5)
+    L, d = 8192, 32
+    lam = np.array([0.999, 0.97])
+    Q = _rand(rng, 1, 2, L, d)
+    K = _rand(rng, 1, 2, L, d) / np.sqrt(d)
+    V = _rand(rng, 1, 2, L, d)
+    S0 = _rand(rng, 1, 2, 1, d, d)
+    _, S_end = lao.fwd(Q, K, V, lam, S0=S0, need_O=False)
+    t = np.arange(1, L + 1)
+    for h in range(2):
+        w = lam[h] ** (L - t)
+        ref = lam[h] ** L * S0[0, h, 0] + K[0, h].T @ (w[:, None] * V[0, h])
+        assert _rel(S_end[0, h, 0], ref) < 1e-11
+
+
+def test_rows_equal_recurrence():
+    rng = np.random.default_rng(9)
+    B, H, L, d = 1, 2, 200, 16
+    Q, K, V = (_rand(rng, B, H, L, d) for _ in range(3))
+    S0 = _rand(rng, B, H, 2, d, d)
+    lam = np.array([0.9, 1.0])
+    O, _ = lao.fwd(Q, K, V, lam, S0=S0, nseg=2)
+    seq = np.array([0, 1, 2, 3, 3, 1])
+    rows = np.array([0, 99, 50, 0, 99, 63])
+    R = lao.fwd_rows(Q, K, V, lam, seq, rows, S0=S0, nseg=2)
+    Of = O.reshape(B * H * 2, L // 2, d)
+    assert _rel(R, Of[seq, rows]) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# invariants
+
+
+def test_segments_with_scanned_starts_equal_monolithic():
+    """Local states from zero, scanned, then used as initial states of each
+    segment, reproduce the monolithic run (ZeCO / LASP-2 abstracts)."""
+    rng = np.random.default_rng(3)
+    B, H, L, d, P = 1, 3, 768, 16, 6
+    Q, K = (_rand(rng, B, H, L, d) / 4 for _ in range(2))
+    V = _rand(rng, B, H, L, d)
+    S0 = _rand(rng, B, H, 1, d, d)
+    lam = np.array([0.95, 0.999, 1.0])
+    O_mono, S_mono = lao.fwd(Q, K, V, lam, S0=S0)
+    _, dS = lao.fwd(Q, K, V, lam, S0=None, nseg=P, need_O=False)
+    S_start, S_end = lao.scan(dS, lam, L // P, S0=S0[:, :, 0])
+    O_seg, S_seg_end = lao.fwd(Q, K, V, lam, S0=S_start, nseg=P)
+    assert _rel(O_seg, O_mono) < 1e-12
+    assert _rel(S_end, S_mono[:, :, 0]) < 1e-12
+    # the end state of segment s is the start state of segment s + 1
+    assert _rel(S_seg_end[:, :, :-1], S_start[:, :, 1:]) < 1e-12
+    assert _rel(S_seg_end[:, :, -1], S_mono[:, :, 0]) < 1e-12
+
+
+def test_scan_special_cases():
+    rng = np.random.default_rng(4)
+    B, H, P, d = 2, 2, 9, 5
+    dS = _rand(rng, B, H, P, d, d)
+    S0 = _rand(rng, B, H, d, d)
+    # lambda^seg_len = 1: prefix sums
+    st, en = lao.scan(dS, np.ones(H), 100, S0=S0)
+    cs = np.cumsum(dS, axis=2)
+    assert _rel(st[:, :, 1:], S0[:, :, None] + cs[:, :, :-1]) < 1e-13
+    assert _rel(en, S0 + cs[:, :, -1]) < 1e-13
+    # lambda = 0: every start is the previous local state
+    st, en = lao.scan(dS, np.zeros(H), 4, S0=S0)
+    np.testing.assert_array_equal(st[:, :, 1:], dS[:, :, :-1])
+    np.testing.assert_array_equal(st[:, :, 0], S0)
+    np.testing.assert_array_equal(en, dS[:, :, -1])
+    # reverse scan = forward scan of the reversed segment order
+    lam = np.array([0.9, 0.5])
+    st_r, en_r = lao.scan(dS, lam, 3, S0=S0, reverse=True)
+    st_f, en_f = lao.scan(dS[:, :, ::-1], lam, 3, S0=S0)
+    np.testing.assert_array_equal(st_r, st_f[:, :, ::-1])
+    np.testing.assert_array_equal(en_r, en_f)
+
+
+def test_streaming_resume():
+    """Running [1..L1] and then [L1+1..L] from the first part's end state
+    equals one run (constant-memory inference, LASP-2 abstract)."""
+    rng = np.random.default_rng(6)
+    B, H, L, d, L1 = 1, 2, 500, 8, 173
+    Q, K, V = (_rand(rng, B, H, L, d) for _ in range(3))
+    S0 = _rand(rng, B, H, 1, d, d)
+    lam = np.array([0.98, 0.7])
+    O, S_end = lao.fwd(Q, K, V, lam, S0=S0)
+    O1, S1 = lao.fwd(Q[:, :, :L1], K[:, :, :L1], V[:, :, :L1], lam, S0=S0)
+    O2, S2 = lao.fwd(Q[:, :, L1:], K[:, :, L1:], V[:, :, L1:], lam, S0=S1)
+    np.testing.assert_allclose(np.concatenate([O1, O2], axis=2), O, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(S2, S_end, rtol=0, atol=1e-12)
+
+
+def test_degenerate_inputs():
+    rng = np.random.default_rng(8)
+    B, H, L, d = 1, 2, 64, 8
+    Q = _rand(rng, B, H, L, d)
+    S0 = _rand(rng, B, H, 1, d, d)
+    lam = np.array([0.9, 0.6])
+    t = np.arange(1, L + 1)
+    # K = 0: only the decayed initial state is seen
+    Z = np.zeros((B, H, L, d))
+    O, S_end = lao.fwd(Q, Z, _rand(rng, B, H, L, d), lam, S0=S0)
+    for h in range(H):
+        ref = (lam[h] ** t)[:, None] * (Q[0, h] @ S0[0, h, 0])
+        assert _rel(O[0, h], ref) < 1e-13
+        assert _rel(S_end[0, h, 0], lam[h] ** L * S0[0, h, 0]) < 1e-13
+    # L = 1
+    K1, V1 = _rand(rng, B, H, 1, d), _rand(rng, B, H, 1, d)
+    O, S_end = lao.fwd(Q[:, :, :1], K1, V1, lam, S0=S0)
+    for h in range(H):
+        S1 = lam[h] * S0[0, h, 0] + np.outer(K1[0, h, 0], V1[0, h, 0])
+        assert _rel(S_end[0, h, 0], S1) < 1e-14
+        assert _rel(O[0, h, 0], Q[0, h, 0] @ S1) < 1e-14
+    # lambda -> 0: o_t = (q_t . k_t) v_t, S_end = k_L v_L^T
+    K, V = _rand(rng, B, H, L, d), _rand(rng, B, H, L, d)
+    O, S_end = lao.fwd(Q, K, V, np.array([1e-30, 1e-30]), S0=S0)
+    ref = np.sum(Q * K, axis=-1, keepdims=True) * V
+    assert _rel(O, ref) < 1e-13  # previous tokens weigh 1e-30: only rounding remains
+    assert _rel(S_end[0, 0, 0], np.outer(K[0, 0, -1], V[0, 0, -1])) < 1e-13
+    # L = 0 is an empty sequence: the end state is the initial state
+    E = np.zeros((B, H, 0, d))
+    O, S_end = lao.fwd(E, E, E, lam, S0=S0)
+    assert O.shape == (B, H, 0, d)
+    np.testing.assert_array_equal(S_end, S0)
+
+
+# --------------------------------------------------------------------------
+# backward
+
+
+def _loss(Q, K, V, lam, S0, dO, dS_end):
+    O, S_end = lao.fwd(Q, K, V, lam, S0=S0)
+    return float(np.sum(O * dO) + np.sum(S_end * dS_end))
+
+
+def test_backward_finite_differences():
+    """Directional derivatives of <dO, O> + <dS_end, S_end> by central
+    differences agree with the oracle backward (the loss is quadratic in the
+    inputs, so the central difference is exact up to rounding)."""
+    rng = np.random.default_rng(12)
+    B, H, L, d = 1, 2, 40, 6
+    Q, K, V, dO = (_rand(rng, B, H, L, d) for _ in range(4))
+    S0, dS_end = _rand(rng, B, H, 1, d, d), _rand(rng, B, H, 1, d, d)
+    lam = np.array([0.9, 0.99])
+    dQ, dK, dV, dS0 = lao.bwd(Q, K, V, lam, dO, S0=S0, dS_end=dS_end)
+    eps = 1e-3
+    for name, X, G in (("Q", Q, dQ), ("K", K, dK), ("V", V, dV), ("S0", S0, dS0)):
+        for trial in range(3):
+            Dir = _rand(rng, *X.shape)
+            args = dict(Q=Q, K=K, V=V, S0=S0)
+            args[name] = X + eps * Dir
+            lp = _loss(args["Q"], args["K"], args["V"], lam, args["S0"], dO, dS_end)
+            args[name] = X - eps * Dir
+            lm = _loss(args["Q"], args["K"], args["V"], lam, args["S0"], dO, dS_end)
+            fd = (lp - lm) / (2 * eps)
+            an = float(np.sum(G * Dir))
+            assert abs(fd - an) <= 1e-8 * max(1.0, abs(an)), (name, fd, an)
+
+
+def test_backward_closed_forms():
+    """dQ = ((dO V^T) * D) K + diag(lam^t) dO S0^T
+       dK = ((dO V^T) * D)^T Q + diag(lam^(L-s)) V dS_end^T
+       dV = ((Q K^T) * D)^T dO + diag(lam^(L-s)) K dS_end
+       dS0 = Q^T diag(lam^t) dO + lam^L dS_end"""
+    rng = np.random.default_rng(13)
+    B, H, L, dk, dv = 1, 2, 150, 12, 20
+    Q, K = (_rand(rng, B, H, L, dk) for _ in range(2))
+    V, dO = (_rand(rng, B, H, L, dv) for _ in range(2))
+    S0, dS_end = _rand(rng, B, H, 1, dk, dv), _rand(rng, B, H, 1, dk, dv)
+    lam = np.array([0.93, 1.0])
+    dQ, dK, dV, dS0 = lao.bwd(Q, K, V, lam, dO, S0=S0, dS_end=dS_end)
+    t = np.arange(1, L + 1, dtype=float)
+    for h in range(H):
+        l = lam[h]
+        diff = t[:, None] - t[None, :]
+        D = np.where(diff >= 0, l ** np.maximum(diff, 0), 0.0)
+        q, k, v, g = Q[0, h], K[0, h], V[0, h], dO[0, h]
+        s0, de = S0[0, h, 0], dS_end[0, h, 0]
+        wt, wr = l ** t, l ** (L - t)
+        assert _rel(dQ[0, h], ((g @ v.T) * D) @ k + wt[:, None] * (g @ s0.T)) < 1e-12
+        assert _rel(dK[0, h], ((g @ v.T) * D).T @ q + wr[:, None] * (v @ de.T)) < 1e-12
+        assert _rel(dV[0, h], ((q @ k.T) * D).T @ g + wr[:, None] * (k @ de)) < 1e-12
+        assert _rel(dS0[0, h, 0], q.T @ (wt[:, None] * g) + l ** L * de) < 1e-12
+
+
+def test_backward_matches_torch_autograd_on_quadratic_form():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(14)
+    L, d = 70, 8
+    lam = 0.95
+    arrs = [_rand(rng, L, d) for _ in range(4)] + [_rand(rng, d, d), _rand(rng, d, d)]
+    Q, K, V, dO, S0, dSe = arrs
+    tq, tk, tv, ts = (torch.tensor(a, dtype=torch.float64, requires_grad=True)
+                      for a in (Q, K, V, S0))
+    t = torch.arange(1, L + 1, dtype=torch.float64)
+    diff = t[:, None] - t[None, :]
+    D = torch.where(diff >= 0, lam ** diff.clamp(min=0), torch.zeros_like(diff))
+    O = ((tq @ tk.T) * D) @ tv + (lam ** t)[:, None] * (tq @ ts)
+    Se = tk.T @ ((lam ** (L - t))[:, None] * tv) + lam ** L * ts
+    loss = (O * torch.tensor(dO)).sum() + (Se * torch.tensor(dSe)).sum()
+    loss.backward()
+    dQ, dK, dV, dS0 = lao.bwd(Q[None, None], K[None, None], V[None, None], np.array([lam]),
+                              dO[None, None], S0=S0[None, None, None],
+                              dS_end=dSe[None, None, None])
+    assert _rel(dQ[0, 0], tq.grad.numpy()) < 1e-12
+    assert _rel(dK[0, 0], tk.grad.numpy()) < 1e-12
+    assert _rel(dV[0, 0], tv.grad.numpy()) < 1e-12
+    assert _rel(dS0[0, 0, 0], ts.grad.numpy()) < 1e-12
+
+
+def test_backward_euler_identities():
+    """l = <dO,O> + <dS_end,S_end> is linear in Q and jointly linear in
+    (K, S0) and in (V, S0), so <dQ,Q> = <dO,O>, <dK,K> + <dS0,S0> = l and
+    <dV,V> + <dS0,S0> = l."""
+    rng = np.random.default_rng(15)
+    B, H, L, d = 2, 2, 128, 8
+    Q, K, V, dO = (_rand(rng, B, H, L, d) for _ in range(4))
+    S0, dS_end = _rand(rng, B, H, 2, d, d), _rand(rng, B, H, 2, d, d)
+    lam = np.array([0.97, 0.8])
+    O, S_end = lao.fwd(Q, K, V, lam, S0=S0, nseg=2)
+    dQ, dK, dV, dS0 = lao.bwd(Q, K, V, lam, dO, S0=S0, dS_end=dS_end, nseg=2)
+    l_o = np.sum(dO * O)
+    l = l_o + np.sum(dS_end * S_end)
+    assert abs(np.sum(dQ * Q) - l_o) < 1e-10 * np.sum(np.abs(dQ * Q))
+    assert abs(np.sum(dK * K) + np.sum(dS0 * S0) - l) < 1e-10 * (np.sum(np.abs(dK * K)) + np.sum(np.abs(dS0 * S0)))
+    assert abs(np.sum(dV * V) + np.sum(dS0 * S0) - l) < 1e-10 * (np.sum(np.abs(dV * V)) + np.sum(np.abs(dS0 * S0)))
+
+
+def test_backward_zero_state_inputs():
+    """With S0 and dS_end absent (zero) the closed forms lose their state terms."""
+    rng = np.random.default_rng(16)
+    L, d = 96, 8
+    Q, K, V, dO = (_rand(rng, 1, 1, L, d) for _ in range(4))
+    lam = np.array([0.9])
+    dQ, dK, dV, dS0 = lao.bwd(Q, K, V, lam, dO)
+    t = np.arange(1, L + 1, dtype=float)
+    diff = t[:, None] - t[None, :]
+    D = np.where(diff >= 0, 0.9 ** np.maximum(diff, 0), 0.0)
+    q, k, v, g = Q[0, 0], K[0, 0], V[0, 0], dO[0, 0]
+    assert _rel(dQ[0, 0], ((g @ v.T) * D) @ k) < 1e-12
+    assert _rel(dK[0, 0], ((g @ v.T) * D).T @ q) < 1e-12
+    assert _rel(dV[0, 0], ((q @ k.T) * D).T @ g) < 1e-12
+    assert _rel(dS0[0, 0, 0], q.T @ ((0.9 ** t)[:, None] * g)) < 1e-12
