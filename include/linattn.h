@@ -1,0 +1,183 @@
+/*
+ * linattn.h -- C ABI of liblinattn.so: chunkwise causal linear attention with
+ * a constant decay per head, for AMD Instinct MI355X (gfx950).
+ *
+ * The method.  For every sequence (b, h) -- or every segment of it, see
+ * `nseg` -- with decay lambda = lambda[h], the library computes
+ *
+ *     S_t = lambda * S_{t-1} + k_t v_t^T          (state, d_k x d_v, fp32)
+ *     o_t = q_t^T S_t                             (output row, length d_v)
+ *
+ * for t = 1..L starting from the initial state S_0 and returns S_end = S_L.
+ *  - The state is the "intermediate memory state whose size is independent of
+ *    the sequence length" and the evaluation is right-product-first: LASP-2
+ *    (Rethinking Sequence Parallelism for Linear Attention and Its Hybrid),
+ *    abstract.
+ *  - Work is tiled into 64-token chunks: exact causal attention inside a
+ *    chunk, the state (kernel trick) between chunks -- the split the
+ *    Lightning Attention-2 entry of the LASP-2 page's related-paper list
+ *    describes.
+ *  - A sequence can be cut into segments that each start from a given initial
+ *    state, and per-segment states combine by the scan of la_state_scan; this
+ *    is what the All-Scan collective of ZeCO (Zero Communication Overhead
+ *    Sequence Parallelism for Linear Attention), abstract, delivers to each
+ *    rank, and what LASP-2's single all-gather of memory states feeds.
+ * There is no feature map, normaliser or softmax scale: callers fold any
+ * scale into q and k.  The current token is included in its own output, and
+ * S_0 is decayed once before the first token is added.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers (including lambda), contiguous,
+ *    row-major, 16-byte aligned.  The caller owns every buffer; the library
+ *    allocates and frees nothing and keeps no device state.
+ *  - Token tensors: Q, K, dQ, dK are [B, H, L, dk]; V, O, dO, dV are
+ *    [B, H, L, dv], all of element type `dtype`.  States (S0, S_end, dS_end,
+ *    dS0) are fp32 [B, H, nseg, dk, dv] with the state row-major as [dk][dv].
+ *    lambda is fp32 [H].
+ *  - Calls are asynchronous and ordered on `stream` (a hipStream_t; NULL is
+ *    the default stream).  The library never synchronises.  Concurrent calls
+ *    on different streams are allowed if their output buffers and workspaces
+ *    do not overlap.
+ *  - Errors: every argument is checked on the host before any HIP call.  A
+ *    check that fails returns LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED or
+ *    LA_ERR_WORKSPACE, launches nothing and writes nothing.  A failed launch
+ *    returns LA_ERR_HIP.  la_last_error() describes the last failure of the
+ *    calling thread.  No C++ exception crosses this interface.
+ *  - Preconditions that are not checked (device data is not read on the
+ *    host): 0 < lambda[h] <= 1.  Other values give undefined numbers (but no
+ *    out-of-bounds access).  NaN and Inf inputs propagate.
+ *  - Outputs are fully overwritten, never accumulated into.  No input may
+ *    overlap an output except where stated.
+ *  - Results are deterministic: the same call on the same inputs gives the
+ *    same bits (no atomics).
+ */
+#ifndef LINATTN_H
+#define LINATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LA_OK = 0,
+  LA_ERR_INVALID_ARG = 1,  /* null required pointer, negative size, misalignment, bad enum */
+  LA_ERR_UNSUPPORTED = 2,  /* valid but not implemented: d not in {64,128}, dk != dv */
+  LA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than *_workspace_bytes() */
+  LA_ERR_HIP = 4           /* a HIP runtime call or launch failed */
+} la_status;
+
+typedef enum {
+  LA_BF16 = 0,             /* bfloat16 tokens; fp32 accumulation and states */
+  LA_FP32 = 1              /* float32 everywhere */
+} la_dtype;
+
+/*
+ * Problem shape.
+ *   B, H, L   batch, heads, tokens per (b, h) sequence; B, H, L >= 0.
+ *   dk, dv    head dimensions; this version needs dk == dv in {64, 128}.
+ *   nseg      >= 1: each (b, h) sequence is cut into nseg consecutive
+ *             segments of L / nseg tokens (L % nseg == 0) that are run
+ *             independently, segment s starting from S0[b, h, s] and
+ *             ending in S_end[b, h, s].  nseg = 1 is the plain call.
+ *   dtype     la_dtype of the token tensors.
+ *   split     internal sub-segments per segment used for parallelism
+ *             (0 = the library's choice).  Any value gives the same result
+ *             up to fp32 rounding; it exists for tuning and testing.
+ *   reserved  must be 0.
+ */
+typedef struct {
+  int64_t B, H, L;
+  int32_t dk, dv;
+  int32_t nseg;
+  int32_t dtype;
+  int32_t split;
+  int32_t reserved;
+} la_shape;
+
+/* Library version (currently 1). */
+int la_version(void);
+
+/* Static string for a status code. */
+const char* la_status_str(la_status status);
+
+/* Message describing the last failed call on this thread ("" if none). */
+const char* la_last_error(void);
+
+/*
+ * Workspace (device memory, 256-byte aligned) that la_chunk_fwd needs for
+ * `shape`, in bytes; 0 means none.  Returns 0 for an invalid shape too (the
+ * call itself then reports the error).
+ */
+size_t la_fwd_workspace_bytes(const la_shape* shape);
+
+/*
+ * Forward pass.
+ *   Q, K [B,H,L,dk], V [B,H,L,dv]     inputs, required (unless B*H*L == 0).
+ *   lambda [H]                         decay per head, required.
+ *   S0 [B,H,nseg,dk,dv] fp32           initial state per segment; NULL = zero.
+ *   O [B,H,L,dv]                       output; NULL = state only (no O).
+ *   S_end [B,H,nseg,dk,dv] fp32        final state per segment; NULL = skip.
+ *   ws, ws_bytes                       workspace of la_fwd_workspace_bytes().
+ * O and S_end must not both be NULL.
+ * Row (b, h, t) of O is o_t of segment s = t / (L/nseg) of sequence (b, h),
+ * computed from S0[b, h, s].
+ */
+la_status la_chunk_fwd(const la_shape* shape, const void* Q, const void* K,
+                       const void* V, const float* lambda, const float* S0,
+                       void* O, float* S_end, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/*
+ * Segment state-combine scan (fp32).  For every (b, h), with
+ * a = lambda[h]^seg_len, X = S0[b, h] (or zero if S0 is NULL):
+ *     for s = 0, 1, ..., P-1   (reverse != 0: s = P-1, ..., 0)
+ *         S_start[b, h, s] = X;   X = a * X + dS[b, h, s]
+ *     S_end[b, h] = X           (if S_end is not NULL)
+ * dS are the per-segment local states (accumulated from zero over seg_len
+ * tokens, e.g. by la_chunk_fwd with nseg = P, S0 = NULL, O = NULL); S_start
+ * are then the initial states that make segmented runs equal one run: the
+ * combine S_end = lambda^seg_len * S_start + dS of the All-Scan of ZeCO and of
+ * the memory-state gather of LASP-2.  The reverse scan is the same combine
+ * for gradient states flowing from the last segment to the first.
+ *   dS [B,H,P,dk,dv]   S_start [B,H,P,dk,dv] (may be the same buffer as dS)
+ *   S0, S_end [B,H,dk,dv]   lambda [H]   seg_len >= 0   P >= 0
+ * lambda^seg_len is evaluated in fp32 as exp2(seg_len * log2(lambda)).
+ */
+la_status la_state_scan(int64_t B, int64_t H, int32_t P, int32_t dk, int32_t dv,
+                        const float* dS, const float* lambda, int64_t seg_len,
+                        const float* S0, float* S_start, float* S_end,
+                        int32_t reverse, void* stream);
+
+/* Workspace bytes la_chunk_bwd needs for `shape` (see la_fwd_workspace_bytes). */
+size_t la_bwd_workspace_bytes(const la_shape* shape);
+
+/*
+ * Backward pass of la_chunk_fwd for the loss
+ *     l = sum_t <dO_t, o_t> + <dS_end, S_end>
+ * (per segment).  Gradients are exact for the recurrence above:
+ *     dq_t = S_t dO_t
+ *     dk_t = G_t v_t,  dv_t = G_t^T k_t,  with G_t = q_t dO_t^T + lambda G_{t+1}
+ *            and lambda G_{L+1} = dS_end
+ *     dS0  = lambda G_1
+ *   Q, K, V, lambda, S0   as for la_chunk_fwd (S0 NULL = zero).
+ *   dO [B,H,L,dv]         upstream gradient of O, required.
+ *   dS_end                upstream gradient of S_end; NULL = zero.
+ *   dQ, dK [B,H,L,dk], dV [B,H,L,dv]   outputs, required, dtype of the inputs.
+ *   dS0 [B,H,nseg,dk,dv] fp32          output; NULL = not returned.
+ *   ws, ws_bytes          workspace of la_bwd_workspace_bytes().
+ * lambda receives no gradient.
+ */
+la_status la_chunk_bwd(const la_shape* shape, const void* Q, const void* K,
+                       const void* V, const float* lambda, const float* S0,
+                       const void* dO, const float* dS_end, void* dQ, void* dK,
+                       void* dV, float* dS0, void* ws, size_t ws_bytes,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINATTN_H */

@@ -1,0 +1,353 @@
+// la_api.cpp -- the C ABI of liblinattn.so (declared in include/linattn.h).
+//
+// Host-side only: argument validation (pure host code, before any HIP call),
+// the launch plan and the sequence of kernel launches on the caller's stream.
+// The library allocates no memory and keeps no device state.
+//
+// Launch plan.  A sequence (one segment of one (b, h)) has a carried state, so
+// one workgroup walks its chunks in order.  When there are fewer sequences
+// than the chip has compute units, each is cut into `split` sub-segments and
+// the dependency between them is resolved the way the sequence-parallel
+// schemes of the pages resolve it between ranks (ZeCO abstract: every rank
+// needs precisely its initial operator state; LASP-2 abstract: one exchange of
+// length-independent memory states):
+//   1. local state of every sub-segment but the last, from a zero state
+//      (state-only chunk kernel);
+//   2. inclusive scan X <- lambda^Lp X + dS over those local states, seeded
+//      with S0, giving the start state of sub-segments 1..split-1;
+//   3. the full chunk kernel over all sub-segments, each from its start state.
+// Step 1 re-reads K and V for (split-1)/split of the tokens: that is the price
+// of the parallelism, traded against running 32 heads on 256 compute units.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "la_internal.h"
+#include "linattn.h"
+
+namespace {
+
+constexpr int kChunk = 64;
+// Workgroups the plan aims for: one per compute unit of an MI355X.
+constexpr int64_t kTargetWG = 256;
+
+thread_local std::string g_last_error;
+
+la_status fail(la_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = std::string(la_status_str(st)) + ": " + buf;
+  return st;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Plan {
+  int64_t nseq = 0;  // B * H * nseg independent sequences
+  int64_t Ls = 0;    // tokens per sequence
+  int split = 1;     // sub-segments per sequence
+  int64_t Lp = kChunk;  // tokens per sub-segment (multiple of 64; the last is shorter)
+  int D = 0;
+};
+
+// Shape checks shared by forward and backward.  No HIP call.
+la_status check_shape(const la_shape* s, Plan* plan) {
+  if (!s) return fail(LA_ERR_INVALID_ARG, "shape is NULL");
+  if (s->B < 0 || s->H < 0 || s->L < 0)
+    return fail(LA_ERR_INVALID_ARG, "negative size (B=%lld H=%lld L=%lld)", (long long)s->B,
+                (long long)s->H, (long long)s->L);
+  if (s->dk <= 0 || s->dv <= 0) return fail(LA_ERR_INVALID_ARG, "dk and dv must be positive");
+  if (s->nseg < 1) return fail(LA_ERR_INVALID_ARG, "nseg must be >= 1");
+  if (s->L % s->nseg != 0)
+    return fail(LA_ERR_INVALID_ARG, "L=%lld is not a multiple of nseg=%d", (long long)s->L, s->nseg);
+  if (s->dtype != LA_BF16 && s->dtype != LA_FP32)
+    return fail(LA_ERR_INVALID_ARG, "unknown dtype %d", s->dtype);
+  if (s->split < 0) return fail(LA_ERR_INVALID_ARG, "split must be >= 0");
+  if (s->reserved != 0) return fail(LA_ERR_INVALID_ARG, "reserved must be 0");
+  if (s->dk != s->dv) return fail(LA_ERR_UNSUPPORTED, "dk != dv (%d, %d)", s->dk, s->dv);
+  if (s->dk != 64 && s->dk != 128) return fail(LA_ERR_UNSUPPORTED, "d=%d not in {64, 128}", s->dk);
+  // sizes must stay far from int64 overflow in element offsets
+  const double elems = (double)s->B * (double)s->H * (double)s->L * (double)s->dk;
+  const double states = (double)s->B * (double)s->H * (double)s->nseg * s->dk * s->dv;
+  if (elems > 4.0e18 || states > 4.0e18) return fail(LA_ERR_INVALID_ARG, "tensor too large");
+  if ((double)s->B * s->H * s->nseg > 2.0e9) return fail(LA_ERR_INVALID_ARG, "too many sequences");
+
+  plan->nseq = s->B * s->H * (int64_t)s->nseg;
+  plan->Ls = s->L / s->nseg;
+  plan->D = s->dk;
+  const int64_t nchunks = (plan->Ls + kChunk - 1) / kChunk;
+  int64_t want = s->split > 0 ? s->split
+                              : (plan->nseq > 0 ? (kTargetWG + plan->nseq - 1) / plan->nseq : 1);
+  if (want > nchunks) want = nchunks;
+  if (want < 1) want = 1;
+  const int64_t cps = nchunks > 0 ? (nchunks + want - 1) / want : 1;  // chunks per sub-segment
+  plan->Lp = cps * kChunk;
+  plan->split = nchunks > 0 ? (int)((nchunks + cps - 1) / cps) : 1;
+  if (plan->nseq * plan->split > 2000000000LL)
+    return fail(LA_ERR_INVALID_ARG, "too many workgroups");
+  return LA_OK;
+}
+
+size_t scan_ws_bytes(const Plan& p) {
+  return (size_t)p.nseq * (size_t)(p.split - 1) * (size_t)p.D * (size_t)p.D * sizeof(float);
+}
+
+la_status hip_fail(hipError_t e, const char* what) {
+  return fail(LA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// One forward recurrence over nseq sequences (optionally in reverse time):
+// pre-pass + scan when split > 1, then the main pass.  `start` [nseq][D][D]
+// may be null (zero).  O may be null (state only); Send may be null.
+la_status run_flow(const Plan& pl, int dtype, int H, int nseg, const void* Q, const void* K,
+                   const void* V, const float* lam, const float* start, void* O, float* Send,
+                   float* W, int reverse, hipStream_t st) {
+  if (pl.nseq == 0 || (!O && !Send)) return LA_OK;
+  la::FwdArgs fa;
+  std::memset(&fa, 0, sizeof(fa));
+  fa.Q = Q;
+  fa.K = K;
+  fa.V = V;
+  fa.lam = lam;
+  fa.H = H;
+  fa.nseg = nseg;
+  fa.Ls = pl.Ls;
+  fa.Lp = pl.Lp;
+  fa.split = pl.split;
+  fa.reverse = reverse;
+  hipError_t e;
+  if (pl.split > 1) {
+    la::FwdArgs pa = fa;
+    pa.p_begin = 0;
+    pa.p_count = pl.split - 1;
+    pa.start_from_state = 0;
+    pa.Sout = W;
+    pa.sout_p0 = 0;
+    pa.sout_np = pl.split - 1;
+    e = la::launch_fwd(pa, dtype, pl.D, false, pl.nseq * (pl.split - 1), st);
+    if (e != hipSuccess) return hip_fail(e, "state pre-pass launch");
+    la::ScanArgs sa;
+    std::memset(&sa, 0, sizeof(sa));
+    sa.nseq = pl.nseq;
+    sa.P = pl.split - 1;
+    sa.E = (int64_t)pl.D * pl.D;
+    sa.dS = W;
+    sa.lam = lam;
+    sa.H = H;
+    sa.hdiv = nseg;
+    sa.seg_len = pl.Lp;
+    sa.S0 = start;
+    sa.Sout = W;
+    sa.Send = nullptr;
+    sa.reverse = 0;
+    sa.inclusive = 1;
+    e = la::launch_scan(sa, st);
+    if (e != hipSuccess) return hip_fail(e, "state scan launch");
+  }
+  la::FwdArgs ma = fa;
+  ma.start_from_state = 1;
+  ma.S0 = start;
+  ma.Sws = W;
+  ma.O = O;
+  ma.Sout = Send;
+  ma.sout_p0 = pl.split - 1;
+  ma.sout_np = 1;
+  if (O) {
+    ma.p_begin = 0;
+    ma.p_count = pl.split;
+  } else {
+    ma.p_begin = pl.split - 1;
+    ma.p_count = 1;
+  }
+  e = la::launch_fwd(ma, dtype, pl.D, O != nullptr, pl.nseq * ma.p_count, st);
+  if (e != hipSuccess) return hip_fail(e, "chunk kernel launch");
+  return LA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int la_version(void) { return 1; }
+
+const char* la_status_str(la_status s) {
+  switch (s) {
+    case LA_OK: return "LA_OK";
+    case LA_ERR_INVALID_ARG: return "LA_ERR_INVALID_ARG";
+    case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED";
+    case LA_ERR_WORKSPACE: return "LA_ERR_WORKSPACE";
+    case LA_ERR_HIP: return "LA_ERR_HIP";
+  }
+  return "LA_ERR_UNKNOWN";
+}
+
+const char* la_last_error(void) { return g_last_error.c_str(); }
+
+size_t la_fwd_workspace_bytes(const la_shape* shape) {
+  Plan pl;
+  std::string keep = g_last_error;
+  if (check_shape(shape, &pl) != LA_OK) {
+    g_last_error = keep;
+    return 0;
+  }
+  return scan_ws_bytes(pl);
+}
+
+size_t la_bwd_workspace_bytes(const la_shape* shape) {
+  Plan pl;
+  std::string keep = g_last_error;
+  if (check_shape(shape, &pl) != LA_OK) {
+    g_last_error = keep;
+    return 0;
+  }
+  // one prepared start state per sequence + the scan states of one pass
+  return (size_t)pl.nseq * pl.D * pl.D * sizeof(float) + scan_ws_bytes(pl);
+}
+
+la_status la_chunk_fwd(const la_shape* s, const void* Q, const void* K, const void* V,
+                       const float* lambda, const float* S0, void* O, float* S_end, void* ws,
+                       size_t ws_bytes, void* stream) {
+  Plan pl;
+  la_status r = check_shape(s, &pl);
+  if (r != LA_OK) return r;
+  const bool has_tokens = pl.nseq > 0 && pl.Ls > 0;
+  if (has_tokens && (!Q || !K || !V)) return fail(LA_ERR_INVALID_ARG, "Q, K and V are required");
+  if (pl.nseq > 0 && !lambda) return fail(LA_ERR_INVALID_ARG, "lambda is required");
+  if (!O && !S_end) return fail(LA_ERR_INVALID_ARG, "O and S_end are both NULL");
+  const void* ptrs[] = {Q, K, V, lambda, S0, O, S_end, ws};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(LA_ERR_INVALID_ARG, "pointer %p is not 16-byte aligned", p);
+  const size_t need = scan_ws_bytes(pl);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                ws ? ws_bytes : (size_t)0);
+  if (pl.nseq == 0) return LA_OK;
+  return run_flow(pl, s->dtype, (int)s->H, s->nseg, Q, K, V, lambda, S0, O, S_end,
+                  static_cast<float*>(ws), 0, static_cast<hipStream_t>(stream));
+}
+
+la_status la_state_scan(int64_t B, int64_t H, int32_t P, int32_t dk, int32_t dv, const float* dS,
+                        const float* lambda, int64_t seg_len, const float* S0, float* S_start,
+                        float* S_end, int32_t reverse, void* stream) {
+  if (B < 0 || H < 0 || P < 0 || seg_len < 0)
+    return fail(LA_ERR_INVALID_ARG, "negative size or length");
+  if (dk <= 0 || dv <= 0) return fail(LA_ERR_INVALID_ARG, "dk and dv must be positive");
+  if ((double)B * H * ((double)P + 1) * dk * dv > 4.0e18)
+    return fail(LA_ERR_INVALID_ARG, "tensor too large");
+  const int64_t nseq = B * H;
+  if (nseq > 0 && !lambda) return fail(LA_ERR_INVALID_ARG, "lambda is required");
+  if (nseq > 0 && P > 0 && (!dS || !S_start))
+    return fail(LA_ERR_INVALID_ARG, "dS and S_start are required");
+  const void* ptrs[] = {dS, lambda, S0, S_start, S_end};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(LA_ERR_INVALID_ARG, "pointer %p is not 16-byte aligned", p);
+  if (nseq == 0) return LA_OK;
+  la::ScanArgs sa;
+  std::memset(&sa, 0, sizeof(sa));
+  sa.nseq = nseq;
+  sa.P = P;
+  sa.E = (int64_t)dk * dv;
+  sa.dS = dS;
+  sa.lam = lambda;
+  sa.H = (int)H;
+  sa.hdiv = 1;
+  sa.seg_len = seg_len;
+  sa.S0 = S0;
+  sa.Sout = S_start;
+  sa.Send = S_end;
+  sa.reverse = reverse != 0;
+  sa.inclusive = 0;
+  if (P == 0 && !S_end) return LA_OK;  // nothing to write
+  hipError_t e = la::launch_scan(sa, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "state scan launch");
+  return LA_OK;
+}
+
+la_status la_chunk_bwd(const la_shape* s, const void* Q, const void* K, const void* V,
+                       const float* lambda, const float* S0, const void* dO, const float* dS_end,
+                       void* dQ, void* dK, void* dV, float* dS0, void* ws, size_t ws_bytes,
+                       void* stream) {
+  Plan pl;
+  la_status r = check_shape(s, &pl);
+  if (r != LA_OK) return r;
+  const bool has_tokens = pl.nseq > 0 && pl.Ls > 0;
+  if (has_tokens && (!Q || !K || !V || !dO || !dQ || !dK || !dV))
+    return fail(LA_ERR_INVALID_ARG, "Q, K, V, dO, dQ, dK and dV are required");
+  if (pl.nseq > 0 && !lambda) return fail(LA_ERR_INVALID_ARG, "lambda is required");
+  const void* ptrs[] = {Q, K, V, lambda, S0, dO, dS_end, dQ, dK, dV, dS0, ws};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(LA_ERR_INVALID_ARG, "pointer %p is not 16-byte aligned", p);
+  const size_t need = (size_t)pl.nseq * pl.D * pl.D * sizeof(float) + scan_ws_bytes(pl);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                ws ? ws_bytes : (size_t)0);
+  if (pl.nseq == 0) return LA_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float* A = static_cast<float*>(ws);          // prepared start state
+  float* W = A + (size_t)pl.nseq * pl.D * pl.D;  // scan states
+  const int H = (int)s->H;
+  la::PrepArgs pa;
+  std::memset(&pa, 0, sizeof(pa));
+  pa.nseq = pl.nseq;
+  pa.D = pl.D;
+  pa.lam = lambda;
+  pa.H = H;
+  pa.hdiv = s->nseg;
+  hipError_t e;
+
+  // dq_t = S_t dO_t: the forward recurrence of S^T = sum v k^T read by dO,
+  // started from S0^T.
+  const float* start = nullptr;
+  if (S0) {
+    pa.src = S0;
+    pa.dst = A;
+    pa.transpose = 1;
+    pa.mode = 0;
+    if ((e = la::launch_prep(pa, st)) != hipSuccess) return hip_fail(e, "prep launch");
+    start = A;
+  }
+  r = run_flow(pl, s->dtype, H, s->nseg, dO, V, K, lambda, start, dQ, nullptr, W, 0, st);
+  if (r != LA_OK) return r;
+
+  // dv_t = G_t^T k_t: in reverse time G accumulates q dO^T like a state,
+  // started from dS_end / lambda; its final value G_1 gives dS0 = lambda G_1.
+  start = nullptr;
+  if (dS_end) {
+    pa.src = dS_end;
+    pa.dst = A;
+    pa.transpose = 0;
+    pa.mode = 2;
+    if ((e = la::launch_prep(pa, st)) != hipSuccess) return hip_fail(e, "prep launch");
+    start = A;
+  }
+  r = run_flow(pl, s->dtype, H, s->nseg, K, Q, dO, lambda, start, dV, dS0, W, 1, st);
+  if (r != LA_OK) return r;
+  if (dS0) {
+    pa.src = dS0;
+    pa.dst = dS0;
+    pa.transpose = 0;
+    pa.mode = 1;
+    if ((e = la::launch_prep(pa, st)) != hipSuccess) return hip_fail(e, "prep launch");
+  }
+
+  // dk_t = G_t v_t: the same reverse recurrence for G^T = sum dO q^T.
+  start = nullptr;
+  if (dS_end) {
+    pa.src = dS_end;
+    pa.dst = A;
+    pa.transpose = 1;
+    pa.mode = 2;
+    if ((e = la::launch_prep(pa, st)) != hipSuccess) return hip_fail(e, "prep launch");
+    start = A;
+  }
+  r = run_flow(pl, s->dtype, H, s->nseg, V, dO, Q, lambda, start, dK, nullptr, W, 1, st);
+  return r;
+}
+
+}  // extern "C"

@@ -1,0 +1,78 @@
+// la_internal.h -- host-side interface between the C ABI layer (la_api.cpp)
+// and the kernel launchers (la_fwd.hip, la_bwd.hip, la_scan.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+// One launch of the chunk kernel over sub-segments [p_begin, p_begin+p_count)
+// of every one of nseq sequences.  Sequence n occupies token rows
+// [n*Ls, (n+1)*Ls) of the flattened [nseq*Ls, D] token tensors; its head is
+// (n / nseg) % H.  Sub-segment p covers tokens [p*Lp, min(Ls, (p+1)*Lp)).
+struct FwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const float* lam;
+  int H;
+  int nseg;
+  int64_t Ls;
+  int64_t Lp;
+  int split;
+  int p_begin;
+  int p_count;
+  // start state: 0 = zero; 1 = S0[n] (zero if S0 is null) for p == 0 and
+  // Sws[n][p-1] for p > 0
+  int start_from_state;
+  const float* S0;   // [nseq][D][D]
+  const float* Sws;  // [nseq][split-1][D][D]
+  void* O;           // [nseq*Ls][D], null in state-only launches
+  // the final state of sub-segment p is written to Sout[n][p - sout_p0] when
+  // p is in [sout_p0, sout_p0 + sout_np)
+  float* Sout;
+  int sout_p0;
+  int sout_np;
+  // reverse time order (token t of a sequence is read as token Ls-1-t); used
+  // by the backward's reverse sweeps
+  int reverse;
+};
+
+// dst[n] = f(src[n]) for nseq D x D fp32 states: optional transpose, then a
+// per-head factor (mode 0: none, 1: * lambda_h, 2: / lambda_h).
+struct PrepArgs {
+  int64_t nseq;
+  int D;
+  const float* src;
+  float* dst;
+  const float* lam;
+  int H;
+  int hdiv;
+  int transpose;
+  int mode;
+};
+
+// Segment scan over nseq sequences of P states of E floats each.
+struct ScanArgs {
+  int64_t nseq;
+  int P;
+  int64_t E;
+  const float* dS;   // [nseq][P][E]
+  const float* lam;  // [H]; head of sequence n is (n / hdiv) % H
+  int H;
+  int hdiv;
+  int64_t seg_len;
+  const float* S0;   // [nseq][E] or null
+  float* Sout;       // [nseq][P][E], may alias dS
+  float* Send;       // [nseq][E] or null
+  int reverse;
+  int inclusive;     // 0: Sout[s] = state before adding dS[s]; 1: after
+};
+
+hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, bool with_o, int64_t nwg,
+                      hipStream_t stream);
+hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
+hipError_t launch_prep(const PrepArgs& a, hipStream_t stream);
+
+}  // namespace la

@@ -1,0 +1,194 @@
+"""ctypes binding of liblinattn.so (C ABI in ``include/linattn.h``).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of the library.  PyTorch provides device memory (outputs and the
+workspace are torch allocations) and the stream (the current torch stream).
+There is no fallback: if the library is missing or cannot be loaded, every
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblinattn.so")
+
+LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_HIP = range(5)
+LA_BF16, LA_FP32 = 0, 1
+
+EXPORTS = ("la_version", "la_status_str", "la_last_error", "la_fwd_workspace_bytes",
+           "la_chunk_fwd", "la_state_scan", "la_bwd_workspace_bytes", "la_chunk_bwd")
+
+
+class LinAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class la_shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("L", ctypes.c_int64),
+                ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("nseg", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("split", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m long_sequence_causal_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
+    sp = ctypes.POINTER(la_shape)
+    L.la_version.restype = ctypes.c_int
+    L.la_version.argtypes = []
+    L.la_status_str.restype = ctypes.c_char_p
+    L.la_status_str.argtypes = [ctypes.c_int]
+    L.la_last_error.restype = ctypes.c_char_p
+    L.la_last_error.argtypes = []
+    L.la_fwd_workspace_bytes.restype = sz
+    L.la_fwd_workspace_bytes.argtypes = [sp]
+    L.la_bwd_workspace_bytes.restype = sz
+    L.la_bwd_workspace_bytes.argtypes = [sp]
+    L.la_chunk_fwd.restype = ctypes.c_int
+    L.la_chunk_fwd.argtypes = [sp] + [vp] * 8 + [sz, vp]
+    L.la_state_scan.restype = ctypes.c_int
+    L.la_state_scan.argtypes = [i64, i64, i32, i32, i32, vp, vp, i64, vp, vp, vp, i32, vp]
+    L.la_chunk_bwd.restype = ctypes.c_int
+    L.la_chunk_bwd.argtypes = [sp] + [vp] * 12 + [sz, vp]
+    _lib = L
+    return L
+
+
+def _check(status: int):
+    if status != LA_OK:
+        L = lib()
+        msg = L.la_last_error().decode()
+        raise LinAttnError(status, msg or L.la_status_str(status).decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return LA_BF16
+    if dt == torch.float32:
+        return LA_FP32
+    raise TypeError(f"unsupported token dtype {dt}")
+
+
+def _need(t, name, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def make_shape(B, H, L, dk, dv, nseg=1, dtype=LA_BF16, split=0) -> la_shape:
+    return la_shape(int(B), int(H), int(L), int(dk), int(dv), int(nseg), int(dtype),
+                    int(split), 0)
+
+
+def la_fwd_workspace_bytes(shape: la_shape) -> int:
+    return int(lib().la_fwd_workspace_bytes(ctypes.byref(shape)))
+
+
+def la_bwd_workspace_bytes(shape: la_shape) -> int:
+    return int(lib().la_bwd_workspace_bytes(ctypes.byref(shape)))
+
+
+def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def la_chunk_fwd(q, k, v, lam, S0=None, nseg: int = 1, need_O: bool = True,
+                 need_S_end: bool = True, split: int = 0, out=None, S_end_out=None,
+                 workspace=None):
+    """Forward pass.  q, k [B,H,L,dk], v [B,H,L,dv] (bf16 or fp32), lam [H] fp32,
+    S0 [B,H,nseg,dk,dv] fp32 or None.  Returns (O or None, S_end or None)."""
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q.dtype)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype)
+    _need(lam, "lam", torch.float32)
+    _need(S0, "S0", torch.float32)
+    shape = make_shape(B, H, L, dk, dv, nseg, dt, split)
+    O = None
+    if need_O:
+        O = out if out is not None else torch.empty((B, H, L, dv), dtype=q.dtype, device=q.device)
+    S_end = None
+    if need_S_end:
+        S_end = S_end_out if S_end_out is not None else torch.empty(
+            (B, H, nseg, dk, dv), dtype=torch.float32, device=q.device)
+    nbytes = la_fwd_workspace_bytes(shape)
+    ws = workspace if workspace is not None else _workspace(nbytes, q.device)
+    _check(lib().la_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(lam),
+                              _ptr(S0), _ptr(O), _ptr(S_end), _ptr(ws),
+                              ws.numel() if ws is not None else 0, _stream()))
+    return O, S_end
+
+
+def la_state_scan(dS, lam, seg_len: int, S0=None, reverse: bool = False, out=None,
+                  need_S_end: bool = True):
+    """Segment scan.  dS [B,H,P,dk,dv] fp32, lam [H], S0 [B,H,dk,dv] or None.
+    Returns (S_start [B,H,P,dk,dv], S_end [B,H,dk,dv] or None); ``out`` may be dS."""
+    B, H, P, dk, dv = dS.shape
+    _need(dS, "dS", torch.float32)
+    _need(lam, "lam", torch.float32)
+    _need(S0, "S0", torch.float32)
+    S_start = out if out is not None else torch.empty_like(dS)
+    S_end = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dS.device) if need_S_end else None
+    _check(lib().la_state_scan(B, H, P, dk, dv, _ptr(dS), _ptr(lam), int(seg_len), _ptr(S0),
+                               _ptr(S_start), _ptr(S_end), int(bool(reverse)), _stream()))
+    return S_start, S_end
+
+
+def la_chunk_bwd(q, k, v, lam, dO, S0=None, dS_end=None, nseg: int = 1,
+                 need_dS0: bool = True, split: int = 0, workspace=None):
+    """Backward pass.  Returns (dQ, dK, dV, dS0 or None)."""
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q.dtype)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (dO, "dO")):
+        _need(t, n, q.dtype)
+    _need(lam, "lam", torch.float32)
+    _need(S0, "S0", torch.float32)
+    _need(dS_end, "dS_end", torch.float32)
+    shape = make_shape(B, H, L, dk, dv, nseg, dt, split)
+    dQ = torch.empty_like(q)
+    dK = torch.empty_like(k)
+    dV = torch.empty_like(v)
+    dS0 = torch.empty((B, H, nseg, dk, dv), dtype=torch.float32, device=q.device) if need_dS0 else None
+    nbytes = la_bwd_workspace_bytes(shape)
+    ws = workspace if workspace is not None else _workspace(nbytes, q.device)
+    _check(lib().la_chunk_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(lam),
+                              _ptr(S0), _ptr(dO), _ptr(dS_end), _ptr(dQ), _ptr(dK), _ptr(dV),
+                              _ptr(dS0), _ptr(ws), ws.numel() if ws is not None else 0,
+                              _stream()))
+    return dQ, dK, dV, dS0

@@ -44,6 +44,7 @@
  * over dk for dv_t) is summed in plain index order by one thread.
  */
 #include <math.h>
+#include <omp.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -352,3 +353,14 @@ int lao_scan(int64_t B, int64_t H, int64_t P, int64_t dk, int64_t dv,
 }
 
 int lao_abi_version(void) { return 1; }
+
+/* Number of OpenMP threads the oracle's parallel loops use. */
+int lao_threads(void) {
+  int n = 1;
+#pragma omp parallel
+  {
+#pragma omp single
+    n = omp_get_num_threads();
+  }
+  return n;
+}

@@ -55,7 +55,14 @@ def bind(lib):
     lib.lao_bwd.restype = ctypes.c_int
     lib.lao_scan.argtypes = [i64] * 5 + [dp, dp, i64, dp, dp, dp, ctypes.c_int]
     lib.lao_scan.restype = ctypes.c_int
+    lib.lao_threads.restype = ctypes.c_int
+    lib.lao_threads.argtypes = []
     return lib
+
+
+def threads() -> int:
+    """OpenMP threads the oracle runs on."""
+    return int(_load().lao_threads())
 
 
 def _f64(x):

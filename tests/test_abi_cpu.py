@@ -1,0 +1,168 @@
+"""The C ABI on the CPU: the library loads, exports every entry point the
+header declares, and rejects bad arguments on the host before any HIP call
+(so these run without a GPU).  No compute call is made here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_sequence_causal_amd import linattn as la
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "linattn.h")
+
+FAKE = 0x100000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(la_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("la_chunk_fwd", "la_state_scan", "la_chunk_bwd",
+                     "la_fwd_workspace_bytes", "la_bwd_workspace_bytes", "la_status_str"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = la.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), f"{name} declared in linattn.h but not exported"
+    assert set(la.EXPORTS) == set(declared_functions())
+
+
+def test_version_and_status_strings():
+    L = la.lib()
+    assert L.la_version() == 1
+    for code, name in enumerate(["LA_OK", "LA_ERR_INVALID_ARG", "LA_ERR_UNSUPPORTED",
+                                 "LA_ERR_WORKSPACE", "LA_ERR_HIP"]):
+        assert L.la_status_str(code).decode() == name
+
+
+def _fwd(shape, Q=FAKE, K=FAKE, V=FAKE, lam=FAKE, S0=None, O=FAKE, S_end=None,
+         ws=None, ws_bytes=0):
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    return la.lib().la_chunk_fwd(ctypes.byref(shape), v(Q), v(K), v(V), v(lam), v(S0), v(O),
+                                 v(S_end), v(ws), ws_bytes, None)
+
+
+def _shape(**kw):
+    base = dict(B=1, H=2, L=128, dk=64, dv=64, nseg=1, dtype=la.LA_BF16, split=1)
+    base.update(kw)
+    return la.make_shape(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), la.LA_ERR_INVALID_ARG),
+    (dict(L=-5), la.LA_ERR_INVALID_ARG),
+    (dict(nseg=0), la.LA_ERR_INVALID_ARG),
+    (dict(L=100, nseg=3), la.LA_ERR_INVALID_ARG),
+    (dict(dtype=7), la.LA_ERR_INVALID_ARG),
+    (dict(split=-1), la.LA_ERR_INVALID_ARG),
+    (dict(dk=0), la.LA_ERR_INVALID_ARG),
+    (dict(dk=64, dv=128), la.LA_ERR_UNSUPPORTED),
+    (dict(dk=96, dv=96), la.LA_ERR_UNSUPPORTED),
+    (dict(dk=256, dv=256), la.LA_ERR_UNSUPPORTED),
+])
+def test_fwd_rejects_bad_shapes(kw, code):
+    assert _fwd(_shape(**kw)) == code
+    assert la.lib().la_last_error().decode().startswith(la.lib().la_status_str(code).decode())
+
+
+def test_fwd_rejects_reserved_field():
+    s = _shape()
+    s.reserved = 1
+    assert _fwd(s) == la.LA_ERR_INVALID_ARG
+
+
+def test_fwd_rejects_null_and_misaligned_pointers():
+    s = _shape()
+    assert _fwd(s, Q=None) == la.LA_ERR_INVALID_ARG
+    assert _fwd(s, V=None) == la.LA_ERR_INVALID_ARG
+    assert _fwd(s, lam=None) == la.LA_ERR_INVALID_ARG
+    assert _fwd(s, O=None, S_end=None) == la.LA_ERR_INVALID_ARG
+    assert _fwd(s, K=FAKE + 8) == la.LA_ERR_INVALID_ARG
+    assert _fwd(s, S0=FAKE + 4) == la.LA_ERR_INVALID_ARG
+
+
+def test_fwd_workspace_rules():
+    s = _shape(L=512, split=4)
+    need = la.la_fwd_workspace_bytes(s)
+    # B*H = 2 sequences, 4 sub-segments of 2 chunks: 3 scanned 64x64 fp32 states each
+    assert need == 2 * 3 * 64 * 64 * 4
+    assert _fwd(s, ws=None, ws_bytes=0) == la.LA_ERR_WORKSPACE
+    assert _fwd(s, ws=FAKE, ws_bytes=need - 1) == la.LA_ERR_WORKSPACE
+    assert la.la_fwd_workspace_bytes(_shape(split=1)) == 0
+
+
+def test_workspace_bytes_of_invalid_shape_is_zero():
+    assert la.la_fwd_workspace_bytes(_shape(dk=96, dv=96)) == 0
+    assert la.la_bwd_workspace_bytes(_shape(nseg=0)) == 0
+
+
+def test_plan_split_normalisation():
+    # 128 tokens = 2 chunks: asking for more sub-segments than chunks gives 2
+    s = _shape(L=128, split=16)
+    assert la.la_fwd_workspace_bytes(s) == 2 * 1 * 64 * 64 * 4
+    # 10 chunks in 3 sub-segments of 4, 4, 2 chunks
+    s = _shape(L=640, split=3, B=1, H=1)
+    assert la.la_fwd_workspace_bytes(s) == 1 * 2 * 64 * 64 * 4
+    # automatic choice: 256 workgroups over B*H*nseg sequences
+    s = la.make_shape(1, 32, 65536, 128, 128, 1, la.LA_BF16, 0)
+    assert la.la_fwd_workspace_bytes(s) == 32 * 7 * 128 * 128 * 4
+
+
+def test_scan_rejects_bad_arguments():
+    L = la.lib()
+    v = ctypes.c_void_p
+    assert L.la_state_scan(-1, 1, 1, 4, 4, v(FAKE), v(FAKE), 1, None, v(FAKE), None, 0, None) == la.LA_ERR_INVALID_ARG
+    assert L.la_state_scan(1, 1, -2, 4, 4, v(FAKE), v(FAKE), 1, None, v(FAKE), None, 0, None) == la.LA_ERR_INVALID_ARG
+    assert L.la_state_scan(1, 1, 2, 0, 4, v(FAKE), v(FAKE), 1, None, v(FAKE), None, 0, None) == la.LA_ERR_INVALID_ARG
+    assert L.la_state_scan(1, 1, 2, 4, 4, None, v(FAKE), 1, None, v(FAKE), None, 0, None) == la.LA_ERR_INVALID_ARG
+    assert L.la_state_scan(1, 1, 2, 4, 4, v(FAKE), None, 1, None, v(FAKE), None, 0, None) == la.LA_ERR_INVALID_ARG
+    assert L.la_state_scan(1, 1, 2, 4, 4, v(FAKE), v(FAKE), -1, None, v(FAKE), None, 0, None) == la.LA_ERR_INVALID_ARG
+    assert L.la_state_scan(1, 1, 2, 4, 4, v(FAKE + 4), v(FAKE), 1, None, v(FAKE), None, 0, None) == la.LA_ERR_INVALID_ARG
+    # nothing to do: no sequences
+    assert L.la_state_scan(0, 3, 2, 4, 4, None, None, 1, None, None, None, 0, None) == la.LA_OK
+
+
+def test_bwd_rejects_bad_arguments():
+    L = la.lib()
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    s = _shape()
+
+    def call(**kw):
+        a = dict(Q=FAKE, K=FAKE, V=FAKE, lam=FAKE, S0=None, dO=FAKE, dSe=None, dQ=FAKE,
+                 dK=FAKE, dV=FAKE, dS0=None, ws=None, nb=0)
+        a.update(kw)
+        return L.la_chunk_bwd(ctypes.byref(s), v(a["Q"]), v(a["K"]), v(a["V"]), v(a["lam"]),
+                              v(a["S0"]), v(a["dO"]), v(a["dSe"]), v(a["dQ"]), v(a["dK"]),
+                              v(a["dV"]), v(a["dS0"]), v(a["ws"]), a["nb"], None)
+
+    assert call(dO=None) == la.LA_ERR_INVALID_ARG
+    assert call(dK=None) == la.LA_ERR_INVALID_ARG
+    assert call(dS0=FAKE + 2) == la.LA_ERR_INVALID_ARG
+    need = la.la_bwd_workspace_bytes(s)
+    assert need == 2 * 64 * 64 * 4
+    assert call(ws=None) == la.LA_ERR_WORKSPACE
+    assert call(ws=FAKE, nb=need - 16) == la.LA_ERR_WORKSPACE
+
+
+def test_empty_problem_is_a_no_op():
+    # B*H = 0: nothing to read or write, no HIP call needed
+    assert _fwd(_shape(B=0), Q=None, K=None, V=None, lam=None) == la.LA_OK
+
+
+def test_product_path_has_no_oracle_dependency():
+    """The library and its binding never reference the CPU oracle."""
+    pkg = os.path.join(ROOT, "long_sequence_causal_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
+                assert "liblao" not in text and "lao_" not in text and "lao.c" not in text, f

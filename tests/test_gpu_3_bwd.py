@@ -1,0 +1,89 @@
+"""Backward parity of la_chunk_bwd (through the C ABI) against the CPU
+oracle's backward, on seeded inputs spanning several chunks, ragged tails,
+segments and internal splits.  Needs a gfx950 GPU."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import TOL, f64, log, rel_err, require_gpu
+from long_sequence_causal_amd import linattn as la
+from long_sequence_causal_amd.inputs import decay_schedule, make_inputs
+from oracle import lao
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _fast_lam(H):
+    return torch.tensor([0.5 + 0.5 * h / max(H - 1, 1) for h in range(H)], dtype=torch.float32)
+
+
+CASES = [
+    # dtype, D, B, H, L, nseg, split, S0 std, dS_end std, fast decay
+    ("bf16", 128, 1, 3, 337, 1, 0, 0.5, 0.5, False),
+    ("bf16", 128, 2, 2, 64 * 8, 1, 3, 0.0, 0.0, True),
+    ("bf16", 64, 1, 2, 64 * 5 + 30, 1, 2, 0.5, 1.0, True),
+    ("bf16", 128, 1, 2, 64 * 6, 3, 2, 0.5, 0.5, False),
+    ("fp32", 64, 1, 2, 1024, 1, 0, 0.0, 0.0, False),
+    ("fp32", 64, 2, 2, 130 * 2, 2, 2, 0.5, 0.5, True),
+    ("fp32", 128, 1, 1, 70, 1, 0, 0.5, 0.5, True),
+]
+
+
+@pytest.mark.parametrize("dtype,D,B,H,L,nseg,split,s0,dse,fast", CASES)
+def test_bwd_matches_oracle(dtype, D, B, H, L, nseg, split, s0, dse, fast):
+    log(f"bwd case dtype={dtype} D={D} B={B} H={H} L={L} nseg={nseg} split={split} s0={s0} dSe={dse}")
+    inp = make_inputs(B, H, L, D, D, dtype=dtype, s0_std=s0, nseg=nseg, need_dO=True,
+                      dS_end_std=dse, seed=2000 + L, device="cuda",
+                      lam=_fast_lam(H) if fast else None)
+    q, k, v, lam, S0, dO, dSe = (inp[x] for x in ("q", "k", "v", "lam", "S0", "dO", "dS_end"))
+    dQ, dK, dV, dS0 = la.la_chunk_bwd(q, k, v, lam, dO, S0=S0, dS_end=dSe, nseg=nseg, split=split)
+    torch.cuda.synchronize()
+    ref = lao.bwd(f64(q), f64(k), f64(v), f64(lam), f64(dO), S0=f64(S0), dS_end=f64(dSe), nseg=nseg)
+    errs = [rel_err(f64(x), r) for x, r in zip((dQ, dK, dV, dS0), ref)]
+    log("  err dQ={:.3e} dK={:.3e} dV={:.3e} dS0={:.3e}".format(*errs))
+    assert max(errs) <= TOL[dtype]
+
+
+def test_bwd_without_dS0():
+    inp = make_inputs(1, 2, 64 * 3, 64, 64, need_dO=True, seed=31, device="cuda")
+    dQ, dK, dV, dS0 = la.la_chunk_bwd(inp["q"], inp["k"], inp["v"], inp["lam"], inp["dO"],
+                                      need_dS0=False)
+    ref = lao.bwd(f64(inp["q"]), f64(inp["k"]), f64(inp["v"]), f64(inp["lam"]), f64(inp["dO"]))
+    assert dS0 is None
+    for x, r in zip((dQ, dK, dV), ref[:3]):
+        assert rel_err(f64(x), r) <= TOL["bf16"]
+
+
+def test_bwd_deterministic_bitwise():
+    inp = make_inputs(1, 2, 64 * 9 + 3, 128, 128, need_dO=True, s0_std=0.1, seed=32, device="cuda")
+    a = la.la_chunk_bwd(inp["q"], inp["k"], inp["v"], inp["lam"], inp["dO"], S0=inp["S0"], split=3)
+    b = la.la_chunk_bwd(inp["q"], inp["k"], inp["v"], inp["lam"], inp["dO"], S0=inp["S0"], split=3)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_bwd_euler_identities():
+    """<dQ,Q> = <dO,O>; <dK,K> + <dS0,S0> = <dV,V> + <dS0,S0> = <dO,O> + <dS_end,S_end>
+    (the loss is linear in Q and jointly linear in (K, S0) and in (V, S0))."""
+    inp = make_inputs(1, 4, 64 * 16 + 5, 128, 128, need_dO=True, s0_std=0.3, dS_end_std=0.3,
+                      seed=33, device="cuda")
+    q, k, v, lam, S0, dO, dSe = (inp[x] for x in ("q", "k", "v", "lam", "S0", "dO", "dS_end"))
+    O, S_end = la.la_chunk_fwd(q, k, v, lam, S0=S0)
+    dQ, dK, dV, dS0 = la.la_chunk_bwd(q, k, v, lam, dO, S0=S0, dS_end=dSe)
+    Q, K, V, G = f64(q), f64(k), f64(v), f64(dO)
+    lo = np.sum(G * f64(O))
+    l = lo + np.sum(f64(dSe) * f64(S_end))
+    s0t = np.sum(f64(dS0) * f64(S0))
+    t_q = np.sum(f64(dQ) * Q)
+    t_k = np.sum(f64(dK) * K)
+    t_v = np.sum(f64(dV) * V)
+    scale = np.sum(np.abs(f64(dQ) * Q)) + np.sum(np.abs(f64(dS0) * f64(S0)))
+    assert abs(t_q - lo) <= 1e-2 * np.sum(np.abs(f64(dQ) * Q))
+    assert abs(t_k + s0t - l) <= 1e-2 * (np.sum(np.abs(f64(dK) * K)) + abs(s0t))
+    assert abs(t_v + s0t - l) <= 1e-2 * (np.sum(np.abs(f64(dV) * V)) + abs(s0t))
+    assert scale > 0
