@@ -1,13 +1,13 @@
 // la_fwd.hip -- chunkwise forward kernel of decayed causal linear attention.
 //
-// One workgroup (4 waves) walks the 64-token chunks of one sub-segment of
+// One workgroup (d/16 waves) walks the 64-token chunks of one sub-segment of
 // one sequence in order, carrying the fp32 state S (D x D) in MFMA
 // accumulators.  Per chunk c with tokens i, j = 0..cl-1 (cl = 64 except for a
 // ragged tail), decay lambda and S the state before the chunk:
 //
 //   P[i][j]   = lambda^(i-j) (q_i . k_j)  for j <= i, else 0     (intra scores)
 //   o_i       = lambda^(i+1) q_i^T S  +  sum_j P[i][j] v_j          (output)
-//   S        <- lambda^cl S + sum_j lambda^(cl-1-j) k_j v_j^T       (state)
+//   S        <- lambda^cl S + sum_j k_j (lambda^(cl-1-j) v_j)^T     (state)
 //
 // which is the token recurrence S_t = lambda S_{t-1} + k_t v_t^T,
 // o_t = q_t^T S_t regrouped: exact attention inside a chunk and the state
@@ -16,25 +16,31 @@
 // abstract).  Only non-negative powers of lambda are formed, so nothing
 // overflows however long the sequence.
 //
-// Work split inside the workgroup (wave w of 4):
+// Work split inside the workgroup (wave w of NW = D/16):
 //   * intra scores: the 10 non-zero 16x16 tiles of P^T = K Q^T are dealt
 //     round-robin to the waves and written to LDS as P[i][j];
-//   * wave w owns state columns v in [w D/4, (w+1) D/4): its slice of S stays
+//   * wave w owns state columns v in [16 w, 16 w + 16): its slice of S stays
 //     in registers, serves directly (rounded to bf16) as the A operand of
-//     O^T = S^T Q^T, and is updated by S += Kt' V with Kt' = (diag(lambda^(cl-1-j)) K)^T;
+//     O^T = S^T Q^T, and is updated by S += K^T (diag(lambda^(cl-1-j)) V);
 //   * outputs are produced as O^T tiles so each lane ends up with 4
 //     consecutive v of one token: one 8-byte (bf16) store per tile.
-// LDS holds the chunk's Q and K (token-major, for the scores and the inter
-// term), K and V transposed (d-major, for the products that contract over
-// tokens) and P.  The next chunk's Q, K, V are loaded into registers while
-// the current chunk computes.
+//
+// Memory pipeline: Q, K, V chunks go from HBM straight into LDS (16 bytes
+// per lane, no register staging) through STAGES buffers, so STAGES-1 chunks
+// are in flight while one is computed.  LDS holds only token-major tiles
+// (XOR-swizzled 16-byte granules, chosen per lane by the global address each
+// lane fetches) plus P; operands that contract over tokens (K^T, V^T) use the
+// gfx950 transposing LDS read, so no transposed copy is ever written.  A
+// ragged tail loads clamped (valid, finite) rows past the end and masks them
+// out through the decay factors.  Two barriers per chunk, without fences:
+// waits are explicit.
 #include "la_device.h"
 #include "la_internal.h"
 
 namespace la {
 
 // The 10 lower-triangular (key block jb <= query block ib) tiles of the
-// 64x64 score matrix, dealt round-robin to the 4 waves (3, 3, 2, 2 tiles).
+// 64x64 score matrix, dealt round-robin to the waves.
 __device__ inline void score_tile(int idx, int& jb, int& ib) {
   if (idx < 4) { jb = idx; ib = idx; }
   else if (idx < 7) { jb = idx - 4; ib = idx - 3; }
@@ -42,51 +48,72 @@ __device__ inline void score_tile(int idx, int& jb, int& ib) {
   else { jb = 0; ib = 3; }
 }
 
-template <typename T, int D, bool WITH_O>
-struct FwdLayout {
-  typedef Tile<T, CH, D, 1> TQ;   // Q, K token-major [token][d]
-  typedef Tile<T, D, CH, 2> TT;   // K', V transposed [d][token]
-  typedef Tile<T, CH, CH, 1> TP;  // P [i][j]
-  static constexpr int OFF_Q = 0;
-  static constexpr int OFF_K = WITH_O ? TQ::BYTES : 0;
-  static constexpr int OFF_KT = WITH_O ? 2 * TQ::BYTES : 0;
-  static constexpr int OFF_VT = OFF_KT + TT::BYTES;
-  static constexpr int OFF_P = OFF_VT + TT::BYTES;
-  static constexpr int BYTES = OFF_P + (WITH_O ? TP::BYTES : 0);
-};
+constexpr int LDS_MAX = 160 * 1024;  // per workgroup on gfx950
 
 template <typename T, int D, bool WITH_O>
-__global__ __launch_bounds__(NTHR) void k_chunk_fwd(FwdArgs a) {
+struct FwdLayout {
+  static constexpr int GPR = D * (int)sizeof(T) / 16;
+  typedef Tile<T, CH, D, (GPR >= 16 ? 3 : 2)> TN;  // Q, K, V token-major [token][d]
+  typedef Tile<T, CH, CH, 1> TP;                    // P [i][j]
+  static constexpr int NTEN = WITH_O ? 3 : 2;       // tensors per stage (Q, K, V or K, V)
+  static constexpr int PBYTES = WITH_O ? TP::BYTES : 0;
+  static constexpr int STAGE = NTEN * TN::BYTES;
+  static constexpr int SMAX = WITH_O ? 3 : 4;
+  static constexpr int SFIT = (LDS_MAX - PBYTES) / STAGE;
+  static constexpr int STAGES = SFIT < SMAX ? SFIT : SMAX;
+  static constexpr int BYTES = STAGES * STAGE + PBYTES;
+  static constexpr int NW = D / 16;  // waves: one per 16 state columns
+  static constexpr int NT = 64 * NW;
+  static constexpr int IPW = TN::BYTES / 1024 / NW;  // 1-KiB loads per wave per tensor
+  static constexpr int LPC = NTEN * IPW;             // loads per wave per chunk
+  // bf16 keeps two waves per SIMD (256 registers per lane)
+  static constexpr int WAVES_PER_EU = sizeof(T) == 2 ? 2 : 1;
+  static_assert(STAGES >= 1 && BYTES <= LDS_MAX, "LDS budget");
+  static_assert(IPW * NW * 1024 == TN::BYTES, "load tiling");
+};
+
+// wait until chunk c's loads have landed (loads of `later` younger chunks may
+// still be in flight), then barrier
+template <int LPC, int MAXLATER>
+__device__ inline void wait_chunk(int later) {
+  if constexpr (MAXLATER >= 2) {
+    if (later >= 2) { wait_vm_barrier<2 * LPC>(); return; }
+  }
+  if constexpr (MAXLATER >= 1) {
+    if (later >= 1) { wait_vm_barrier<LPC>(); return; }
+  }
+  wait_vm_barrier<0>();
+}
+
+template <typename T, int D, bool WITH_O>
+__global__ __launch_bounds__((FwdLayout<T, D, WITH_O>::NT),
+                             (FwdLayout<T, D, WITH_O>::WAVES_PER_EU)) void k_chunk_fwd(
+    FwdArgs a) {
   typedef Elt<T> X;
   typedef typename X::op_t op_t;
   typedef FwdLayout<T, D, WITH_O> LY;
-  typedef typename LY::TQ TQ;
-  typedef typename LY::TT TT;
+  typedef typename LY::TN TN;
   typedef typename LY::TP TP;
   constexpr int E = X::E;           // operand elements per lane
   constexpr int KS = 4 * E;         // MFMA contraction step
+  constexpr int NW = LY::NW;        // waves
+  constexpr int NT = LY::NT;        // threads
   constexpr int EP = 16 / (int)sizeof(T);  // elements per 16-byte piece
-  constexpr int PPR = D / EP;       // pieces per token row
-  constexpr int RPP = 2 * NTHR / PPR;  // token rows per load pass
-  constexpr int NPASS = CH / RPP;   // load passes per chunk
-  constexpr int NVT = D / 64;       // 16-wide state-column tiles per wave
   constexpr int NKT = D / 16;       // 16-high state-row tiles
+  constexpr int NST = (10 + NW - 1) / NW;  // score tiles per wave (at most)
   constexpr int NKS = D / KS;       // contraction steps over d
   constexpr int NJS = CH / KS;      // contraction steps over a chunk
-  static_assert(NPASS >= 1 && RPP * NPASS == CH, "load tiling");
+  constexpr int S = LY::STAGES;
 
-  __shared__ __attribute__((aligned(16))) char smem[LY::BYTES];
-  char* const sQ = smem + LY::OFF_Q;
-  char* const sK = smem + LY::OFF_K;
-  char* const sKt = smem + LY::OFF_KT;
-  char* const sVt = smem + LY::OFF_VT;
-  char* const sP = smem + LY::OFF_P;
+  __shared__ __attribute__((aligned(1024))) char smem[LY::BYTES];
+  char* const sP = smem + S * LY::STAGE;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int l16 = lane & 15;
   const int g = lane >> 4;
+  const int col = 16 * w;  // this wave's state columns [col, col + 16)
 
   // ---- work item
   const int64_t n = (int64_t)blockIdx.x / a.p_count;
@@ -108,8 +135,28 @@ __global__ __launch_bounds__(NTHR) void k_chunk_fwd(FwdArgs a) {
     return seq_row0 + (a.reverse ? (a.Ls - 1 - tt) : tt);
   };
 
-  // ---- start state -> accumulators (wave w: columns [w D/4, (w+1) D/4))
-  f32x4 accS[NKT][NVT];
+  // ---- chunk loads: HBM -> LDS stage (c % S), 16 B per lane, swizzled by
+  // the global piece each lane fetches.  Rows past the end are clamped.
+  auto issue = [&](int64_t c) {
+    char* const stage = smem + (int)(c % S) * LY::STAGE;
+#pragma unroll
+    for (int q = 0; q < LY::IPW; ++q) {
+      const int blk = w * LY::IPW + q;  // 1-KiB block of the tile
+      const int o = blk * 1024 + lane * 16;
+      const int row = o / TN::ROWB;
+      const int lgr = ((o % TN::ROWB) >> 4) ^ TN::swz(row);
+      int64_t tt = c * CH + row;
+      if (tt >= len) tt = len - 1;
+      const int64_t off = row_of(t0 + tt) * D + lgr * EP;
+      int tsr = 0;
+      if (WITH_O) dma16(Qg + off, stage + (tsr++) * TN::BYTES + blk * 1024);
+      dma16(Kg + off, stage + (tsr++) * TN::BYTES + blk * 1024);
+      dma16(Vg + off, stage + tsr * TN::BYTES + blk * 1024);
+    }
+  };
+
+  // ---- start state -> accumulators (wave w: columns [16 w, 16 w + 16))
+  f32x4 accS[NKT];
   {
     const float* sp = nullptr;
     if (a.start_from_state) {
@@ -121,120 +168,91 @@ __global__ __launch_bounds__(NTHR) void k_chunk_fwd(FwdArgs a) {
 #pragma unroll
     for (int tk = 0; tk < NKT; ++tk)
 #pragma unroll
-      for (int vt = 0; vt < NVT; ++vt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          accS[tk][vt][r] =
-              sp ? sp[(16 * tk + 4 * g + r) * D + 16 * (w * NVT + vt) + l16] : 0.0f;
+      for (int r = 0; r < 4; ++r)
+        accS[tk][r] = sp ? sp[(16 * tk + 4 * g + r) * D + col + l16] : 0.0f;
   }
 
-  // ---- chunk-independent factors
+  // first chunks in flight while the factors are computed
+#pragma unroll
+  for (int pc = 0; pc < S - 1; ++pc)
+    if (pc < nch) issue(pc);
+
+  // ---- factors
   float qf[4];        // lambda^(i+1) for the lane's query i of each 16-row block
-  float pf[3][4];     // lambda^(i-j) (or 0) for the wave's score tiles
-  int njs[4];         // contraction steps over keys j < 16 (it+1)
-  if (WITH_O) {
+  float pf[NST][4];   // lambda^(i-j) (or 0) for the wave's score tiles
+  auto set_pf = [&](int cl) {
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      qf[it] = pow_lam(lg, (float)(16 * it + l16 + 1));
-      njs[it] = (16 * (it + 1) + KS - 1) / KS;
-    }
-#pragma unroll
-    for (int s = 0; s < 3; ++s) {
-      const int idx = w + 4 * s;
+    for (int s = 0; s < NST; ++s) {
+      const int idx = w + NW * s;
       int jb = 0, ib = 0;
       if (idx < 10) score_tile(idx, jb, ib);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * ib + l16, j = 16 * jb + 4 * g + r;
-        pf[s][r] = (idx < 10 && j <= i) ? pow_lam(lg, (float)(i - j)) : 0.0f;
+        pf[s][r] = (idx < 10 && j <= i && j < cl) ? pow_lam(lg, (float)(i - j)) : 0.0f;
       }
     }
+  };
+  if (WITH_O) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) qf[it] = pow_lam(lg, (float)(16 * it + l16 + 1));
+    set_pf(CH);
     // upper score tiles are never written: clear P once
-    for (int o = tid * 16; o < TP::BYTES; o += NTHR * 16)
+    for (int o = tid * 16; o < TP::BYTES; o += NT * 16)
       lds_store16<T>(sP, o, u32x4{0u, 0u, 0u, 0u});
   }
   const float lamC = pow_lam(lg, (float)CH);
-
-  // ---- global -> register staging of one chunk (16-byte pieces)
-  const int pe = tid % PPR;  // piece (column group) of this thread
-  const int prp = tid / PPR; // row pair inside a pass
-  u32x4 rq[NPASS][2], rk[NPASS][2], rv[NPASS][2];
-  auto load_chunk = [&](int64_t c) {
+  // lambda^(cl-1-j) (0 past the tail) for the lane's contraction slots j of the update
+  float wv[NJS][E];
+  auto set_wv = [&](int cl) {
 #pragma unroll
-    for (int ps = 0; ps < NPASS; ++ps)
+    for (int js = 0; js < NJS; ++js)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int r = ps * RPP + 2 * prp + hh;
-        const int64_t tt = c * CH + r;
-        const bool ok = (tt < len);
-        const int64_t off = ok ? (row_of(t0 + tt) * D + pe * EP) : 0;
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        if (WITH_O) rq[ps][hh] = ok ? *reinterpret_cast<const u32x4*>(Qg + off) : z;
-        rk[ps][hh] = ok ? *reinterpret_cast<const u32x4*>(Kg + off) : z;
-        rv[ps][hh] = ok ? *reinterpret_cast<const u32x4*>(Vg + off) : z;
+      for (int x = 0; x < E; ++x) {
+        const int j = js * KS + g * E + x;
+        wv[js][x] = (j < cl) ? pow_lam(lg, (float)(cl - 1 - j)) : 0.0f;
       }
   };
-
-  // ---- registers -> LDS (token-major Q, K; transposed K' and V)
-  auto store_chunk = [&](int cl) {
-#pragma unroll
-    for (int ps = 0; ps < NPASS; ++ps) {
-      const int r0 = ps * RPP + 2 * prp;
-      if (WITH_O) {
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          lds_store16<T>(sQ, TQ::off(r0 + hh, pe * EP), rq[ps][hh]);
-          lds_store16<T>(sK, TQ::off(r0 + hh, pe * EP), rk[ps][hh]);
-        }
-      }
-      const float wk0 = (r0 < cl) ? pow_lam(lg, (float)(cl - 1 - r0)) : 0.0f;
-      const float wk1 = (r0 + 1 < cl) ? pow_lam(lg, (float)(cl - 2 - r0)) : 0.0f;
-      union U { u32x4 u; T e[EP]; };
-      U k0, k1, v0, v1;
-      k0.u = rk[ps][0];
-      k1.u = rk[ps][1];
-      v0.u = rv[ps][0];
-      v1.u = rv[ps][1];
-#pragma unroll
-      for (int x = 0; x < EP; ++x) {
-        const int row = pe * EP + x;
-        T kp[2] = {X::from_f(X::to_f(k0.e[x]) * wk0), X::from_f(X::to_f(k1.e[x]) * wk1)};
-        T vp[2] = {v0.e[x], v1.e[x]};
-        if (sizeof(T) == 2) {
-          *reinterpret_cast<unsigned int*>(sKt + TT::off(row, r0)) =
-              *reinterpret_cast<unsigned int*>(kp);
-          *reinterpret_cast<unsigned int*>(sVt + TT::off(row, r0)) =
-              *reinterpret_cast<unsigned int*>(vp);
-        } else {
-          *reinterpret_cast<u32x2*>(sKt + TT::off(row, r0)) = *reinterpret_cast<u32x2*>(kp);
-          *reinterpret_cast<u32x2*>(sVt + TT::off(row, r0)) = *reinterpret_cast<u32x2*>(vp);
-        }
-      }
-    }
-  };
-
-  if (nch > 0) load_chunk(0);
+  set_wv(CH);
 
   for (int64_t c = 0; c < nch; ++c) {
     const int cl = (int)((len - c * CH < CH) ? (len - c * CH) : CH);
-    __syncthreads();  // the previous chunk's LDS reads are done
-    store_chunk(cl);
-    __syncthreads();
-    if (c + 1 < nch) load_chunk(c + 1);  // in flight during this chunk's math
+    if constexpr (S == 1) {
+      lds_barrier();  // the previous chunk's LDS reads are done
+      issue(c);
+      wait_vm_barrier<0>();
+    } else {
+      const int64_t later = (nch - 1 - c < S - 2) ? nch - 1 - c : S - 2;
+      wait_chunk<LY::LPC, S - 2>((int)later);  // chunk c landed; chunk c-1 fully consumed
+      if (c + S - 1 < nch) issue(c + S - 1);     // into the stage chunk c-1 used
+    }
+    if (cl != CH) {
+      set_wv(cl);
+      if (WITH_O) set_pf(cl);
+    }
+    const char* const stage = smem + (int)(c % S) * LY::STAGE;
+    const char* const sQ = stage;
+    const char* const sK = stage + (WITH_O ? TN::BYTES : 0);
+    const char* const sV = sK + TN::BYTES;
+
+    // V^T operands of this wave's columns (intra A operand; scaled: update B operand)
+    op_t Vop[NJS];
+#pragma unroll
+    for (int js = 0; js < NJS; ++js) Vop[js] = tr_op<T, TN>(sV, js * KS, col, lane);
 
     if (WITH_O) {
       // ---- intra scores: P^T tiles = K Q^T, masked and decayed, to LDS as P[i][j]
 #pragma unroll
-      for (int s = 0; s < 3; ++s) {
-        const int idx = w + 4 * s;
+      for (int s = 0; s < NST; ++s) {
+        const int idx = w + NW * s;
         if (idx < 10) {
           int jb, ib;
           score_tile(idx, jb, ib);
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) {
-            const op_t A = lds_op<T>(sK, TQ::off(16 * jb + l16, ks * KS + g * E));
-            const op_t B = lds_op<T>(sQ, TQ::off(16 * ib + l16, ks * KS + g * E));
+            const op_t A = lds_op<T>(sK, TN::off(16 * jb + l16, ks * KS + g * E));
+            const op_t B = lds_op<T>(sQ, TN::off(16 * ib + l16, ks * KS + g * E));
             acc = X::mfma(A, B, acc);
           }
           T pv[4];
@@ -247,101 +265,90 @@ __global__ __launch_bounds__(NTHR) void k_chunk_fwd(FwdArgs a) {
             *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<u32x4*>(pv);
         }
       }
-      __syncthreads();
+      lds_barrier();  // P complete
 
       // ---- state before this chunk as the A operand of O^T = S^T Q^T
-      op_t Sop[NVT][NKS];
+      op_t Sop[NKS];
 #pragma unroll
-      for (int vt = 0; vt < NVT; ++vt)
+      for (int ks = 0; ks < NKS; ++ks) {
+        if constexpr (E == 8) {
+          bf16x8 o;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          if constexpr (E == 8) {
-            bf16x8 o;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              o[r] = (__bf16)accS[2 * ks][vt][r];
-              o[4 + r] = (__bf16)accS[2 * ks + 1][vt][r];
-            }
-            Sop[vt][ks] = o;
-          } else {
-            Sop[vt][ks] = accS[ks / 4][vt][ks % 4];
+          for (int r = 0; r < 4; ++r) {
+            o[r] = (__bf16)accS[2 * ks][r];
+            o[4 + r] = (__bf16)accS[2 * ks + 1][r];
           }
+          Sop[ks] = o;
+        } else {
+          Sop[ks] = accS[ks / 4][ks % 4];
         }
+      }
 
       // ---- outputs, one 16-token block at a time
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
         const int i = 16 * it + l16;
-        f32x4 o[NVT];
-#pragma unroll
-        for (int vt = 0; vt < NVT; ++vt) o[vt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 o = {0.f, 0.f, 0.f, 0.f};
         // inter: sum_k S[k][v] q_i[k], with Q read in the permuted slot order
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
           op_t B;
           if constexpr (E == 8) {
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(sQ + TQ::off(i, 32 * ks + 4 * g));
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(sQ + TQ::off(i, 32 * ks + 16 + 4 * g));
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(sQ + TN::off(i, 32 * ks + 4 * g));
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(sQ + TN::off(i, 32 * ks + 16 + 4 * g));
             const u32x4 both = {lo[0], lo[1], hi[0], hi[1]};
             B = __builtin_bit_cast(bf16x8, both);
           } else {
-            B = *reinterpret_cast<const float*>(sQ + TQ::off(i, 16 * (ks / 4) + 4 * g + (ks % 4)));
+            B = *reinterpret_cast<const float*>(sQ + TN::off(i, 16 * (ks / 4) + 4 * g + (ks % 4)));
           }
-#pragma unroll
-          for (int vt = 0; vt < NVT; ++vt) o[vt] = X::mfma(Sop[vt][ks], B, o[vt]);
+          o = X::mfma(Sop[ks], B, o);
         }
-#pragma unroll
-        for (int vt = 0; vt < NVT; ++vt) o[vt] *= qf[it];
+        o *= qf[it];
         // intra: sum_j V^T[v][j] P[i][j] over key blocks j < 16 (it + 1)
 #pragma unroll
         for (int js = 0; js < NJS; ++js) {
-          if (js < njs[it]) {
+          if (js * KS < 16 * (it + 1)) {
             const op_t Bp = lds_op<T>(sP, TP::off(i, js * KS + g * E));
-#pragma unroll
-            for (int vt = 0; vt < NVT; ++vt) {
-              const op_t Av = lds_op<T>(sVt, TT::off(16 * (w * NVT + vt) + l16, js * KS + g * E));
-              o[vt] = X::mfma(Av, Bp, o[vt]);
-            }
+            o = X::mfma(Vop[js], Bp, o);
           }
         }
         // store: lane holds O[token i][v0 .. v0+3]
         if (c * CH + i < len) {
-          T* orow = Og + row_of(t0 + c * CH + i) * D;
+          T* orow = Og + row_of(t0 + c * CH + i) * D + col + 4 * g;
+          T ov[4];
 #pragma unroll
-          for (int vt = 0; vt < NVT; ++vt) {
-            const int v0 = 16 * (w * NVT + vt) + 4 * g;
-            T ov[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) ov[r] = X::from_f(o[vt][r]);
-            if (sizeof(T) == 2)
-              *reinterpret_cast<u32x2*>(orow + v0) = *reinterpret_cast<u32x2*>(ov);
-            else
-              *reinterpret_cast<u32x4*>(orow + v0) = *reinterpret_cast<u32x4*>(ov);
-          }
+          for (int r = 0; r < 4; ++r) ov[r] = X::from_f(o[r]);
+          if (sizeof(T) == 2)
+            *reinterpret_cast<u32x2*>(orow) = *reinterpret_cast<u32x2*>(ov);
+          else
+            *reinterpret_cast<u32x4*>(orow) = *reinterpret_cast<u32x4*>(ov);
         }
       }
     }
 
-    // ---- state update: S = lambda^cl S + Kt' V
+    // ---- state update: S = lambda^cl S + K^T (diag(lambda^(cl-1-j)) V)
     {
       const float dc = (cl == CH) ? lamC : pow_lam(lg, (float)cl);
 #pragma unroll
-      for (int tk = 0; tk < NKT; ++tk)
+      for (int tk = 0; tk < NKT; ++tk) accS[tk] *= dc;
+      op_t Bv[NJS];
 #pragma unroll
-        for (int vt = 0; vt < NVT; ++vt) accS[tk][vt] *= dc;
-      op_t Bv[NVT][NJS];
+      for (int js = 0; js < NJS; ++js) {
+        if constexpr (E == 8) {
+          bf16x8 b;
 #pragma unroll
-      for (int vt = 0; vt < NVT; ++vt)
-#pragma unroll
-        for (int js = 0; js < NJS; ++js)
-          Bv[vt][js] = lds_op<T>(sVt, TT::off(16 * (w * NVT + vt) + l16, js * KS + g * E));
+          for (int x = 0; x < 8; ++x) b[x] = (__bf16)((float)Vop[js][x] * wv[js][x]);
+          Bv[js] = b;
+        } else {
+          Bv[js] = Vop[js] * wv[js][0];
+        }
+      }
 #pragma unroll
       for (int tk = 0; tk < NKT; ++tk)
 #pragma unroll
         for (int js = 0; js < NJS; ++js) {
-          const op_t Ak = lds_op<T>(sKt, TT::off(16 * tk + l16, js * KS + g * E));
-#pragma unroll
-          for (int vt = 0; vt < NVT; ++vt) accS[tk][vt] = X::mfma(Ak, Bv[vt][js], accS[tk][vt]);
+          const op_t Ak = tr_op<T, TN>(sK, js * KS, 16 * tk, lane);
+          accS[tk] = X::mfma(Ak, Bv[js], accS[tk]);
         }
     }
   }
@@ -352,19 +359,18 @@ __global__ __launch_bounds__(NTHR) void k_chunk_fwd(FwdArgs a) {
 #pragma unroll
     for (int tk = 0; tk < NKT; ++tk)
 #pragma unroll
-      for (int vt = 0; vt < NVT; ++vt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          dst[(16 * tk + 4 * g + r) * D + 16 * (w * NVT + vt) + l16] = accS[tk][vt][r];
+      for (int r = 0; r < 4; ++r) dst[(16 * tk + 4 * g + r) * D + col + l16] = accS[tk][r];
   }
 }
 
 template <typename T, int D>
 static hipError_t launch_fwd_t(const FwdArgs& a, bool with_o, int64_t nwg, hipStream_t s) {
   if (with_o)
-    hipLaunchKernelGGL((k_chunk_fwd<T, D, true>), dim3((unsigned)nwg), dim3(NTHR), 0, s, a);
+    hipLaunchKernelGGL((k_chunk_fwd<T, D, true>), dim3((unsigned)nwg),
+                       dim3(FwdLayout<T, D, true>::NT), 0, s, a);
   else
-    hipLaunchKernelGGL((k_chunk_fwd<T, D, false>), dim3((unsigned)nwg), dim3(NTHR), 0, s, a);
+    hipLaunchKernelGGL((k_chunk_fwd<T, D, false>), dim3((unsigned)nwg),
+                       dim3(FwdLayout<T, D, false>::NT), 0, s, a);
   return hipGetLastError();
 }
 
