@@ -80,6 +80,11 @@ la_status check_shape(const la_shape* s, Plan* plan) {
 
   plan->nseq = s->B * s->H * (int64_t)s->nseg;
   plan->Ls = s->L / s->nseg;
+  // the kernels address one sequence's tokens with 32-bit byte offsets
+  const int64_t elt = s->dtype == LA_FP32 ? 4 : 2;
+  if ((double)plan->Ls * s->dk * elt >= 4294967296.0)
+    return fail(LA_ERR_UNSUPPORTED, "one segment spans %lld tokens; at most 2^32 bytes per segment",
+                (long long)plan->Ls);
   plan->D = s->dk;
   const int64_t nchunks = (plan->Ls + kChunk - 1) / kChunk;
   int64_t want = s->split > 0 ? s->split

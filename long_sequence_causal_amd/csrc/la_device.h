@@ -54,28 +54,37 @@ struct Elt<float> {
 };
 
 // ---------------------------------------------------------------- LDS tiles
-// A ROWS x COLS tile of T in LDS, each row cut into 16-byte granules whose
-// order is XOR-swizzled per row so that the reads of 16 consecutive rows, and
-// the transposed reads of rows {8g + e : g, e < 4}, hit distinct banks.
-//   SW = 1: granule ^= row & 7
-//   SW = 2: granule ^= (row ^ (row >> 3)) & 7
-//   SW = 3: granule ^= (row & 15) ^ (((row >> 4) & 1) << 2)   (16+ granules per row)
-template <typename T, int ROWS, int COLS, int SW>
-struct Tile {
+// A ROWS x COLS tile of T in LDS, token-major, each row padded by 16 bytes.
+// With a row stride of an odd number of 16-byte granules, 16 consecutive rows
+// start on 16 different bank groups, so the reads this code makes -- 16 B
+// (or two 8 B pieces) from each of 16 consecutive rows, and transposing
+// reads over 16 consecutive rows -- take the minimum number of LDS cycles.
+// Addresses stay affine in (row, col): unrolled accesses share one base
+// register and differ by immediates.
+template <typename T, int ROWS, int COLS>
+struct PadTile {
   static constexpr int ROWB = COLS * (int)sizeof(T);
-  static constexpr int GPR = ROWB / 16;
-  static constexpr int TPG = 16 / (int)sizeof(T);
-  static constexpr int BYTES = ROWS * ROWB;
-  static_assert(GPR >= 8, "swizzle needs at least 8 granules per row");
-  static_assert(SW != 3 || GPR >= 16, "SW=3 needs 16 granules per row");
-  __device__ static inline int swz(int row) {
-    if (SW == 1) return row & 7;
-    if (SW == 2) return (row ^ (row >> 3)) & 7;
-    return (row & 15) ^ (((row >> 4) & 1) << 2);
-  }
-  // byte offset of element (row, col)
-  __device__ static inline int off(int row, int col) {
-    return row * ROWB + (((col / TPG) ^ swz(row)) << 4) + (col % TPG) * (int)sizeof(T);
+  static constexpr int RS = ROWB + 16;  // row stride in bytes
+  static constexpr int G = RS / 16;     // 16-byte granules per row (odd)
+  static constexpr int BYTES = ROWS * RS;
+  static_assert(ROWB % 32 == 0 && (G & 1) == 1, "row stride must be an odd number of granules");
+  __device__ static inline int off(int row, int col) { return row * RS + col * (int)sizeof(T); }
+};
+
+// The 10 nonzero 16x16 blocks (key block jb <= query block ib) of the 64x64
+// intra-chunk score matrix P, stored compactly, block (jb, ib) at slot
+// ib (ib + 1) / 2 + jb.  Inside a block the 16 keys are split into 4 slabs of
+// 4 (the keys one MFMA lane group holds, see perm16), each slab stored
+// [query row][4 keys]: a 16-lane group touching one slab covers 16
+// consecutive 8-byte (bf16) pieces, so 8-byte accesses by lanes 0..31 or
+// 32..63 hit all 64 banks once.
+template <typename T>
+struct PBlocks {
+  static constexpr int SLAB = 16 * 4 * (int)sizeof(T);
+  static constexpr int BLK = 4 * SLAB;
+  static constexpr int BYTES = 10 * BLK;
+  __device__ static inline int at(int ib, int jb, int slab, int row) {
+    return (ib * (ib + 1) / 2 + jb) * BLK + slab * SLAB + row * 4 * (int)sizeof(T);
   }
 };
 
@@ -93,16 +102,18 @@ __device__ inline void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// 16 bytes per lane from global memory straight into LDS: lane l's bytes
-// land at lds_block + 16 l (lds_block must be wave-uniform; M0 holds it).
+// 16 bytes per lane from global memory straight into LDS: lane l reads
+// sbase + voff (sbase wave-uniform, voff a 32-bit byte offset) and its bytes
+// land at lds_block + 16 l (lds_block wave-uniform; M0 holds it).
 // Issued as inline asm so that the compiler does not treat later
 // transposing LDS reads as aliasing an in-flight load and wait for every
 // outstanding load before them: completion is waited for explicitly
 // (wait_vm_barrier) before a chunk is read.
-__device__ inline void dma16(const void* gsrc, char* lds_block) {
+__device__ inline void dma16(const void* sbase, unsigned voff, char* lds_block) {
   const unsigned lds = __builtin_amdgcn_readfirstlane(
       (unsigned)(size_t)(__attribute__((address_space(3))) char*)lds_block);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(lds)
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(lds)
                : "memory", "m0");
 }
 
@@ -123,14 +134,51 @@ __device__ inline typename Elt<T>::op_t lds_op(const char* lds, int off) {
   return *reinterpret_cast<const typename Elt<T>::op_t*>(lds + off);
 }
 
+// ---------------------------------------------------------------- token order
+// LDS bank model of gfx950 (64 banks of 4 bytes), as measured with the
+// hardware's bank-conflict counter: 8-byte reads, including the transposing
+// ones, serve lanes 0..31 in one cycle and 32..63 in the next; 16-byte reads
+// serve 16 lanes per cycle, in each half of the wave the lane quads 0, 3, 5, 6
+// and then 1, 2, 4, 7 (quads of even, then odd, bit count).  The paired-offset
+// forms (two 8-byte pieces per lane) run at half rate and are avoided.
+//
+// With rows padded to an odd number of 16-byte granules (PadTile), row r
+// starts on bank 4 r mod 64 (d = 128) and the orders below make every
+// transposing read, score-operand read and P access conflict-free:
+//   tr_row(g, e): row of contraction slot e (0..3) of lane group g within a
+//     16-token block.  Groups 0, 1 get the even rows, 2, 3 the odd ones, so an
+//     8-byte transposing read over lanes 0..31 touches 8 rows 8 banks apart.
+//   perm16(s) = tr_row(s / 4, s % 4): the token held by row s of a 16-row
+//     score operand; rows 0..3, 12..15 map to {0..3, 8..11}, a set closed
+//     under +8, and the rest to its complement.
+//   score_granule<D>(ks, g): 16-byte feature granule of slot group g in step
+//     ks.  d = 128: groups 0/1 and 2/3 sit 8 granules apart, which with the
+//     row sets above gives each 16-lane cycle of a 16-byte read 16 distinct
+//     bank quads.  d = 64 has only 8 granules per row and keeps the natural
+//     order (its 16-byte score reads then meet two-way conflicts).
+__device__ inline int tr_row(int g, int e) {
+  return ((0x1540 >> (4 * g)) & 15) + 2 * (e & 1) + 8 * (e >> 1);
+}
+template <typename T>
+__device__ inline int perm16(int s) {
+  if constexpr (sizeof(T) == 2) return tr_row(s >> 2, s & 3);
+  else return s;
+}
+template <int D>
+__device__ inline int score_granule(int ks, int g) {
+  if constexpr (D == 128) return ks + 8 * (g & 1) + 4 * (g >> 1);
+  else return 4 * ks + g;
+}
+
 // ---------------------------------------------------------------- transposed operand
 // MFMA operand that contracts over tokens, read from a token-major tile:
-// lane (g = lane / 16, n = lane % 16) receives column col0 + n of the E
-// consecutive tokens j0 + E g .. j0 + E g + E - 1 (the lane's contraction
-// slots).  bf16: two ds_read_b64_tr_b16.  Within each 16-lane group that
-// instruction hands output lane d the element (d % 4) of source lane
-// 4 e + d / 4, e = 0..3; so source lane s points at token j0 + 8 g + s / 4
-// (+ 4 for the second read) and columns col0 + 4 (s % 4) .. + 3.
+// lane (g = lane / 16, n = lane % 16) receives column col0 + n of the tokens
+// of its contraction slots.  bf16: slot e = 0..3 is token j0 + tr_row(g, e)
+// and slot 4 + e is token j0 + 16 + tr_row(g, e), read by two
+// ds_read_b64_tr_b16.  Within each 16-lane group that instruction hands
+// output lane d the element (d % 4) of source lane 4 e + d / 4, e = 0..3; so
+// source lane s points at the row of slot s / 4 and columns col0 + 4 (s % 4)
+// .. + 3.  Every operand paired with this one uses the same slot order.
 // fp32: one scalar read of token j0 + g, column col0 + n.
 template <typename T, class TL>
 __device__ inline typename Elt<T>::op_t tr_op(const char* tile, int j0, int col0, int lane) {
@@ -138,16 +186,31 @@ __device__ inline typename Elt<T>::op_t tr_op(const char* tile, int j0, int col0
   if constexpr (sizeof(T) == 2) {
     typedef short v4i16 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) v4i16 lds_v4;
-    const int row = j0 + 8 * g + (s >> 2);
+    const int row = j0 + tr_row(g, s >> 2);
     const int col = col0 + 4 * (s & 3);
     const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(tile + TL::off(row, col)));
-    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(tile + TL::off(row + 4, col)));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(tile + TL::off(row + 16, col)));
     typedef short v8i16 __attribute__((ext_vector_type(8)));
     const v8i16 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(bf16x8, both);
   } else {
     return *reinterpret_cast<const float*>(tile + TL::off(j0 + g, col0 + s));
   }
+}
+
+// token of contraction slot x of lane group g in the step starting at j0
+// (the order tr_op uses)
+template <typename T>
+__device__ inline int slot_token(int j0, int g, int x) {
+  if constexpr (sizeof(T) == 2) return j0 + (x < 4 ? tr_row(g, x) : 16 + tr_row(g, x - 4));
+  else return j0 + g;
+}
+
+// Separate 8-byte LDS read that the compiler may not fuse with a neighbour
+// into the half-rate paired form.
+__device__ inline u32x2 lds_read8(const char* p) {
+  typedef const volatile __attribute__((address_space(3))) u32x2 lds_u32x2;
+  return *(lds_u32x2*)((const __attribute__((address_space(3))) char*)p);
 }
 
 }  // namespace la

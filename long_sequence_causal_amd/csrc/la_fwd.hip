@@ -28,9 +28,11 @@
 // Memory pipeline: Q, K, V chunks go from HBM straight into LDS (16 bytes
 // per lane, no register staging) through STAGES buffers, so STAGES-1 chunks
 // are in flight while one is computed.  LDS holds only token-major tiles
-// (XOR-swizzled 16-byte granules, chosen per lane by the global address each
-// lane fetches) plus P; operands that contract over tokens (K^T, V^T) use the
-// gfx950 transposing LDS read, so no transposed copy is ever written.  A
+// (rows padded to an odd number of 16-byte granules; each lane's 16 B of a
+// load land where its row and piece put them) plus P; operands that contract
+// over tokens (K^T, V^T) use the gfx950 transposing LDS read, so no
+// transposed copy is ever written.  Token and feature orders inside the MFMA
+// steps are chosen so that no LDS access has a bank conflict.  A
 // ragged tail loads clamped (valid, finite) rows past the end and masks them
 // out through the decay factors.  Two barriers per chunk, without fences:
 // waits are explicit.
@@ -52,30 +54,36 @@ constexpr int LDS_MAX = 160 * 1024;  // per workgroup on gfx950
 
 template <typename T, int D, bool WITH_O>
 struct FwdLayout {
-  static constexpr int GPR = D * (int)sizeof(T) / 16;
-  typedef Tile<T, CH, D, (GPR >= 16 ? 3 : 2)> TN;  // Q, K, V token-major [token][d]
-  typedef Tile<T, CH, CH, 1> TP;                    // P [i][j]
-  static constexpr int NTEN = WITH_O ? 3 : 2;       // tensors per stage (Q, K, V or K, V)
+  typedef PadTile<T, CH, D> TN;                // Q, K, V token-major [token][d]
+  typedef PBlocks<T> TP;                       // P, its 10 nonzero 16x16 blocks
+  static constexpr int NTEN = WITH_O ? 3 : 2;  // tensors per stage (Q, K, V or K, V)
+  static constexpr int TB = TN::BYTES;         // one tensor tile
+  static constexpr int STAGE = NTEN * TB;
   static constexpr int PBYTES = WITH_O ? TP::BYTES : 0;
-  static constexpr int STAGE = NTEN * TN::BYTES;
-  static constexpr int SMAX = WITH_O ? 3 : 4;
+  static constexpr int SMAX = WITH_O ? 3 : 5;
   static constexpr int SFIT = (LDS_MAX - PBYTES) / STAGE;
   static constexpr int STAGES = SFIT < SMAX ? SFIT : SMAX;
-  static constexpr int BYTES = STAGES * STAGE + PBYTES;
+  static constexpr int OFF_P = STAGES * STAGE;
+  static constexpr int BYTES = OFF_P + PBYTES;
   static constexpr int NW = D / 16;  // waves: one per 16 state columns
   static constexpr int NT = 64 * NW;
-  static constexpr int IPW = TN::BYTES / 1024 / NW;  // 1-KiB loads per wave per tensor
-  static constexpr int LPC = NTEN * IPW;             // loads per wave per chunk
+  // one chunk is NTEN * G loads of 1 KiB (64 lanes x 16 B); wave w issues
+  // loads w, w + NW, ...: LPC_HI or LPC_HI - 1 of them
+  static constexpr int NBLK = NTEN * TN::G;
+  static constexpr int LPC_HI = (NBLK + NW - 1) / NW;
   // bf16 keeps two waves per SIMD (256 registers per lane)
   static constexpr int WAVES_PER_EU = sizeof(T) == 2 ? 2 : 1;
-  static_assert(STAGES >= 1 && BYTES <= LDS_MAX, "LDS budget");
-  static_assert(IPW * NW * 1024 == TN::BYTES, "load tiling");
+  static_assert(STAGES >= 1 && STAGES <= 5 && BYTES <= LDS_MAX, "LDS budget");
+  static_assert(TB == TN::G * 1024, "a tile is G loads of 1 KiB");
 };
 
-// wait until chunk c's loads have landed (loads of `later` younger chunks may
-// still be in flight), then barrier
+// wait until chunk c's loads have landed (loads of `later` younger chunks,
+// LPC per chunk, may still be in flight), then barrier
 template <int LPC, int MAXLATER>
-__device__ inline void wait_chunk(int later) {
+__device__ inline void wait_chunk_n(int later) {
+  if constexpr (MAXLATER >= 3) {
+    if (later >= 3) { wait_vm_barrier<3 * LPC>(); return; }
+  }
   if constexpr (MAXLATER >= 2) {
     if (later >= 2) { wait_vm_barrier<2 * LPC>(); return; }
   }
@@ -83,6 +91,13 @@ __device__ inline void wait_chunk(int later) {
     if (later >= 1) { wait_vm_barrier<LPC>(); return; }
   }
   wait_vm_barrier<0>();
+}
+template <int LPC_HI, int MAXLATER>
+__device__ inline void wait_chunk(bool hi, int later) {
+  if (hi || LPC_HI == 1)
+    wait_chunk_n<LPC_HI, MAXLATER>(later);
+  else
+    wait_chunk_n<(LPC_HI > 1 ? LPC_HI - 1 : 1), MAXLATER>(later);
 }
 
 template <typename T, int D, bool WITH_O>
@@ -97,20 +112,22 @@ __global__ __launch_bounds__((FwdLayout<T, D, WITH_O>::NT),
   constexpr int E = X::E;           // operand elements per lane
   constexpr int KS = 4 * E;         // MFMA contraction step
   constexpr int NW = LY::NW;        // waves
-  constexpr int NT = LY::NT;        // threads
   constexpr int EP = 16 / (int)sizeof(T);  // elements per 16-byte piece
   constexpr int NKT = D / 16;       // 16-high state-row tiles
   constexpr int NST = (10 + NW - 1) / NW;  // score tiles per wave (at most)
   constexpr int NKS = D / KS;       // contraction steps over d
   constexpr int NJS = CH / KS;      // contraction steps over a chunk
   constexpr int S = LY::STAGES;
+  constexpr int TB = LY::TB;
+  constexpr int G = TN::G;
+  constexpr int LPC_HI = LY::LPC_HI;
 
   __shared__ __attribute__((aligned(1024))) char smem[LY::BYTES];
-  char* const sP = smem + S * LY::STAGE;
+  char* const sP = smem + LY::OFF_P;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15;
   const int g = lane >> 4;
   const int col = 16 * w;  // this wave's state columns [col, col + 16)
@@ -125,33 +142,55 @@ __global__ __launch_bounds__((FwdLayout<T, D, WITH_O>::NT),
   const int64_t len = (t1 > t0) ? t1 - t0 : 0;
   const int64_t nch = (len + CH - 1) / CH;
 
-  const T* const Qg = reinterpret_cast<const T*>(a.Q);
-  const T* const Kg = reinterpret_cast<const T*>(a.K);
-  const T* const Vg = reinterpret_cast<const T*>(a.V);
-  T* const Og = reinterpret_cast<T*>(a.O);
-  const int64_t seq_row0 = n * a.Ls;  // first token row of sequence n
-  // token row (in the flattened tensor) of position tt of sequence n
-  auto row_of = [&](int64_t tt) -> int64_t {
-    return seq_row0 + (a.reverse ? (a.Ls - 1 - tt) : tt);
-  };
+  // Rows of sequence n are addressed relative to its first row (byte offsets
+  // within one sequence fit in 32 bits; the host checks that).  relrow(tt)
+  // is the row of position tt of this sub-segment; consecutive chunks are
+  // `dir * CH` rows apart.
+  const int64_t seq_elem0 = n * a.Ls * D;
+  auto relrow = [&](int64_t tt) -> int64_t { return a.reverse ? (a.Ls - 1 - (t0 + tt)) : (t0 + tt); };
+  const int cstride_b = (a.reverse ? -1 : 1) * CH * D * (int)sizeof(T);  // bytes per chunk
 
-  // ---- chunk loads: HBM -> LDS stage (c % S), 16 B per lane, swizzled by
-  // the global piece each lane fetches.  Rows past the end are clamped.
-  auto issue = [&](int64_t c) {
-    char* const stage = smem + (int)(c % S) * LY::STAGE;
+  // ---- chunk loads: HBM -> LDS, 1 KiB (64 lanes x 16 B) per instruction.
+  // Load b of a chunk fills granules 64 (b % G) .. + 63 of tensor b / G's
+  // tile; lane l's granule is (row, piece) = divmod(64 (b % G) + l, G), the
+  // last piece of a row being padding (it loads the row's first piece).
+  // Offsets of chunk 0 are precomputed; a ragged last chunk clamps rows past
+  // the end to the last valid token.
+  const bool lpc_hi = (w < LY::NBLK - (LPC_HI - 1) * NW);
+  auto blk_of = [&](int q) { const int bq = w + NW * q; return bq < LY::NBLK ? bq : 0; };
+  auto tensor_base = [&](int ten) -> const T* {
+    const void* bp = WITH_O ? (ten == 0 ? a.Q : (ten == 1 ? a.K : a.V)) : (ten == 0 ? a.K : a.V);
+    return reinterpret_cast<const T*>(bp) + seq_elem0;
+  };
+  unsigned voff0[LPC_HI];  // chunk-0 byte offset of this lane's piece, per load
 #pragma unroll
-    for (int q = 0; q < LY::IPW; ++q) {
-      const int blk = w * LY::IPW + q;  // 1-KiB block of the tile
-      const int o = blk * 1024 + lane * 16;
-      const int row = o / TN::ROWB;
-      const int lgr = ((o % TN::ROWB) >> 4) ^ TN::swz(row);
-      int64_t tt = c * CH + row;
-      if (tt >= len) tt = len - 1;
-      const int64_t off = row_of(t0 + tt) * D + lgr * EP;
-      int tsr = 0;
-      if (WITH_O) dma16(Qg + off, stage + (tsr++) * TN::BYTES + blk * 1024);
-      dma16(Kg + off, stage + (tsr++) * TN::BYTES + blk * 1024);
-      dma16(Vg + off, stage + tsr * TN::BYTES + blk * 1024);
+  for (int q = 0; q < LPC_HI; ++q) {
+    const int bb = blk_of(q);
+    const int pos = 64 * (bb % G) + lane;
+    const int row = pos / G, pc = pos % G;
+    const int piece = (pc == G - 1) ? 0 : pc;
+    voff0[q] = (unsigned)((relrow(row) * D + piece * EP) * (int64_t)sizeof(T));
+  }
+  auto issue = [&](int64_t c) {
+    const int sb = (int)(c % S) * LY::STAGE;
+    const bool full = (c + 1) * CH <= len;
+#pragma unroll
+    for (int q = 0; q < LPC_HI; ++q) {
+      if (q < LPC_HI - 1 || lpc_hi) {
+        const int bb = blk_of(q);
+        const int ten = bb / G;
+        unsigned voff;
+        if (full) {
+          voff = voff0[q] + (unsigned)(c * cstride_b);
+        } else {
+          const int pos = 64 * (bb % G) + lane;
+          const int row = pos / G, pc = pos % G;
+          const int piece = (pc == G - 1) ? 0 : pc;
+          const int64_t tt = (c * CH + row < len) ? c * CH + row : len - 1;
+          voff = (unsigned)((relrow(tt) * D + piece * EP) * (int64_t)sizeof(T));
+        }
+        dma16(tensor_base(ten), voff, smem + sb + ten * TB + (bb % G) * 1024);
+      }
     }
   };
 
@@ -170,10 +209,13 @@ __global__ __launch_bounds__((FwdLayout<T, D, WITH_O>::NT),
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         accS[tk][r] = sp ? sp[(16 * tk + 4 * g + r) * D + col + l16] : 0.0f;
+    // Retire these loads here, visibly to the compiler (vmcnt(0) only):
+    // otherwise it waits for them at their first use inside the chunk loop,
+    // i.e. on every chunk, which would also drain the chunk prefetches.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
   }
 
   // first chunks in flight while the factors are computed
-#pragma unroll
   for (int pc = 0; pc < S - 1; ++pc)
     if (pc < nch) issue(pc);
 
@@ -182,24 +224,27 @@ __global__ __launch_bounds__((FwdLayout<T, D, WITH_O>::NT),
   float pf[NST][4];   // lambda^(i-j) (or 0) for the wave's score tiles
   auto set_pf = [&](int cl) {
 #pragma unroll
-    for (int s = 0; s < NST; ++s) {
-      const int idx = w + NW * s;
+    for (int st = 0; st < NST; ++st) {
+      const int idx = w + NW * st;
       int jb = 0, ib = 0;
       if (idx < 10) score_tile(idx, jb, ib);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = 16 * ib + l16, j = 16 * jb + 4 * g + r;
-        pf[s][r] = (idx < 10 && j <= i && j < cl) ? pow_lam(lg, (float)(i - j)) : 0.0f;
+        // accumulator (row 4 g + r, column l16) of tile (jb, ib) holds P[i][j]
+        const int i = 16 * ib + perm16<T>(l16), j = 16 * jb + perm16<T>(4 * g + r);
+        pf[st][r] = (idx < 10 && j <= i && j < cl) ? pow_lam(lg, (float)(i - j)) : 0.0f;
       }
     }
   };
+  T* const Oseq = reinterpret_cast<T*>(a.O) + seq_elem0;  // sequence n of O
+  unsigned ooff0[4];  // element offset (chunk 0) of the lane's outputs in each 16-row block
   if (WITH_O) {
 #pragma unroll
-    for (int it = 0; it < 4; ++it) qf[it] = pow_lam(lg, (float)(16 * it + l16 + 1));
+    for (int it = 0; it < 4; ++it) {
+      qf[it] = pow_lam(lg, (float)(16 * it + l16 + 1));
+      ooff0[it] = (unsigned)(relrow(16 * it + l16) * D + col + 4 * g);
+    }
     set_pf(CH);
-    // upper score tiles are never written: clear P once
-    for (int o = tid * 16; o < TP::BYTES; o += NT * 16)
-      lds_store16<T>(sP, o, u32x4{0u, 0u, 0u, 0u});
   }
   const float lamC = pow_lam(lg, (float)CH);
   // lambda^(cl-1-j) (0 past the tail) for the lane's contraction slots j of the update
@@ -209,7 +254,7 @@ __global__ __launch_bounds__((FwdLayout<T, D, WITH_O>::NT),
     for (int js = 0; js < NJS; ++js)
 #pragma unroll
       for (int x = 0; x < E; ++x) {
-        const int j = js * KS + g * E + x;
+        const int j = slot_token<T>(js * KS, g, x);
         wv[js][x] = (j < cl) ? pow_lam(lg, (float)(cl - 1 - j)) : 0.0f;
       }
   };
@@ -223,8 +268,8 @@ __global__ __launch_bounds__((FwdLayout<T, D, WITH_O>::NT),
       wait_vm_barrier<0>();
     } else {
       const int64_t later = (nch - 1 - c < S - 2) ? nch - 1 - c : S - 2;
-      wait_chunk<LY::LPC, S - 2>((int)later);  // chunk c landed; chunk c-1 fully consumed
-      if (c + S - 1 < nch) issue(c + S - 1);     // into the stage chunk c-1 used
+      wait_chunk<LPC_HI, S - 2>(lpc_hi, (int)later);  // chunk c landed; chunk c-1 consumed
+      if (c + S - 1 < nch) issue(c + S - 1);             // into the stage chunk c-1 used
     }
     if (cl != CH) {
       set_wv(cl);
@@ -232,8 +277,8 @@ __global__ __launch_bounds__((FwdLayout<T, D, WITH_O>::NT),
     }
     const char* const stage = smem + (int)(c % S) * LY::STAGE;
     const char* const sQ = stage;
-    const char* const sK = stage + (WITH_O ? TN::BYTES : 0);
-    const char* const sV = sK + TN::BYTES;
+    const char* const sK = stage + (WITH_O ? TB : 0);
+    const char* const sV = sK + TB;
 
     // V^T operands of this wave's columns (intra A operand; scaled: update B operand)
     op_t Vop[NJS];
@@ -243,22 +288,27 @@ __global__ __launch_bounds__((FwdLayout<T, D, WITH_O>::NT),
     if (WITH_O) {
       // ---- intra scores: P^T tiles = K Q^T, masked and decayed, to LDS as P[i][j]
 #pragma unroll
-      for (int s = 0; s < NST; ++s) {
-        const int idx = w + NW * s;
+      for (int st = 0; st < NST; ++st) {
+        const int idx = w + NW * st;
         if (idx < 10) {
           int jb, ib;
           score_tile(idx, jb, ib);
+          // operand row l16 is token perm16(l16) of the block; the
+          // contraction over d visits features in score_granule order
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          const int rk = 16 * jb + perm16<T>(l16), rq = 16 * ib + perm16<T>(l16);
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) {
-            const op_t A = lds_op<T>(sK, TN::off(16 * jb + l16, ks * KS + g * E));
-            const op_t B = lds_op<T>(sQ, TN::off(16 * ib + l16, ks * KS + g * E));
+            const int f = (E == 8) ? 8 * score_granule<D>(ks, g) : ks * KS + g;
+            const op_t A = lds_op<T>(sK, TN::off(rk, f));
+            const op_t B = lds_op<T>(sQ, TN::off(rq, f));
             acc = X::mfma(A, B, acc);
           }
           T pv[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) pv[r] = X::from_f(acc[r] * pf[s][r]);
-          char* dst = sP + TP::off(16 * ib + l16, 16 * jb + 4 * g);
+          for (int r = 0; r < 4; ++r) pv[r] = X::from_f(acc[r] * pf[st][r]);
+          // keys perm16(4 g + r), r = 0..3, form slab g; query row perm16(l16)
+          char* dst = sP + TP::at(ib, jb, g, perm16<T>(l16));
           if (sizeof(T) == 2)
             *reinterpret_cast<u32x2*>(dst) = *reinterpret_cast<u32x2*>(pv);
           else
@@ -294,8 +344,8 @@ __global__ __launch_bounds__((FwdLayout<T, D, WITH_O>::NT),
         for (int ks = 0; ks < NKS; ++ks) {
           op_t B;
           if constexpr (E == 8) {
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(sQ + TN::off(i, 32 * ks + 4 * g));
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(sQ + TN::off(i, 32 * ks + 16 + 4 * g));
+            const u32x2 lo = lds_read8(sQ + TN::off(i, 32 * ks + 4 * g));
+            const u32x2 hi = lds_read8(sQ + TN::off(i, 32 * ks + 16 + 4 * g));
             const u32x4 both = {lo[0], lo[1], hi[0], hi[1]};
             B = __builtin_bit_cast(bf16x8, both);
           } else {
@@ -304,17 +354,31 @@ __global__ __launch_bounds__((FwdLayout<T, D, WITH_O>::NT),
           o = X::mfma(Sop[ks], B, o);
         }
         o *= qf[it];
-        // intra: sum_j V^T[v][j] P[i][j] over key blocks j < 16 (it + 1)
+        // intra: sum_j V^T[v][j] P[i][j] over key blocks jb <= it; slab g of
+        // a block holds exactly the keys of lane group g's slots
 #pragma unroll
         for (int js = 0; js < NJS; ++js) {
           if (js * KS < 16 * (it + 1)) {
-            const op_t Bp = lds_op<T>(sP, TP::off(i, js * KS + g * E));
+            op_t Bp;
+            if constexpr (E == 8) {
+              const u32x2 z = {0u, 0u};
+              const u32x2 lo = lds_read8(sP + TP::at(it, 2 * js, g, l16));
+              const u32x2 hi = (2 * js + 1 <= it) ? lds_read8(sP + TP::at(it, 2 * js + 1, g, l16)) : z;
+              const u32x4 both = {lo[0], lo[1], hi[0], hi[1]};
+              Bp = __builtin_bit_cast(bf16x8, both);
+            } else {
+              const int j = js * KS + g;
+              Bp = ((j >> 4) <= it)
+                       ? *reinterpret_cast<const float*>(sP + TP::at(it, j >> 4, (j & 15) >> 2, l16) +
+                                                         (j & 3) * (int)sizeof(T))
+                       : 0.0f;
+            }
             o = X::mfma(Vop[js], Bp, o);
           }
         }
         // store: lane holds O[token i][v0 .. v0+3]
         if (c * CH + i < len) {
-          T* orow = Og + row_of(t0 + c * CH + i) * D + col + 4 * g;
+          T* orow = Oseq + (ooff0[it] + (unsigned)(c * (cstride_b / (int)sizeof(T))));
           T ov[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) ov[r] = X::from_f(o[r]);
