@@ -102,18 +102,22 @@ __device__ inline void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// LDS address (byte offset in the workgroup's LDS) of a pointer into a
+// __shared__ array.
+__device__ inline unsigned lds_address(const void* p) {
+  return (unsigned)(size_t)(const __attribute__((address_space(3))) char*)p;
+}
+
 // 16 bytes per lane from global memory straight into LDS: lane l reads
 // sbase + voff (sbase wave-uniform, voff a 32-bit byte offset) and its bytes
-// land at lds_block + 16 l (lds_block wave-uniform; M0 holds it).
+// land at LDS address lds + 16 l (lds wave-uniform; M0 holds it).
 // Issued as inline asm so that the compiler does not treat later
 // transposing LDS reads as aliasing an in-flight load and wait for every
 // outstanding load before them: completion is waited for explicitly
 // (wait_vm_barrier) before a chunk is read.
-__device__ inline void dma16(const void* sbase, unsigned voff, char* lds_block) {
-  const unsigned lds = __builtin_amdgcn_readfirstlane(
-      (unsigned)(size_t)(__attribute__((address_space(3))) char*)lds_block);
+__device__ inline void dma16(const void* sbase, unsigned voff, unsigned lds) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
-               "s"(lds)
+               "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory", "m0");
 }
 

@@ -139,8 +139,9 @@ __global__ __launch_bounds__((FwdLayout<T, D, WITH_O>::NT),
   const float lg = log2f(a.lam[h]);
   const int64_t t0 = (int64_t)p * a.Lp;
   const int64_t t1 = (t0 + a.Lp < a.Ls) ? t0 + a.Lp : a.Ls;
-  const int64_t len = (t1 > t0) ? t1 - t0 : 0;
-  const int64_t nch = (len + CH - 1) / CH;
+  // (a sub-segment's tokens fit in int: one sequence spans under 4 GiB)
+  const int len = (int)((t1 > t0) ? t1 - t0 : 0);
+  const int nch = (len + CH - 1) / CH;
 
   // Rows of sequence n are addressed relative to its first row (byte offsets
   // within one sequence fit in 32 bits; the host checks that).  relrow(tt)
@@ -171,25 +172,36 @@ __global__ __launch_bounds__((FwdLayout<T, D, WITH_O>::NT),
     const int piece = (pc == G - 1) ? 0 : pc;
     voff0[q] = (unsigned)((relrow(row) * D + piece * EP) * (int64_t)sizeof(T));
   }
-  auto issue = [&](int64_t c) {
-    const int sb = (int)(c % S) * LY::STAGE;
+  // wave-uniform per load: source tensor and LDS destination within a stage
+  const T* src_of[LPC_HI];
+  unsigned dst_of[LPC_HI];
+  const unsigned smem_lds = lds_address(smem);
+#pragma unroll
+  for (int q = 0; q < LPC_HI; ++q) {
+    const int bb = blk_of(q);
+    src_of[q] = tensor_base(bb / G);
+    dst_of[q] = smem_lds + (unsigned)((bb / G) * TB + (bb % G) * 1024);
+  }
+  // chunk c into stage `stage`; offsets wrap modulo 2^32 like the byte
+  // offsets they stand for (the host keeps one sequence below 4 GiB)
+  auto issue = [&](int c, int stage) {
+    const unsigned sb = (unsigned)(stage * LY::STAGE);
     const bool full = (c + 1) * CH <= len;
 #pragma unroll
     for (int q = 0; q < LPC_HI; ++q) {
       if (q < LPC_HI - 1 || lpc_hi) {
-        const int bb = blk_of(q);
-        const int ten = bb / G;
         unsigned voff;
         if (full) {
-          voff = voff0[q] + (unsigned)(c * cstride_b);
+          voff = voff0[q] + (unsigned)c * (unsigned)cstride_b;
         } else {
+          const int bb = blk_of(q);
           const int pos = 64 * (bb % G) + lane;
           const int row = pos / G, pc = pos % G;
           const int piece = (pc == G - 1) ? 0 : pc;
-          const int64_t tt = (c * CH + row < len) ? c * CH + row : len - 1;
+          const int tt = (c * CH + row < len) ? c * CH + row : len - 1;
           voff = (unsigned)((relrow(tt) * D + piece * EP) * (int64_t)sizeof(T));
         }
-        dma16(tensor_base(ten), voff, smem + sb + ten * TB + (bb % G) * 1024);
+        dma16(src_of[q], voff, dst_of[q] + sb);
       }
     }
   };
@@ -217,7 +229,7 @@ __global__ __launch_bounds__((FwdLayout<T, D, WITH_O>::NT),
 
   // first chunks in flight while the factors are computed
   for (int pc = 0; pc < S - 1; ++pc)
-    if (pc < nch) issue(pc);
+    if (pc < nch) issue(pc, pc);
 
   // ---- factors
   float qf[4];        // lambda^(i+1) for the lane's query i of each 16-row block
@@ -260,22 +272,26 @@ __global__ __launch_bounds__((FwdLayout<T, D, WITH_O>::NT),
   };
   set_wv(CH);
 
-  for (int64_t c = 0; c < nch; ++c) {
-    const int cl = (int)((len - c * CH < CH) ? (len - c * CH) : CH);
+  int st = 0;             // stage holding chunk c
+  int st_next = S - 1;    // stage for chunk c + S - 1 (the one chunk c - 1 used)
+  for (int c = 0; c < nch; ++c) {
+    const int cl = (len - c * CH < CH) ? (len - c * CH) : CH;
     if constexpr (S == 1) {
       lds_barrier();  // the previous chunk's LDS reads are done
-      issue(c);
+      issue(c, 0);
       wait_vm_barrier<0>();
     } else {
-      const int64_t later = (nch - 1 - c < S - 2) ? nch - 1 - c : S - 2;
-      wait_chunk<LPC_HI, S - 2>(lpc_hi, (int)later);  // chunk c landed; chunk c-1 consumed
-      if (c + S - 1 < nch) issue(c + S - 1);             // into the stage chunk c-1 used
+      const int later = (nch - 1 - c < S - 2) ? nch - 1 - c : S - 2;
+      wait_chunk<LPC_HI, S - 2>(lpc_hi, later);  // chunk c landed; chunk c-1 consumed
+      if (c + S - 1 < nch) issue(c + S - 1, st_next);
+      st_next = (st_next + 1 == S) ? 0 : st_next + 1;
     }
     if (cl != CH) {
       set_wv(cl);
       if (WITH_O) set_pf(cl);
     }
-    const char* const stage = smem + (int)(c % S) * LY::STAGE;
+    const char* const stage = smem + st * LY::STAGE;
+    st = (st + 1 == S) ? 0 : st + 1;
     const char* const sQ = stage;
     const char* const sK = stage + (WITH_O ? TB : 0);
     const char* const sV = sK + TB;
@@ -378,11 +394,14 @@ __global__ __launch_bounds__((FwdLayout<T, D, WITH_O>::NT),
         }
         // store: lane holds O[token i][v0 .. v0+3]
         if (c * CH + i < len) {
-          T* orow = Oseq + (ooff0[it] + (unsigned)(c * (cstride_b / (int)sizeof(T))));
+          T* orow = Oseq + (ooff0[it] + (unsigned)c * (unsigned)(cstride_b / (int)sizeof(T)));
           T ov[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) ov[r] = X::from_f(o[r]);
           if (sizeof(T) == 2)
+            // (a plain store: each instruction writes 32-byte pieces of 16
+            // rows whose other pieces come from the other waves, and L2 merges
+            // them; non-temporal stores measured far slower here)
             *reinterpret_cast<u32x2*>(orow) = *reinterpret_cast<u32x2*>(ov);
           else
             *reinterpret_cast<u32x4*>(orow) = *reinterpret_cast<u32x4*>(ov);

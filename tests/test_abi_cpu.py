@@ -67,10 +67,23 @@ def _shape(**kw):
     (dict(dk=64, dv=128), la.LA_ERR_UNSUPPORTED),
     (dict(dk=96, dv=96), la.LA_ERR_UNSUPPORTED),
     (dict(dk=256, dv=256), la.LA_ERR_UNSUPPORTED),
+    # one segment of 2^24 tokens x 128 bf16 = 2^32 bytes: beyond 32-bit offsets
+    (dict(L=1 << 24, dk=128, dv=128), la.LA_ERR_UNSUPPORTED),
+    (dict(L=1 << 23, dk=128, dv=128, dtype=la.LA_FP32), la.LA_ERR_UNSUPPORTED),
 ])
 def test_fwd_rejects_bad_shapes(kw, code):
     assert _fwd(_shape(**kw)) == code
     assert la.lib().la_last_error().decode().startswith(la.lib().la_status_str(code).decode())
+
+
+def test_segment_size_limit_counts_one_segment():
+    # Host-side query only: a valid shape with split=2 needs a workspace, a
+    # rejected one reports 0.  2^24 tokens of d=128 bf16 in one segment is
+    # 2^32 bytes (rejected); the same tokens as two segments, or one chunk
+    # fewer, are accepted.
+    assert la.la_fwd_workspace_bytes(_shape(L=1 << 24, dk=128, dv=128, split=2)) == 0
+    assert la.la_fwd_workspace_bytes(_shape(L=1 << 24, dk=128, dv=128, nseg=2, split=2)) > 0
+    assert la.la_fwd_workspace_bytes(_shape(L=(1 << 24) - 64, dk=128, dv=128, split=2)) > 0
 
 
 def test_fwd_rejects_reserved_field():
