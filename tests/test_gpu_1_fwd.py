@@ -45,6 +45,9 @@ CASES = [
     ("fp32", 128, 1, 2, 200, 1, 2, 0.5, "schedule"),
     ("fp32", 128, 1, 1, 64, 1, 0, 0.5, "fast"),
     ("bf16", 128, 1, 1, 1, 1, 0, 0.5, "fast"),
+    # 32 sequences of 72 (73) chunks: 8 sub-segments of 9 (10) chunks each
+    ("bf16", 128, 2, 16, 64 * 72, 1, 0, 0.5, "schedule"),
+    ("fp32", 64, 1, 32, 64 * 72 + 17, 1, 0, 0.5, "fast"),
 ]
 
 
