@@ -45,6 +45,28 @@ def alg_flops(B, H, L, d):
     return B * H * L * (4 * d * d + (CHUNK + 1) * 2 * d)
 
 
+def measured_traffic():
+    """HBM bytes per launch of the main chunk kernel from the committed
+    FETCH_SIZE / WRITE_SIZE profile, or None once the kernel sources differ
+    from the ones profiled (SHA-256 over the csrc files in name order, each
+    name followed by its bytes)."""
+    import hashlib
+    import re
+    prof = os.path.join(ROOT, "profiles", "k_chunk_fwd_segment_64k_hbm_bytes.md")
+    try:
+        m = re.search(r"```json\n(\{.*?\})\n```", open(prof).read(), re.S)
+        rec = json.loads(m.group(1))
+    except (OSError, AttributeError, ValueError):
+        return None
+    src = os.path.join(ROOT, "long_sequence_causal_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(src)):
+        h.update(name.encode())
+        with open(os.path.join(src, name), "rb") as f:
+            h.update(f.read())
+    return rec["traffic_bytes"] if h.hexdigest() == rec.get("sources_sha256") else None
+
+
 def time_events(fn, iters, stream):
     import torch
 
@@ -59,13 +81,13 @@ def time_events(fn, iters, stream):
 
 
 def cpu_baseline(inp, H, L, d):
-    """The CPU oracle (fp64 token recurrence, OpenMP) on a bounded sample of
-    the same workload: every head, the first `T` tokens, with S0.  Scaled to
-    tokens/s of the full workload (a token counts once, across all heads)."""
+    """The CPU oracle (fp64 token recurrence, OpenMP) on the same workload:
+    every head, the first `T` tokens (default: all of them, about 1.5 s on 16
+    cores), with S0.  Tokens/s counts a token once, across all heads."""
     import numpy as np
     from oracle import lao
 
-    T = int(os.environ.get("LA_BENCH_CPU_TOKENS", "32768"))
+    T = int(os.environ.get("LA_BENCH_CPU_TOKENS", str(L)))
     T = min(T, L)
 
     def f64(t):
@@ -169,6 +191,7 @@ def main():
     else:
         main_ms = ms_ev
 
+    traffic = measured_traffic()
     nbytes = alg_bytes(B, H, L, d)
     flops = alg_flops(B, H, L, d)
     t = ms_ev / 1e3
@@ -192,7 +215,7 @@ def main():
         "tflops_alg": flops / t / 1e12,
         "frac_hbm_whole_op": nbytes / t / 1e9 / HBM_PEAK_GBS,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "k_chunk_fwd<bf16,128,with O>",
                      "alg_bytes_per_launch": nbytes, "kernel_us": main_ms * 1e3},
     }
