@@ -1,0 +1,437 @@
+// la_walk.h -- one workgroup walking the 64-token chunks of a range of one
+// sequence: the chunk pipeline and per-chunk arithmetic shared by the chunk
+// kernels.
+//
+// Per chunk c with tokens i, j = 0..cl-1 (cl = 64 except for a ragged tail),
+// decay lambda and S the state before the chunk:
+//
+//   P[i][j]   = lambda^(i-j) (q_i . k_j)  for j <= i, else 0     (intra scores)
+//   o_i       = lambda^(i+1) q_i^T S  +  sum_j P[i][j] v_j          (output)
+//   S        <- lambda^cl S + sum_j k_j (lambda^(cl-1-j) v_j)^T     (state)
+//
+// which is the token recurrence S_t = lambda S_{t-1} + k_t v_t^T,
+// o_t = q_t^T S_t regrouped: exact attention inside a chunk and the state
+// between chunks (the Lightning Attention-2 split named in the LASP-2 page's
+// related-paper list), with the state evaluated right-product-first (LASP-2
+// abstract).  Only non-negative powers of lambda are formed, so nothing
+// overflows however long the sequence.
+//
+// Work split inside the workgroup (wave w of NW = D/16):
+//   * intra scores: the 10 non-zero 16x16 tiles of P^T = K Q^T are dealt
+//     round-robin to the waves and written to LDS as P[i][j];
+//   * wave w owns state columns v in [16 w, 16 w + 16): its slice of S stays
+//     in registers, serves directly (rounded to bf16) as the A operand of
+//     O^T = S^T Q^T, and is updated by S += K^T (diag(lambda^(cl-1-j)) V);
+//   * outputs are produced as O^T tiles so each lane ends up with 4
+//     consecutive v of one token: one 8-byte (bf16) store per tile.
+//
+// Memory pipeline: Q, K, V chunks go from HBM straight into LDS (16 bytes
+// per lane, no register staging) through STAGES buffers, so STAGES-1 chunks
+// are in flight while one is computed.  LDS holds only token-major tiles
+// (rows padded to an odd number of 16-byte granules; each lane's 16 B of a
+// load land where its row and piece put them) plus P; operands that contract
+// over tokens (K^T, V^T) use the gfx950 transposing LDS read, so no
+// transposed copy is ever written.  Token and feature orders inside the MFMA
+// steps are chosen so that no LDS access has a bank conflict.  A
+// ragged tail loads clamped (valid, finite) rows past the end and masks them
+// out through the decay factors.  Two barriers per chunk, without fences:
+// waits are explicit.
+#pragma once
+
+#include "la_device.h"
+
+namespace la {
+
+
+// The 10 lower-triangular (key block jb <= query block ib) tiles of the
+// 64x64 score matrix, dealt round-robin to the waves.
+__device__ inline void score_tile(int idx, int& jb, int& ib) {
+  if (idx < 4) { jb = idx; ib = idx; }
+  else if (idx < 7) { jb = idx - 4; ib = idx - 3; }
+  else if (idx < 9) { jb = idx - 7; ib = idx - 5; }
+  else { jb = 0; ib = 3; }
+}
+
+constexpr int LDS_MAX = 160 * 1024;  // per workgroup on gfx950
+
+// LDS of a workgroup: STAGES stages of NSLOT token-major tiles (Q, K, V when
+// NSLOT = 3, K, V when NSLOT = 2), plus P when NSLOT = 3.
+template <typename T, int D, int NSLOT>
+struct FwdLayout {
+  typedef PadTile<T, CH, D> TN;                // Q, K, V token-major [token][d]
+  typedef PBlocks<T> TP;                       // P, its 10 nonzero 16x16 blocks
+  static constexpr int NTEN = NSLOT;           // tensor tiles per stage
+  static constexpr int TB = TN::BYTES;         // one tensor tile
+  static constexpr int STAGE = NTEN * TB;
+  static constexpr int PBYTES = NSLOT == 3 ? TP::BYTES : 0;
+  static constexpr int SMAX = NSLOT == 3 ? 3 : 5;
+  static constexpr int SFIT = (LDS_MAX - PBYTES) / STAGE;
+  static constexpr int STAGES = SFIT < SMAX ? SFIT : SMAX;
+  static constexpr int OFF_P = STAGES * STAGE;
+  static constexpr int BYTES = OFF_P + PBYTES;
+  static constexpr int NW = D / 16;  // waves: one per 16 state columns
+  static constexpr int NT = 64 * NW;
+  // bf16 keeps two waves per SIMD (256 registers per lane)
+  static constexpr int WAVES_PER_EU = sizeof(T) == 2 ? 2 : 1;
+  static_assert(STAGES >= 1 && STAGES <= 5 && BYTES <= LDS_MAX, "LDS budget");
+  static_assert(TB == TN::G * 1024, "a tile is G loads of 1 KiB");
+};
+
+// wait until chunk c's loads have landed (loads of `later` younger chunks,
+// LPC per chunk, may still be in flight), then barrier
+template <int LPC, int MAXLATER>
+__device__ inline void wait_chunk_n(int later) {
+  if constexpr (MAXLATER >= 3) {
+    if (later >= 3) { wait_vm_barrier<3 * LPC>(); return; }
+  }
+  if constexpr (MAXLATER >= 2) {
+    if (later >= 2) { wait_vm_barrier<2 * LPC>(); return; }
+  }
+  if constexpr (MAXLATER >= 1) {
+    if (later >= 1) { wait_vm_barrier<LPC>(); return; }
+  }
+  wait_vm_barrier<0>();
+}
+template <int LPC_HI, int MAXLATER>
+__device__ inline void wait_chunk(bool hi, int later) {
+  if (hi || LPC_HI == 1)
+    wait_chunk_n<LPC_HI, MAXLATER>(later);
+  else
+    wait_chunk_n<(LPC_HI > 1 ? LPC_HI - 1 : 1), MAXLATER>(later);
+}
+
+
+// A range of one sequence for walk(): positions t0 .. t0+len-1 (position tt
+// is row tt, or row Ls-1-tt when reverse), all pointers at the sequence's
+// first row.
+struct WalkJob {
+  const void* Q;  // read only when outputs are formed
+  const void* K;
+  const void* V;
+  void* O;        // written when outputs are formed
+  int64_t t0;
+  int len;        // positions; fits in int (one sequence spans under 4 GiB)
+  int64_t Ls;
+  int reverse;
+  float lg;       // log2 lambda
+};
+
+// Walk the range with the state in accS (wave w: columns [16 w, 16 w + 16),
+// accumulator tile tk holds rows 16 tk + 4 g + r); accS ends as the state
+// after the range.  OUT: also form and store the outputs.  NSLOT: tiles per
+// LDS stage of the caller's layout (the K, V slots are the last two).  All
+// of the workgroup's threads call it; LDS is free again on return.
+template <typename T, int D, bool OUT, int NSLOT>
+__device__ __forceinline__ void walk(char* smem, const WalkJob& jb, f32x4 (&accS)[D / 16]) {
+  typedef Elt<T> X;
+  typedef typename X::op_t op_t;
+  typedef FwdLayout<T, D, NSLOT> LY;
+  static_assert(NSLOT == 3 || !OUT, "outputs need the Q slot and P");
+  typedef typename LY::TN TN;
+  typedef typename LY::TP TP;
+  constexpr int E = X::E;           // operand elements per lane
+  constexpr int KS = 4 * E;         // MFMA contraction step
+  constexpr int NW = LY::NW;        // waves
+  constexpr int EP = 16 / (int)sizeof(T);  // elements per 16-byte piece
+  constexpr int NKT = D / 16;       // 16-high state-row tiles
+  constexpr int NST = (10 + NW - 1) / NW;  // score tiles per wave (at most)
+  constexpr int NKS = D / KS;       // contraction steps over d
+  constexpr int NJS = CH / KS;      // contraction steps over a chunk
+  constexpr int S = LY::STAGES;
+  constexpr int TB = LY::TB;
+  constexpr int G = TN::G;
+  // one chunk is NLOAD * G loads of 1 KiB (64 lanes x 16 B) into slots
+  // SLOT0..; wave w issues loads w, w + NW, ...: LPC_HI or LPC_HI - 1 of them
+  constexpr int NLOAD = OUT ? 3 : 2;
+  constexpr int SLOT0 = NSLOT - NLOAD;
+  constexpr int NBLK = NLOAD * G;
+  constexpr int LPC_HI = (NBLK + NW - 1) / NW;
+  char* const sP = smem + LY::OFF_P;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15;
+  const int g = lane >> 4;
+  const int col = 16 * w;  // this wave's state columns [col, col + 16)
+
+  const float lg = jb.lg;
+  const int64_t t0 = jb.t0;
+  const int len = jb.len;
+  const int nch = (len + CH - 1) / CH;
+
+  // Rows of sequence n are addressed relative to its first row (byte offsets
+  // within one sequence fit in 32 bits; the host checks that).  relrow(tt)
+  // is the row of position tt of this sub-segment; consecutive chunks are
+  // `dir * CH` rows apart.
+  auto relrow = [&](int64_t tt) -> int64_t { return jb.reverse ? (jb.Ls - 1 - (t0 + tt)) : (t0 + tt); };
+  const int cstride_b = (jb.reverse ? -1 : 1) * CH * D * (int)sizeof(T);  // bytes per chunk
+
+  // ---- chunk loads: HBM -> LDS, 1 KiB (64 lanes x 16 B) per instruction.
+  // Load b of a chunk fills granules 64 (b % G) .. + 63 of tensor b / G's
+  // tile; lane l's granule is (row, piece) = divmod(64 (b % G) + l, G), the
+  // last piece of a row being padding (it loads the row's first piece).
+  // Offsets of chunk 0 are precomputed; a ragged last chunk clamps rows past
+  // the end to the last valid token.
+  const bool lpc_hi = (w < NBLK - (LPC_HI - 1) * NW);
+  auto blk_of = [&](int q) { const int bq = w + NW * q; return bq < NBLK ? bq : 0; };
+  auto tensor_base = [&](int ten) -> const T* {
+    const void* bp = OUT ? (ten == 0 ? jb.Q : (ten == 1 ? jb.K : jb.V)) : (ten == 0 ? jb.K : jb.V);
+    return reinterpret_cast<const T*>(bp);
+  };
+  unsigned voff0[LPC_HI];  // chunk-0 byte offset of this lane's piece, per load
+#pragma unroll
+  for (int q = 0; q < LPC_HI; ++q) {
+    const int bb = blk_of(q);
+    const int pos = 64 * (bb % G) + lane;
+    const int row = pos / G, pc = pos % G;
+    const int piece = (pc == G - 1) ? 0 : pc;
+    voff0[q] = (unsigned)((relrow(row) * D + piece * EP) * (int64_t)sizeof(T));
+  }
+  // wave-uniform per load: source tensor and LDS destination within a stage
+  const T* src_of[LPC_HI];
+  unsigned dst_of[LPC_HI];
+  const unsigned smem_lds = lds_address(smem);
+#pragma unroll
+  for (int q = 0; q < LPC_HI; ++q) {
+    const int bb = blk_of(q);
+    src_of[q] = tensor_base(bb / G);
+    dst_of[q] = smem_lds + (unsigned)((SLOT0 + bb / G) * TB + (bb % G) * 1024);
+  }
+  // chunk c into stage `stage`; offsets wrap modulo 2^32 like the byte
+  // offsets they stand for (the host keeps one sequence below 4 GiB)
+  auto issue = [&](int c, int stage) {
+    const unsigned sb = (unsigned)(stage * LY::STAGE);
+    const bool full = (c + 1) * CH <= len;
+#pragma unroll
+    for (int q = 0; q < LPC_HI; ++q) {
+      if (q < LPC_HI - 1 || lpc_hi) {
+        unsigned voff;
+        if (full) {
+          voff = voff0[q] + (unsigned)c * (unsigned)cstride_b;
+        } else {
+          const int bb = blk_of(q);
+          const int pos = 64 * (bb % G) + lane;
+          const int row = pos / G, pc = pos % G;
+          const int piece = (pc == G - 1) ? 0 : pc;
+          const int tt = (c * CH + row < len) ? c * CH + row : len - 1;
+          voff = (unsigned)((relrow(tt) * D + piece * EP) * (int64_t)sizeof(T));
+        }
+        dma16(src_of[q], voff, dst_of[q] + sb);
+      }
+    }
+  };
+
+  // first chunks in flight while the factors are computed
+  for (int pc = 0; pc < S - 1; ++pc)
+    if (pc < nch) issue(pc, pc);
+
+  // ---- factors
+  float qf[4];        // lambda^(i+1) for the lane's query i of each 16-row block
+  float pf[NST][4];   // lambda^(i-j) (or 0) for the wave's score tiles
+  auto set_pf = [&](int cl) {
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      const int idx = w + NW * st;
+      int jb = 0, ib = 0;
+      if (idx < 10) score_tile(idx, jb, ib);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        // accumulator (row 4 g + r, column l16) of tile (jb, ib) holds P[i][j]
+        const int i = 16 * ib + perm16<T>(l16), j = 16 * jb + perm16<T>(4 * g + r);
+        pf[st][r] = (idx < 10 && j <= i && j < cl) ? pow_lam(lg, (float)(i - j)) : 0.0f;
+      }
+    }
+  };
+  T* const Oseq = reinterpret_cast<T*>(jb.O);  // sequence base of O
+  unsigned ooff0[4];  // element offset (chunk 0) of the lane's outputs in each 16-row block
+  if (OUT) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      qf[it] = pow_lam(lg, (float)(16 * it + l16 + 1));
+      ooff0[it] = (unsigned)(relrow(16 * it + l16) * D + col + 4 * g);
+    }
+    set_pf(CH);
+  }
+  const float lamC = pow_lam(lg, (float)CH);
+  // lambda^(cl-1-j) (0 past the tail) for the lane's contraction slots j of the update
+  float wv[NJS][E];
+  auto set_wv = [&](int cl) {
+#pragma unroll
+    for (int js = 0; js < NJS; ++js)
+#pragma unroll
+      for (int x = 0; x < E; ++x) {
+        const int j = slot_token<T>(js * KS, g, x);
+        wv[js][x] = (j < cl) ? pow_lam(lg, (float)(cl - 1 - j)) : 0.0f;
+      }
+  };
+  set_wv(CH);
+
+  int st = 0;             // stage holding chunk c
+  int st_next = S - 1;    // stage for chunk c + S - 1 (the one chunk c - 1 used)
+  for (int c = 0; c < nch; ++c) {
+    const int cl = (len - c * CH < CH) ? (len - c * CH) : CH;
+    if constexpr (S == 1) {
+      lds_barrier();  // the previous chunk's LDS reads are done
+      issue(c, 0);
+      wait_vm_barrier<0>();
+    } else {
+      const int later = (nch - 1 - c < S - 2) ? nch - 1 - c : S - 2;
+      wait_chunk<LPC_HI, S - 2>(lpc_hi, later);  // chunk c landed; chunk c-1 consumed
+      if (c + S - 1 < nch) issue(c + S - 1, st_next);
+      st_next = (st_next + 1 == S) ? 0 : st_next + 1;
+    }
+    if (cl != CH) {
+      set_wv(cl);
+      if (OUT) set_pf(cl);
+    }
+    const char* const stage = smem + st * LY::STAGE;
+    st = (st + 1 == S) ? 0 : st + 1;
+    const char* const sQ = stage;
+    const char* const sK = stage + (NSLOT == 3 ? TB : 0);
+    const char* const sV = sK + TB;
+
+    // V^T operands of this wave's columns (intra A operand; scaled: update B operand)
+    op_t Vop[NJS];
+#pragma unroll
+    for (int js = 0; js < NJS; ++js) Vop[js] = tr_op<T, TN>(sV, js * KS, col, lane);
+
+    if (OUT) {
+      // ---- intra scores: P^T tiles = K Q^T, masked and decayed, to LDS as P[i][j]
+#pragma unroll
+      for (int st = 0; st < NST; ++st) {
+        const int idx = w + NW * st;
+        if (idx < 10) {
+          int jb, ib;
+          score_tile(idx, jb, ib);
+          // operand row l16 is token perm16(l16) of the block; the
+          // contraction over d visits features in score_granule order
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          const int rk = 16 * jb + perm16<T>(l16), rq = 16 * ib + perm16<T>(l16);
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) {
+            const int f = (E == 8) ? 8 * score_granule<D>(ks, g) : ks * KS + g;
+            const op_t A = lds_op<T>(sK, TN::off(rk, f));
+            const op_t B = lds_op<T>(sQ, TN::off(rq, f));
+            acc = X::mfma(A, B, acc);
+          }
+          T pv[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) pv[r] = X::from_f(acc[r] * pf[st][r]);
+          // keys perm16(4 g + r), r = 0..3, form slab g; query row perm16(l16)
+          char* dst = sP + TP::at(ib, jb, g, perm16<T>(l16));
+          if (sizeof(T) == 2)
+            *reinterpret_cast<u32x2*>(dst) = *reinterpret_cast<u32x2*>(pv);
+          else
+            *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<u32x4*>(pv);
+        }
+      }
+      lds_barrier();  // P complete
+
+      // ---- state before this chunk as the A operand of O^T = S^T Q^T
+      op_t Sop[NKS];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        if constexpr (E == 8) {
+          bf16x8 o;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            o[r] = (__bf16)accS[2 * ks][r];
+            o[4 + r] = (__bf16)accS[2 * ks + 1][r];
+          }
+          Sop[ks] = o;
+        } else {
+          Sop[ks] = accS[ks / 4][ks % 4];
+        }
+      }
+
+      // ---- outputs, one 16-token block at a time
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int i = 16 * it + l16;
+        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+        // inter: sum_k S[k][v] q_i[k], with Q read in the permuted slot order
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          op_t B;
+          if constexpr (E == 8) {
+            const u32x2 lo = lds_read8(sQ + TN::off(i, 32 * ks + 4 * g));
+            const u32x2 hi = lds_read8(sQ + TN::off(i, 32 * ks + 16 + 4 * g));
+            const u32x4 both = {lo[0], lo[1], hi[0], hi[1]};
+            B = __builtin_bit_cast(bf16x8, both);
+          } else {
+            B = *reinterpret_cast<const float*>(sQ + TN::off(i, 16 * (ks / 4) + 4 * g + (ks % 4)));
+          }
+          o = X::mfma(Sop[ks], B, o);
+        }
+        o *= qf[it];
+        // intra: sum_j V^T[v][j] P[i][j] over key blocks jb <= it; slab g of
+        // a block holds exactly the keys of lane group g's slots
+#pragma unroll
+        for (int js = 0; js < NJS; ++js) {
+          if (js * KS < 16 * (it + 1)) {
+            op_t Bp;
+            if constexpr (E == 8) {
+              const u32x2 z = {0u, 0u};
+              const u32x2 lo = lds_read8(sP + TP::at(it, 2 * js, g, l16));
+              const u32x2 hi = (2 * js + 1 <= it) ? lds_read8(sP + TP::at(it, 2 * js + 1, g, l16)) : z;
+              const u32x4 both = {lo[0], lo[1], hi[0], hi[1]};
+              Bp = __builtin_bit_cast(bf16x8, both);
+            } else {
+              const int j = js * KS + g;
+              Bp = ((j >> 4) <= it)
+                       ? *reinterpret_cast<const float*>(sP + TP::at(it, j >> 4, (j & 15) >> 2, l16) +
+                                                         (j & 3) * (int)sizeof(T))
+                       : 0.0f;
+            }
+            o = X::mfma(Vop[js], Bp, o);
+          }
+        }
+        // store: lane holds O[token i][v0 .. v0+3]
+        if (c * CH + i < len) {
+          T* orow = Oseq + (ooff0[it] + (unsigned)c * (unsigned)(cstride_b / (int)sizeof(T)));
+          T ov[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ov[r] = X::from_f(o[r]);
+          if (sizeof(T) == 2)
+            // (a plain store: each instruction writes 32-byte pieces of 16
+            // rows whose other pieces come from the other waves, and L2 merges
+            // them; non-temporal stores measured far slower here)
+            *reinterpret_cast<u32x2*>(orow) = *reinterpret_cast<u32x2*>(ov);
+          else
+            *reinterpret_cast<u32x4*>(orow) = *reinterpret_cast<u32x4*>(ov);
+        }
+      }
+    }
+
+    // ---- state update: S = lambda^cl S + K^T (diag(lambda^(cl-1-j)) V)
+    {
+      const float dc = (cl == CH) ? lamC : pow_lam(lg, (float)cl);
+#pragma unroll
+      for (int tk = 0; tk < NKT; ++tk) accS[tk] *= dc;
+      op_t Bv[NJS];
+#pragma unroll
+      for (int js = 0; js < NJS; ++js) {
+        if constexpr (E == 8) {
+          bf16x8 b;
+#pragma unroll
+          for (int x = 0; x < 8; ++x) b[x] = (__bf16)((float)Vop[js][x] * wv[js][x]);
+          Bv[js] = b;
+        } else {
+          Bv[js] = Vop[js] * wv[js][0];
+        }
+      }
+#pragma unroll
+      for (int tk = 0; tk < NKT; ++tk)
+#pragma unroll
+        for (int js = 0; js < NJS; ++js) {
+          const op_t Ak = tr_op<T, TN>(sK, js * KS, 16 * tk, lane);
+          accS[tk] = X::mfma(Ak, Bv[js], accS[tk]);
+        }
+    }
+  }
+
+  lds_barrier();  // every wave is done with the last chunk's LDS
+}
+
+}  // namespace la
