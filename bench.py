@@ -67,6 +67,38 @@ def measured_traffic():
     return rec["traffic_bytes"] if h.hexdigest() == rec.get("sources_sha256") else None
 
 
+def backward_leg(torch, la, workload_inputs, WORKLOADS, dev, iters):
+    """la_chunk_bwd at the training workload (B=1, H=16, L=262144, d=128,
+    bf16; dO ~ N(0,1), S0 = dS_end = 0): time per call with events, against
+    the backward's algorithmic bytes (Q, K, V, dO read and dQ, dK, dV written
+    once: 7 d elements per token-head, plus the fp32 dS0 written)."""
+    w = WORKLOADS["train_256k"]
+    B, H, L, d = w.B, w.H, w.L, w.d
+    inp = workload_inputs(w.name, device=dev)
+    q, k, v, lam, dO = inp["q"], inp["k"], inp["v"], inp["lam"], inp["dO"]
+    S0, dSe = inp.get("S0"), inp.get("dS_end")
+    out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+           torch.empty((B, H, 1, d, d), dtype=torch.float32, device=dev))
+    shape = la.make_shape(B, H, L, d, d, 1, la.LA_BF16, 0)
+    ws = torch.empty(max(la.la_bwd_workspace_bytes(shape), 1), dtype=torch.uint8, device=dev)
+
+    def call():
+        la.la_chunk_bwd(q, k, v, lam, dO, S0=S0, dS_end=dSe, out=out, workspace=ws)
+
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    ms = time_events(call, iters, torch.cuda.current_stream())
+    nbytes = B * H * L * 7 * d * 2 + B * H * d * d * 4 * (1 + int(S0 is not None) + int(dSe is not None))
+    flops = B * H * L * 205440
+    t = ms / 1e3
+    rec = {"workload": w.name, "B": B, "H": H, "L": L, "d": d, "us_per_call": ms * 1e3,
+           "tokens_per_s": B * L / t, "alg_bytes": nbytes, "achieved_GBs": nbytes / t / 1e9,
+           "frac_hbm": nbytes / t / 1e9 / HBM_PEAK_GBS, "tflops_alg": flops / t / 1e12}
+    del inp, q, k, v, dO, out, ws
+    return rec
+
+
 def time_events(fn, iters, stream):
     import torch
 
@@ -115,6 +147,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--split", type=int, default=0, help="internal split (0 = library choice)")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward leg")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -219,6 +252,12 @@ def main():
                      "kernel": "k_chunk_fwd<bf16,128,with O>",
                      "alg_bytes_per_launch": nbytes, "kernel_us": main_ms * 1e3},
     }
+    if not args.no_bwd:
+        del O, ws
+        bw = backward_leg(torch, la, workload_inputs, WORKLOADS, dev, max(3, args.steps // 5))
+        eprint(f"[bench] backward ({bw['workload']}): {bw['us_per_call']:.1f} us/call, "
+               f"{bw['achieved_GBs']:.0f} GB/s algorithmic")
+        rec["backward"] = bw
     if not args.no_cpu:
         eprint("[bench] CPU oracle baseline ...")
         rec["cpu_baseline"] = cpu_baseline(inp, H, L, d)

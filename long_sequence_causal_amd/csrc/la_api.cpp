@@ -107,13 +107,9 @@ la_status hip_fail(hipError_t e, const char* what) {
   return fail(LA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// One forward recurrence over nseq sequences (optionally in reverse time):
-// pre-pass + scan when split > 1, then the main pass.  `start` [nseq][D][D]
-// may be null (zero).  O may be null (state only); Send may be null.
-la_status run_flow(const Plan& pl, int dtype, int H, int nseg, const void* Q, const void* K,
-                   const void* V, const float* lam, const float* start, void* O, float* Send,
-                   float* W, int reverse, hipStream_t st) {
-  if (pl.nseq == 0 || (!O && !Send)) return LA_OK;
+// Arguments of the chunk kernel shared by every launch of one recurrence.
+la::FwdArgs flow_args(const Plan& pl, int H, int nseg, const void* Q, const void* K, const void* V,
+                      const float* lam, int reverse) {
   la::FwdArgs fa;
   std::memset(&fa, 0, sizeof(fa));
   fa.Q = Q;
@@ -126,36 +122,53 @@ la_status run_flow(const Plan& pl, int dtype, int H, int nseg, const void* Q, co
   fa.Lp = pl.Lp;
   fa.split = pl.split;
   fa.reverse = reverse;
-  hipError_t e;
-  if (pl.split > 1) {
-    la::FwdArgs pa = fa;
-    pa.p_begin = 0;
-    pa.p_count = pl.split - 1;
-    pa.start_from_state = 0;
-    pa.Sout = W;
-    pa.sout_p0 = 0;
-    pa.sout_np = pl.split - 1;
-    e = la::launch_fwd(pa, dtype, pl.D, false, pl.nseq * (pl.split - 1), st);
-    if (e != hipSuccess) return hip_fail(e, "state pre-pass launch");
-    la::ScanArgs sa;
-    std::memset(&sa, 0, sizeof(sa));
-    sa.nseq = pl.nseq;
-    sa.P = pl.split - 1;
-    sa.E = (int64_t)pl.D * pl.D;
-    sa.dS = W;
-    sa.lam = lam;
-    sa.H = H;
-    sa.hdiv = nseg;
-    sa.seg_len = pl.Lp;
-    sa.S0 = start;
-    sa.Sout = W;
-    sa.Send = nullptr;
-    sa.reverse = 0;
-    sa.inclusive = 1;
-    e = la::launch_scan(sa, st);
-    if (e != hipSuccess) return hip_fail(e, "state scan launch");
-  }
-  la::FwdArgs ma = fa;
+  return fa;
+}
+
+// Start states of sub-segments 1..split-1 of one recurrence into W
+// ([nseq][split-1][D][D]): state-only pre-pass over sub-segments
+// 0..split-2 from zero, then an inclusive scan seeded with `start` (null =
+// zero).  Nothing to do when split == 1.
+la_status run_states(const Plan& pl, int dtype, int H, int nseg, const void* K, const void* V,
+                     const float* lam, const float* start, float* W, int reverse, hipStream_t st) {
+  if (pl.nseq == 0 || pl.split <= 1) return LA_OK;
+  la::FwdArgs pa = flow_args(pl, H, nseg, nullptr, K, V, lam, reverse);
+  pa.p_begin = 0;
+  pa.p_count = pl.split - 1;
+  pa.start_from_state = 0;
+  pa.Sout = W;
+  pa.sout_p0 = 0;
+  pa.sout_np = pl.split - 1;
+  hipError_t e = la::launch_fwd(pa, dtype, pl.D, false, pl.nseq * (pl.split - 1), st);
+  if (e != hipSuccess) return hip_fail(e, "state pre-pass launch");
+  la::ScanArgs sa;
+  std::memset(&sa, 0, sizeof(sa));
+  sa.nseq = pl.nseq;
+  sa.P = pl.split - 1;
+  sa.E = (int64_t)pl.D * pl.D;
+  sa.dS = W;
+  sa.lam = lam;
+  sa.H = H;
+  sa.hdiv = nseg;
+  sa.seg_len = pl.Lp;
+  sa.S0 = start;
+  sa.Sout = W;
+  sa.Send = nullptr;
+  sa.reverse = 0;
+  sa.inclusive = 1;
+  e = la::launch_scan(sa, st);
+  if (e != hipSuccess) return hip_fail(e, "state scan launch");
+  return LA_OK;
+}
+
+// The chunk kernel over every sub-segment from its start state (`start` for
+// sub-segment 0, W for the others), writing O and/or Send.  With O null only
+// the last sub-segment runs (state only).
+la_status run_main(const Plan& pl, int dtype, int H, int nseg, const void* Q, const void* K,
+                   const void* V, const float* lam, const float* start, void* O, float* Send,
+                   const float* W, int reverse, hipStream_t st) {
+  if (pl.nseq == 0 || (!O && !Send)) return LA_OK;
+  la::FwdArgs ma = flow_args(pl, H, nseg, Q, K, V, lam, reverse);
   ma.start_from_state = 1;
   ma.S0 = start;
   ma.Sws = W;
@@ -170,9 +183,21 @@ la_status run_flow(const Plan& pl, int dtype, int H, int nseg, const void* Q, co
     ma.p_begin = pl.split - 1;
     ma.p_count = 1;
   }
-  e = la::launch_fwd(ma, dtype, pl.D, O != nullptr, pl.nseq * ma.p_count, st);
+  hipError_t e = la::launch_fwd(ma, dtype, pl.D, O != nullptr, pl.nseq * ma.p_count, st);
   if (e != hipSuccess) return hip_fail(e, "chunk kernel launch");
   return LA_OK;
+}
+
+// One forward recurrence over nseq sequences (optionally in reverse time):
+// start states when split > 1, then the main pass.  `start` [nseq][D][D]
+// may be null (zero).  O may be null (state only); Send may be null.
+la_status run_flow(const Plan& pl, int dtype, int H, int nseg, const void* Q, const void* K,
+                   const void* V, const float* lam, const float* start, void* O, float* Send,
+                   float* W, int reverse, hipStream_t st) {
+  if (pl.nseq == 0 || (!O && !Send)) return LA_OK;
+  la_status r = run_states(pl, dtype, H, nseg, K, V, lam, start, W, reverse, st);
+  if (r != LA_OK) return r;
+  return run_main(pl, dtype, H, nseg, Q, K, V, lam, start, O, Send, W, reverse, st);
 }
 
 }  // namespace
@@ -333,6 +358,14 @@ la_status la_chunk_bwd(const la_shape* s, const void* Q, const void* K, const vo
   }
   r = run_flow(pl, s->dtype, H, s->nseg, K, Q, dO, lambda, start, dV, dS0, W, 1, st);
   if (r != LA_OK) return r;
+  // The dK recurrence below runs over the same pairs (q_t, dO_t) with the
+  // roles swapped and is seeded with the transposed seed, so its sub-segment
+  // start states are the transposes of the ones just used: transpose W in
+  // place instead of a second pre-pass and scan.
+  if (pl.split > 1) {
+    e = la::launch_transpose(W, pl.nseq * (pl.split - 1), pl.D, st);
+    if (e != hipSuccess) return hip_fail(e, "transpose launch");
+  }
   if (dS0) {
     pa.src = dS0;
     pa.dst = dS0;
@@ -351,8 +384,7 @@ la_status la_chunk_bwd(const la_shape* s, const void* Q, const void* K, const vo
     if ((e = la::launch_prep(pa, st)) != hipSuccess) return hip_fail(e, "prep launch");
     start = A;
   }
-  r = run_flow(pl, s->dtype, H, s->nseg, V, dO, Q, lambda, start, dK, nullptr, W, 1, st);
-  return r;
+  return run_main(pl, s->dtype, H, s->nseg, V, dO, Q, lambda, start, dK, nullptr, W, 1, st);
 }
 
 }  // extern "C"

@@ -74,5 +74,7 @@ hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, bool with_o, int64_t n
                       hipStream_t stream);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
 hipError_t launch_prep(const PrepArgs& a, hipStream_t stream);
+// In-place transpose of nmat consecutive D x D fp32 matrices.
+hipError_t launch_transpose(float* W, int64_t nmat, int D, hipStream_t stream);
 
 }  // namespace la

@@ -48,6 +48,29 @@ __global__ __launch_bounds__(256) void k_prep_state(PrepArgs a) {
   a.dst[gid] = x;
 }
 
+// One thread per element (i, j) with i < j of a matrix swaps it with (j, i).
+__global__ __launch_bounds__(256) void k_transpose_inplace(float* W, int64_t nmat, int D) {
+  const int64_t DD = (int64_t)D * D;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= nmat * DD) return;
+  const int64_t m = gid / DD;
+  const int64_t e = gid - m * DD;
+  const int i = (int)(e / D), j = (int)(e % D);
+  if (i >= j) return;
+  float* M = W + m * DD;
+  const float x = M[(int64_t)i * D + j];
+  M[(int64_t)i * D + j] = M[(int64_t)j * D + i];
+  M[(int64_t)j * D + i] = x;
+}
+
+hipError_t launch_transpose(float* W, int64_t nmat, int D, hipStream_t s) {
+  const int64_t tot = nmat * (int64_t)D * D;
+  if (tot <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_transpose_inplace, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, W,
+                     nmat, D);
+  return hipGetLastError();
+}
+
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
   const int64_t tot = a.nseq * a.E;
   if (tot <= 0) return hipSuccess;

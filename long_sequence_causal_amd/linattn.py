@@ -170,8 +170,9 @@ def la_state_scan(dS, lam, seg_len: int, S0=None, reverse: bool = False, out=Non
 
 
 def la_chunk_bwd(q, k, v, lam, dO, S0=None, dS_end=None, nseg: int = 1,
-                 need_dS0: bool = True, split: int = 0, workspace=None):
-    """Backward pass.  Returns (dQ, dK, dV, dS0 or None)."""
+                 need_dS0: bool = True, split: int = 0, workspace=None, out=None):
+    """Backward pass.  Returns (dQ, dK, dV, dS0 or None).  `out`, if given, is
+    a (dQ, dK, dV, dS0-or-None) tuple of preallocated outputs."""
     B, H, L, dk = q.shape
     dv = v.shape[-1]
     dt = _dtype_code(q.dtype)
@@ -181,10 +182,18 @@ def la_chunk_bwd(q, k, v, lam, dO, S0=None, dS_end=None, nseg: int = 1,
     _need(S0, "S0", torch.float32)
     _need(dS_end, "dS_end", torch.float32)
     shape = make_shape(B, H, L, dk, dv, nseg, dt, split)
-    dQ = torch.empty_like(q)
-    dK = torch.empty_like(k)
-    dV = torch.empty_like(v)
-    dS0 = torch.empty((B, H, nseg, dk, dv), dtype=torch.float32, device=q.device) if need_dS0 else None
+    if out is not None:
+        dQ, dK, dV, dS0 = out
+        for t, ref, n in ((dQ, q, "dQ"), (dK, k, "dK"), (dV, v, "dV")):
+            _need(t, n, q.dtype)
+            if t.shape != ref.shape:
+                raise ValueError(f"{n} has shape {tuple(t.shape)}, expected {tuple(ref.shape)}")
+        _need(dS0, "dS0", torch.float32)
+    else:
+        dQ = torch.empty_like(q)
+        dK = torch.empty_like(k)
+        dV = torch.empty_like(v)
+        dS0 = torch.empty((B, H, nseg, dk, dv), dtype=torch.float32, device=q.device) if need_dS0 else None
     nbytes = la_bwd_workspace_bytes(shape)
     ws = workspace if workspace is not None else _workspace(nbytes, q.device)
     _check(lib().la_chunk_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(lam),
