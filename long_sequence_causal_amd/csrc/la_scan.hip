@@ -48,26 +48,40 @@ __global__ __launch_bounds__(256) void k_prep_state(PrepArgs a) {
   a.dst[gid] = x;
 }
 
-// One thread per element (i, j) with i < j of a matrix swaps it with (j, i).
-__global__ __launch_bounds__(256) void k_transpose_inplace(float* W, int64_t nmat, int D) {
-  const int64_t DD = (int64_t)D * D;
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gid >= nmat * DD) return;
-  const int64_t m = gid / DD;
-  const int64_t e = gid - m * DD;
-  const int i = (int)(e / D), j = (int)(e % D);
-  if (i >= j) return;
-  float* M = W + m * DD;
-  const float x = M[(int64_t)i * D + j];
-  M[(int64_t)i * D + j] = M[(int64_t)j * D + i];
-  M[(int64_t)j * D + i] = x;
+// In-place transpose of D x D matrices (D a multiple of 32) in 32 x 32
+// tiles: workgroup (m, pair) reads tiles (bi, bj) and (bj, bi), bi <= bj, of
+// matrix m into LDS and writes each back transposed into the other's place,
+// with every global access a coalesced row segment.
+__global__ __launch_bounds__(256) void k_transpose_inplace(float* W, int D) {
+  __shared__ float ta[32][33], tb[32][33];
+  const int nt = D / 32;
+  const int npair = nt * (nt + 1) / 2;
+  const int64_t m = blockIdx.x / npair;
+  int pr = (int)(blockIdx.x % npair);
+  int bi = 0;
+  while (pr >= nt - bi) {
+    pr -= nt - bi;
+    ++bi;
+  }
+  const int bj = bi + pr;
+  float* M = W + m * (int64_t)D * D;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  for (int r = ty; r < 32; r += 8) {
+    ta[r][tx] = M[(int64_t)(32 * bi + r) * D + 32 * bj + tx];
+    tb[r][tx] = M[(int64_t)(32 * bj + r) * D + 32 * bi + tx];
+  }
+  __syncthreads();
+  for (int r = ty; r < 32; r += 8) {
+    M[(int64_t)(32 * bj + r) * D + 32 * bi + tx] = ta[tx][r];
+    M[(int64_t)(32 * bi + r) * D + 32 * bj + tx] = tb[tx][r];
+  }
 }
 
 hipError_t launch_transpose(float* W, int64_t nmat, int D, hipStream_t s) {
-  const int64_t tot = nmat * (int64_t)D * D;
-  if (tot <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_transpose_inplace, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, W,
-                     nmat, D);
+  const int nt = D / 32;
+  const int64_t nwg = nmat * (nt * (nt + 1) / 2);
+  if (nwg <= 0 || D % 32 != 0) return nwg <= 0 ? hipSuccess : hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_transpose_inplace, dim3((unsigned)nwg), dim3(256), 0, s, W, D);
   return hipGetLastError();
 }
 
