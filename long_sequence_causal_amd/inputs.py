@@ -117,6 +117,21 @@ def make_inputs(B: int, H: int, L: int, dk: int, dv: int, *, dtype: str = "bf16"
             "dS_end": dS_end}
 
 
+def gate_logs(lam: torch.Tensor, B: int, L: int, seed: int, device="cpu") -> torch.Tensor:
+    """Seeded per-token log-gates g = log(alpha) [B, H, L] float32 for the
+    gated recurrence: g[b, h, t] = log(lam_h) * 2 sigmoid(z), z ~ N(0, 1) --
+    on average the head's fixed decay, varying per token within
+    (2 log lam_h, 0).  A separate generator stream (seed + 7919) leaves the
+    other inputs of a seed unchanged."""
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(int(seed) + 7919)
+    H = lam.numel()
+    z = torch.randn((B, H, L), generator=gen, device=dev, dtype=torch.float32)
+    loglam = torch.log(lam.to(dev, torch.float64)).to(torch.float32).view(1, H, 1)
+    return (loglam * (2.0 * torch.sigmoid(z))).contiguous()
+
+
 def workload_inputs(name: str, device="cpu", **over):
     """Inputs of a named workload (keyword overrides allowed, e.g. L=...)."""
     w = WORKLOADS[name]

@@ -352,6 +352,98 @@ int lao_scan(int64_t B, int64_t H, int64_t P, int64_t dk, int64_t dv,
   return LAO_OK;
 }
 
+/*
+ * Gated forward recurrence: the decay becomes a per-token, per-head scalar
+ * gate alpha_t = exp(g_t), g_t = log alpha_t <= 0,
+ *
+ *   S_t = alpha_t * S_{t-1} + k_t v_t^T        o_t = q_t^T S_t
+ *
+ * the data-dependent-gate generalisation named in the "Gated Linear Attention
+ * Transformers with Hardware-Efficient Training" entry of the LASP-2 page's
+ * related-paper list, in its plainest reading (one scalar gate per token and
+ * head; see the design notes).  G holds g in the token layout of Q without
+ * the feature axis: [B, H, L].  Everything else as lao_fwd.
+ */
+int lao_fwd_gated(int64_t B, int64_t H, int64_t L, int64_t dk, int64_t dv,
+                  int64_t nseg, const double* Q, const double* K, const double* V,
+                  const double* G, const double* S0, double* O, double* S_end) {
+  if (!lao_check(B, H, L, dk, dv, nseg)) return LAO_EINVAL;
+  const int64_t Ls = L / nseg;
+  const int64_t nseq = B * H * nseg;
+  const int64_t ncb = (dv + LAO_BLK - 1) / LAO_BLK;
+  int fail = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+  for (int64_t n = 0; n < nseq; ++n) {
+    for (int64_t cb = 0; cb < ncb; ++cb) {
+      const int64_t c0 = cb * LAO_BLK;
+      const int64_t c1 = (c0 + LAO_BLK < dv) ? c0 + LAO_BLK : dv;
+      const int64_t w = c1 - c0;
+      double* S = (double*)malloc(sizeof(double) * (size_t)(dk * w));
+      if (!S) {
+        fail = 1;
+        continue;
+      }
+      const double* s0 = S0 ? S0 + n * dk * dv : NULL;
+      for (int64_t i = 0; i < dk; ++i)
+        for (int64_t j = 0; j < w; ++j) S[i * w + j] = s0 ? s0[i * dv + c0 + j] : 0.0;
+      const double* q = Q + n * Ls * dk;
+      const double* k = K + n * Ls * dk;
+      const double* v = V + n * Ls * dv;
+      const double* g = G + n * Ls;
+      for (int64_t t = 0; t < Ls; ++t) {
+        /* S = alpha_t * S + k_t v_t^T */
+        const double a = exp(g[t]);
+        for (int64_t i = 0; i < dk; ++i) {
+          const double ki = k[t * dk + i];
+          for (int64_t j = 0; j < w; ++j)
+            S[i * w + j] = a * S[i * w + j] + ki * v[t * dv + c0 + j];
+        }
+        if (O) {
+          for (int64_t j = 0; j < w; ++j) {
+            double o = 0.0;
+            for (int64_t i = 0; i < dk; ++i) o += S[i * w + j] * q[t * dk + i];
+            O[(n * Ls + t) * dv + c0 + j] = o;
+          }
+        }
+      }
+      if (S_end)
+        for (int64_t i = 0; i < dk; ++i)
+          for (int64_t j = 0; j < w; ++j)
+            S_end[(n * dk + i) * dv + c0 + j] = S[i * w + j];
+      free(S);
+    }
+  }
+  return fail ? LAO_ENOMEM : LAO_OK;
+}
+
+/*
+ * Segment combine with a decay per segment: LD[b, h, s] is the log of the
+ * product of the gates over segment s, so
+ *   X = S0 (or 0)
+ *   for s in 0..P-1 (reverse: P-1..0):  S_start[s] = X;  X = exp(LD[s]) X + dS[s]
+ *   S_end = X
+ * (lao_scan with a = lambda^seg_len replaced by the segment's own product).
+ */
+int lao_scan_gated(int64_t B, int64_t H, int64_t P, int64_t dk, int64_t dv,
+                   const double* dS, const double* LD, const double* S0, double* S_start,
+                   double* S_end, int reverse) {
+  if (B < 0 || H < 0 || P < 0 || dk <= 0 || dv <= 0) return LAO_EINVAL;
+  const int64_t E = dk * dv;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t bh = 0; bh < B * H; ++bh) {
+    for (int64_t e = 0; e < E; ++e) {
+      double X = S0 ? S0[bh * E + e] : 0.0;
+      for (int64_t it = 0; it < P; ++it) {
+        const int64_t s = reverse ? (P - 1 - it) : it;
+        S_start[(bh * P + s) * E + e] = X;
+        X = exp(LD[bh * P + s]) * X + dS[(bh * P + s) * E + e];
+      }
+      if (S_end) S_end[bh * E + e] = X;
+    }
+  }
+  return LAO_OK;
+}
+
 int lao_abi_version(void) { return 1; }
 
 /* Number of OpenMP threads the oracle's parallel loops use. */

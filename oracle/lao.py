@@ -55,6 +55,10 @@ def bind(lib):
     lib.lao_bwd.restype = ctypes.c_int
     lib.lao_scan.argtypes = [i64] * 5 + [dp, dp, i64, dp, dp, dp, ctypes.c_int]
     lib.lao_scan.restype = ctypes.c_int
+    lib.lao_fwd_gated.argtypes = [i64] * 6 + [dp] * 7
+    lib.lao_fwd_gated.restype = ctypes.c_int
+    lib.lao_scan_gated.argtypes = [i64] * 5 + [dp] * 5 + [ctypes.c_int]
+    lib.lao_scan_gated.restype = ctypes.c_int
     lib.lao_threads.restype = ctypes.c_int
     lib.lao_threads.argtypes = []
     return lib
@@ -146,4 +150,37 @@ def scan(dS, lam, seg_len: int, S0=None, reverse: bool = False):
     rc = _load().lao_scan(B, H, P, dk, dv, _ptr(dS), _ptr(lam), int(seg_len),
                           _ptr(S0), _ptr(S_start), _ptr(S_end), int(bool(reverse)))
     _check(rc, "scan")
+    return S_start, S_end
+
+
+def fwd_gated(Q, K, V, G, S0=None, nseg: int = 1, need_O: bool = True):
+    """Gated token recurrence forward: S_t = exp(g_t) S_{t-1} + k_t v_t^T.
+
+    Q, K: [B,H,L,dk]; V: [B,H,L,dv]; G = log alpha: [B,H,L];
+    S0: [B,H,nseg,dk,dv] or None.  Returns (O or None, S_end [B,H,nseg,dk,dv]).
+    """
+    Q, K, V, G, S0 = map(_f64, (Q, K, V, G, S0))
+    B, H, L, dk = Q.shape
+    dv = V.shape[-1]
+    O = np.empty((B, H, L, dv)) if need_O else None
+    S_end = np.empty((B, H, nseg, dk, dv))
+    rc = _load().lao_fwd_gated(B, H, L, dk, dv, nseg, _ptr(Q), _ptr(K), _ptr(V),
+                               _ptr(G), _ptr(S0), _ptr(O), _ptr(S_end))
+    _check(rc, "fwd_gated")
+    return O, S_end
+
+
+def scan_gated(dS, LD, S0=None, reverse: bool = False):
+    """Segment combine with per-segment log decays LD [B,H,P].
+
+    dS: [B,H,P,dk,dv]; S0: [B,H,dk,dv] or None.
+    Returns (S_start [B,H,P,dk,dv], S_end [B,H,dk,dv]).
+    """
+    dS, LD, S0 = map(_f64, (dS, LD, S0))
+    B, H, P, dk, dv = dS.shape
+    S_start = np.empty_like(dS)
+    S_end = np.empty((B, H, dk, dv))
+    rc = _load().lao_scan_gated(B, H, P, dk, dv, _ptr(dS), _ptr(LD), _ptr(S0),
+                                _ptr(S_start), _ptr(S_end), int(bool(reverse)))
+    _check(rc, "scan_gated")
     return S_start, S_end

@@ -50,6 +50,25 @@ MUTATIONS = [
      "const double w0 = lao_pow(l, t + 1);",
      "const double w0 = lao_pow(l, t);",
      [pins.test_hand_example_rows]),
+    ("gate applied after the new token is added",
+     "S[i * w + j] = a * S[i * w + j] + ki * v[t * dv + c0 + j];",
+     "S[i * w + j] = a * (S[i * w + j] + ki * v[t * dv + c0 + j]);",
+     [pins.test_gated_hand_example,
+      lambda: pins.test_gated_recurrence_equals_quadratic_form(77, 16, 24)]),
+    ("initial state skipped in the gated recurrence",
+     "S[i * w + j] = s0 ? s0[i * dv + c0 + j] : 0.0;",
+     "S[i * w + j] = 0.0;",
+     [pins.test_gated_hand_example,
+      lambda: pins.test_gated_recurrence_equals_quadratic_form(77, 16, 24)]),
+    ("gate of the previous token",
+     "const double a = exp(g[t]);",
+     "const double a = exp(g[t > 0 ? t - 1 : 0]);",
+     [pins.test_gated_hand_example,
+      lambda: pins.test_gated_recurrence_equals_quadratic_form(300, 64, 64)]),
+    ("segment decay of the neighbouring segment in the gated scan",
+     "X = exp(LD[bh * P + s]) * X + dS[(bh * P + s) * E + e];",
+     "X = exp(LD[bh * P + (s + 1) % P]) * X + dS[(bh * P + s) * E + e];",
+     [pins.test_gated_hand_example_scan, pins.test_gated_segments_with_scanned_starts_equal_monolithic]),
 ]
 
 

@@ -380,3 +380,102 @@ def test_backward_zero_state_inputs():
     assert _rel(dK[0, 0], ((g @ v.T) * D).T @ q) < 1e-12
     assert _rel(dV[0, 0], ((q @ k.T) * D).T @ g) < 1e-12
     assert _rel(dS0[0, 0, 0], q.T @ ((0.9 ** t)[:, None] * g)) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# gated recurrence: S_t = alpha_t S_{t-1} + k_t v_t^T with a per-token gate
+
+
+def gated_quadratic_form(Q, K, V, G, S0):
+    """O and S_end of the gated recurrence in closed form (numpy matmul and
+    cumsum): with c_t = sum_{u<=t} g_u,
+      O = ((Q K^T) * D) V + diag(exp(c)) Q S0,   D_ts = exp(c_t - c_s) [s <= t]
+      S_end = exp(c_L) S0 + K^T diag(exp(c_L - c)) V."""
+    L = Q.shape[0]
+    c = np.cumsum(G)
+    Dm = np.tril(np.exp(c[:, None] - c[None, :]))
+    O = ((Q @ K.T) * Dm) @ V
+    S_end = np.zeros((K.shape[1], V.shape[1]))
+    if S0 is not None:
+        O = O + np.exp(c)[:, None] * (Q @ S0)
+        S_end = np.exp(c[-1]) * S0
+    S_end = S_end + K.T @ (np.exp(c[-1] - c)[:, None] * V) if L else S_end
+    return O, S_end
+
+
+def test_gated_hand_example():
+    g = json.load(open(os.path.join(GOLDEN, "hand_gated.json")))
+    Q = np.array(g["q"], float)[None, None]
+    K = np.array(g["k"], float)[None, None]
+    V = np.array(g["v"], float)[None, None]
+    S0 = np.array(g["S0"], float)[None, None, None]
+    G = np.log(np.array(g["alpha"], float))[None, None]
+    O, S_end = lao.fwd_gated(Q, K, V, G, S0=S0)
+    # exp(log(alpha)) may differ from alpha in the last bit
+    np.testing.assert_allclose(O[0, 0], np.array(g["O"], float), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(S_end[0, 0, 0], np.array(g["S_end"], float), rtol=0, atol=1e-14)
+
+
+def test_gated_hand_example_scan():
+    g = json.load(open(os.path.join(GOLDEN, "hand_gated.json")))["scan"]
+    dS = np.array(g["dS"], float).reshape(1, 1, 3, 1, 1)
+    LD = np.log(np.array(g["decay"], float)).reshape(1, 1, 3)
+    S0 = np.array([[[[g["S0"]]]]], float)
+    for key, rev in (("forward", False), ("reverse", True)):
+        st, en = lao.scan_gated(dS, LD, S0=S0, reverse=rev)
+        np.testing.assert_allclose(st.reshape(-1), np.array(g[key]["S_start"]), rtol=0, atol=1e-14)
+        assert abs(en.reshape(-1)[0] - g[key]["S_end"]) <= 1e-14
+
+
+@pytest.mark.parametrize("L,dk,dv", [(1, 4, 4), (77, 16, 24), (300, 64, 64)])
+def test_gated_recurrence_equals_quadratic_form(L, dk, dv):
+    rng = np.random.default_rng(100 + L)
+    Q, K, V = _rand(rng, 1, 2, L, dk), _rand(rng, 1, 2, L, dk), _rand(rng, 1, 2, L, dv)
+    G = -rng.uniform(0.0, 0.2, size=(1, 2, L))
+    S0 = _rand(rng, 1, 2, 1, dk, dv)
+    O, S_end = lao.fwd_gated(Q, K, V, G, S0=S0)
+    for h in range(2):
+        Or, Sr = gated_quadratic_form(Q[0, h], K[0, h], V[0, h], G[0, h], S0[0, h, 0])
+        assert _rel(O[0, h], Or) < 1e-12
+        assert _rel(S_end[0, h, 0], Sr) < 1e-12
+
+
+def test_gated_unit_gate_is_a_cumulative_sum():
+    rng = np.random.default_rng(7)
+    L, dk, dv = 200, 8, 5
+    Q, K, V = _rand(rng, 1, 1, L, dk), _rand(rng, 1, 1, L, dk), _rand(rng, 1, 1, L, dv)
+    S0 = _rand(rng, 1, 1, 1, dk, dv)
+    O, S_end = lao.fwd_gated(Q, K, V, np.zeros((1, 1, L)), S0=S0)
+    S = S0[0, 0, 0] + np.cumsum(K[0, 0][:, :, None] * V[0, 0][:, None, :], axis=0)
+    assert _rel(O[0, 0], np.einsum("tk,tkv->tv", Q[0, 0], S)) < 1e-12
+    assert _rel(S_end[0, 0, 0], S[-1]) < 1e-12
+
+
+def test_gated_constant_gate_is_the_fixed_decay():
+    rng = np.random.default_rng(8)
+    L, dk, dv, H = 150, 16, 16, 3
+    Q, K, V = _rand(rng, 1, H, L, dk), _rand(rng, 1, H, L, dk), _rand(rng, 1, H, L, dv)
+    lam = np.array([0.5, 0.9, 0.999])
+    G = np.broadcast_to(np.log(lam)[None, :, None], (1, H, L)).copy()
+    S0 = _rand(rng, 1, H, 1, dk, dv)
+    O, S = lao.fwd_gated(Q, K, V, G, S0=S0)
+    Or, Sr = quadratic_form(Q[0, 0], K[0, 0], V[0, 0], lam[0], S0[0, 0, 0])
+    assert _rel(O[0, 0], Or) < 1e-12 and _rel(S[0, 0, 0], Sr) < 1e-12
+
+
+def test_gated_segments_with_scanned_starts_equal_monolithic():
+    rng = np.random.default_rng(9)
+    P, Ls, dk, dv = 5, 40, 8, 6
+    L = P * Ls
+    Q, K, V = _rand(rng, 1, 2, L, dk), _rand(rng, 1, 2, L, dk), _rand(rng, 1, 2, L, dv)
+    G = -rng.uniform(0.0, 0.1, size=(1, 2, L))
+    S0 = _rand(rng, 1, 2, 1, dk, dv)
+    O_ref, S_ref = lao.fwd_gated(Q, K, V, G, S0=S0)
+    # local states of each segment from zero, combined with the product of
+    # the gates over each segment
+    _, dS = lao.fwd_gated(Q, K, V, G, nseg=P, need_O=False)
+    LD = G.reshape(1, 2, P, Ls).sum(axis=-1)
+    S_start, S_end = lao.scan_gated(dS, LD, S0=S0[:, :, 0])
+    O, _ = lao.fwd_gated(Q, K, V, G, S0=S_start, nseg=P)
+    assert _rel(O, O_ref) < 1e-12
+    assert _rel(S_end, S_ref[:, :, 0]) < 1e-12
