@@ -176,6 +176,46 @@ la_status la_chunk_bwd(const la_shape* shape, const void* Q, const void* K,
                        void* dV, float* dS0, void* ws, size_t ws_bytes,
                        void* stream);
 
+/*
+ * Gated recurrence: the fixed decay becomes a per-token, per-head gate,
+ *     S_t = alpha_t * S_{t-1} + k_t v_t^T        o_t = q_t^T S_t
+ * the data-dependent gates of the "Gated Linear Attention Transformers with
+ * Hardware-Efficient Training" entry of the LASP-2 page's related-paper
+ * list, taken as one scalar gate per token and head.  Same chunkwise
+ * evaluation as la_chunk_fwd with every lambda power replaced by a product
+ * of gates (exp of a difference of chunk-local cumulative log-gates, all
+ * <= 1); segments combine with the product of their gates.
+ */
+
+/* Workspace bytes la_chunk_fwd_gated needs for `shape`; 0 = none (or an
+ * invalid shape). */
+size_t la_fwd_gated_workspace_bytes(const la_shape* shape);
+
+/*
+ * Gated forward pass.  As la_chunk_fwd, with
+ *   log_alpha [B,H,L] fp32   log of the gates, log(alpha_t) <= 0 (alpha_t in
+ *                            (0, 1]); required (no lambda argument).
+ * Segment s of (b, h) (nseg > 1) starts from S0[b, h, s] and uses the gates
+ * of its own tokens only.  ws: workspace of la_fwd_gated_workspace_bytes().
+ * Errors as la_chunk_fwd; nothing is written when validation fails.
+ */
+la_status la_chunk_fwd_gated(const la_shape* shape, const void* Q, const void* K,
+                             const void* V, const float* log_alpha, const float* S0,
+                             void* O, float* S_end, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/*
+ * Gated segment combine: la_state_scan with the decay of segment s of (b, h)
+ * given as its log, log_decay[b, h, s] (the sum of the segment's log-gates):
+ *     S_start[b, h, s] = X;   X = exp(log_decay[b, h, s]) * X + dS[b, h, s]
+ *   dS, S_start [B,H,P,dk,dv] (may be the same buffer)   log_decay [B,H,P] fp32
+ *   S0, S_end [B,H,dk,dv] (S0 NULL = zero, S_end NULL = not written)
+ * Errors as la_state_scan.
+ */
+la_status la_state_scan_gated(int64_t B, int64_t H, int32_t P, int32_t dk, int32_t dv,
+                              const float* dS, const float* log_decay, const float* S0,
+                              float* S_start, float* S_end, int32_t reverse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -130,9 +130,13 @@ la::FwdArgs flow_args(const Plan& pl, int H, int nseg, const void* Q, const void
 // 0..split-2 from zero, then an inclusive scan seeded with `start` (null =
 // zero).  Nothing to do when split == 1.
 la_status run_states(const Plan& pl, int dtype, int H, int nseg, const void* K, const void* V,
-                     const float* lam, const float* start, float* W, int reverse, hipStream_t st) {
+                     const float* lam, const float* start, float* W, int reverse, hipStream_t st,
+                     bool gated = false, const float* G = nullptr, float* LDw = nullptr) {
   if (pl.nseq == 0 || pl.split <= 1) return LA_OK;
   la::FwdArgs pa = flow_args(pl, H, nseg, nullptr, K, V, lam, reverse);
+  pa.gated = gated;  // gated: sub-segment log-gates to LDw for the combine
+  pa.G = G;
+  pa.LDout = LDw;
   pa.p_begin = 0;
   pa.p_count = pl.split - 1;
   pa.start_from_state = 0;
@@ -156,6 +160,8 @@ la_status run_states(const Plan& pl, int dtype, int H, int nseg, const void* K, 
   sa.Send = nullptr;
   sa.reverse = 0;
   sa.inclusive = 1;
+  sa.gated = gated;
+  sa.LD = LDw;
   e = la::launch_scan(sa, st);
   if (e != hipSuccess) return hip_fail(e, "state scan launch");
   return LA_OK;
@@ -166,9 +172,12 @@ la_status run_states(const Plan& pl, int dtype, int H, int nseg, const void* K, 
 // the last sub-segment runs (state only).
 la_status run_main(const Plan& pl, int dtype, int H, int nseg, const void* Q, const void* K,
                    const void* V, const float* lam, const float* start, void* O, float* Send,
-                   const float* W, int reverse, hipStream_t st) {
+                   const float* W, int reverse, hipStream_t st, bool gated = false,
+                   const float* G = nullptr) {
   if (pl.nseq == 0 || (!O && !Send)) return LA_OK;
   la::FwdArgs ma = flow_args(pl, H, nseg, Q, K, V, lam, reverse);
+  ma.gated = gated;
+  ma.G = G;
   ma.start_from_state = 1;
   ma.S0 = start;
   ma.Sws = W;
@@ -193,11 +202,18 @@ la_status run_main(const Plan& pl, int dtype, int H, int nseg, const void* Q, co
 // may be null (zero).  O may be null (state only); Send may be null.
 la_status run_flow(const Plan& pl, int dtype, int H, int nseg, const void* Q, const void* K,
                    const void* V, const float* lam, const float* start, void* O, float* Send,
-                   float* W, int reverse, hipStream_t st) {
+                   float* W, int reverse, hipStream_t st, bool gated = false,
+                   const float* G = nullptr, float* LDw = nullptr) {
   if (pl.nseq == 0 || (!O && !Send)) return LA_OK;
-  la_status r = run_states(pl, dtype, H, nseg, K, V, lam, start, W, reverse, st);
+  la_status r = run_states(pl, dtype, H, nseg, K, V, lam, start, W, reverse, st, gated, G, LDw);
   if (r != LA_OK) return r;
-  return run_main(pl, dtype, H, nseg, Q, K, V, lam, start, O, Send, W, reverse, st);
+  return run_main(pl, dtype, H, nseg, Q, K, V, lam, start, O, Send, W, reverse, st, gated, G);
+}
+
+// gated forward workspace: the start states, then the sub-segment log-gates
+size_t gated_ws_bytes(const Plan& p) {
+  if (p.split <= 1) return 0;
+  return scan_ws_bytes(p) + ((size_t)p.nseq * (size_t)(p.split - 1) * sizeof(float) + 255) / 256 * 256;
 }
 
 }  // namespace
@@ -260,6 +276,76 @@ la_status la_chunk_fwd(const la_shape* s, const void* Q, const void* K, const vo
   if (pl.nseq == 0) return LA_OK;
   return run_flow(pl, s->dtype, (int)s->H, s->nseg, Q, K, V, lambda, S0, O, S_end,
                   static_cast<float*>(ws), 0, static_cast<hipStream_t>(stream));
+}
+
+size_t la_fwd_gated_workspace_bytes(const la_shape* shape) {
+  Plan pl;
+  std::string keep = g_last_error;
+  if (check_shape(shape, &pl) != LA_OK) {
+    g_last_error = keep;
+    return 0;
+  }
+  return gated_ws_bytes(pl);
+}
+
+la_status la_chunk_fwd_gated(const la_shape* s, const void* Q, const void* K, const void* V,
+                             const float* log_alpha, const float* S0, void* O, float* S_end,
+                             void* ws, size_t ws_bytes, void* stream) {
+  Plan pl;
+  la_status r = check_shape(s, &pl);
+  if (r != LA_OK) return r;
+  const bool has_tokens = pl.nseq > 0 && pl.Ls > 0;
+  if (has_tokens && (!Q || !K || !V || !log_alpha))
+    return fail(LA_ERR_INVALID_ARG, "Q, K, V and log_alpha are required");
+  if (!O && !S_end) return fail(LA_ERR_INVALID_ARG, "O and S_end are both NULL");
+  const void* ptrs[] = {Q, K, V, log_alpha, S0, O, S_end, ws};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(LA_ERR_INVALID_ARG, "pointer %p is not 16-byte aligned", p);
+  const size_t need = gated_ws_bytes(pl);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                ws ? ws_bytes : (size_t)0);
+  if (pl.nseq == 0) return LA_OK;
+  float* W = static_cast<float*>(ws);
+  float* LDw = W ? W + scan_ws_bytes(pl) / sizeof(float) : nullptr;
+  return run_flow(pl, s->dtype, (int)s->H, s->nseg, Q, K, V, nullptr, S0, O, S_end, W, 0,
+                  static_cast<hipStream_t>(stream), true, log_alpha, LDw);
+}
+
+la_status la_state_scan_gated(int64_t B, int64_t H, int32_t P, int32_t dk, int32_t dv,
+                              const float* dS, const float* log_decay, const float* S0,
+                              float* S_start, float* S_end, int32_t reverse, void* stream) {
+  if (B < 0 || H < 0 || P < 0) return fail(LA_ERR_INVALID_ARG, "negative size");
+  if (dk <= 0 || dv <= 0) return fail(LA_ERR_INVALID_ARG, "dk and dv must be positive");
+  if ((double)B * H * ((double)P + 1) * dk * dv > 4.0e18)
+    return fail(LA_ERR_INVALID_ARG, "tensor too large");
+  const int64_t nseq = B * H;
+  if (nseq > 0 && P > 0 && (!dS || !S_start || !log_decay))
+    return fail(LA_ERR_INVALID_ARG, "dS, log_decay and S_start are required");
+  const void* ptrs[] = {dS, log_decay, S0, S_start, S_end};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(LA_ERR_INVALID_ARG, "pointer %p is not 16-byte aligned", p);
+  if (nseq == 0 || (P == 0 && !S_end)) return LA_OK;
+  la::ScanArgs sa;
+  std::memset(&sa, 0, sizeof(sa));
+  sa.nseq = nseq;
+  sa.P = P;
+  sa.E = (int64_t)dk * dv;
+  sa.dS = dS;
+  sa.lam = nullptr;
+  sa.H = (int)H;
+  sa.hdiv = 1;
+  sa.seg_len = 0;
+  sa.S0 = S0;
+  sa.Sout = S_start;
+  sa.Send = S_end;
+  sa.reverse = reverse != 0;
+  sa.inclusive = 0;
+  sa.gated = 1;
+  sa.LD = log_decay;  // with P == 0 the kernel only writes S_end = S0 (or zero)
+  hipError_t e = la::launch_scan(sa, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "state scan launch");
+  return LA_OK;
 }
 
 la_status la_state_scan(int64_t B, int64_t H, int32_t P, int32_t dk, int32_t dv, const float* dS,

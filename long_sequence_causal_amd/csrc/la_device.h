@@ -121,6 +121,14 @@ __device__ inline void dma16(const void* sbase, unsigned voff, unsigned lds) {
                : "memory", "m0");
 }
 
+// 4 bytes per lane from global memory straight into LDS: lane l's 4 B land
+// at LDS address lds + 4 l (as dma16, one dword per lane).
+__device__ inline void dma4(const void* sbase, unsigned voff, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
+
 // ---------------------------------------------------------------- small helpers
 __device__ inline float pow_lam(float lg2, float n) {
   // lambda^n = 2^(n log2 lambda); only non-negative n are formed.

@@ -10,12 +10,12 @@
 
 namespace la {
 
-template <typename T, int D, bool WITH_O>
-__global__ __launch_bounds__((FwdLayout<T, D, WITH_O ? 3 : 2>::NT),
-                             (FwdLayout<T, D, WITH_O ? 3 : 2>::WAVES_PER_EU)) void k_chunk_fwd(
+template <typename T, int D, bool WITH_O, bool GATED>
+__global__ __launch_bounds__((FwdLayout<T, D, WITH_O ? 3 : 2, GATED>::NT),
+                             (FwdLayout<T, D, WITH_O ? 3 : 2, GATED>::WAVES_PER_EU)) void k_chunk_fwd(
     FwdArgs a) {
   constexpr int NSLOT = WITH_O ? 3 : 2;
-  typedef FwdLayout<T, D, NSLOT> LY;
+  typedef FwdLayout<T, D, NSLOT, GATED> LY;
   constexpr int NKT = D / 16;
   __shared__ __attribute__((aligned(1024))) char smem[LY::BYTES];
 
@@ -40,7 +40,8 @@ __global__ __launch_bounds__((FwdLayout<T, D, WITH_O ? 3 : 2>::NT),
   jb.len = (int)((t1 > t0) ? t1 - t0 : 0);
   jb.Ls = a.Ls;
   jb.reverse = a.reverse;
-  jb.lg = log2f(a.lam[h]);
+  jb.lg = GATED ? 0.0f : log2f(a.lam[h]);
+  jb.G = GATED ? a.G + n * a.Ls : nullptr;
 
   // ---- start state -> accumulators (wave w: columns [16 w, 16 w + 16))
   f32x4 accS[NKT];
@@ -63,10 +64,11 @@ __global__ __launch_bounds__((FwdLayout<T, D, WITH_O ? 3 : 2>::NT),
     __builtin_amdgcn_s_waitcnt(0x0F70);
   }
 
-  walk<T, D, WITH_O, NSLOT>(smem, jb, accS);
+  const float lgate = walk<T, D, WITH_O, NSLOT, GATED>(smem, jb, accS);
 
-  // ---- final state of this sub-segment
+  // ---- final state of this sub-segment (and its total log-gate)
   if (a.Sout && p >= a.sout_p0 && p < a.sout_p0 + a.sout_np) {
+    if (GATED && a.LDout && threadIdx.x == 0) a.LDout[n * a.sout_np + (p - a.sout_p0)] = lgate;
     float* dst = a.Sout + (n * a.sout_np + (p - a.sout_p0)) * (int64_t)D * D;
 #pragma unroll
     for (int tk = 0; tk < NKT; ++tk)
@@ -75,26 +77,32 @@ __global__ __launch_bounds__((FwdLayout<T, D, WITH_O ? 3 : 2>::NT),
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool GATED>
 static hipError_t launch_fwd_t(const FwdArgs& a, bool with_o, int64_t nwg, hipStream_t s) {
   if (with_o)
-    hipLaunchKernelGGL((k_chunk_fwd<T, D, true>), dim3((unsigned)nwg),
-                       dim3(FwdLayout<T, D, 3>::NT), 0, s, a);
+    hipLaunchKernelGGL((k_chunk_fwd<T, D, true, GATED>), dim3((unsigned)nwg),
+                       dim3(FwdLayout<T, D, 3, GATED>::NT), 0, s, a);
   else
-    hipLaunchKernelGGL((k_chunk_fwd<T, D, false>), dim3((unsigned)nwg),
-                       dim3(FwdLayout<T, D, 2>::NT), 0, s, a);
+    hipLaunchKernelGGL((k_chunk_fwd<T, D, false, GATED>), dim3((unsigned)nwg),
+                       dim3(FwdLayout<T, D, 2, GATED>::NT), 0, s, a);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_fwd_g(const FwdArgs& a, bool with_o, int64_t nwg, hipStream_t s) {
+  return a.gated ? launch_fwd_t<T, D, true>(a, with_o, nwg, s)
+                 : launch_fwd_t<T, D, false>(a, with_o, nwg, s);
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, bool with_o, int64_t nwg,
                       hipStream_t s) {
   if (nwg <= 0) return hipSuccess;
   if (dtype == 0) {
-    if (D == 64) return launch_fwd_t<__bf16, 64>(a, with_o, nwg, s);
-    if (D == 128) return launch_fwd_t<__bf16, 128>(a, with_o, nwg, s);
+    if (D == 64) return launch_fwd_g<__bf16, 64>(a, with_o, nwg, s);
+    if (D == 128) return launch_fwd_g<__bf16, 128>(a, with_o, nwg, s);
   } else {
-    if (D == 64) return launch_fwd_t<float, 64>(a, with_o, nwg, s);
-    if (D == 128) return launch_fwd_t<float, 128>(a, with_o, nwg, s);
+    if (D == 64) return launch_fwd_g<float, 64>(a, with_o, nwg, s);
+    if (D == 128) return launch_fwd_g<float, 128>(a, with_o, nwg, s);
   }
   return hipErrorInvalidValue;
 }

@@ -37,6 +37,12 @@ struct FwdArgs {
   // reverse time order (token t of a sequence is read as token Ls-1-t); used
   // by the backward's reverse sweeps
   int reverse;
+  // gated recurrence (gated != 0): log-gates G [nseq*Ls], read only for the
+  // chunks walked, and lam is never read; state-only launches write the total
+  // log-gate of each sub-segment to LDout[n][p - sout_p0] beside Sout
+  int gated;
+  const float* G;
+  float* LDout;
 };
 
 // dst[n] = f(src[n]) for nseq D x D fp32 states: optional transpose, then a
@@ -68,6 +74,10 @@ struct ScanArgs {
   float* Send;       // [nseq][E] or null
   int reverse;
   int inclusive;     // 0: Sout[s] = state before adding dS[s]; 1: after
+  // gated != 0: segment s of sequence n decays by exp(LD[n][s]) instead of
+  // lambda^seg_len (lam is then never read, LD only for s < P)
+  int gated;
+  const float* LD;   // [nseq][P]
 };
 
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, bool with_o, int64_t nwg,

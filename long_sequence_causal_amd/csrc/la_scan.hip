@@ -17,16 +17,17 @@ __global__ __launch_bounds__(256) void k_state_scan(ScanArgs a) {
   if (gid >= a.nseq * a.E) return;
   const int64_t n = gid / a.E;
   const int64_t e = gid - n * a.E;
-  const int h = (int)((n / a.hdiv) % a.H);
   // lambda^seg_len = 2^(seg_len log2 lambda); underflow to 0 is intended
-  const float dec = exp2f((float)a.seg_len * log2f(a.lam[h]));
+  const float dec =
+      a.gated ? 0.0f : exp2f((float)a.seg_len * log2f(a.lam[(int)((n / a.hdiv) % a.H)]));
   float x = a.S0 ? a.S0[n * a.E + e] : 0.0f;
   for (int it = 0; it < a.P; ++it) {
     const int s = a.reverse ? (a.P - 1 - it) : it;
     const int64_t idx = (n * a.P + s) * a.E + e;
     const float d = a.dS[idx];
     if (!a.inclusive) a.Sout[idx] = x;
-    x = dec * x + d;
+    // gated: the segment's own product of gates, exp(LD)
+    x = (a.gated ? expf(a.LD[n * a.P + s]) : dec) * x + d;
     if (a.inclusive) a.Sout[idx] = x;
   }
   if (a.Send) a.Send[n * a.E + e] = x;

@@ -55,8 +55,9 @@ __device__ inline void score_tile(int idx, int& jb, int& ib) {
 constexpr int LDS_MAX = 160 * 1024;  // per workgroup on gfx950
 
 // LDS of a workgroup: STAGES stages of NSLOT token-major tiles (Q, K, V when
-// NSLOT = 3, K, V when NSLOT = 2), plus P when NSLOT = 3.
-template <typename T, int D, int NSLOT>
+// NSLOT = 3, K, V when NSLOT = 2), plus P when NSLOT = 3, plus (gated walks)
+// the 64 log-gates of each stage's chunk.
+template <typename T, int D, int NSLOT, bool GATED = false>
 struct FwdLayout {
   typedef PadTile<T, CH, D> TN;                // Q, K, V token-major [token][d]
   typedef PBlocks<T> TP;                       // P, its 10 nonzero 16x16 blocks
@@ -65,10 +66,12 @@ struct FwdLayout {
   static constexpr int STAGE = NTEN * TB;
   static constexpr int PBYTES = NSLOT == 3 ? TP::BYTES : 0;
   static constexpr int SMAX = NSLOT == 3 ? 3 : 5;
-  static constexpr int SFIT = (LDS_MAX - PBYTES) / STAGE;
+  static constexpr int GB = GATED ? CH * 4 : 0;  // log-gates of one chunk
+  static constexpr int SFIT = (LDS_MAX - PBYTES) / (STAGE + GB);
   static constexpr int STAGES = SFIT < SMAX ? SFIT : SMAX;
   static constexpr int OFF_P = STAGES * STAGE;
-  static constexpr int BYTES = OFF_P + PBYTES;
+  static constexpr int OFF_G = OFF_P + PBYTES;
+  static constexpr int BYTES = OFF_G + STAGES * GB;
   static constexpr int NW = D / 16;  // waves: one per 16 state columns
   static constexpr int NT = 64 * NW;
   // bf16 keeps two waves per SIMD (256 registers per lane)
@@ -113,7 +116,8 @@ struct WalkJob {
   int len;        // positions; fits in int (one sequence spans under 4 GiB)
   int64_t Ls;
   int reverse;
-  float lg;       // log2 lambda
+  float lg;       // log2 lambda (fixed-decay walks)
+  const float* G; // log-gates of the sequence, [Ls] (gated walks)
 };
 
 // Walk the range with the state in accS (wave w: columns [16 w, 16 w + 16),
@@ -121,11 +125,22 @@ struct WalkJob {
 // after the range.  OUT: also form and store the outputs.  NSLOT: tiles per
 // LDS stage of the caller's layout (the K, V slots are the last two).  All
 // of the workgroup's threads call it; LDS is free again on return.
-template <typename T, int D, bool OUT, int NSLOT>
-__device__ __forceinline__ void walk(char* smem, const WalkJob& jb, f32x4 (&accS)[D / 16]) {
+//
+// GATED: the decay is a per-token gate alpha_t = exp(g_t) (the data-dependent
+// gates of the Gated Linear Attention entry of the LASP-2 page's
+// related-paper list, one scalar per token and head):
+//   S_t = alpha_t S_{t-1} + k_t v_t^T.
+// With c_i = g_0 + .. + g_i the chunk-local cumulative log-gate, every
+// factor above becomes a difference of c: lambda^(i-j) -> exp(c_i - c_j),
+// lambda^(i+1) -> exp(c_i), lambda^(cl-1-j) -> exp(c_{cl-1} - c_j),
+// lambda^cl -> exp(c_{cl-1}); all are <= 1.  Wave NW-1 brings the chunk's 64
+// gates to LDS with the tiles; every wave forms c with a wave-wide prefix sum
+// (lane = token).  Returns the range's total log-gate (0 if not GATED).
+template <typename T, int D, bool OUT, int NSLOT, bool GATED = false>
+__device__ __forceinline__ float walk(char* smem, const WalkJob& jb, f32x4 (&accS)[D / 16]) {
   typedef Elt<T> X;
   typedef typename X::op_t op_t;
-  typedef FwdLayout<T, D, NSLOT> LY;
+  typedef FwdLayout<T, D, NSLOT, GATED> LY;
   static_assert(NSLOT == 3 || !OUT, "outputs need the Q slot and P");
   typedef typename LY::TN TN;
   typedef typename LY::TP TP;
@@ -173,7 +188,13 @@ __device__ __forceinline__ void walk(char* smem, const WalkJob& jb, f32x4 (&accS
   // last piece of a row being padding (it loads the row's first piece).
   // Offsets of chunk 0 are precomputed; a ragged last chunk clamps rows past
   // the end to the last valid token.
-  const bool lpc_hi = (w < NBLK - (LPC_HI - 1) * NW);
+  // The gate load rides with wave NW-1, which otherwise issues one load fewer
+  // than the busiest wave (NBLK is never a multiple of NW here), so every
+  // wave's per-chunk count stays LPC_HI or LPC_HI - 1.
+  static_assert(!GATED || NBLK % NW != 0, "the gate load needs a wave with a spare slot");
+  const bool gwave = GATED && (w == NW - 1);
+  const bool lpc_hi = (w < NBLK - (LPC_HI - 1) * NW);  // issues LPC_HI tile loads
+  const bool wait_hi = lpc_hi || gwave;                // LPC_HI loads in all
   auto blk_of = [&](int q) { const int bq = w + NW * q; return bq < NBLK ? bq : 0; };
   auto tensor_base = [&](int ten) -> const T* {
     const void* bp = OUT ? (ten == 0 ? jb.Q : (ten == 1 ? jb.K : jb.V)) : (ten == 0 ? jb.K : jb.V);
@@ -220,6 +241,10 @@ __device__ __forceinline__ void walk(char* smem, const WalkJob& jb, f32x4 (&accS
         dma16(src_of[q], voff, dst_of[q] + sb);
       }
     }
+    if (GATED && gwave) {
+      const int tt = (c * CH + lane < len) ? c * CH + lane : len - 1;
+      dma4(jb.G, (unsigned)(relrow(tt) * 4), smem_lds + (unsigned)(LY::OFF_G + stage * LY::GB));
+    }
   };
 
   // first chunks in flight while the factors are computed
@@ -248,12 +273,12 @@ __device__ __forceinline__ void walk(char* smem, const WalkJob& jb, f32x4 (&accS
   if (OUT) {
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      qf[it] = pow_lam(lg, (float)(16 * it + l16 + 1));
+      if (!GATED) qf[it] = pow_lam(lg, (float)(16 * it + l16 + 1));
       ooff0[it] = (unsigned)(relrow(16 * it + l16) * D + col + 4 * g);
     }
-    set_pf(CH);
+    if (!GATED) set_pf(CH);
   }
-  const float lamC = pow_lam(lg, (float)CH);
+  const float lamC = GATED ? 0.0f : pow_lam(lg, (float)CH);
   // lambda^(cl-1-j) (0 past the tail) for the lane's contraction slots j of the update
   float wv[NJS][E];
   auto set_wv = [&](int cl) {
@@ -265,7 +290,8 @@ __device__ __forceinline__ void walk(char* smem, const WalkJob& jb, f32x4 (&accS
         wv[js][x] = (j < cl) ? pow_lam(lg, (float)(cl - 1 - j)) : 0.0f;
       }
   };
-  set_wv(CH);
+  if (!GATED) set_wv(CH);
+  float gsum2 = 0.0f;  // total log2-gate of the chunks walked (GATED)
 
   int st = 0;             // stage holding chunk c
   int st_next = S - 1;    // stage for chunk c + S - 1 (the one chunk c - 1 used)
@@ -277,13 +303,55 @@ __device__ __forceinline__ void walk(char* smem, const WalkJob& jb, f32x4 (&accS
       wait_vm_barrier<0>();
     } else {
       const int later = (nch - 1 - c < S - 2) ? nch - 1 - c : S - 2;
-      wait_chunk<LPC_HI, S - 2>(lpc_hi, later);  // chunk c landed; chunk c-1 consumed
+      wait_chunk<LPC_HI, S - 2>(wait_hi, later);  // chunk c landed; chunk c-1 consumed
       if (c + S - 1 < nch) issue(c + S - 1, st_next);
       st_next = (st_next + 1 == S) ? 0 : st_next + 1;
     }
-    if (cl != CH) {
-      set_wv(cl);
-      if (OUT) set_pf(cl);
+    float dc;  // decay of the state over the chunk
+    if constexpr (GATED) {
+      // chunk-local cumulative log-gate in log2 units, lane = token
+      float c2 = *reinterpret_cast<const float*>(smem + LY::OFF_G + st * LY::GB + 4 * lane) *
+                 1.4426950408889634f;
+#pragma unroll
+      for (int d = 1; d < CH; d <<= 1) {
+        const float y = __shfl_up(c2, d, 64);
+        if (lane >= d) c2 += y;
+      }
+      const float clast = __shfl(c2, cl - 1, 64);
+      gsum2 += clast;
+      dc = exp2f(clast);
+#pragma unroll
+      for (int js = 0; js < NJS; ++js)
+#pragma unroll
+        for (int x = 0; x < E; ++x) {
+          const int j = slot_token<T>(js * KS, g, x);
+          const float cj = __shfl(c2, j, 64);
+          wv[js][x] = (j < cl) ? exp2f(clast - cj) : 0.0f;
+        }
+      if (OUT) {
+#pragma unroll
+        for (int it = 0; it < 4; ++it) qf[it] = exp2f(__shfl(c2, 16 * it + l16, 64));
+#pragma unroll
+        for (int sti = 0; sti < NST; ++sti) {
+          const int idx = w + NW * sti;
+          int jb_ = 0, ib_ = 0;
+          if (idx < 10) score_tile(idx, jb_, ib_);
+          const int i = 16 * ib_ + perm16<T>(l16);
+          const float ci = __shfl(c2, i, 64);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = 16 * jb_ + perm16<T>(4 * g + r);
+            const float cj = __shfl(c2, j, 64);
+            pf[sti][r] = (idx < 10 && j <= i && j < cl) ? exp2f(ci - cj) : 0.0f;
+          }
+        }
+      }
+    } else {
+      if (cl != CH) {
+        set_wv(cl);
+        if (OUT) set_pf(cl);
+      }
+      dc = (cl == CH) ? lamC : pow_lam(lg, (float)cl);
     }
     const char* const stage = smem + st * LY::STAGE;
     st = (st + 1 == S) ? 0 : st + 1;
@@ -406,7 +474,6 @@ __device__ __forceinline__ void walk(char* smem, const WalkJob& jb, f32x4 (&accS
 
     // ---- state update: S = lambda^cl S + K^T (diag(lambda^(cl-1-j)) V)
     {
-      const float dc = (cl == CH) ? lamC : pow_lam(lg, (float)cl);
 #pragma unroll
       for (int tk = 0; tk < NKT; ++tk) accS[tk] *= dc;
       op_t Bv[NJS];
@@ -432,6 +499,7 @@ __device__ __forceinline__ void walk(char* smem, const WalkJob& jb, f32x4 (&accS
   }
 
   lds_barrier();  // every wave is done with the last chunk's LDS
+  return gsum2 * 0.6931471805599453f;
 }
 
 }  // namespace la

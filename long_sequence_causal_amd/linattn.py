@@ -21,7 +21,8 @@ LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE, LA_ERR_HIP = ra
 LA_BF16, LA_FP32 = 0, 1
 
 EXPORTS = ("la_version", "la_status_str", "la_last_error", "la_fwd_workspace_bytes",
-           "la_chunk_fwd", "la_state_scan", "la_bwd_workspace_bytes", "la_chunk_bwd")
+           "la_chunk_fwd", "la_state_scan", "la_bwd_workspace_bytes", "la_chunk_bwd",
+           "la_fwd_gated_workspace_bytes", "la_chunk_fwd_gated", "la_state_scan_gated")
 
 
 class LinAttnError(RuntimeError):
@@ -67,6 +68,12 @@ def lib():
     L.la_state_scan.argtypes = [i64, i64, i32, i32, i32, vp, vp, i64, vp, vp, vp, i32, vp]
     L.la_chunk_bwd.restype = ctypes.c_int
     L.la_chunk_bwd.argtypes = [sp] + [vp] * 12 + [sz, vp]
+    L.la_fwd_gated_workspace_bytes.restype = sz
+    L.la_fwd_gated_workspace_bytes.argtypes = [sp]
+    L.la_chunk_fwd_gated.restype = ctypes.c_int
+    L.la_chunk_fwd_gated.argtypes = [sp] + [vp] * 8 + [sz, vp]
+    L.la_state_scan_gated.restype = ctypes.c_int
+    L.la_state_scan_gated.argtypes = [i64, i64, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp]
     _lib = L
     return L
 
@@ -152,6 +159,55 @@ def la_chunk_fwd(q, k, v, lam, S0=None, nseg: int = 1, need_O: bool = True,
                               _ptr(S0), _ptr(O), _ptr(S_end), _ptr(ws),
                               ws.numel() if ws is not None else 0, _stream()))
     return O, S_end
+
+
+def la_fwd_gated_workspace_bytes(shape: la_shape) -> int:
+    return int(lib().la_fwd_gated_workspace_bytes(ctypes.byref(shape)))
+
+
+def la_chunk_fwd_gated(q, k, v, log_alpha, S0=None, nseg: int = 1, need_O: bool = True,
+                       need_S_end: bool = True, split: int = 0, out=None, S_end_out=None,
+                       workspace=None):
+    """Gated forward pass.  As la_chunk_fwd with log_alpha [B,H,L] fp32 (the
+    log of the per-token gates) in place of lam.  Returns (O or None, S_end or None)."""
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q.dtype)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype)
+    _need(log_alpha, "log_alpha", torch.float32)
+    if log_alpha.shape != (B, H, L):
+        raise ValueError(f"log_alpha has shape {tuple(log_alpha.shape)}, expected {(B, H, L)}")
+    _need(S0, "S0", torch.float32)
+    shape = make_shape(B, H, L, dk, dv, nseg, dt, split)
+    O = None
+    if need_O:
+        O = out if out is not None else torch.empty((B, H, L, dv), dtype=q.dtype, device=q.device)
+    S_end = None
+    if need_S_end:
+        S_end = S_end_out if S_end_out is not None else torch.empty(
+            (B, H, nseg, dk, dv), dtype=torch.float32, device=q.device)
+    nbytes = la_fwd_gated_workspace_bytes(shape)
+    ws = workspace if workspace is not None else _workspace(nbytes, q.device)
+    _check(lib().la_chunk_fwd_gated(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
+                                    _ptr(log_alpha), _ptr(S0), _ptr(O), _ptr(S_end), _ptr(ws),
+                                    ws.numel() if ws is not None else 0, _stream()))
+    return O, S_end
+
+
+def la_state_scan_gated(dS, log_decay, S0=None, reverse: bool = False, out=None,
+                        need_S_end: bool = True):
+    """Gated segment combine.  dS [B,H,P,dk,dv] fp32, log_decay [B,H,P] fp32,
+    S0 [B,H,dk,dv] or None.  Returns (S_start, S_end or None)."""
+    B, H, P, dk, dv = dS.shape
+    _need(dS, "dS", torch.float32)
+    _need(log_decay, "log_decay", torch.float32)
+    _need(S0, "S0", torch.float32)
+    S_start = out if out is not None else torch.empty_like(dS)
+    S_end = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dS.device) if need_S_end else None
+    _check(lib().la_state_scan_gated(B, H, P, dk, dv, _ptr(dS), _ptr(log_decay), _ptr(S0),
+                                     _ptr(S_start), _ptr(S_end), int(bool(reverse)), _stream()))
+    return S_start, S_end
 
 
 def la_state_scan(dS, lam, seg_len: int, S0=None, reverse: bool = False, out=None,

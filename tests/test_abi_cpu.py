@@ -165,6 +165,28 @@ def test_bwd_rejects_bad_arguments():
     assert call(ws=FAKE, nb=need - 16) == la.LA_ERR_WORKSPACE
 
 
+def test_gated_entry_points_validate_on_the_host():
+    L = la.lib()
+    s = _shape(L=512, split=4)
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    call = lambda G, ws=None, nb=0, O=FAKE: L.la_chunk_fwd_gated(
+        ctypes.byref(s), v(FAKE), v(FAKE), v(FAKE), v(G), None, v(O), None, v(ws), nb, None)
+    assert call(None) == la.LA_ERR_INVALID_ARG          # log_alpha required
+    assert call(FAKE + 4) == la.LA_ERR_INVALID_ARG      # misaligned
+    assert call(FAKE) == la.LA_ERR_WORKSPACE            # split 4 needs a workspace
+    need = la.la_fwd_gated_workspace_bytes(s)
+    # start states of 3 sub-segments and their log-gates, per sequence
+    assert need == la.la_fwd_workspace_bytes(s) + 256
+    assert call(FAKE, FAKE, need - 1) == la.LA_ERR_WORKSPACE
+    assert call(FAKE, O=None) == la.LA_ERR_INVALID_ARG  # O and S_end both NULL
+    scan = lambda dS, LD, St, P=3: L.la_state_scan_gated(1, 2, P, 64, 64, v(dS), v(LD), None,
+                                                         v(St), None, 0, None)
+    assert scan(FAKE, None, FAKE) == la.LA_ERR_INVALID_ARG
+    assert scan(None, FAKE, FAKE) == la.LA_ERR_INVALID_ARG
+    assert scan(FAKE, FAKE + 8, FAKE) == la.LA_ERR_INVALID_ARG
+    assert scan(FAKE, FAKE, FAKE, P=-1) == la.LA_ERR_INVALID_ARG
+
+
 def test_empty_problem_is_a_no_op():
     # B*H = 0: nothing to read or write, no HIP call needed
     assert _fwd(_shape(B=0), Q=None, K=None, V=None, lam=None) == la.LA_OK

@@ -1,0 +1,169 @@
+"""Parity of the gated recurrence S_t = alpha_t S_{t-1} + k_t v_t^T (one
+scalar gate per token and head) between the HIP path and the CPU oracle
+(lao.fwd_gated, lao.scan_gated), through the C ABI.  Needs a gfx950 GPU."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import TOL, f64, log, rel_err, require_gpu
+from long_sequence_causal_amd import linattn as la
+from long_sequence_causal_amd.inputs import decay_schedule, gate_logs, make_inputs, workload_inputs
+from oracle import lao
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _inputs(dtype, D, B, H, L, nseg, s0, seed):
+    inp = make_inputs(B, H, L, D, D, dtype=dtype, s0_std=s0, nseg=nseg, seed=seed, device="cuda")
+    G = gate_logs(decay_schedule(H, True), B, L, seed, device="cuda")
+    return inp, G
+
+
+CASES = [
+    # dtype, D, B, H, L, nseg, split, S0 std
+    ("bf16", 128, 2, 3, 337, 1, 0, 0.5),
+    ("bf16", 128, 1, 2, 64 * 9, 1, 4, 0.5),
+    ("bf16", 128, 1, 2, 64 * 9 + 5, 1, 3, 0.0),
+    ("bf16", 64, 1, 4, 64 * 7, 1, 0, 0.5),
+    ("bf16", 128, 1, 2, 64 * 6, 3, 2, 0.5),
+    ("bf16", 128, 2, 16, 64 * 72, 1, 0, 0.5),
+    ("fp32", 64, 1, 2, 1024, 1, 0, 0.0),
+    ("fp32", 64, 2, 2, 130 * 4, 4, 2, 0.5),
+    ("fp32", 128, 1, 2, 200, 1, 2, 0.5),
+    ("bf16", 128, 1, 1, 1, 1, 0, 0.5),
+]
+
+
+@pytest.mark.parametrize("dtype,D,B,H,L,nseg,split,s0", CASES)
+def test_gated_fwd_matches_oracle(dtype, D, B, H, L, nseg, split, s0):
+    log(f"gated fwd dtype={dtype} D={D} B={B} H={H} L={L} nseg={nseg} split={split} s0={s0}")
+    inp, G = _inputs(dtype, D, B, H, L, nseg, s0, 3000 + L + D)
+    q, k, v, S0 = inp["q"], inp["k"], inp["v"], inp["S0"]
+    O, S_end = la.la_chunk_fwd_gated(q, k, v, G, S0=S0, nseg=nseg, split=split)
+    torch.cuda.synchronize()
+    O_ref, S_ref = lao.fwd_gated(f64(q), f64(k), f64(v), f64(G), S0=f64(S0), nseg=nseg)
+    eo, es = rel_err(f64(O), O_ref), rel_err(f64(S_end), S_ref)
+    log(f"  err O={eo:.3e} S_end={es:.3e}")
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+def test_gated_constant_gate_matches_oracle_and_fixed_decay():
+    B, H, L, D = 1, 4, 64 * 11 + 9, 128
+    inp = make_inputs(B, H, L, D, D, dtype="bf16", s0_std=0.5, seed=31, device="cuda")
+    q, k, v, lam, S0 = inp["q"], inp["k"], inp["v"], inp["lam"], inp["S0"]
+    G = torch.log(lam.double()).float().view(1, H, 1).expand(B, H, L).contiguous()
+    Og, Sg = la.la_chunk_fwd_gated(q, k, v, G, S0=S0)
+    Of, Sf = la.la_chunk_fwd(q, k, v, lam, S0=S0)
+    torch.cuda.synchronize()
+    O_ref, S_ref = lao.fwd(f64(q), f64(k), f64(v), f64(lam), S0=f64(S0))
+    errs = [rel_err(f64(Og), O_ref), rel_err(f64(Sg), S_ref), rel_err(f64(Og), f64(Of))]
+    log("  constant gate: O err {:.3e}, S_end err {:.3e}, vs fixed-decay path {:.3e}".format(*errs))
+    assert errs[0] <= TOL["bf16"] and errs[1] <= TOL["bf16"] and errs[2] <= 2 * TOL["bf16"]
+
+
+def test_gated_extreme_and_unit_gates():
+    """Gates that reset the state (log alpha = -30), that keep it (0) and
+    everything between, mixed token by token: finite, and equal to the oracle."""
+    B, H, L, D = 1, 2, 64 * 5 + 17, 128
+    inp = make_inputs(B, H, L, D, D, dtype="bf16", s0_std=0.5, seed=32, device="cuda")
+    q, k, v, S0 = inp["q"], inp["k"], inp["v"], inp["S0"]
+    gen = torch.Generator(device="cuda").manual_seed(33)
+    pick = torch.randint(0, 3, (B, H, L), generator=gen, device="cuda")
+    G = torch.where(pick == 0, torch.full_like(pick, -30, dtype=torch.float32),
+                    torch.where(pick == 1, torch.zeros_like(pick, dtype=torch.float32),
+                                -torch.rand((B, H, L), generator=gen, device="cuda")))
+    G = G.float().contiguous()
+    O, S_end = la.la_chunk_fwd_gated(q, k, v, G, S0=S0)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(O.float()).all()) and bool(torch.isfinite(S_end).all())
+    O_ref, S_ref = lao.fwd_gated(f64(q), f64(k), f64(v), f64(G), S0=f64(S0))
+    eo, es = rel_err(f64(O), O_ref), rel_err(f64(S_end), S_ref)
+    log(f"  extreme gates: err O={eo:.3e} S_end={es:.3e}")
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("P,reverse", [(1, False), (5, False), (7, True), (0, False)])
+def test_gated_scan_matches_oracle(P, reverse):
+    B, H, D = 2, 3, 64
+    gen = torch.Generator(device="cuda").manual_seed(40 + P)
+    dS = torch.randn((B, H, P, D, D), generator=gen, device="cuda")
+    LD = -torch.rand((B, H, P), generator=gen, device="cuda") * 3.0
+    S0 = torch.randn((B, H, D, D), generator=gen, device="cuda")
+    st, en = la.la_state_scan_gated(dS, LD, S0=S0, reverse=reverse)
+    torch.cuda.synchronize()
+    st_ref, en_ref = lao.scan_gated(f64(dS), f64(LD), S0=f64(S0), reverse=reverse)
+    if P:
+        assert rel_err(f64(st), st_ref) <= TOL["fp32"]
+    assert rel_err(f64(en), en_ref) <= TOL["fp32"]
+
+
+def test_gated_segmented_flow_equals_monolithic():
+    """Segment-local states from zero, combined by the gated scan with each
+    segment's total log-gate, restart the segments exactly where one run
+    over the whole sequence is."""
+    B, H, P, Ls, D = 1, 4, 6, 64 * 5 + 32, 128
+    L = P * Ls
+    inp, G = _inputs("bf16", D, B, H, L, 1, 0.3, 41)
+    q, k, v, S0 = inp["q"], inp["k"], inp["v"], inp["S0"]
+    O_mono, S_mono = la.la_chunk_fwd_gated(q, k, v, G, S0=S0)
+    _, dS = la.la_chunk_fwd_gated(q, k, v, G, nseg=P, need_O=False)
+    LD = G.view(B, H, P, Ls).double().sum(-1).float().contiguous()
+    S_start, S_end = la.la_state_scan_gated(dS, LD, S0=S0[:, :, 0].contiguous())
+    O_seg, _ = la.la_chunk_fwd_gated(q, k, v, G, S0=S_start, nseg=P)
+    torch.cuda.synchronize()
+    e1 = rel_err(f64(O_seg), f64(O_mono))
+    e2 = rel_err(f64(S_end), f64(S_mono[:, :, 0]))
+    log(f"  segmented vs monolithic: O {e1:.3e}, S_end {e2:.3e}")
+    assert e1 <= TOL["bf16"] and e2 <= TOL["bf16"]
+
+
+def test_gated_invalid_call_writes_nothing():
+    B, H, L, D = 1, 2, 128, 64
+    inp, G = _inputs("bf16", D, B, H, L, 1, 0.0, 42)
+    O = torch.full((B, H, L, D), 7.0, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        la.la_chunk_fwd_gated(inp["q"], inp["k"], inp["v"], G[:, :, :-1].contiguous(), out=O)
+    shape = la.make_shape(B, H, L, D, D, 1, la.LA_BF16, 0)
+    st = la.lib().la_chunk_fwd_gated(shape, inp["q"].data_ptr(), inp["k"].data_ptr(),
+                                     inp["v"].data_ptr(), None, None, O.data_ptr(), None,
+                                     None, 0, None)
+    assert st == la.LA_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert bool((O.float() == 7.0).all())
+
+
+def test_gated_segment_64k_sampled_heads():
+    """The 64K-token, 32-head benchmark shape with gates, in the automatic
+    launch configuration; the oracle checks the fastest- and slowest-gated
+    heads in full."""
+    inp = workload_inputs("segment_64k", device="cuda")
+    q, k, v, lam, S0 = inp["q"], inp["k"], inp["v"], inp["lam"], inp["S0"]
+    B, H, L, D = q.shape
+    G = gate_logs(lam, B, L, 3, device="cuda")
+    O, S_end = la.la_chunk_fwd_gated(q, k, v, G, S0=S0)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(O.float()).all())
+    for h in (0, H - 1):
+        sl = slice(h, h + 1)
+        O_ref, S_ref = lao.fwd_gated(f64(q[:, sl]), f64(k[:, sl]), f64(v[:, sl]), f64(G[:, sl]),
+                                     S0=f64(S0[:, sl]))
+        eo, es = rel_err(f64(O[:, sl]), O_ref), rel_err(f64(S_end[:, sl]), S_ref)
+        log(f"  head {h}: err O={eo:.3e} S_end={es:.3e}")
+        assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+def test_gated_empty_sequence_returns_initial_state():
+    """No tokens (the log-gate tensor is empty and reaches the boundary as a
+    null pointer): S_end is S0, and no gate or decay is read."""
+    B, H, L, D, nseg = 1, 2, 0, 128, 1
+    q = torch.empty((B, H, L, D), dtype=torch.bfloat16, device="cuda")
+    G = torch.empty((B, H, L), dtype=torch.float32, device="cuda")
+    S0 = torch.randn((B, H, nseg, D, D), device="cuda")
+    _, S_end = la.la_chunk_fwd_gated(q, q, q, G, S0=S0, need_O=False)
+    torch.cuda.synchronize()
+    assert bool((S_end == S0).all())
