@@ -99,6 +99,33 @@ def backward_leg(torch, la, workload_inputs, WORKLOADS, dev, iters):
     return rec
 
 
+def gated_leg(torch, la, inp, dev, iters, gate_logs):
+    """la_chunk_fwd_gated on the same 64K x 32 inputs with seeded per-token
+    log-gates (on average each head's fixed decay): time per call, against
+    the forward's algorithmic bytes plus the gates read once (4 B per
+    token-head)."""
+    q, k, v, lam, S0 = inp["q"], inp["k"], inp["v"], inp["lam"], inp["S0"]
+    B, H, L, d = q.shape
+    G = gate_logs(lam, B, L, 3, device=dev)
+    shape = la.make_shape(B, H, L, d, d, 1, la.LA_BF16, 0)
+    ws = torch.empty(max(la.la_fwd_gated_workspace_bytes(shape), 1), dtype=torch.uint8, device=dev)
+    O = torch.empty_like(q)
+    S_end = torch.empty((B, H, 1, d, d), dtype=torch.float32, device=dev)
+
+    def call():
+        la.la_chunk_fwd_gated(q, k, v, G, S0=S0, out=O, S_end_out=S_end, workspace=ws)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    ms = time_events(call, iters, torch.cuda.current_stream())
+    nbytes = alg_bytes(B, H, L, d) + B * H * L * 4
+    t = ms / 1e3
+    return {"workload": "segment_64k with per-token gates", "us_per_call": ms * 1e3,
+            "tokens_per_s": B * L / t, "alg_bytes": nbytes, "achieved_GBs": nbytes / t / 1e9,
+            "frac_hbm": nbytes / t / 1e9 / HBM_PEAK_GBS}
+
+
 def time_events(fn, iters, stream):
     import torch
 
@@ -148,6 +175,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--split", type=int, default=0, help="internal split (0 = library choice)")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward leg")
+    ap.add_argument("--no-gated", action="store_true", help="skip the gated-forward leg")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -252,6 +280,12 @@ def main():
                      "kernel": "k_chunk_fwd<bf16,128,with O>",
                      "alg_bytes_per_launch": nbytes, "kernel_us": main_ms * 1e3},
     }
+    if not args.no_gated:
+        from long_sequence_causal_amd.inputs import gate_logs
+        gl = gated_leg(torch, la, inp, dev, args.steps, gate_logs)
+        eprint(f"[bench] gated forward: {gl['us_per_call']:.1f} us/call, "
+               f"{gl['achieved_GBs']:.0f} GB/s algorithmic")
+        rec["gated"] = gl
     if not args.no_bwd:
         del O, ws
         bw = backward_leg(torch, la, workload_inputs, WORKLOADS, dev, max(3, args.steps // 5))

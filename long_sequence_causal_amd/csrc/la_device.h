@@ -129,6 +129,30 @@ __device__ inline void dma4(const void* sbase, unsigned voff, unsigned lds) {
                : "memory", "m0");
 }
 
+// ---------------------------------------------------------------- wave-wide prefix sum
+// Inclusive prefix sum over the 64 lanes of a wave with DPP (VALU only, no
+// LDS round trip): Hillis-Steele inside each row of 16 lanes (row_shr 1, 2,
+// 4, 8; lanes whose source lies outside the row add 0), then the last lane of
+// row 0 into row 1 and of row 2 into row 3 (row_bcast:15), then lane 31 into
+// rows 2 and 3 (row_bcast:31).
+template <int CTRL, int ROWMASK>
+__device__ inline float dpp_or_zero(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWMASK, 0xF, false));
+}
+__device__ inline float wave_prefix_sum(float x) {
+  x += dpp_or_zero<0x111, 0xF>(x);  // row_shr:1
+  x += dpp_or_zero<0x112, 0xF>(x);  // row_shr:2
+  x += dpp_or_zero<0x114, 0xF>(x);  // row_shr:4
+  x += dpp_or_zero<0x118, 0xF>(x);  // row_shr:8
+  x += dpp_or_zero<0x142, 0xA>(x);  // row_bcast:15 -> rows 1, 3
+  x += dpp_or_zero<0x143, 0xC>(x);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
+__device__ inline float lane_value(float x, int lane) {  // x of a wave-uniform lane
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+
 // ---------------------------------------------------------------- small helpers
 __device__ inline float pow_lam(float lg2, float n) {
   // lambda^n = 2^(n log2 lambda); only non-negative n are formed.

@@ -310,27 +310,22 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob& jb, f32x4 (&acc
     float dc;  // decay of the state over the chunk
     if constexpr (GATED) {
       // chunk-local cumulative log-gate in log2 units, lane = token
-      float c2 = *reinterpret_cast<const float*>(smem + LY::OFF_G + st * LY::GB + 4 * lane) *
-                 1.4426950408889634f;
-#pragma unroll
-      for (int d = 1; d < CH; d <<= 1) {
-        const float y = __shfl_up(c2, d, 64);
-        if (lane >= d) c2 += y;
-      }
-      const float clast = __shfl(c2, cl - 1, 64);
+      const float c2 = wave_prefix_sum(
+          *reinterpret_cast<const float*>(smem + LY::OFF_G + st * LY::GB + 4 * lane) *
+          1.4426950408889634f);
+      const float clast = lane_value(c2, cl - 1);
       gsum2 += clast;
       dc = exp2f(clast);
+      // factors of this lane's own token, gathered by the slots that need them
+      const float ew = (lane < cl) ? exp2f(clast - c2) : 0.0f;  // update weight
 #pragma unroll
       for (int js = 0; js < NJS; ++js)
 #pragma unroll
-        for (int x = 0; x < E; ++x) {
-          const int j = slot_token<T>(js * KS, g, x);
-          const float cj = __shfl(c2, j, 64);
-          wv[js][x] = (j < cl) ? exp2f(clast - cj) : 0.0f;
-        }
+        for (int x = 0; x < E; ++x) wv[js][x] = __shfl(ew, slot_token<T>(js * KS, g, x), 64);
       if (OUT) {
+        const float eq = exp2f(c2);  // inter-chunk factor of query token i
 #pragma unroll
-        for (int it = 0; it < 4; ++it) qf[it] = exp2f(__shfl(c2, 16 * it + l16, 64));
+        for (int it = 0; it < 4; ++it) qf[it] = __shfl(eq, 16 * it + l16, 64);
 #pragma unroll
         for (int sti = 0; sti < NST; ++sti) {
           const int idx = w + NW * sti;
