@@ -444,6 +444,192 @@ int lao_scan_gated(int64_t B, int64_t H, int64_t P, int64_t dk, int64_t dv,
   return LAO_OK;
 }
 
+/*
+ * Backward of the gated recurrence (lao_fwd_gated) for the same loss
+ *   l = sum_t <do_t, o_t> + <dS_end, S_end>,
+ * with G_t = dl/dS_t and the gate of token t scaling S_{t-1}:
+ *   G_t  = q_t do_t^T + U_t,   U_L = dS_end,   U_{t-1} = alpha_t G_t
+ *   dq_t = S_t do_t            dk_t = G_t v_t        dv_t = G_t^T k_t
+ *   dS0  = U_0 = alpha_1 G_1
+ *   dg_t = d l / d log(alpha_t) = alpha_t <G_t, S_{t-1}>   (Frobenius)
+ * The last term needs S_{t-1} during the reverse sweep: each row block keeps
+ * its state every LAO_CKPT tokens on the way forward and recomputes the
+ * states of one stretch at a time on the way back (the same recurrence,
+ * re-run).  Per row block the products are summed over the block's rows,
+ * and the blocks' partial sums are added in block order afterwards.
+ * S0, dS_end may be NULL (zero); dS0 may be NULL.  dG is [B, H, L].
+ */
+#define LAO_CKPT 64
+int lao_bwd_gated(int64_t B, int64_t H, int64_t L, int64_t dk, int64_t dv, int64_t nseg,
+                  const double* Q, const double* K, const double* V, const double* Gl,
+                  const double* S0, const double* dO, const double* dS_end, double* dQ,
+                  double* dK, double* dV, double* dS0, double* dG) {
+  if (!lao_check(B, H, L, dk, dv, nseg)) return LAO_EINVAL;
+  const int64_t Ls = L / nseg;
+  const int64_t nseq = B * H * nseg;
+  const int64_t nrb = (dk + LAO_BLK - 1) / LAO_BLK;
+  const int64_t ncb = (dv + LAO_BLK - 1) / LAO_BLK;
+  const int64_t nck = Ls / LAO_CKPT + 1;
+  double* part = (double*)calloc((size_t)(nseq * nrb * (Ls > 0 ? Ls : 1)), sizeof(double));
+  if (!part) return LAO_ENOMEM;
+  int fail = 0;
+
+  /* (1) dq_t = S_t do_t: forward sweep, rows of S split over threads. */
+#pragma omp parallel for collapse(2) schedule(dynamic)
+  for (int64_t n = 0; n < nseq; ++n) {
+    for (int64_t rb = 0; rb < nrb; ++rb) {
+      const int64_t r0 = rb * LAO_BLK;
+      const int64_t w = ((r0 + LAO_BLK < dk) ? r0 + LAO_BLK : dk) - r0;
+      double* S = (double*)malloc(sizeof(double) * (size_t)(w * dv));
+      if (!S) {
+        fail = 1;
+        continue;
+      }
+      for (int64_t i = 0; i < w; ++i)
+        for (int64_t j = 0; j < dv; ++j) S[i * dv + j] = S0 ? S0[(n * dk + r0 + i) * dv + j] : 0.0;
+      const double* k = K + n * Ls * dk;
+      const double* v = V + n * Ls * dv;
+      const double* go = dO + n * Ls * dv;
+      const double* gl = Gl + n * Ls;
+      for (int64_t t = 0; t < Ls; ++t) {
+        const double a = exp(gl[t]);
+        for (int64_t i = 0; i < w; ++i) {
+          const double ki = k[t * dk + r0 + i];
+          double acc = 0.0;
+          for (int64_t j = 0; j < dv; ++j) {
+            S[i * dv + j] = a * S[i * dv + j] + ki * v[t * dv + j];
+            acc += S[i * dv + j] * go[t * dv + j];
+          }
+          dQ[(n * Ls + t) * dk + r0 + i] = acc;
+        }
+      }
+      free(S);
+    }
+  }
+
+  /* (2) dk_t = G_t v_t, dS0 and the row block's share of <G_t, S_{t-1}>:
+   * reverse sweep, rows split; S_{t-1} recomputed from checkpoints. */
+#pragma omp parallel for collapse(2) schedule(dynamic)
+  for (int64_t n = 0; n < nseq; ++n) {
+    for (int64_t rb = 0; rb < nrb; ++rb) {
+      const int64_t r0 = rb * LAO_BLK;
+      const int64_t w = ((r0 + LAO_BLK < dk) ? r0 + LAO_BLK : dk) - r0;
+      const size_t blk = (size_t)(w * dv);
+      double* U = (double*)malloc(sizeof(double) * blk);
+      double* ck = (double*)malloc(sizeof(double) * blk * (size_t)nck);
+      double* run = (double*)malloc(sizeof(double) * blk * (LAO_CKPT + 1));
+      if (!U || !ck || !run) {
+        free(U), free(ck), free(run);
+        fail = 1;
+        continue;
+      }
+      const double* q = Q + n * Ls * dk;
+      const double* k = K + n * Ls * dk;
+      const double* v = V + n * Ls * dv;
+      const double* go = dO + n * Ls * dv;
+      const double* gl = Gl + n * Ls;
+      /* forward: S_t of this row block, kept at t = 0, LAO_CKPT, 2 LAO_CKPT, ... */
+      double* S = run;
+      for (int64_t i = 0; i < w; ++i)
+        for (int64_t j = 0; j < dv; ++j) S[i * dv + j] = S0 ? S0[(n * dk + r0 + i) * dv + j] : 0.0;
+      for (int64_t t = 0; t < Ls; ++t) {
+        if (t % LAO_CKPT == 0) memcpy(ck + (size_t)(t / LAO_CKPT) * blk, S, sizeof(double) * blk);
+        const double a = exp(gl[t]);
+        for (int64_t i = 0; i < w; ++i)
+          for (int64_t j = 0; j < dv; ++j)
+            S[i * dv + j] = a * S[i * dv + j] + k[t * dk + r0 + i] * v[t * dv + j];
+      }
+      for (int64_t i = 0; i < w; ++i)
+        for (int64_t j = 0; j < dv; ++j)
+          U[i * dv + j] = dS_end ? dS_end[(n * dk + r0 + i) * dv + j] : 0.0;
+      /* backward, one stretch [t0, t1) at a time, last stretch first */
+      for (int64_t t0 = ((Ls - 1) / LAO_CKPT) * LAO_CKPT; t0 >= 0 && Ls > 0; t0 -= LAO_CKPT) {
+        const int64_t t1 = (t0 + LAO_CKPT < Ls) ? t0 + LAO_CKPT : Ls;
+        /* run[m] = S_{t0 + m}, i.e. the state before token t0 + m */
+        memcpy(run, ck + (size_t)(t0 / LAO_CKPT) * blk, sizeof(double) * blk);
+        for (int64_t t = t0; t < t1 - 1; ++t) {
+          const double a = exp(gl[t]);
+          double* prev = run + (size_t)(t - t0) * blk;
+          double* next = prev + blk;
+          for (int64_t i = 0; i < w; ++i)
+            for (int64_t j = 0; j < dv; ++j)
+              next[i * dv + j] = a * prev[i * dv + j] + k[t * dk + r0 + i] * v[t * dv + j];
+        }
+        for (int64_t t = t1 - 1; t >= t0; --t) {
+          const double a = exp(gl[t]);
+          const double* Sprev = run + (size_t)(t - t0) * blk; /* S_{t-1} */
+          double dot = 0.0;
+          for (int64_t i = 0; i < w; ++i) {
+            const double qi = q[t * dk + r0 + i];
+            double acc = 0.0;
+            for (int64_t j = 0; j < dv; ++j) {
+              const double G = qi * go[t * dv + j] + U[i * dv + j];
+              acc += G * v[t * dv + j];
+              dot += G * Sprev[i * dv + j];
+              U[i * dv + j] = a * G;
+            }
+            dK[(n * Ls + t) * dk + r0 + i] = acc;
+          }
+          part[(n * nrb + rb) * Ls + t] = dot;
+        }
+      }
+      if (dS0)
+        for (int64_t i = 0; i < w; ++i)
+          for (int64_t j = 0; j < dv; ++j) dS0[(n * dk + r0 + i) * dv + j] = U[i * dv + j];
+      free(U), free(ck), free(run);
+    }
+  }
+
+  /* (3) dv_t = G_t^T k_t: the same reverse sweep, columns split. */
+#pragma omp parallel for collapse(2) schedule(dynamic)
+  for (int64_t n = 0; n < nseq; ++n) {
+    for (int64_t cb = 0; cb < ncb; ++cb) {
+      const int64_t c0 = cb * LAO_BLK;
+      const int64_t w = ((c0 + LAO_BLK < dv) ? c0 + LAO_BLK : dv) - c0;
+      double* U = (double*)malloc(sizeof(double) * (size_t)(dk * w));
+      double* acc = (double*)malloc(sizeof(double) * (size_t)w);
+      if (!U || !acc) {
+        free(U), free(acc);
+        fail = 1;
+        continue;
+      }
+      for (int64_t i = 0; i < dk; ++i)
+        for (int64_t j = 0; j < w; ++j)
+          U[i * w + j] = dS_end ? dS_end[(n * dk + i) * dv + c0 + j] : 0.0;
+      const double* q = Q + n * Ls * dk;
+      const double* k = K + n * Ls * dk;
+      const double* go = dO + n * Ls * dv;
+      const double* gl = Gl + n * Ls;
+      for (int64_t t = Ls - 1; t >= 0; --t) {
+        const double a = exp(gl[t]);
+        for (int64_t j = 0; j < w; ++j) acc[j] = 0.0;
+        for (int64_t i = 0; i < dk; ++i) {
+          const double qi = q[t * dk + i];
+          const double ki = k[t * dk + i];
+          for (int64_t j = 0; j < w; ++j) {
+            const double G = qi * go[t * dv + c0 + j] + U[i * w + j];
+            acc[j] += ki * G;
+            U[i * w + j] = a * G;
+          }
+        }
+        for (int64_t j = 0; j < w; ++j) dV[(n * Ls + t) * dv + c0 + j] = acc[j];
+      }
+      free(acc), free(U);
+    }
+  }
+
+  /* dg_t = alpha_t * sum over row blocks (in block order) */
+  if (!fail)
+    for (int64_t n = 0; n < nseq; ++n)
+      for (int64_t t = 0; t < Ls; ++t) {
+        double sum = 0.0;
+        for (int64_t rb = 0; rb < nrb; ++rb) sum += part[(n * nrb + rb) * Ls + t];
+        dG[n * Ls + t] = exp(Gl[n * Ls + t]) * sum;
+      }
+  free(part);
+  return fail ? LAO_ENOMEM : LAO_OK;
+}
+
 int lao_abi_version(void) { return 1; }
 
 /* Number of OpenMP threads the oracle's parallel loops use. */

@@ -59,6 +59,8 @@ def bind(lib):
     lib.lao_fwd_gated.restype = ctypes.c_int
     lib.lao_scan_gated.argtypes = [i64] * 5 + [dp] * 5 + [ctypes.c_int]
     lib.lao_scan_gated.restype = ctypes.c_int
+    lib.lao_bwd_gated.argtypes = [i64] * 6 + [dp] * 12
+    lib.lao_bwd_gated.restype = ctypes.c_int
     lib.lao_threads.restype = ctypes.c_int
     lib.lao_threads.argtypes = []
     return lib
@@ -184,3 +186,21 @@ def scan_gated(dS, LD, S0=None, reverse: bool = False):
                                 _ptr(S_start), _ptr(S_end), int(bool(reverse)))
     _check(rc, "scan_gated")
     return S_start, S_end
+
+
+def bwd_gated(Q, K, V, G, dO, S0=None, dS_end=None, nseg: int = 1):
+    """Backward of the gated recurrence; returns (dQ, dK, dV, dS0, dG) with
+    dG = d loss / d log(alpha) [B,H,L]."""
+    Q, K, V, G, dO, S0, dS_end = map(_f64, (Q, K, V, G, dO, S0, dS_end))
+    B, H, L, dk = Q.shape
+    dv = V.shape[-1]
+    dQ = np.empty((B, H, L, dk))
+    dK = np.empty((B, H, L, dk))
+    dV = np.empty((B, H, L, dv))
+    dS0 = np.empty((B, H, nseg, dk, dv))
+    dG = np.empty((B, H, L))
+    rc = _load().lao_bwd_gated(B, H, L, dk, dv, nseg, _ptr(Q), _ptr(K), _ptr(V), _ptr(G),
+                               _ptr(S0), _ptr(dO), _ptr(dS_end), _ptr(dQ), _ptr(dK), _ptr(dV),
+                               _ptr(dS0), _ptr(dG))
+    _check(rc, "bwd_gated")
+    return dQ, dK, dV, dS0, dG

@@ -69,6 +69,22 @@ MUTATIONS = [
      "X = exp(LD[bh * P + s]) * X + dS[(bh * P + s) * E + e];",
      "X = exp(LD[bh * P + (s + 1) % P]) * X + dS[(bh * P + s) * E + e];",
      [pins.test_gated_hand_example_scan, pins.test_gated_segments_with_scanned_starts_equal_monolithic]),
+    ("gate of the wrong token in the gated reverse sweep (dv)",
+     """      for (int64_t t = Ls - 1; t >= 0; --t) {
+        const double a = exp(gl[t]);
+        for (int64_t j = 0; j < w; ++j) acc[j] = 0.0;""",
+     """      for (int64_t t = Ls - 1; t >= 0; --t) {
+        const double a = exp(gl[t > 0 ? t - 1 : 0]);
+        for (int64_t j = 0; j < w; ++j) acc[j] = 0.0;""",
+     [lambda: pins.test_gated_backward_finite_differences(150)]),
+    ("gate factor dropped from the log-gate gradient",
+     "dG[n * Ls + t] = exp(Gl[n * Ls + t]) * sum;",
+     "dG[n * Ls + t] = sum;",
+     [lambda: pins.test_gated_backward_finite_differences(65), pins.test_gated_log_gate_gradient_identity]),
+    ("state after the token instead of before it in the log-gate gradient",
+     "const double* Sprev = run + (size_t)(t - t0) * blk; /* S_{t-1} */",
+     "const double* Sprev = run + (size_t)(t - t0 + (t + 1 < t1 ? 1 : 0)) * blk; /* S_{t-1} */",
+     [lambda: pins.test_gated_backward_finite_differences(150)]),
 ]
 
 

@@ -479,3 +479,70 @@ def test_gated_segments_with_scanned_starts_equal_monolithic():
     O, _ = lao.fwd_gated(Q, K, V, G, S0=S_start, nseg=P)
     assert _rel(O, O_ref) < 1e-12
     assert _rel(S_end, S_ref[:, :, 0]) < 1e-12
+
+
+def _gated_loss(Q, K, V, G, dO, S0, dS_end, nseg=1):
+    O, S = lao.fwd_gated(Q, K, V, G, S0=S0, nseg=nseg)
+    return float((O * dO).sum() + (S * dS_end).sum())
+
+
+@pytest.mark.parametrize("L", [1, 63, 64, 65, 150])
+def test_gated_backward_finite_differences(L):
+    rng = np.random.default_rng(200 + L)
+    B, H, dk, dv = 1, 1, 8, 6
+    Q, K, V, dO = (_rand(rng, B, H, L, d) for d in (dk, dk, dv, dv))
+    G = -rng.uniform(0.0, 0.3, size=(B, H, L))
+    S0, dSe = _rand(rng, B, H, 1, dk, dv), _rand(rng, B, H, 1, dk, dv)
+    dQ, dK, dV, dS0, dG = lao.bwd_gated(Q, K, V, G, dO, S0=S0, dS_end=dSe)
+    f = lambda **kw: _gated_loss(*(kw.get(n, x) for n, x in
+                                   (("Q", Q), ("K", K), ("V", V), ("G", G), ("dO", dO),
+                                    ("S0", S0), ("dS_end", dSe))))
+    eps = 1e-6
+    for t in sorted({0, L // 2, L - 1}):
+        e = np.zeros_like(G)
+        e[0, 0, t] = eps
+        fd = (f(G=G + e) - f(G=G - e)) / (2 * eps)
+        assert abs(dG[0, 0, t] - fd) <= 1e-6 * max(1.0, abs(fd))
+        for name, X, dX in (("Q", Q, dQ), ("K", K, dK), ("V", V, dV)):
+            e = np.zeros_like(X)
+            e[0, 0, t, 1] = eps
+            fd = (f(**{name: X + e}) - f(**{name: X - e})) / (2 * eps)
+            assert abs(dX[0, 0, t, 1] - fd) <= 1e-6 * max(1.0, abs(fd))
+    e = np.zeros_like(S0)
+    e[0, 0, 0, 2, 3] = eps
+    fd = (f(S0=S0 + e) - f(S0=S0 - e)) / (2 * eps)
+    assert abs(dS0[0, 0, 0, 2, 3] - fd) <= 1e-6 * max(1.0, abs(fd))
+
+
+def test_gated_backward_constant_gate_is_the_fixed_decay():
+    rng = np.random.default_rng(210)
+    B, H, L, dk, dv = 1, 2, 130, 16, 8
+    Q, K, V, dO = (_rand(rng, B, H, L, d) for d in (dk, dk, dv, dv))
+    lam = np.array([0.7, 0.99])
+    G = np.broadcast_to(np.log(lam)[None, :, None], (B, H, L)).copy()
+    S0, dSe = _rand(rng, B, H, 1, dk, dv), _rand(rng, B, H, 1, dk, dv)
+    gated = lao.bwd_gated(Q, K, V, G, dO, S0=S0, dS_end=dSe)
+    fixed = lao.bwd(Q, K, V, lam, dO, S0=S0, dS_end=dSe)
+    for a, b in zip(gated[:4], fixed):
+        assert _rel(a, b) < 1e-12
+
+
+def test_gated_log_gate_gradient_identity():
+    """g_t enters only through the cumulative log-gates, which multiply q_u
+    by exp(c_u) and k_u by exp(-c_u) (u >= t) and S_end by exp(c_L), so
+        dg_t = sum_{u >= t} (q_u . dq_u - k_u . dk_u) + <dS_end, S_end>
+    within each segment; checked on segments of uneven content."""
+    rng = np.random.default_rng(211)
+    B, H, nseg, Ls, dk, dv = 1, 2, 3, 70, 8, 8
+    L = nseg * Ls
+    Q, K, V, dO = (_rand(rng, B, H, L, d) for d in (dk, dk, dv, dv))
+    G = -rng.uniform(0.0, 0.5, size=(B, H, L))
+    S0, dSe = _rand(rng, B, H, nseg, dk, dv), _rand(rng, B, H, nseg, dk, dv)
+    dQ, dK, dV, dS0, dG = lao.bwd_gated(Q, K, V, G, dO, S0=S0, dS_end=dSe, nseg=nseg)
+    _, S_end = lao.fwd_gated(Q, K, V, G, S0=S0, nseg=nseg, need_O=False)
+    r = (Q * dQ).sum(-1) - (K * dK).sum(-1)
+    for s in range(nseg):
+        sl = slice(s * Ls, (s + 1) * Ls)
+        tail = np.flip(np.cumsum(np.flip(r[..., sl], -1), -1), -1)
+        ref = tail + (dSe[:, :, s] * S_end[:, :, s]).sum((-1, -2))[..., None]
+        assert _rel(dG[..., sl], ref) < 1e-11
