@@ -216,6 +216,34 @@ la_status la_state_scan_gated(int64_t B, int64_t H, int32_t P, int32_t dk, int32
                               const float* dS, const float* log_decay, const float* S0,
                               float* S_start, float* S_end, int32_t reverse, void* stream);
 
+/* Workspace bytes la_chunk_bwd_gated needs for `shape`. */
+size_t la_bwd_gated_workspace_bytes(const la_shape* shape);
+
+/*
+ * Backward pass of la_chunk_fwd_gated for the loss
+ *     l = sum_t <dO_t, o_t> + <dS_end, S_end>   (per segment):
+ *     dq_t = S_t dO_t
+ *     dk_t = G_t v_t,  dv_t = G_t^T k_t,  G_t = q_t dO_t^T + alpha_{t+1} G_{t+1},
+ *            alpha_{L+1} G_{L+1} = dS_end
+ *     dS0  = alpha_1 G_1
+ *     d l / d log(alpha_t) = alpha_t <G_t, S_{t-1}>
+ *                          = sum_{u >= t} (q_u . dq_u - k_u . dk_u) + <dS_end, S_end>
+ * (the second form, used here, holds because log(alpha_t) enters only through
+ * the cumulative log-gates).
+ *   Q, K, V, log_alpha, S0   as for la_chunk_fwd_gated (S0 NULL = zero).
+ *   dO [B,H,L,dv] required; dS_end NULL = zero.
+ *   dQ, dK, dV                outputs, required, dtype of the inputs.
+ *   dS0 [B,H,nseg,dk,dv] fp32 output; NULL = not returned.
+ *   dlog_alpha [B,H,L] fp32   output; NULL = not returned.
+ *   ws, ws_bytes              workspace of la_bwd_gated_workspace_bytes().
+ * Errors as la_chunk_bwd.
+ */
+la_status la_chunk_bwd_gated(const la_shape* shape, const void* Q, const void* K,
+                             const void* V, const float* log_alpha, const float* S0,
+                             const void* dO, const float* dS_end, void* dQ, void* dK,
+                             void* dV, float* dS0, float* dlog_alpha, void* ws,
+                             size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -312,6 +312,126 @@ la_status la_chunk_fwd_gated(const la_shape* s, const void* Q, const void* K, co
                   static_cast<hipStream_t>(stream), true, log_alpha, LDw);
 }
 
+// gated backward workspace (in order): prepared start state [nseq][D][D],
+// start states and log-gates of the sweeps, shifted gates [nseq][Ls], the
+// final dQ-sweep state [nseq][D][D] and the gate-gradient block totals
+struct GatedBwdWs {
+  size_t A, W, LD, Gs, SE, TOT, total;
+};
+GatedBwdWs gated_bwd_ws(const Plan& p) {
+  GatedBwdWs w;
+  auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+  const size_t DD4 = (size_t)p.D * p.D * sizeof(float);
+  size_t o = 0;
+  w.A = o;  o += up((size_t)p.nseq * DD4);
+  w.W = o;  o += up(scan_ws_bytes(p));
+  w.LD = o; o += up((size_t)p.nseq * (size_t)(p.split > 1 ? p.split - 1 : 0) * sizeof(float));
+  w.Gs = o; o += up((size_t)p.nseq * (size_t)p.Ls * sizeof(float));
+  w.SE = o; o += up((size_t)p.nseq * DD4);
+  w.TOT = o; o += up((size_t)p.nseq * (size_t)la::gate_grad_blocks(p.Ls) * sizeof(float));
+  w.total = o;
+  return w;
+}
+
+size_t la_bwd_gated_workspace_bytes(const la_shape* shape) {
+  Plan pl;
+  std::string keep = g_last_error;
+  if (check_shape(shape, &pl) != LA_OK) {
+    g_last_error = keep;
+    return 0;
+  }
+  return gated_bwd_ws(pl).total;
+}
+
+la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, const void* V,
+                             const float* log_alpha, const float* S0, const void* dO,
+                             const float* dS_end, void* dQ, void* dK, void* dV, float* dS0,
+                             float* dlog_alpha, void* ws, size_t ws_bytes, void* stream) {
+  Plan pl;
+  la_status r = check_shape(s, &pl);
+  if (r != LA_OK) return r;
+  const bool has_tokens = pl.nseq > 0 && pl.Ls > 0;
+  if (has_tokens && (!Q || !K || !V || !log_alpha || !dO || !dQ || !dK || !dV))
+    return fail(LA_ERR_INVALID_ARG, "Q, K, V, log_alpha, dO, dQ, dK and dV are required");
+  const void* ptrs[] = {Q, K, V, log_alpha, S0, dO, dS_end, dQ, dK, dV, dS0, dlog_alpha, ws};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(LA_ERR_INVALID_ARG, "pointer %p is not 16-byte aligned", p);
+  const GatedBwdWs L = gated_bwd_ws(pl);
+  if (L.total > 0 && (!ws || ws_bytes < L.total))
+    return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
+                ws ? ws_bytes : (size_t)0);
+  if (pl.nseq == 0) return LA_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  float* A = reinterpret_cast<float*>(base + L.A);
+  float* W = reinterpret_cast<float*>(base + L.W);
+  float* LDw = reinterpret_cast<float*>(base + L.LD);
+  float* Gs = reinterpret_cast<float*>(base + L.Gs);
+  float* SE = reinterpret_cast<float*>(base + L.SE);
+  float* TOT = reinterpret_cast<float*>(base + L.TOT);
+  const int H = (int)s->H;
+  la::PrepArgs pa;
+  std::memset(&pa, 0, sizeof(pa));
+  pa.nseq = pl.nseq;
+  pa.D = pl.D;
+  pa.lam = nullptr;
+  pa.H = H;
+  pa.hdiv = s->nseg;
+  hipError_t e;
+
+  // dq_t = S_t dO_t: the gated forward recurrence of S^T read by dO, from
+  // S0^T; it ends with S_end^T, kept for the log-gate gradient
+  const float* start = nullptr;
+  if (S0) {
+    pa.src = S0;
+    pa.dst = A;
+    pa.transpose = 1;
+    pa.mode = 0;
+    if ((e = la::launch_prep(pa, st)) != hipSuccess) return hip_fail(e, "prep launch");
+    start = A;
+  }
+  const bool need_send = dlog_alpha && dS_end;
+  r = run_flow(pl, s->dtype, H, s->nseg, dO, V, K, nullptr, start, dQ, need_send ? SE : nullptr,
+               W, 0, st, true, log_alpha, LDw);
+  if (r != LA_OK) return r;
+
+  // reverse sweeps: from token t+1 back to t with alpha_{t+1}
+  if ((e = la::launch_shift_gates(log_alpha, Gs, pl.nseq, pl.Ls, st)) != hipSuccess)
+    return hip_fail(e, "gate shift launch");
+  // dv_t = G_t^T k_t, G accumulating q dO^T from dS_end (the first reverse
+  // step multiplies by 1); its final value G_1 gives dS0 = alpha_1 G_1
+  r = run_flow(pl, s->dtype, H, s->nseg, K, Q, dO, nullptr, dS_end, dV, dS0, W, 1, st, true, Gs,
+               LDw);
+  if (r != LA_OK) return r;
+  if (dS0 && (e = la::launch_scale_first_gate(dS0, log_alpha, pl.nseq, pl.Ls, pl.D, st)) != hipSuccess)
+    return hip_fail(e, "dS0 scale launch");
+  // dk_t = G_t v_t: the same reverse recurrence for G^T, whose sub-segment
+  // start states are the transposes of the ones just used
+  if (pl.split > 1) {
+    e = la::launch_transpose(W, pl.nseq * (pl.split - 1), pl.D, st);
+    if (e != hipSuccess) return hip_fail(e, "transpose launch");
+  }
+  start = nullptr;
+  if (dS_end) {
+    pa.src = dS_end;
+    pa.dst = A;
+    pa.transpose = 1;
+    pa.mode = 0;
+    if ((e = la::launch_prep(pa, st)) != hipSuccess) return hip_fail(e, "prep launch");
+    start = A;
+  }
+  r = run_main(pl, s->dtype, H, s->nseg, V, dO, Q, nullptr, start, dK, nullptr, W, 1, st, true, Gs);
+  if (r != LA_OK) return r;
+
+  // d l / d log(alpha_t) = sum_{u >= t} (q_u . dq_u - k_u . dk_u) + <dS_end, S_end>
+  if (dlog_alpha) {
+    e = la::launch_gate_grad(s->dtype, pl.D, Q, dQ, K, dK, dlog_alpha, TOT, dS_end,
+                             need_send ? SE : nullptr, pl.nseq, pl.Ls, st);
+    if (e != hipSuccess) return hip_fail(e, "gate gradient launch");
+  }
+  return LA_OK;
+}
+
 la_status la_state_scan_gated(int64_t B, int64_t H, int32_t P, int32_t dk, int32_t dv,
                               const float* dS, const float* log_decay, const float* S0,
                               float* S_start, float* S_end, int32_t reverse, void* stream) {

@@ -1,0 +1,201 @@
+// la_gate.hip -- the small kernels of the gated backward.
+//
+// Gated recurrence S_t = alpha_t S_{t-1} + k_t v_t^T (the data-dependent
+// gates of the Gated Linear Attention entry of the LASP-2 page's
+// related-paper list, one scalar gate per token and head), loss
+// l = sum_t <do_t, o_t> + <dS_end, S_end>:
+//
+//   * the reverse sweeps step from token t+1 back to t with alpha_{t+1}:
+//     k_shift_gates writes g'_t = g_{t+1} (0 for a segment's last token);
+//   * dS0 = alpha_1 G_1: k_scale_first_gate;
+//   * d l / d log(alpha_t) = sum_{u >= t} (q_u . dq_u - k_u . dk_u)
+//     + <dS_end, S_end> within each segment (g_t enters only through the
+//     cumulative log-gates, which scale q_u by exp(c_u), k_u by exp(-c_u) and
+//     S_end by exp(c_L)): k_gate_grad_blocks forms r_u = q_u . dq_u - k_u . dk_u
+//     and its reverse cumulative sum inside blocks of 1024 tokens,
+//     k_gate_grad_totals the suffix sums of the block totals (plus the S_end
+//     term) per sequence, and k_gate_grad_finish adds them.
+#include "la_device.h"
+#include "la_internal.h"
+
+namespace la {
+
+constexpr int GBLK = 1024;  // tokens per block of the gate-gradient scan
+
+__global__ __launch_bounds__(256) void k_shift_gates(const float* G, float* Gs, int64_t nseq,
+                                                     int64_t Ls) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= nseq * Ls) return;
+  const int64_t t = i % Ls;
+  Gs[i] = (t + 1 < Ls) ? G[i + 1] : 0.0f;
+}
+
+// X[n] *= exp(G[n][0]) for nseq D x D states
+__global__ __launch_bounds__(256) void k_scale_first_gate(float* X, const float* G, int64_t nseq,
+                                                          int64_t Ls, int64_t DD) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= nseq * DD) return;
+  const int64_t n = i / DD;
+  X[i] *= expf(G[n * Ls]);
+}
+
+template <typename T>
+__device__ inline float dot8(const T* a, const T* b) {
+  float s = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s += (float)a[e] * (float)b[e];
+  return s;
+}
+
+// One workgroup per (sequence, block of GBLK tokens).  Sixteen lanes share a
+// token (8 features each, D / 8 lanes in use), reduce across the 16 with
+// shuffles, then the block's reverse cumulative sum is taken in LDS:
+// dG[t] = sum_{u >= t in block} r_u, and the block total goes to tot[n][b].
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_gate_grad_blocks(const T* Q, const T* dQ, const T* K,
+                                                          const T* dK, float* dG, float* tot,
+                                                          int64_t Ls, int64_t nb) {
+  static_assert(D / 8 <= 16, "16 lanes of 8 features cover a row");
+  __shared__ float r[GBLK];
+  const int64_t n = blockIdx.x / nb;
+  const int64_t b = blockIdx.x % nb;
+  const int64_t t0 = b * GBLK;
+  const int len = (int)((t0 + GBLK < Ls) ? GBLK : Ls - t0);
+  const int sub = threadIdx.x & 15;   // lane within the token's group
+  const int tok = threadIdx.x >> 4;   // 16 tokens per pass
+  for (int i = tok; i < GBLK; i += 16) {
+    float s = 0.0f;
+    if (i < len && sub < D / 8) {
+      const int64_t row = (n * Ls + t0 + i) * D + 8 * sub;
+      s = dot8(Q + row, dQ + row) - dot8(K + row, dK + row);
+    }
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) s += __shfl_xor(s, m, 16);
+    if (sub == 0) r[i] = s;  // tokens past the end hold 0
+  }
+  __syncthreads();
+  // reverse inclusive scan of r[0 .. GBLK) (Hillis-Steele, ping-pong free:
+  // each step reads before the barrier, writes after it)
+  for (int d = 1; d < GBLK; d <<= 1) {
+    float add[GBLK / 256];
+#pragma unroll
+    for (int j = 0; j < GBLK / 256; ++j) {
+      const int i = threadIdx.x + 256 * j;
+      add[j] = (i + d < GBLK) ? r[i + d] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < GBLK / 256; ++j) r[threadIdx.x + 256 * j] += add[j];
+    __syncthreads();
+  }
+  for (int i = threadIdx.x; i < len; i += 256) dG[n * Ls + t0 + i] = r[i];
+  if (threadIdx.x == 0) tot[n * nb + b] = r[0];
+}
+
+// One workgroup per sequence: tot[n][b] <- sum of tot[n][b'] for b' > b, plus
+// <dS_end[n], S_end[n]> (S_end given transposed, as the dQ sweep ends with
+// S^T; either may be null: no such term).  Thread j owns the run of blocks
+// [j m, (j+1) m), m = ceil(nb / 256): run sums, a reverse exclusive scan of
+// the 256 run sums in LDS, then each run written back from its own end.
+__global__ __launch_bounds__(256) void k_gate_grad_totals(float* tot, int64_t nb, const float* dSe,
+                                                          const float* SendT, int D) {
+  __shared__ float red[256];
+  const int64_t n = blockIdx.x;
+  const int j = threadIdx.x;
+  float e = 0.0f;
+  if (dSe && SendT) {
+    const int64_t DD = (int64_t)D * D;
+    for (int64_t i = j; i < DD; i += 256) {
+      const int64_t kk = i / D, vv = i % D;
+      e += dSe[n * DD + i] * SendT[n * DD + vv * D + kk];
+    }
+  }
+  red[j] = e;
+  __syncthreads();
+  for (int s2 = 128; s2 > 0; s2 >>= 1) {
+    if (j < s2) red[j] += red[j + s2];
+    __syncthreads();
+  }
+  const float end_term = red[0];
+  __syncthreads();
+  const int64_t m = (nb + 255) / 256;
+  const int64_t b0 = j * m, b1 = (b0 + m < nb) ? b0 + m : nb;
+  float run = 0.0f;
+  for (int64_t b = b0; b < b1; ++b) run += tot[n * nb + b];
+  red[j] = run;
+  __syncthreads();
+  // reverse exclusive scan over the runs: after = sum of runs j' > j
+  for (int d = 1; d < 256; d <<= 1) {
+    const float add = (j + d < 256) ? red[j + d] : 0.0f;
+    __syncthreads();
+    red[j] += add;
+    __syncthreads();
+  }
+  float acc = end_term + red[j] - run;  // sum of the runs after this one
+  for (int64_t b = b1 - 1; b >= b0; --b) {
+    const float x = tot[n * nb + b];
+    tot[n * nb + b] = acc;
+    acc += x;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_gate_grad_finish(float* dG, const float* tot, int64_t nseq,
+                                                          int64_t Ls, int64_t nb) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= nseq * Ls) return;
+  const int64_t n = i / Ls, t = i % Ls;
+  dG[i] += tot[n * nb + t / GBLK];
+}
+
+hipError_t launch_shift_gates(const float* G, float* Gs, int64_t nseq, int64_t Ls, hipStream_t s) {
+  const int64_t tot = nseq * Ls;
+  if (tot <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_shift_gates, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, G, Gs,
+                     nseq, Ls);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale_first_gate(float* X, const float* G, int64_t nseq, int64_t Ls, int D,
+                                   hipStream_t s) {
+  const int64_t DD = (int64_t)D * D, tot = nseq * DD;
+  if (tot <= 0 || Ls <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_scale_first_gate, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, X,
+                     G, nseq, Ls, DD);
+  return hipGetLastError();
+}
+
+int64_t gate_grad_blocks(int64_t Ls) { return (Ls + GBLK - 1) / GBLK; }
+
+template <typename T, int D>
+static hipError_t gate_grad_t(const void* Q, const void* dQ, const void* K, const void* dK,
+                              float* dG, float* tot, const float* dSe, const float* SendT,
+                              int64_t nseq, int64_t Ls, hipStream_t s) {
+  const int64_t nb = gate_grad_blocks(Ls);
+  hipLaunchKernelGGL((k_gate_grad_blocks<T, D>), dim3((unsigned)(nseq * nb)), dim3(256), 0, s,
+                     (const T*)Q, (const T*)dQ, (const T*)K, (const T*)dK, dG, tot, Ls, nb);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_gate_grad_totals, dim3((unsigned)nseq), dim3(256), 0, s, tot, nb, dSe,
+                     SendT, D);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t all = nseq * Ls;
+  hipLaunchKernelGGL(k_gate_grad_finish, dim3((unsigned)((all + 255) / 256)), dim3(256), 0, s, dG,
+                     tot, nseq, Ls, nb);
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_grad(int dtype, int D, const void* Q, const void* dQ, const void* K,
+                            const void* dK, float* dG, float* tot, const float* dSe,
+                            const float* SendT, int64_t nseq, int64_t Ls, hipStream_t s) {
+  if (nseq <= 0 || Ls <= 0) return hipSuccess;
+  if (dtype == 0) {
+    if (D == 64) return gate_grad_t<__bf16, 64>(Q, dQ, K, dK, dG, tot, dSe, SendT, nseq, Ls, s);
+    if (D == 128) return gate_grad_t<__bf16, 128>(Q, dQ, K, dK, dG, tot, dSe, SendT, nseq, Ls, s);
+  } else {
+    if (D == 64) return gate_grad_t<float, 64>(Q, dQ, K, dK, dG, tot, dSe, SendT, nseq, Ls, s);
+    if (D == 128) return gate_grad_t<float, 128>(Q, dQ, K, dK, dG, tot, dSe, SendT, nseq, Ls, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace la

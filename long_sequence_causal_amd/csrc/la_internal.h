@@ -84,6 +84,17 @@ hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, bool with_o, int64_t n
                       hipStream_t stream);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
 hipError_t launch_prep(const PrepArgs& a, hipStream_t stream);
+// Gated backward helpers (la_gate.hip): shifted gates for the reverse
+// sweeps, dS0 scaled by the first gate of each sequence, and the log-gate
+// gradient from Q, dQ, K, dK (tot: [nseq][gate_grad_blocks(Ls)] floats of
+// workspace; dSe and SendT may be null).
+hipError_t launch_shift_gates(const float* G, float* Gs, int64_t nseq, int64_t Ls, hipStream_t s);
+hipError_t launch_scale_first_gate(float* X, const float* G, int64_t nseq, int64_t Ls, int D,
+                                   hipStream_t s);
+int64_t gate_grad_blocks(int64_t Ls);
+hipError_t launch_gate_grad(int dtype, int D, const void* Q, const void* dQ, const void* K,
+                            const void* dK, float* dG, float* tot, const float* dSe,
+                            const float* SendT, int64_t nseq, int64_t Ls, hipStream_t s);
 // In-place transpose of nmat consecutive D x D fp32 matrices.
 hipError_t launch_transpose(float* W, int64_t nmat, int D, hipStream_t stream);
 

@@ -22,7 +22,8 @@ LA_BF16, LA_FP32 = 0, 1
 
 EXPORTS = ("la_version", "la_status_str", "la_last_error", "la_fwd_workspace_bytes",
            "la_chunk_fwd", "la_state_scan", "la_bwd_workspace_bytes", "la_chunk_bwd",
-           "la_fwd_gated_workspace_bytes", "la_chunk_fwd_gated", "la_state_scan_gated")
+           "la_fwd_gated_workspace_bytes", "la_chunk_fwd_gated", "la_state_scan_gated",
+           "la_bwd_gated_workspace_bytes", "la_chunk_bwd_gated")
 
 
 class LinAttnError(RuntimeError):
@@ -72,6 +73,10 @@ def lib():
     L.la_fwd_gated_workspace_bytes.argtypes = [sp]
     L.la_chunk_fwd_gated.restype = ctypes.c_int
     L.la_chunk_fwd_gated.argtypes = [sp] + [vp] * 8 + [sz, vp]
+    L.la_bwd_gated_workspace_bytes.restype = sz
+    L.la_bwd_gated_workspace_bytes.argtypes = [sp]
+    L.la_chunk_bwd_gated.restype = ctypes.c_int
+    L.la_chunk_bwd_gated.argtypes = [sp] + [vp] * 13 + [sz, vp]
     L.la_state_scan_gated.restype = ctypes.c_int
     L.la_state_scan_gated.argtypes = [i64, i64, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp]
     _lib = L
@@ -257,3 +262,39 @@ def la_chunk_bwd(q, k, v, lam, dO, S0=None, dS_end=None, nseg: int = 1,
                               _ptr(dS0), _ptr(ws), ws.numel() if ws is not None else 0,
                               _stream()))
     return dQ, dK, dV, dS0
+
+
+def la_bwd_gated_workspace_bytes(shape: la_shape) -> int:
+    return int(lib().la_bwd_gated_workspace_bytes(ctypes.byref(shape)))
+
+
+def la_chunk_bwd_gated(q, k, v, log_alpha, dO, S0=None, dS_end=None, nseg: int = 1,
+                       need_dS0: bool = True, need_dlog_alpha: bool = True, split: int = 0,
+                       workspace=None, out=None):
+    """Backward of the gated forward.  Returns (dQ, dK, dV, dS0 or None,
+    dlog_alpha or None); `out` may give all five preallocated (None entries
+    are not returned)."""
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q.dtype)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (dO, "dO")):
+        _need(t, n, q.dtype)
+    _need(log_alpha, "log_alpha", torch.float32)
+    if log_alpha.shape != (B, H, L):
+        raise ValueError(f"log_alpha has shape {tuple(log_alpha.shape)}, expected {(B, H, L)}")
+    _need(S0, "S0", torch.float32)
+    _need(dS_end, "dS_end", torch.float32)
+    shape = make_shape(B, H, L, dk, dv, nseg, dt, split)
+    if out is not None:
+        dQ, dK, dV, dS0, dG = out
+    else:
+        dQ, dK, dV = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dS0 = torch.empty((B, H, nseg, dk, dv), dtype=torch.float32, device=q.device) if need_dS0 else None
+        dG = torch.empty((B, H, L), dtype=torch.float32, device=q.device) if need_dlog_alpha else None
+    nbytes = la_bwd_gated_workspace_bytes(shape)
+    ws = workspace if workspace is not None else _workspace(nbytes, q.device)
+    _check(lib().la_chunk_bwd_gated(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                                    _ptr(S0), _ptr(dO), _ptr(dS_end), _ptr(dQ), _ptr(dK), _ptr(dV),
+                                    _ptr(dS0), _ptr(dG), _ptr(ws), ws.numel() if ws is not None else 0,
+                                    _stream()))
+    return dQ, dK, dV, dS0, dG

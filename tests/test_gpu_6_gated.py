@@ -167,3 +167,49 @@ def test_gated_empty_sequence_returns_initial_state():
     _, S_end = la.la_chunk_fwd_gated(q, q, q, G, S0=S0, need_O=False)
     torch.cuda.synchronize()
     assert bool((S_end == S0).all())
+
+
+BWD_CASES = [
+    # dtype, D, B, H, L, nseg, split, S0 std, dS_end std
+    ("bf16", 128, 1, 3, 337, 1, 0, 0.5, 0.5),
+    ("bf16", 128, 2, 2, 64 * 8, 1, 3, 0.0, 0.0),
+    ("bf16", 64, 1, 2, 64 * 5 + 30, 1, 2, 0.5, 1.0),
+    ("bf16", 128, 1, 2, 64 * 6, 3, 2, 0.5, 0.5),
+    ("bf16", 128, 2, 16, 64 * 20, 1, 0, 0.5, 0.5),
+    ("fp32", 64, 1, 2, 1024 + 17, 1, 0, 0.0, 0.0),
+    ("fp32", 64, 2, 2, 130 * 2, 2, 2, 0.5, 0.5),
+    ("fp32", 128, 1, 1, 70, 1, 0, 0.5, 0.5),
+]
+
+
+@pytest.mark.parametrize("dtype,D,B,H,L,nseg,split,s0,dse", BWD_CASES)
+def test_gated_bwd_matches_oracle(dtype, D, B, H, L, nseg, split, s0, dse):
+    log(f"gated bwd dtype={dtype} D={D} B={B} H={H} L={L} nseg={nseg} split={split} s0={s0} dSe={dse}")
+    inp = make_inputs(B, H, L, D, D, dtype=dtype, s0_std=s0, nseg=nseg, need_dO=True,
+                      dS_end_std=dse, seed=4000 + L + D, device="cuda")
+    G = gate_logs(decay_schedule(H, True), B, L, 4000 + L, device="cuda")
+    q, k, v, S0, dO, dSe = (inp[x] for x in ("q", "k", "v", "S0", "dO", "dS_end"))
+    got = la.la_chunk_bwd_gated(q, k, v, G, dO, S0=S0, dS_end=dSe, nseg=nseg, split=split)
+    torch.cuda.synchronize()
+    ref = lao.bwd_gated(f64(q), f64(k), f64(v), f64(G), f64(dO), S0=f64(S0), dS_end=f64(dSe),
+                        nseg=nseg)
+    errs = [rel_err(f64(x), r) for x, r in zip(got, ref)]
+    log("  err dQ={:.3e} dK={:.3e} dV={:.3e} dS0={:.3e} dlogalpha={:.3e}".format(*errs))
+    assert max(errs) <= TOL[dtype]
+
+
+def test_gated_bwd_optional_outputs():
+    """dS0 and the log-gate gradient may be skipped; the other gradients do
+    not change."""
+    B, H, L, D = 1, 2, 64 * 4 + 3, 128
+    inp = make_inputs(B, H, L, D, D, dtype="bf16", s0_std=0.5, need_dO=True, dS_end_std=0.5,
+                      seed=4100, device="cuda")
+    G = gate_logs(decay_schedule(H, True), B, L, 4100, device="cuda")
+    q, k, v, S0, dO, dSe = (inp[x] for x in ("q", "k", "v", "S0", "dO", "dS_end"))
+    full = la.la_chunk_bwd_gated(q, k, v, G, dO, S0=S0, dS_end=dSe)
+    part = la.la_chunk_bwd_gated(q, k, v, G, dO, S0=S0, dS_end=dSe, need_dS0=False,
+                                 need_dlog_alpha=False)
+    torch.cuda.synchronize()
+    assert part[3] is None and part[4] is None
+    for a, b in zip(full[:3], part[:3]):
+        assert bool(torch.equal(a, b))
