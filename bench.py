@@ -95,7 +95,26 @@ def backward_leg(torch, la, workload_inputs, WORKLOADS, dev, iters):
     rec = {"workload": w.name, "B": B, "H": H, "L": L, "d": d, "us_per_call": ms * 1e3,
            "tokens_per_s": B * L / t, "alg_bytes": nbytes, "achieved_GBs": nbytes / t / 1e9,
            "frac_hbm": nbytes / t / 1e9 / HBM_PEAK_GBS, "tflops_alg": flops / t / 1e12}
-    del inp, q, k, v, dO, out, ws
+    # the same with per-token gates: adds the gates read and their gradient
+    # written (4 B each per token-head)
+    from long_sequence_causal_amd.inputs import gate_logs
+    G = gate_logs(lam, B, L, w.seed, device=dev)
+    dG = torch.empty((B, H, L), dtype=torch.float32, device=dev)
+    gout = out + (dG,)
+    gws = torch.empty(max(la.la_bwd_gated_workspace_bytes(shape), 1), dtype=torch.uint8, device=dev)
+
+    def gcall():
+        la.la_chunk_bwd_gated(q, k, v, G, dO, S0=S0, dS_end=dSe, out=gout, workspace=gws)
+
+    for _ in range(2):
+        gcall()
+    torch.cuda.synchronize()
+    gms = time_events(gcall, iters, torch.cuda.current_stream())
+    gbytes = nbytes + B * H * L * 8
+    gt = gms / 1e3
+    rec["gated"] = {"us_per_call": gms * 1e3, "tokens_per_s": B * L / gt, "alg_bytes": gbytes,
+                    "achieved_GBs": gbytes / gt / 1e9, "frac_hbm": gbytes / gt / 1e9 / HBM_PEAK_GBS}
+    del inp, q, k, v, dO, out, ws, G, dG, gout, gws
     return rec
 
 
@@ -290,7 +309,7 @@ def main():
         del O, ws
         bw = backward_leg(torch, la, workload_inputs, WORKLOADS, dev, max(3, args.steps // 5))
         eprint(f"[bench] backward ({bw['workload']}): {bw['us_per_call']:.1f} us/call, "
-               f"{bw['achieved_GBs']:.0f} GB/s algorithmic")
+               f"{bw['achieved_GBs']:.0f} GB/s algorithmic; gated {bw['gated']['us_per_call']:.1f} us/call")
         rec["backward"] = bw
     if not args.no_cpu:
         eprint("[bench] CPU oracle baseline ...")
