@@ -204,3 +204,17 @@ def bwd_gated(Q, K, V, G, dO, S0=None, dS_end=None, nseg: int = 1):
                                _ptr(dS0), _ptr(dG))
     _check(rc, "bwd_gated")
     return dQ, dK, dV, dS0, dG
+
+
+def dlambda(Q, K, V, lam, dO, S0=None, dS_end=None, nseg: int = 1):
+    """Gradient of the loss sum_t <do_t, o_t> + <dS_end, S_end> with respect
+    to the per-head decay lambda [H]: every token's gate is lambda_h, so by
+    the chain rule dl/dlambda_h = sum over the head's tokens of
+    d l / d log(alpha_t) divided by lambda_h (the gated backward with
+    constant gates)."""
+    Q = _f64(Q)
+    B, H, L, _ = Q.shape
+    lam = _f64(lam)
+    G = np.broadcast_to(np.log(lam)[None, :, None], (B, H, L)).copy()
+    dG = bwd_gated(Q, K, V, G, dO, S0=S0, dS_end=dS_end, nseg=nseg)[4]
+    return dG.sum(axis=(0, 2)) / lam

@@ -546,3 +546,22 @@ def test_gated_log_gate_gradient_identity():
         tail = np.flip(np.cumsum(np.flip(r[..., sl], -1), -1), -1)
         ref = tail + (dSe[:, :, s] * S_end[:, :, s]).sum((-1, -2))[..., None]
         assert _rel(dG[..., sl], ref) < 1e-11
+
+
+def test_decay_gradient_finite_differences():
+    rng = np.random.default_rng(220)
+    B, H, nseg, L, dk, dv = 2, 2, 2, 2 * 75, 8, 6
+    Q, K, V, dO = (_rand(rng, B, H, L, d) for d in (dk, dk, dv, dv))
+    lam = np.array([0.8, 0.97])
+    S0, dSe = _rand(rng, B, H, nseg, dk, dv), _rand(rng, B, H, nseg, dk, dv)
+
+    def loss(l):
+        O, S = lao.fwd(Q, K, V, l, S0=S0, nseg=nseg)
+        return float((O * dO).sum() + (S * dSe).sum())
+
+    dl = lao.dlambda(Q, K, V, lam, dO, S0=S0, dS_end=dSe, nseg=nseg)
+    for h in range(H):
+        e = np.zeros(H)
+        e[h] = 1e-7
+        fd = (loss(lam + e) - loss(lam - e)) / 2e-7
+        assert abs(dl[h] - fd) <= 1e-5 * max(1.0, abs(fd))
