@@ -114,7 +114,24 @@ def backward_leg(torch, la, workload_inputs, WORKLOADS, dev, iters):
     gt = gms / 1e3
     rec["gated"] = {"us_per_call": gms * 1e3, "tokens_per_s": B * L / gt, "alg_bytes": gbytes,
                     "achieved_GBs": gbytes / gt / 1e9, "frac_hbm": gbytes / gt / 1e9 / HBM_PEAK_GBS}
-    del inp, q, k, v, dO, out, ws, G, dG, gout, gws
+    # the decay gradient (forward-mode tangent walk) on the same inputs: reads
+    # Q, K, V, dO once (4 d elements per token-head)
+    dlam = torch.empty((H,), dtype=torch.float32, device=dev)
+    tws = torch.empty(max(la.la_decay_grad_workspace_bytes(shape), 1), dtype=torch.uint8, device=dev)
+
+    def tcall():
+        la.la_decay_grad(q, k, v, lam, dO, S0=S0, dS_end=dSe, out=dlam, workspace=tws)
+
+    for _ in range(2):
+        tcall()
+    torch.cuda.synchronize()
+    tms = time_events(tcall, iters, torch.cuda.current_stream())
+    tbytes = B * H * L * 4 * d * 2
+    tt = tms / 1e3
+    rec["decay_grad"] = {"us_per_call": tms * 1e3, "tokens_per_s": B * L / tt, "alg_bytes": tbytes,
+                         "achieved_GBs": tbytes / tt / 1e9,
+                         "frac_hbm": tbytes / tt / 1e9 / HBM_PEAK_GBS}
+    del inp, q, k, v, dO, out, ws, G, dG, gout, gws, dlam, tws
     return rec
 
 
@@ -309,7 +326,8 @@ def main():
         del O, ws
         bw = backward_leg(torch, la, workload_inputs, WORKLOADS, dev, max(3, args.steps // 5))
         eprint(f"[bench] backward ({bw['workload']}): {bw['us_per_call']:.1f} us/call, "
-               f"{bw['achieved_GBs']:.0f} GB/s algorithmic; gated {bw['gated']['us_per_call']:.1f} us/call")
+               f"{bw['achieved_GBs']:.0f} GB/s algorithmic; gated {bw['gated']['us_per_call']:.1f} us/call; "
+               f"decay gradient {bw['decay_grad']['us_per_call']:.1f} us/call")
         rec["backward"] = bw
     if not args.no_cpu:
         eprint("[bench] CPU oracle baseline ...")

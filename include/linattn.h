@@ -168,7 +168,7 @@ size_t la_bwd_workspace_bytes(const la_shape* shape);
  *   dQ, dK [B,H,L,dk], dV [B,H,L,dv]   outputs, required, dtype of the inputs.
  *   dS0 [B,H,nseg,dk,dv] fp32          output; NULL = not returned.
  *   ws, ws_bytes          workspace of la_bwd_workspace_bytes().
- * lambda receives no gradient.
+ * lambda receives no gradient here; la_decay_grad computes it.
  */
 la_status la_chunk_bwd(const la_shape* shape, const void* Q, const void* K,
                        const void* V, const float* lambda, const float* S0,
@@ -243,6 +243,33 @@ la_status la_chunk_bwd_gated(const la_shape* shape, const void* Q, const void* K
                              const void* dO, const float* dS_end, void* dQ, void* dK,
                              void* dV, float* dS0, float* dlog_alpha, void* ws,
                              size_t ws_bytes, void* stream);
+
+/* Workspace bytes la_decay_grad needs for `shape`; 0 for an invalid shape. */
+size_t la_decay_grad_workspace_bytes(const la_shape* shape);
+
+/*
+ * Gradient of the loss of la_chunk_bwd with respect to the decays, for a
+ * trainable lambda (the per-head decay rate of the Lightning Attention-2
+ * entry of the LASP-2 page's related-paper list, there a fixed constant):
+ *     d l / d lambda_h,   l = sum_t <dO_t, o_t> + <dS_end, S_end>
+ * summed over every sequence (batch entry and segment) of head h.  Computed
+ * by forward-mode differentiation: the tangent state T_t = d S_t / d lambda
+ * obeys T_t = lambda T_{t-1} + S_{t-1}, T_0 = 0, and
+ *     d l / d lambda = sum_t dO_t . (q_t^T T_t) + <dS_end, T_end>
+ *                    = sum_t <G_t, S_{t-1}>     (G_t as in la_chunk_bwd).
+ * The tangent walk is chunked like la_chunk_fwd (state and tangent fp32,
+ * per-workgroup shares summed in fp64 in a fixed order).
+ *   Q, K, V, lambda, S0, shape   as for la_chunk_fwd (S0 NULL = zero).
+ *   dO [B,H,L,dv]                upstream gradient of O, required.
+ *   dS_end [B,H,nseg,dk,dv] fp32 upstream gradient of S_end; NULL = zero.
+ *   dlambda [H] fp32             output.
+ *   ws, ws_bytes                 workspace of la_decay_grad_workspace_bytes().
+ * Errors as la_chunk_bwd.
+ */
+la_status la_decay_grad(const la_shape* shape, const void* Q, const void* K,
+                        const void* V, const float* lambda, const float* S0,
+                        const void* dO, const float* dS_end, float* dlambda,
+                        void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

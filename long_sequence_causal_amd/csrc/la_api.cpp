@@ -211,6 +211,22 @@ la_status run_flow(const Plan& pl, int dtype, int H, int nseg, const void* Q, co
 }
 
 // gated forward workspace: the start states, then the sub-segment log-gates
+// Workspace of la_decay_grad: local, then start pairs (S, T) of sub-segments
+// 1..split-1 and one fp64 share per sub-segment.
+struct TangentWs {
+  size_t WS = 0, WT = 0, part = 0, total = 0;
+};
+TangentWs tangent_ws(const Plan& p) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  TangentWs w;
+  const size_t st = scan_ws_bytes(p);
+  w.WS = 0;
+  w.WT = up(st);
+  w.part = w.WT + up(st);
+  w.total = w.part + up((size_t)p.nseq * (size_t)p.split * sizeof(double));
+  return w;
+}
+
 size_t gated_ws_bytes(const Plan& p) {
   if (p.split <= 1) return 0;
   return scan_ws_bytes(p) + ((size_t)p.nseq * (size_t)(p.split - 1) * sizeof(float) + 255) / 256 * 256;
@@ -429,6 +445,63 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
                              need_send ? SE : nullptr, pl.nseq, pl.Ls, st);
     if (e != hipSuccess) return hip_fail(e, "gate gradient launch");
   }
+  return LA_OK;
+}
+
+size_t la_decay_grad_workspace_bytes(const la_shape* shape) {
+  Plan pl;
+  std::string keep = g_last_error;
+  if (check_shape(shape, &pl) != LA_OK) {
+    g_last_error = keep;
+    return 0;
+  }
+  return tangent_ws(pl).total;
+}
+
+la_status la_decay_grad(const la_shape* s, const void* Q, const void* K, const void* V,
+                        const float* lambda, const float* S0, const void* dO,
+                        const float* dS_end, float* dlambda, void* ws, size_t ws_bytes,
+                        void* stream) {
+  Plan pl;
+  la_status r = check_shape(s, &pl);
+  if (r != LA_OK) return r;
+  const bool has_tokens = pl.nseq > 0 && pl.Ls > 0;
+  if (has_tokens && (!Q || !K || !V || !dO))
+    return fail(LA_ERR_INVALID_ARG, "Q, K, V and dO are required");
+  if (s->H > 0 && (!lambda || !dlambda))
+    return fail(LA_ERR_INVALID_ARG, "lambda and dlambda are required");
+  const void* ptrs[] = {Q, K, V, lambda, S0, dO, dS_end, dlambda, ws};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(LA_ERR_INVALID_ARG, "pointer %p is not 16-byte aligned", p);
+  const TangentWs L = tangent_ws(pl);
+  if (L.total > 0 && (!ws || ws_bytes < L.total))
+    return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
+                ws ? ws_bytes : (size_t)0);
+  // the scan runs one thread per state element of every sequence
+  if (pl.split > 1 && (double)pl.nseq * pl.D * pl.D / 256.0 >= 2147483648.0)
+    return fail(LA_ERR_UNSUPPORTED, "too many sequences for a split plan");
+  if (s->H == 0) return LA_OK;
+  char* base = static_cast<char*>(ws);
+  la::TanArgs ta;
+  std::memset(&ta, 0, sizeof(ta));
+  ta.Q = Q;
+  ta.K = K;
+  ta.V = V;
+  ta.dO = dO;
+  ta.lam = lambda;
+  ta.S0 = S0;
+  ta.dSe = dS_end;
+  ta.WS = reinterpret_cast<float*>(base + L.WS);
+  ta.WT = reinterpret_cast<float*>(base + L.WT);
+  ta.part = reinterpret_cast<double*>(base + L.part);
+  ta.H = (int)s->H;
+  ta.nseg = s->nseg;
+  ta.split = pl.split;
+  ta.Ls = pl.Ls;
+  ta.Lp = pl.Lp;
+  hipError_t e = la::launch_tangent(ta, s->dtype, pl.D, pl.nseq, dlambda,
+                                    static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decay gradient launch");
   return LA_OK;
 }
 

@@ -22,6 +22,8 @@ namespace la {
 
 constexpr int GBLK = 1024;  // tokens per block of the gate-gradient scan
 
+int64_t gate_grad_blocks(int64_t Ls) { return (Ls + GBLK - 1) / GBLK; }
+
 __global__ __launch_bounds__(256) void k_shift_gates(const float* G, float* Gs, int64_t nseq,
                                                      int64_t Ls) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -163,8 +165,6 @@ hipError_t launch_scale_first_gate(float* X, const float* G, int64_t nseq, int64
                      G, nseq, Ls, DD);
   return hipGetLastError();
 }
-
-int64_t gate_grad_blocks(int64_t Ls) { return (Ls + GBLK - 1) / GBLK; }
 
 template <typename T, int D>
 static hipError_t gate_grad_t(const void* Q, const void* dQ, const void* K, const void* dK,

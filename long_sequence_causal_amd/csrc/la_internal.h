@@ -80,6 +80,30 @@ struct ScanArgs {
   const float* LD;   // [nseq][P]
 };
 
+// Decay gradient by the tangent recurrence (la_tangent.hip).  Sequence n has
+// head (n / nseg) % H and Ls tokens cut into `split` sub-segments of Lp.
+struct TanArgs {
+  const void* Q;     // [nseq][Ls][D] (main pass only)
+  const void* K;
+  const void* V;
+  const void* dO;    // (main pass only)
+  const float* lam;  // [H]
+  const float* S0;   // [nseq][D][D] or null
+  const float* dSe;  // [nseq][D][D] or null
+  float* WS;         // [nseq][split-1][D][D]: local, then start states
+  float* WT;         // the same for the tangent state
+  double* part;      // [nseq][split]: each sub-segment's share of the gradient
+  int H;
+  int nseg;
+  int split;
+  int64_t Ls;
+  int64_t Lp;
+};
+// Pre-pass over sub-segments 0..split-2, the scan of (state, tangent) pairs,
+// the main pass over every sub-segment and the per-head sum into dlam.
+hipError_t launch_tangent(const TanArgs& a, int dtype, int D, int64_t nseq, float* dlam,
+                          hipStream_t stream);
+
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, bool with_o, int64_t nwg,
                       hipStream_t stream);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);

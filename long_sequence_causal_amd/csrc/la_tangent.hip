@@ -1,0 +1,468 @@
+// la_tangent.hip -- gradient of the loss with respect to the fixed decay of
+// each head, by forward-mode differentiation of the chunkwise recurrence.
+//
+// With T_t = d S_t / d lambda (the tangent state), differentiating
+//   S_t = lambda S_{t-1} + k_t v_t^T,   o_t = q_t^T S_t
+// gives T_t = lambda T_{t-1} + S_{t-1} with T_0 = 0 (S_0 is an input), and
+// for the loss l = sum_t <dO_t, o_t> + <dS_end, S_end>
+//   d l / d lambda = sum_t dO_t . (q_t^T T_t) + <dS_end, T_end>.
+// The kernels carry U = lambda T, which obeys U_t = lambda (U_{t-1} + S_{t-1})
+// and takes the same powers of lambda as the forward pass.  Per 64-token
+// chunk (tokens i, j = 0..cl-1; S, U the states before it):
+//   sum_i dO_i . (q_i^T U_i) = <U, M1> + <S, M2>
+//                            + sum_{j<i} (i-j) lambda^(i-j) (q_i . k_j) (dO_i . v_j)
+//   M1 = sum_i lambda^(i+1) q_i dO_i^T,   M2 = sum_i (i+1) lambda^(i+1) q_i dO_i^T
+//   U <- lambda^cl (U + cl S) + sum_j (cl-1-j) lambda^(cl-1-j) k_j v_j^T
+//   S <- lambda^cl S + sum_j lambda^(cl-1-j) k_j v_j^T
+// and d l / d lambda = (1 / lambda) (sum_t dO_t . (q_t^T U_t) + <dS_end, U_end>).
+// Every term enters the result as it is; no partial sums cancel.  Still,
+// the result is a small difference of many terms (their absolute sum can be
+// hundreds of times larger), and U varies slowly along the sequence, so a
+// per-token rounding feeding U or M would add up coherently: in bf16 every
+// operand that carries a decay factor (the weighted dO of M1, M2 and the
+// weighted V of both updates) goes through the MFMA as hi + lo, and U, S
+// never leave fp32.  (The
+// reverse-mode identity d l / d lambda = (1 / lambda) sum_u u (q_u . dq_u -
+// k_u . dk_u) + ... does cancel: its terms exceed the result by a factor
+// that grows with the sequence length, which bf16 gradients cannot carry.)
+//
+// Parallel plan, as the forward's: sub-segments of Lp tokens.  Over n tokens
+// the pair moves as
+//   U <- lambda^n (U + n S) + dU,   S <- lambda^n S + dS
+// (the Jordan block of the derivative of lambda^n) with (dS, dU) the
+// sub-segment's local pair from zero.  The pre-pass forms
+// the local pairs (K, V only), the scan chains them from (S0, 0), the main
+// pass walks every sub-segment from its start pair and sums its share, and
+// the last kernel adds each head's shares in a fixed order.
+//
+// Inside a workgroup the layout is the forward walker's: wave w holds state
+// columns [16 w, 16 w + 16) of S and of U in MFMA accumulators; Q, K, V, dO
+// chunks go from HBM straight to padded token-major LDS tiles (double
+// buffered where two stages fit).  Intra-chunk scores K Q^T and V dO^T are
+// formed tile by tile in the same accumulator layout, so their product is
+// taken in registers without a P matrix in LDS; M1 and M2 are formed tile
+// by tile in the state's layout (the same transposed operands as the
+// update) and dotted with U and S at once, so neither is ever stored.
+#include "la_internal.h"
+#include "la_walk.h"
+
+namespace la {
+
+namespace {
+
+template <typename T, int D, bool MAIN>
+struct TanLayout {
+  typedef PadTile<T, CH, D> TN;
+  static constexpr int NTEN = MAIN ? 4 : 2;  // Q, K, V, dO  or  K, V
+  static constexpr int TB = TN::BYTES;
+  static constexpr int STAGE = NTEN * TB;
+  static constexpr int STAGES = 2 * STAGE <= LDS_MAX ? 2 : 1;
+  static constexpr int BYTES = STAGES * STAGE;
+  static constexpr int NW = D / 16;  // waves: one per 16 state columns
+  static constexpr int NT = 64 * NW;
+  static constexpr int WAVES_PER_EU = sizeof(T) == 2 ? 2 : 1;
+  static_assert(BYTES <= LDS_MAX, "LDS budget");
+  static_assert(TB == TN::G * 1024, "a tile is G loads of 1 KiB");
+};
+
+template <typename T, int D, bool MAIN>
+__global__ __launch_bounds__((TanLayout<T, D, MAIN>::NT), (TanLayout<T, D, MAIN>::WAVES_PER_EU)) void
+k_tangent(TanArgs a) {
+  typedef TanLayout<T, D, MAIN> LY;
+  typedef typename LY::TN TN;
+  typedef Elt<T> X;
+  typedef typename X::op_t op_t;
+  constexpr int E = X::E;
+  constexpr int KS = 4 * E;                // MFMA contraction step
+  constexpr int NW = LY::NW;
+  constexpr int EP = 16 / (int)sizeof(T);  // elements per 16-byte piece
+  constexpr int NKT = D / 16;
+  constexpr int NST = (10 + NW - 1) / NW;  // score tiles per wave (at most)
+  constexpr int NKS = D / KS;
+  constexpr int NJS = CH / KS;
+  constexpr int S = LY::STAGES;
+  constexpr int G = TN::G;
+  constexpr int NBLK = LY::NTEN * G;       // 1 KiB loads per chunk
+  constexpr int NLW = (NBLK + NW - 1) / NW;
+  __shared__ __attribute__((aligned(1024))) char smem[LY::BYTES];
+  __shared__ double red[NW];
+  // per-token factors of the current chunk in operand slot order (entry
+  // 16 g + E js + x is slot x of lane group g in contraction step js):
+  // update weights lambda^(cl-1-j) and query factors lambda^(j+1), 0 past cl
+  __shared__ __attribute__((aligned(16))) float tabW[64];
+  __shared__ __attribute__((aligned(16))) float tabQ[64];
+  static_assert(NJS * E == 16, "16 update slots per lane");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15;
+  const int g = lane >> 4;
+  const int col = 16 * w;
+
+  // ---- work item: sub-segment p of sequence n
+  const int np = MAIN ? a.split : a.split - 1;
+  const int64_t n = (int64_t)blockIdx.x / np;
+  const int p = (int)((int64_t)blockIdx.x % np);
+  const int h = (int)((n / a.nseg) % a.H);
+  const int64_t t0 = (int64_t)p * a.Lp;
+  const int64_t t1 = (t0 + a.Lp < a.Ls) ? t0 + a.Lp : a.Ls;
+  const int len = (int)(t1 > t0 ? t1 - t0 : 0);
+  const int nch = (len + CH - 1) / CH;
+  const float lg = log2f(a.lam[h]);
+  const int64_t DD = (int64_t)D * D;
+  const int64_t seq0 = n * a.Ls * D;  // element offset of the sequence's first row
+
+  // ---- start pair -> accumulators (S0 or a scanned pair; zero in the pre-pass)
+  f32x4 accS[NKT], accT[NKT];  // S and U
+  {
+    const float* sp = nullptr;
+    const float* tp = nullptr;
+    if (MAIN) {
+      if (p == 0) {
+        sp = a.S0 ? a.S0 + n * DD : nullptr;
+      } else {
+        const int64_t o = (n * (a.split - 1) + (p - 1)) * DD;
+        sp = a.WS + o;
+        tp = a.WT + o;
+      }
+    }
+#pragma unroll
+    for (int tk = 0; tk < NKT; ++tk)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int idx = (16 * tk + 4 * g + r) * D + col + l16;
+        accS[tk][r] = sp ? sp[idx] : 0.0f;
+        accT[tk][r] = tp ? tp[idx] : 0.0f;
+      }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): retire them before the chunk loop
+  }
+
+  // ---- chunk loads: load b fills granules 64 (b % G) .. + 63 of tile b / G;
+  // lane l's granule (row, piece) = divmod(64 (b % G) + l, G), the padding
+  // piece of a row loading the row's first piece.  Rows past the end are
+  // clamped to the last token (masked by the factors).  Offsets are 32-bit
+  // bytes from the sequence's first row (the host keeps a sequence below 4 GiB).
+  auto tensor = [&](int ten) -> const T* {
+    const void* bp;
+    if (MAIN)
+      bp = ten == 0 ? a.Q : (ten == 1 ? a.K : (ten == 2 ? a.V : a.dO));
+    else
+      bp = ten == 0 ? a.K : a.V;
+    return reinterpret_cast<const T*>(bp) + seq0;
+  };
+  const unsigned smem_lds = lds_address(smem);
+  auto issue = [&](int c, int stage) {
+#pragma unroll
+    for (int q = 0; q < NLW; ++q) {
+      const int b = w + NW * q;
+      if (b < NBLK) {
+        const int ten = b / G, blk = b % G;
+        const int pos = 64 * blk + lane;
+        const int row = pos / G, pc = pos % G;
+        const int piece = (pc == G - 1) ? 0 : pc;
+        const int tt = (c * CH + row < len) ? c * CH + row : len - 1;
+        const unsigned voff = (unsigned)(((t0 + tt) * D + piece * EP) * (int64_t)sizeof(T));
+        dma16(tensor(ten), voff,
+              smem_lds + (unsigned)(stage * LY::STAGE + ten * LY::TB + blk * 1024));
+      }
+    }
+  };
+
+  // ---- factors of a chunk of cl tokens (0 past the tail)
+  float wt[NST][4];    // (i-j) lambda^(i-j) for j < i on the wave's score tiles
+  float dc = 1.0f;     // lambda^cl
+  int clf = CH;        // cl
+  auto set_factors = [&](int cl) {
+    if (MAIN) {
+#pragma unroll
+      for (int st = 0; st < NST; ++st) {
+        const int idx = w + NW * st;
+        int jb = 0, ib = 0;
+        if (idx < 10) score_tile(idx, jb, ib);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          // accumulator (row 4 g + r, column l16) of tile (jb, ib): key j, query i
+          const int i = 16 * ib + perm16<T>(l16), j = 16 * jb + perm16<T>(4 * g + r);
+          wt[st][r] = (idx < 10 && j < i && i < cl) ? (float)(i - j) * pow_lam(lg, (float)(i - j)) : 0.0f;
+        }
+      }
+    }
+    if (tid < 64) {
+      const int js = (tid & 15) / E, x = (tid & 15) % E;
+      const int j = slot_token<T>(js * KS, tid >> 4, x);
+      tabW[tid] = j < cl ? pow_lam(lg, (float)(cl - 1 - j)) : 0.0f;
+      tabQ[tid] = j < cl ? pow_lam(lg, (float)(j + 1)) : 0.0f;
+    }
+    dc = pow_lam(lg, (float)cl);
+    clf = cl;
+  };
+  set_factors(CH);  // tabW is complete at the loop's first barrier
+
+  double dsum = 0.0;  // this lane's share of lambda * gradient (main pass)
+  if (S > 1 && nch > 0) issue(0, 0);
+  for (int c = 0; c < nch; ++c) {
+    const int cl = (len - c * CH < CH) ? (len - c * CH) : CH;
+    int stg = 0;
+    if constexpr (S == 1) {
+      lds_barrier();  // every wave is done with the previous chunk
+      issue(c, 0);
+      wait_vm_barrier<0>();
+    } else {
+      wait_vm_barrier<0>();  // chunk c landed; every wave is done with chunk c - 1
+      if (c + 1 < nch) issue(c + 1, (c + 1) & 1);
+      stg = c & 1;
+    }
+    if (cl != CH) {  // the tail (every wave is past its previous use of tabW)
+      set_factors(cl);
+      lds_barrier();
+    }
+    const char* const stage = smem + stg * LY::STAGE;
+    const char* const sQ = stage;
+    const char* const sK = stage + (MAIN ? LY::TB : 0);
+    const char* const sV = sK + LY::TB;
+    const char* const sD = sV + LY::TB;
+
+    if constexpr (MAIN) {
+      float part = 0.0f;
+      // ---- intra: sum_{j<i} (i-j) lambda^(i-j) (q_i . k_j)(dO_i . v_j), wave's tiles
+#pragma unroll
+      for (int st = 0; st < NST; ++st) {
+        const int idx = w + NW * st;
+        if (idx < 10) {
+          int jb, ib;
+          score_tile(idx, jb, ib);
+          f32x4 aqk = {0.f, 0.f, 0.f, 0.f};
+          f32x4 avd = {0.f, 0.f, 0.f, 0.f};
+          const int rk = 16 * jb + perm16<T>(l16), rq = 16 * ib + perm16<T>(l16);
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) {
+            const int f = (E == 8) ? 8 * score_granule<D>(ks, g) : ks * KS + g;
+            aqk = X::mfma(lds_op<T>(sK, TN::off(rk, f)), lds_op<T>(sQ, TN::off(rq, f)), aqk);
+            avd = X::mfma(lds_op<T>(sV, TN::off(rk, f)), lds_op<T>(sD, TN::off(rq, f)), avd);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) part += aqk[r] * avd[r] * wt[st][r];
+        }
+      }
+
+      // ---- inter: <U, M1> + <S, M2>, tile tk of M1, M2 = Q^T diag(.) dO at a time
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        const float* tq = tabQ + 16 * g;
+        op_t D1[NJS], D1l[NJS], D2[NJS], D2l[NJS];
+#pragma unroll
+        for (int js = 0; js < NJS; ++js) {
+          const op_t Dop = tr_op<T, TN>(sD, js * KS, col, lane);
+          if constexpr (E == 8) {
+            bf16x8 h1, l1, h2, l2;
+#pragma unroll
+            for (int x = 0; x < 8; ++x) {
+              const float a1 = (float)Dop[x] * tq[8 * js + x];
+              const float a2 = a1 * (float)(1 + slot_token<T>(js * KS, g, x));
+              h1[x] = (__bf16)a1;
+              l1[x] = (__bf16)(a1 - (float)h1[x]);
+              h2[x] = (__bf16)a2;
+              l2[x] = (__bf16)(a2 - (float)h2[x]);
+            }
+            D1[js] = h1;
+            D1l[js] = l1;
+            D2[js] = h2;
+            D2l[js] = l2;
+          } else {
+            D1[js] = Dop * tq[js];
+            D2[js] = D1[js] * (float)(1 + slot_token<T>(js * KS, g, 0));
+          }
+        }
+#pragma unroll
+        for (int tk = 0; tk < NKT; ++tk) {
+          f32x4 m1 = {0.f, 0.f, 0.f, 0.f};
+          f32x4 m2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int js = 0; js < NJS; ++js) {
+            const op_t Aq = tr_op<T, TN>(sQ, js * KS, 16 * tk, lane);
+            m1 = X::mfma(Aq, D1[js], m1);
+            m2 = X::mfma(Aq, D2[js], m2);
+            if constexpr (E == 8) {
+              m1 = X::mfma(Aq, D1l[js], m1);
+              m2 = X::mfma(Aq, D2l[js], m2);
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) part += accT[tk][r] * m1[r] + accS[tk][r] * m2[r];
+        }
+      }
+      dsum += (double)part;
+    }
+
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- updates: U = lambda^cl (U + cl S) + K^T diag((cl-1-j) lambda^(cl-1-j)) V,
+    //               S = lambda^cl S + K^T diag(lambda^(cl-1-j)) V
+    {
+      const float dcu = dc * (float)clf;
+#pragma unroll
+      for (int tk = 0; tk < NKT; ++tk) {
+        accT[tk] = dc * accT[tk] + dcu * accS[tk];
+        accS[tk] *= dc;
+      }
+      // V^T operands of this wave's columns, scaled per token (hi + lo in bf16)
+      const float* tw = tabW + 16 * g;
+      op_t B1[NJS], B1l[NJS], B2[NJS], B2l[NJS];
+#pragma unroll
+      for (int js = 0; js < NJS; ++js) {
+        const op_t Vop = tr_op<T, TN>(sV, js * KS, col, lane);
+        if constexpr (E == 8) {
+          bf16x8 b1, b1l, b2, b2l;
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            const float vw = (float)Vop[x] * tw[8 * js + x];
+            const float vu = vw * (float)(clf - 1 - slot_token<T>(js * KS, g, x));
+            b1[x] = (__bf16)vw;
+            b1l[x] = (__bf16)(vw - (float)b1[x]);
+            b2[x] = (__bf16)vu;
+            b2l[x] = (__bf16)(vu - (float)b2[x]);
+          }
+          B1[js] = b1;
+          B1l[js] = b1l;
+          B2[js] = b2;
+          B2l[js] = b2l;
+        } else {
+          B1[js] = Vop * tw[js];
+          B2[js] = B1[js] * (float)(clf - 1 - slot_token<T>(js * KS, g, 0));
+        }
+      }
+#pragma unroll
+      for (int tk = 0; tk < NKT; ++tk)
+#pragma unroll
+        for (int js = 0; js < NJS; ++js) {
+          const op_t Ak = tr_op<T, TN>(sK, js * KS, 16 * tk, lane);
+          accS[tk] = X::mfma(Ak, B1[js], accS[tk]);
+          accT[tk] = X::mfma(Ak, B2[js], accT[tk]);
+          if constexpr (E == 8) {
+            accS[tk] = X::mfma(Ak, B1l[js], accS[tk]);
+            accT[tk] = X::mfma(Ak, B2l[js], accT[tk]);
+          }
+        }
+    }
+  }
+
+  if constexpr (MAIN) {
+    // the state term <dS_end, U_end>, on the sequence's last sub-segment
+    if (p == a.split - 1 && a.dSe) {
+      const float* ds = a.dSe + n * DD;
+      float e = 0.0f;
+#pragma unroll
+      for (int tk = 0; tk < NKT; ++tk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) e += ds[(16 * tk + 4 * g + r) * D + col + l16] * accT[tk][r];
+      dsum += (double)e;
+    }
+    // workgroup sum in a fixed order
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) dsum += __shfl_xor(dsum, m, 64);
+    if (lane == 0) red[w] = dsum;
+    __syncthreads();
+    if (tid == 0) {
+      double t = 0.0;
+#pragma unroll
+      for (int i = 0; i < NW; ++i) t += red[i];
+      a.part[n * a.split + p] = t;
+    }
+  } else {
+    const int64_t o = (n * (a.split - 1) + p) * DD;
+#pragma unroll
+    for (int tk = 0; tk < NKT; ++tk)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int idx = (16 * tk + 4 * g + r) * D + col + l16;
+        a.WS[o + idx] = accS[tk][r];
+        a.WT[o + idx] = accT[tk][r];
+      }
+  }
+}
+
+// Chain the local pairs (S, U) of sub-segments 0..split-2 of every sequence
+// from (S0, 0), in place: entry p becomes the start pair of sub-segment p + 1.
+// One thread per (sequence, state element).
+__global__ __launch_bounds__(256) void k_tangent_scan(TanArgs a, int64_t total, int D) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int64_t DD = (int64_t)D * D;
+  const int64_t n = idx / DD, e = idx % DD;
+  const int h = (int)((n / a.nseg) % a.H);
+  const float lg = log2f(a.lam[h]);
+  const float Lp = (float)a.Lp;  // a multiple of 64, at most 2^24: exact
+  const float dl = exp2f(Lp * lg);
+  const float dw = Lp * dl;
+  float x = a.S0 ? a.S0[n * DD + e] : 0.0f;
+  float y = 0.0f;
+  for (int p = 0; p < a.split - 1; ++p) {
+    const int64_t o = (n * (a.split - 1) + p) * DD + e;
+    y = dl * y + dw * x + a.WT[o];
+    x = dl * x + a.WS[o];
+    a.WS[o] = x;
+    a.WT[o] = y;
+  }
+}
+
+// dlam[h] = (1 / lambda_h) * the sum of the shares of head h's sequences
+// n = (b H + h) nseg + s, in a fixed order (thread-strided sums, then a tree).
+__global__ __launch_bounds__(256) void k_tangent_sum(const double* part, const float* lam,
+                                                     float* dlam, int64_t nseq, int H, int nseg,
+                                                     int split) {
+  __shared__ double red[256];
+  const int h = blockIdx.x;
+  const int64_t per = nseq / H * split;  // B nseg sequences of head h, split shares each
+  double acc = 0.0;
+  for (int64_t m = threadIdx.x; m < per; m += 256) {
+    const int64_t q = m / split, pp = m % split;
+    const int64_t n = (q / nseg * H + h) * nseg + q % nseg;
+    acc += part[n * split + pp];
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if ((int)threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) dlam[h] = (float)(red[0] / (double)lam[h]);
+}
+
+template <typename T, int D>
+hipError_t tangent_t(const TanArgs& a, int64_t nseq, float* dlam, hipStream_t s) {
+  hipError_t e;
+  if (nseq > 0 && a.split > 1) {
+    hipLaunchKernelGGL((k_tangent<T, D, false>), dim3((unsigned)(nseq * (a.split - 1))),
+                       dim3(TanLayout<T, D, false>::NT), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t total = nseq * (int64_t)D * D;
+    hipLaunchKernelGGL(k_tangent_scan, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a,
+                       total, D);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (nseq > 0) {
+    hipLaunchKernelGGL((k_tangent<T, D, true>), dim3((unsigned)(nseq * a.split)),
+                       dim3(TanLayout<T, D, true>::NT), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_tangent_sum, dim3((unsigned)a.H), dim3(256), 0, s, a.part, a.lam, dlam,
+                     nseq, a.H, a.nseg, a.split);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_tangent(const TanArgs& a, int dtype, int D, int64_t nseq, float* dlam,
+                          hipStream_t s) {
+  if (a.H <= 0) return hipSuccess;
+  if (dtype == 0) {
+    if (D == 64) return tangent_t<__bf16, 64>(a, nseq, dlam, s);
+    if (D == 128) return tangent_t<__bf16, 128>(a, nseq, dlam, s);
+  } else {
+    if (D == 64) return tangent_t<float, 64>(a, nseq, dlam, s);
+    if (D == 128) return tangent_t<float, 128>(a, nseq, dlam, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace la

@@ -23,7 +23,8 @@ LA_BF16, LA_FP32 = 0, 1
 EXPORTS = ("la_version", "la_status_str", "la_last_error", "la_fwd_workspace_bytes",
            "la_chunk_fwd", "la_state_scan", "la_bwd_workspace_bytes", "la_chunk_bwd",
            "la_fwd_gated_workspace_bytes", "la_chunk_fwd_gated", "la_state_scan_gated",
-           "la_bwd_gated_workspace_bytes", "la_chunk_bwd_gated")
+           "la_bwd_gated_workspace_bytes", "la_chunk_bwd_gated",
+           "la_decay_grad_workspace_bytes", "la_decay_grad")
 
 
 class LinAttnError(RuntimeError):
@@ -79,6 +80,10 @@ def lib():
     L.la_chunk_bwd_gated.argtypes = [sp] + [vp] * 13 + [sz, vp]
     L.la_state_scan_gated.restype = ctypes.c_int
     L.la_state_scan_gated.argtypes = [i64, i64, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp]
+    L.la_decay_grad_workspace_bytes.restype = sz
+    L.la_decay_grad_workspace_bytes.argtypes = [sp]
+    L.la_decay_grad.restype = ctypes.c_int
+    L.la_decay_grad.argtypes = [sp] + [vp] * 9 + [sz, vp]
     _lib = L
     return L
 
@@ -298,3 +303,29 @@ def la_chunk_bwd_gated(q, k, v, log_alpha, dO, S0=None, dS_end=None, nseg: int =
                                     _ptr(dS0), _ptr(dG), _ptr(ws), ws.numel() if ws is not None else 0,
                                     _stream()))
     return dQ, dK, dV, dS0, dG
+
+
+def la_decay_grad_workspace_bytes(shape: la_shape) -> int:
+    return int(lib().la_decay_grad_workspace_bytes(ctypes.byref(shape)))
+
+
+def la_decay_grad(q, k, v, lam, dO, S0=None, dS_end=None, nseg: int = 1, split: int = 0,
+                  workspace=None, out=None):
+    """Gradient [H] fp32 of l = sum_t <dO_t, o_t> + <dS_end, S_end> with
+    respect to the per-head decays lam, summed over the batch and segments."""
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q.dtype)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (dO, "dO")):
+        _need(t, n, q.dtype)
+    _need(lam, "lam", torch.float32)
+    _need(S0, "S0", torch.float32)
+    _need(dS_end, "dS_end", torch.float32)
+    shape = make_shape(B, H, L, dk, dv, nseg, dt, split)
+    dlam = out if out is not None else torch.empty((H,), dtype=torch.float32, device=q.device)
+    nbytes = la_decay_grad_workspace_bytes(shape)
+    ws = workspace if workspace is not None else _workspace(nbytes, q.device)
+    _check(lib().la_decay_grad(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(lam), _ptr(S0),
+                               _ptr(dO), _ptr(dS_end), _ptr(dlam), _ptr(ws),
+                               ws.numel() if ws is not None else 0, _stream()))
+    return dlam

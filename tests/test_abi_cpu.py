@@ -187,6 +187,29 @@ def test_gated_entry_points_validate_on_the_host():
     assert scan(FAKE, FAKE, FAKE, P=-1) == la.LA_ERR_INVALID_ARG
 
 
+def test_decay_gradient_validates_on_the_host():
+    L = la.lib()
+    s = _shape(L=3000, split=4)
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    need = la.la_decay_grad_workspace_bytes(s)
+    # start pairs (S, U) of 3 sub-segments and one fp64 share per sub-segment
+    nseq, D = s.B * s.H, s.dk
+    assert need == 2 * nseq * 3 * D * D * 4 + 256
+    assert la.la_decay_grad_workspace_bytes(_shape(dk=96, dv=96)) == 0
+
+    def call(Q=FAKE, K=FAKE, V=FAKE, lam=FAKE, S0=None, dO=FAKE, dSe=None, out=FAKE,
+             ws=FAKE, nb=need):
+        return L.la_decay_grad(ctypes.byref(s), v(Q), v(K), v(V), v(lam), v(S0), v(dO),
+                               v(dSe), v(out), v(ws), nb, None)
+    assert call(dO=None) == la.LA_ERR_INVALID_ARG
+    assert call(V=None) == la.LA_ERR_INVALID_ARG
+    assert call(lam=None) == la.LA_ERR_INVALID_ARG
+    assert call(out=None) == la.LA_ERR_INVALID_ARG
+    assert call(dSe=FAKE + 8) == la.LA_ERR_INVALID_ARG    # misaligned
+    assert call(ws=None) == la.LA_ERR_WORKSPACE
+    assert call(nb=need - 1) == la.LA_ERR_WORKSPACE
+
+
 def test_empty_problem_is_a_no_op():
     # B*H = 0: nothing to read or write, no HIP call needed
     assert _fwd(_shape(B=0), Q=None, K=None, V=None, lam=None) == la.LA_OK

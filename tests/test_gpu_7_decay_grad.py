@@ -1,0 +1,100 @@
+"""Parity of the decay gradient d l / d lambda_h (la_decay_grad, forward-mode
+tangent walk) between the HIP path and the CPU oracle (lao.dlambda, the
+gated backward with every gate at log lambda_h, pinned by finite
+differences), through the C ABI.  Needs a gfx950 GPU."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import TOL, f64, log, rel_err, require_gpu
+from long_sequence_causal_amd import linattn as la
+from long_sequence_causal_amd.inputs import make_inputs, workload_inputs
+from oracle import lao
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+CASES = [
+    # dtype, D, B, H, L, nseg, split, S0 std, dS_end std, decay
+    ("fp32", 64, 2, 2, 200, 1, 0, 0.5, 0.5, True),
+    ("fp32", 128, 1, 2, 64 * 6, 2, 3, 0.5, 0.5, True),
+    ("fp32", 64, 1, 3, 1000, 1, 1, 0.0, 0.0, True),
+    ("fp32", 64, 1, 2, 300, 1, 0, 0.5, 0.5, False),
+    ("bf16", 128, 2, 3, 337, 1, 0, 0.5, 0.5, True),
+    ("bf16", 128, 1, 4, 5000, 1, 0, 0.0, 0.5, True),
+    ("bf16", 64, 1, 4, 64 * 7 + 3, 1, 0, 0.5, 0.0, True),
+    ("bf16", 128, 1, 2, 64 * 6, 3, 2, 0.5, 0.5, True),
+    ("bf16", 128, 2, 16, 64 * 72, 1, 0, 0.5, 0.5, True),
+    ("bf16", 128, 1, 2, 2000, 1, 0, 0.5, 0.5, False),
+    ("bf16", 128, 1, 1, 1, 1, 0, 0.5, 0.5, True),
+]
+
+
+@pytest.mark.parametrize("dtype,D,B,H,L,nseg,split,s0,dse,decay", CASES)
+def test_decay_grad_matches_oracle(dtype, D, B, H, L, nseg, split, s0, dse, decay):
+    log(f"decay grad dtype={dtype} D={D} B={B} H={H} L={L} nseg={nseg} split={split} "
+        f"s0={s0} dS_end={dse} decay={decay}")
+    inp = make_inputs(B, H, L, D, D, dtype=dtype, decay=decay, s0_std=s0, nseg=nseg,
+                      need_dO=True, dS_end_std=dse, seed=4000 + L + D + H, device="cuda")
+    q, k, v, lam, S0, dO, dSe = (inp[x] for x in ("q", "k", "v", "lam", "S0", "dO", "dS_end"))
+    got = la.la_decay_grad(q, k, v, lam, dO, S0=S0, dS_end=dSe, nseg=nseg, split=split)
+    torch.cuda.synchronize()
+    ref = lao.dlambda(f64(q), f64(k), f64(v), f64(lam), f64(dO), S0=f64(S0), dS_end=f64(dSe),
+                      nseg=nseg)
+    e = rel_err(f64(got), ref)
+    log(f"  dlambda {f64(got)} ref {ref} err {e:.3e}")
+    assert e <= TOL[dtype]
+
+
+def test_decay_grad_is_deterministic_and_split_independent():
+    B, H, L, D = 1, 4, 64 * 40 + 17, 128
+    inp = make_inputs(B, H, L, D, D, s0_std=0.5, need_dO=True, dS_end_std=0.5, seed=41,
+                      device="cuda")
+    args = (inp["q"], inp["k"], inp["v"], inp["lam"], inp["dO"])
+    kw = dict(S0=inp["S0"], dS_end=inp["dS_end"])
+    a = la.la_decay_grad(*args, **kw)
+    b = la.la_decay_grad(*args, **kw)
+    c = la.la_decay_grad(*args, split=1, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    e = rel_err(f64(a), f64(c))
+    log(f"  split auto vs 1: err {e:.3e}")
+    assert e <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("B,L", [(1, 0), (0, 128)])
+def test_decay_grad_of_empty_problem_is_zero(B, L):
+    H, D = 3, 64
+    q = torch.zeros((B, H, L, D), dtype=torch.bfloat16, device="cuda")
+    lam = torch.full((H,), 0.9, dtype=torch.float32, device="cuda")
+    S0 = torch.randn((B, H, 1, D, D), device="cuda")
+    dSe = torch.randn((B, H, 1, D, D), device="cuda")
+    out = torch.full((H,), float("nan"), device="cuda")
+    la.la_decay_grad(q, q, q, lam, q, S0=S0, dS_end=dSe, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, torch.zeros_like(out))
+
+
+@pytest.mark.parametrize("name,heads,dse", [("segment_64k", (0, 13, 31), 0.02),
+                                            ("train_256k", (0, 15), 0.0)])
+def test_decay_grad_at_full_size_on_sampled_heads(name, heads, dse):
+    """The workloads at full size in the launch configuration the benchmark
+    times; the oracle checks whole heads (every token of a sampled head)."""
+    log(f"decay grad full size: {name}, heads {heads}")
+    inp = workload_inputs(name, device="cuda", need_dO=True, dS_end_std=dse)
+    q, k, v, lam, S0, dO, dSe = (inp[x] for x in ("q", "k", "v", "lam", "S0", "dO", "dS_end"))
+    got = f64(la.la_decay_grad(q, k, v, lam, dO, S0=S0, dS_end=dSe))
+    torch.cuda.synchronize()
+    for h in heads:
+        sl = lambda t: None if t is None else f64(t[:, h:h + 1])
+        ref = lao.dlambda(sl(q), sl(k), sl(v), f64(lam[h:h + 1]), sl(dO), S0=sl(S0),
+                          dS_end=sl(dSe))
+        e = rel_err(got[h:h + 1], ref)
+        log(f"  head {h}: {got[h]:.6e} ref {ref[0]:.6e} err {e:.3e}")
+        assert e <= TOL["bf16"]
+    del q, k, v, dO
