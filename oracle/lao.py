@@ -218,3 +218,21 @@ def dlambda(Q, K, V, lam, dO, S0=None, dS_end=None, nseg: int = 1):
     G = np.broadcast_to(np.log(lam)[None, :, None], (B, H, L)).copy()
     dG = bwd_gated(Q, K, V, G, dO, S0=S0, dS_end=dS_end, nseg=nseg)[4]
     return dG.sum(axis=(0, 2)) / lam
+
+
+def step(q, k, v, lam, S=None):
+    """One token of the recurrence for every (b, h): S' = lambda_h S + k v^T,
+    o = q^T S' (the recurrent, constant-memory form of the LASP-2 page's
+    abstract; the same update as the token loop of ``lao.c``).  q, k [B,H,dk],
+    v [B,H,dv], lam [H], S [B,H,dk,dv] (None = zero).  Returns (o, S')."""
+    q, k, v, lam = _f64(q), _f64(k), _f64(v), _f64(lam)
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    S = np.zeros((B, H, dk, dv)) if S is None else _f64(S)
+    S1 = np.empty((B, H, dk, dv))
+    o = np.empty((B, H, dv))
+    for b in range(B):
+        for h in range(H):
+            S1[b, h] = lam[h] * S[b, h] + np.outer(k[b, h], v[b, h])
+            o[b, h] = q[b, h] @ S1[b, h]
+    return o, S1

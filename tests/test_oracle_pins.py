@@ -565,3 +565,32 @@ def test_decay_gradient_finite_differences():
         e[h] = 1e-7
         fd = (loss(lam + e) - loss(lam - e)) / 2e-7
         assert abs(dl[h] - fd) <= 1e-5 * max(1.0, abs(fd))
+
+
+def test_step_closed_form_on_a_tiny_case():
+    # dk = dv = 1: s' = lambda s + k v, o = q s'
+    o, S1 = lao.step(np.array([[[2.0]]]), np.array([[[3.0]]]), np.array([[[5.0]]]),
+                     np.array([0.5]), np.array([[[[4.0]]]]))
+    assert S1[0, 0, 0, 0] == 0.5 * 4.0 + 3.0 * 5.0
+    assert o[0, 0, 0] == 2.0 * 17.0
+    # zero state: S' = k v^T exactly
+    rng = np.random.default_rng(230)
+    q, k = rng.standard_normal((1, 1, 3)), rng.standard_normal((1, 1, 3))
+    v = rng.standard_normal((1, 1, 2))
+    o, S1 = lao.step(q, k, v, np.array([0.9]))
+    assert np.array_equal(S1[0, 0], np.outer(k[0, 0], v[0, 0]))
+
+
+def test_a_chain_of_steps_is_the_forward_pass():
+    # L steps from S0 reproduce the pinned C forward over the same L tokens
+    rng = np.random.default_rng(231)
+    B, H, L, dk, dv = 2, 3, 37, 5, 4
+    Q, K, V = (_rand(rng, B, H, L, d) for d in (dk, dk, dv))
+    S0 = _rand(rng, B, H, 1, dk, dv)
+    lam = np.array([0.7, 0.95, 1.0])
+    O, S_end = lao.fwd(Q, K, V, lam, S0=S0)
+    S = S0[:, :, 0]
+    for t in range(L):
+        o, S = lao.step(Q[:, :, t], K[:, :, t], V[:, :, t], lam, S)
+        assert _rel(o, O[:, :, t]) < 1e-13
+    assert _rel(S, S_end[:, :, 0]) < 1e-13
