@@ -162,6 +162,32 @@ def gated_leg(torch, la, inp, dev, iters, gate_logs):
             "frac_hbm": nbytes / t / 1e9 / HBM_PEAK_GBS}
 
 
+def decode_leg(torch, la, dev, iters):
+    """la_step on the decode batch (64 sequences x 32 heads, d = 128, bf16,
+    state updated in place): time per step, against its algorithmic bytes
+    (the fp32 state read and written once, q, k, v read and o written)."""
+    from long_sequence_causal_amd.inputs import DECODE, decode_inputs
+    w = DECODE["decode_b64"]
+    inp = decode_inputs("decode_b64", device=dev)
+    q, k, v, lam, S = inp["q"], inp["k"], inp["v"], inp["lam"], inp["S"]
+    B, H, d = q.shape
+    o = torch.empty_like(v)
+
+    def call():
+        la.la_step(q, k, v, lam, S, out=o, S_out=S)
+
+    for _ in range(5):
+        call()
+    torch.cuda.synchronize()
+    ms = time_events(call, iters, torch.cuda.current_stream())
+    nbytes = B * H * (2 * d * d * 4 + 4 * d * 2)
+    t = ms / 1e3
+    del inp, q, k, v, S, o
+    return {"workload": "decode_b64", "B": B, "H": H, "d": d, "dtype": w["dtype"],
+            "us_per_call": ms * 1e3, "tokens_per_s": B / t, "alg_bytes": nbytes,
+            "achieved_GBs": nbytes / t / 1e9, "frac_hbm": nbytes / t / 1e9 / HBM_PEAK_GBS}
+
+
 def time_events(fn, iters, stream):
     import torch
 
@@ -212,6 +238,7 @@ def main():
     ap.add_argument("--split", type=int, default=0, help="internal split (0 = library choice)")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward leg")
     ap.add_argument("--no-gated", action="store_true", help="skip the gated-forward leg")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-step leg")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -329,6 +356,11 @@ def main():
                f"{bw['achieved_GBs']:.0f} GB/s algorithmic; gated {bw['gated']['us_per_call']:.1f} us/call; "
                f"decay gradient {bw['decay_grad']['us_per_call']:.1f} us/call")
         rec["backward"] = bw
+    if not args.no_decode:
+        dl = decode_leg(torch, la, dev, max(20, args.steps))
+        eprint(f"[bench] decode step ({dl['workload']}): {dl['us_per_call']:.1f} us/call, "
+               f"{dl['achieved_GBs']:.0f} GB/s algorithmic")
+        rec["decode"] = dl
     if not args.no_cpu:
         eprint("[bench] CPU oracle baseline ...")
         rec["cpu_baseline"] = cpu_baseline(inp, H, L, d)

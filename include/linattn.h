@@ -271,6 +271,27 @@ la_status la_decay_grad(const la_shape* shape, const void* Q, const void* K,
                         const void* dO, const float* dS_end, float* dlambda,
                         void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * One recurrent decode step for a batch of B * H sequences: the token
+ * recurrence above applied to one new token per sequence (the
+ * "constant-memory inference" of the LASP-2 page's abstract):
+ *     S_out = lambda_h S + k v^T          o = q^T S_out
+ *   q, k [B,H,dk], v [B,H,dv], o [B,H,dv]   element type `dtype`
+ *                                           (LA_BF16 or LA_FP32).
+ *   lambda [H] fp32.
+ *   S, S_out [B,H,dk,dv] fp32   state before / after the token.  S NULL =
+ *                               zero (a sequence's first token).  S_out may
+ *                               be S itself (in place) but may not overlap
+ *                               it otherwise.
+ *   o                           output; NULL = state update only.
+ * dk == dv in {64, 128}.  The state is read and written once (fp32
+ * arithmetic throughout); o is rounded to `dtype`.  B * H == 0 is a no-op.
+ * Errors as la_chunk_fwd.
+ */
+la_status la_step(int64_t B, int64_t H, int32_t dk, int32_t dv, int32_t dtype,
+                  const void* q, const void* k, const void* v, const float* lambda,
+                  const float* S, float* S_out, void* o, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

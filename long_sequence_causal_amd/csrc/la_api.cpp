@@ -505,6 +505,46 @@ la_status la_decay_grad(const la_shape* s, const void* Q, const void* K, const v
   return LA_OK;
 }
 
+la_status la_step(int64_t B, int64_t H, int32_t dk, int32_t dv, int32_t dtype, const void* q,
+                  const void* k, const void* v, const float* lambda, const float* S,
+                  float* S_out, void* o, void* stream) {
+  if (B < 0 || H < 0) return fail(LA_ERR_INVALID_ARG, "negative size (B=%lld H=%lld)",
+                                  (long long)B, (long long)H);
+  if (dk <= 0 || dv <= 0) return fail(LA_ERR_INVALID_ARG, "dk and dv must be positive");
+  if (dtype != LA_BF16 && dtype != LA_FP32) return fail(LA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (dk != dv) return fail(LA_ERR_UNSUPPORTED, "dk != dv (%d, %d)", dk, dv);
+  if (dk != 64 && dk != 128) return fail(LA_ERR_UNSUPPORTED, "d=%d not in {64, 128}", dk);
+  if ((double)B * (double)H * (dk / 32) >= 2147483648.0)
+    return fail(LA_ERR_INVALID_ARG, "too many sequences");
+  const int64_t nseq = B * H;
+  if (nseq == 0) return LA_OK;
+  if (!q || !k || !v || !lambda || !S_out)
+    return fail(LA_ERR_INVALID_ARG, "q, k, v, lambda and S_out are required");
+  const void* ptrs[] = {q, k, v, lambda, S, S_out, o};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return fail(LA_ERR_INVALID_ARG, "pointer %p is not 16-byte aligned", p);
+  const size_t sbytes = (size_t)nseq * (size_t)dk * (size_t)dv * sizeof(float);
+  if (S && S != S_out) {
+    const char* a0 = reinterpret_cast<const char*>(S);
+    const char* b0 = reinterpret_cast<const char*>(S_out);
+    if (a0 < b0 + sbytes && b0 < a0 + sbytes)
+      return fail(LA_ERR_INVALID_ARG, "S and S_out overlap without being the same buffer");
+  }
+  la::StepArgs sa;
+  std::memset(&sa, 0, sizeof(sa));
+  sa.q = q;
+  sa.k = k;
+  sa.v = v;
+  sa.lam = lambda;
+  sa.S = S;
+  sa.Sout = S_out;
+  sa.o = o;
+  sa.H = (int)H;
+  hipError_t e = la::launch_step(sa, dtype, dk, nseq, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode step launch");
+  return LA_OK;
+}
+
 la_status la_state_scan_gated(int64_t B, int64_t H, int32_t P, int32_t dk, int32_t dv,
                               const float* dS, const float* log_decay, const float* S0,
                               float* S_start, float* S_end, int32_t reverse, void* stream) {

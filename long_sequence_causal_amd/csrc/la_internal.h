@@ -104,6 +104,20 @@ struct TanArgs {
 hipError_t launch_tangent(const TanArgs& a, int dtype, int D, int64_t nseq, float* dlam,
                           hipStream_t stream);
 
+// One decode step for nseq = B * H sequences (la_step.hip); head of
+// sequence n is n % H.
+struct StepArgs {
+  const void* q;     // [nseq][D]
+  const void* k;     // [nseq][D]
+  const void* v;     // [nseq][D]
+  const float* lam;  // [H]
+  const float* S;    // [nseq][D][D] or null (zero)
+  float* Sout;       // [nseq][D][D], may equal S
+  void* o;           // [nseq][D] or null
+  int H;
+};
+hipError_t launch_step(const StepArgs& a, int dtype, int D, int64_t nseq, hipStream_t stream);
+
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, bool with_o, int64_t nwg,
                       hipStream_t stream);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);

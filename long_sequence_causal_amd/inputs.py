@@ -132,6 +132,32 @@ def gate_logs(lam: torch.Tensor, B: int, L: int, seed: int, device="cpu") -> tor
     return (loglam * (2.0 * torch.sigmoid(z))).contiguous()
 
 
+# Decode workloads: one new token for each of B sequences x H heads, with a
+# carried state.  Drawn like the sequence workloads (q, k scaled by
+# 1/sqrt(d), v at unit variance, rounded to the dtype), in the order q, k, v,
+# S; the state S ~ N(0, s_std^2) fp32 stands for the state a prefill left.
+DECODE = {
+    "decode_b64": dict(B=64, H=32, d=128, dtype="bf16", s_std=0.02, seed=5,
+                       note="one decode step of 64 sequences x 32 heads, d = 128"),
+}
+
+
+def decode_inputs(name: str, device="cpu"):
+    """Inputs of a named decode workload: q, k [B,H,d], v [B,H,d] (dtype),
+    lam [H] float32 (the per-head schedule), S [B,H,d,d] float32."""
+    w = DECODE[name]
+    B, H, d = w["B"], w["H"], w["d"]
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(int(w["seed"]))
+    td = torch_dtype(w["dtype"])
+    q = _draw(gen, (B, H, d), 1.0 / math.sqrt(d), td, dev)
+    k = _draw(gen, (B, H, d), 1.0 / math.sqrt(d), td, dev)
+    v = _draw(gen, (B, H, d), 1.0, td, dev)
+    S = _draw(gen, (B, H, d, d), float(w["s_std"]), torch.float32, dev)
+    return {"q": q, "k": k, "v": v, "lam": decay_schedule(H).to(dev), "S": S}
+
+
 def workload_inputs(name: str, device="cpu", **over):
     """Inputs of a named workload (keyword overrides allowed, e.g. L=...)."""
     w = WORKLOADS[name]

@@ -24,7 +24,7 @@ EXPORTS = ("la_version", "la_status_str", "la_last_error", "la_fwd_workspace_byt
            "la_chunk_fwd", "la_state_scan", "la_bwd_workspace_bytes", "la_chunk_bwd",
            "la_fwd_gated_workspace_bytes", "la_chunk_fwd_gated", "la_state_scan_gated",
            "la_bwd_gated_workspace_bytes", "la_chunk_bwd_gated",
-           "la_decay_grad_workspace_bytes", "la_decay_grad")
+           "la_decay_grad_workspace_bytes", "la_decay_grad", "la_step")
 
 
 class LinAttnError(RuntimeError):
@@ -80,6 +80,8 @@ def lib():
     L.la_chunk_bwd_gated.argtypes = [sp] + [vp] * 13 + [sz, vp]
     L.la_state_scan_gated.restype = ctypes.c_int
     L.la_state_scan_gated.argtypes = [i64, i64, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp]
+    L.la_step.restype = ctypes.c_int
+    L.la_step.argtypes = [i64, i64, i32, i32, i32] + [vp] * 7 + [vp]
     L.la_decay_grad_workspace_bytes.restype = sz
     L.la_decay_grad_workspace_bytes.argtypes = [sp]
     L.la_decay_grad.restype = ctypes.c_int
@@ -329,3 +331,24 @@ def la_decay_grad(q, k, v, lam, dO, S0=None, dS_end=None, nseg: int = 1, split: 
                                _ptr(dO), _ptr(dS_end), _ptr(dlam), _ptr(ws),
                                ws.numel() if ws is not None else 0, _stream()))
     return dlam
+
+
+def la_step(q, k, v, lam, S=None, out=None, S_out=None, need_o: bool = True):
+    """One decode step: S' = lam_h S + k v^T, o = q^T S' for q, k [B,H,dk],
+    v [B,H,dv] and S [B,H,dk,dv] fp32 (None = zero).  S_out may be S (in
+    place).  Returns (o or None, S')."""
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q.dtype)
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, q.dtype)
+    _need(lam, "lam", torch.float32)
+    _need(S, "S", torch.float32)
+    if S_out is None:
+        S_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    _need(S_out, "S_out", torch.float32)
+    o = out if out is not None else (
+        torch.empty((B, H, dv), dtype=q.dtype, device=q.device) if need_o else None)
+    _check(lib().la_step(B, H, dk, dv, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(lam), _ptr(S),
+                         _ptr(S_out), _ptr(o), _stream()))
+    return o, S_out

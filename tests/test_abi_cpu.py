@@ -210,6 +210,25 @@ def test_decay_gradient_validates_on_the_host():
     assert call(nb=need - 1) == la.LA_ERR_WORKSPACE
 
 
+def test_decode_step_validates_on_the_host():
+    L = la.lib()
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+
+    def call(B=2, H=3, dk=64, dv=64, dt=la.LA_BF16, q=FAKE, k=FAKE, vv=FAKE, lam=FAKE, S=None,
+             So=FAKE + (1 << 24), o=FAKE):
+        return L.la_step(B, H, dk, dv, dt, v(q), v(k), v(vv), v(lam), v(S), v(So), v(o), None)
+    assert call(B=0, q=None, k=None, vv=None, lam=None, So=None) == la.LA_OK  # no-op
+    assert call(q=None) == la.LA_ERR_INVALID_ARG
+    assert call(So=None) == la.LA_ERR_INVALID_ARG
+    assert call(B=-1) == la.LA_ERR_INVALID_ARG
+    assert call(dt=7) == la.LA_ERR_INVALID_ARG
+    assert call(dk=64, dv=128) == la.LA_ERR_UNSUPPORTED
+    assert call(dk=96, dv=96) == la.LA_ERR_UNSUPPORTED
+    assert call(k=FAKE + 4) == la.LA_ERR_INVALID_ARG
+    # S_out overlapping S without being S
+    assert call(S=FAKE + (1 << 24), So=FAKE + (1 << 24) + 4096) == la.LA_ERR_INVALID_ARG
+
+
 def test_empty_problem_is_a_no_op():
     # B*H = 0: nothing to read or write, no HIP call needed
     assert _fwd(_shape(B=0), Q=None, K=None, V=None, lam=None) == la.LA_OK

@@ -1,0 +1,101 @@
+"""Parity of the recurrent decode step (la_step) with the CPU oracle
+(lao.step, pinned against the forward pass) and with the chunked forward
+of the HIP path over the same tokens, through the C ABI.  Needs a gfx950
+GPU."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import TOL, f64, log, rel_err, require_gpu
+from long_sequence_causal_amd import linattn as la
+from long_sequence_causal_amd.inputs import decode_inputs, decay_schedule, make_inputs
+from oracle import lao
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _draw(B, H, D, dtype, s_std, seed, decay=True):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q = (torch.randn((B, H, D), generator=g, device="cuda") * D ** -0.5).to(td)
+    k = (torch.randn((B, H, D), generator=g, device="cuda") * D ** -0.5).to(td)
+    v = torch.randn((B, H, D), generator=g, device="cuda").to(td)
+    S = torch.randn((B, H, D, D), generator=g, device="cuda") * s_std if s_std > 0 else None
+    return q, k, v, decay_schedule(H, decay).cuda(), S
+
+
+CASES = [
+    # dtype, D, B, H, S std, decay
+    ("fp32", 64, 2, 3, 0.5, True),
+    ("fp32", 128, 1, 4, 0.5, True),
+    ("fp32", 128, 3, 2, 0.0, True),
+    ("bf16", 128, 4, 8, 0.5, True),
+    ("bf16", 64, 5, 3, 0.5, False),
+    ("bf16", 128, 1, 1, 0.0, True),
+]
+
+
+@pytest.mark.parametrize("dtype,D,B,H,s_std,decay", CASES)
+def test_step_matches_oracle(dtype, D, B, H, s_std, decay):
+    log(f"step dtype={dtype} D={D} B={B} H={H} S_std={s_std} decay={decay}")
+    q, k, v, lam, S = _draw(B, H, D, dtype, s_std, 500 + D + B + H, decay)
+    o, S1 = la.la_step(q, k, v, lam, S)
+    torch.cuda.synchronize()
+    o_r, S1_r = lao.step(f64(q), f64(k), f64(v), f64(lam), None if S is None else f64(S))
+    eo, es = rel_err(f64(o), o_r), rel_err(f64(S1), S1_r)
+    log(f"  err o={eo:.3e} S'={es:.3e}")
+    # the state is fp32 arithmetic on exact inputs whatever the token dtype
+    assert eo <= TOL[dtype] and es <= TOL["fp32"]
+
+
+def test_step_in_place_and_state_only():
+    q, k, v, lam, S = _draw(2, 4, 128, "bf16", 0.5, 77)
+    o_ref, S_ref = la.la_step(q, k, v, lam, S)
+    S2 = S.clone()
+    o2, S2b = la.la_step(q, k, v, lam, S2, S_out=S2)
+    _, S3 = la.la_step(q, k, v, lam, S, need_o=False)
+    torch.cuda.synchronize()
+    assert S2b.data_ptr() == S2.data_ptr()
+    assert torch.equal(S2, S_ref) and torch.equal(o2, o_ref) and torch.equal(S3, S_ref)
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp32", 64)])
+def test_a_chain_of_steps_matches_the_chunked_forward(dtype, D):
+    """T decode steps from S0 give the outputs and final state of the
+    chunked forward over the same T tokens."""
+    B, H, T = 2, 3, 70
+    inp = make_inputs(B, H, T, D, D, dtype=dtype, s0_std=0.5, seed=88, device="cuda")
+    q, k, v, lam, S0 = inp["q"], inp["k"], inp["v"], inp["lam"], inp["S0"]
+    O, S_end = la.la_chunk_fwd(q, k, v, lam, S0=S0)
+    S = S0[:, :, 0].clone()  # the chain updates S in place; S0 stays the input
+    outs = []
+    for t in range(T):
+        o, S = la.la_step(q[:, :, t].contiguous(), k[:, :, t].contiguous(), v[:, :, t].contiguous(),
+                          lam, S, S_out=S)
+        outs.append(o)
+    torch.cuda.synchronize()
+    Os = torch.stack(outs, dim=2)
+    O_r, S_r = lao.fwd(f64(q), f64(k), f64(v), f64(lam), S0=f64(S0))
+    e = [rel_err(f64(Os), O_r), rel_err(f64(S), S_r[:, :, 0]), rel_err(f64(Os), f64(O)),
+         rel_err(f64(S), f64(S_end)[:, :, 0])]
+    log("  chain err vs oracle o={:.3e} S={:.3e}; vs chunked forward o={:.3e} S={:.3e}".format(*e))
+    assert max(e) <= TOL[dtype]
+
+
+def test_step_at_the_decode_batch():
+    """The decode workload at full size (64 sequences x 32 heads, d = 128,
+    bf16), every head checked."""
+    inp = decode_inputs("decode_b64", device="cuda")
+    q, k, v, lam, S = inp["q"], inp["k"], inp["v"], inp["lam"], inp["S"]
+    log(f"step decode batch {tuple(q.shape)}")
+    o, S1 = la.la_step(q, k, v, lam, S)
+    torch.cuda.synchronize()
+    o_r, S1_r = lao.step(f64(q), f64(k), f64(v), f64(lam), f64(S))
+    eo, es = rel_err(f64(o), o_r), rel_err(f64(S1), S1_r)
+    log(f"  err o={eo:.3e} S'={es:.3e}")
+    assert eo <= TOL["bf16"] and es <= TOL["fp32"]
