@@ -45,11 +45,15 @@ def alg_flops(B, H, L, d):
     return B * H * L * (4 * d * d + (CHUNK + 1) * 2 * d)
 
 
+# the files k_chunk_fwd is compiled from
+FWD_KERNEL_SOURCES = ("la_device.h", "la_fwd.hip", "la_internal.h", "la_walk.h")
+
+
 def measured_traffic():
     """HBM bytes per launch of the main chunk kernel from the committed
-    FETCH_SIZE / WRITE_SIZE profile, or None once the kernel sources differ
-    from the ones profiled (SHA-256 over the csrc files in name order, each
-    name followed by its bytes)."""
+    FETCH_SIZE / WRITE_SIZE profile, or None once the kernel's sources differ
+    from the ones profiled (SHA-256 over FWD_KERNEL_SOURCES in that order,
+    each name followed by its bytes)."""
     import hashlib
     import re
     prof = os.path.join(ROOT, "profiles", "k_chunk_fwd_segment_64k_hbm_bytes.md")
@@ -60,7 +64,7 @@ def measured_traffic():
         return None
     src = os.path.join(ROOT, "long_sequence_causal_amd", "csrc")
     h = hashlib.sha256()
-    for name in sorted(os.listdir(src)):
+    for name in FWD_KERNEL_SOURCES:
         h.update(name.encode())
         with open(os.path.join(src, name), "rb") as f:
             h.update(f.read())
