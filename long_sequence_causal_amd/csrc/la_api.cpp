@@ -54,6 +54,7 @@ struct Plan {
   int split = 1;     // sub-segments per sequence
   int64_t Lp = kChunk;  // tokens per sub-segment (multiple of 64; the last is shorter)
   int D = 0;
+  bool ragged_first = false;  // the short sub-segment first (gated reverse sweeps)
 };
 
 // Shape checks shared by forward and backward.  No HIP call.
@@ -122,6 +123,7 @@ la::FwdArgs flow_args(const Plan& pl, int H, int nseg, const void* Q, const void
   fa.Lp = pl.Lp;
   fa.split = pl.split;
   fa.reverse = reverse;
+  fa.ragged_first = pl.ragged_first;
   return fa;
 }
 
@@ -331,16 +333,33 @@ la_status la_chunk_fwd_gated(const la_shape* s, const void* Q, const void* K, co
 // gated backward workspace (in order): prepared start state [nseq][D][D],
 // start states and log-gates of the sweeps, shifted gates [nseq][Ls], the
 // final dQ-sweep state [nseq][D][D] and the gate-gradient block totals
+// The gated backward cuts every sequence into sub-segments of exactly 1024
+// tokens (whatever `split` asks for): the sweeps' start states at their
+// boundaries anchor the log-gate gradient (k_gate_anchors), so that its suffix
+// sums never run over more than 1024 tokens.  The reverse sweeps take the
+// short sub-segment first, which puts their boundaries on the same rows.
+constexpr int64_t kGateBlock = 1024;
+Plan gated_bwd_plan(const Plan& p) {
+  Plan g = p;
+  const int64_t nchunks = (p.Ls + kChunk - 1) / kChunk;
+  const int64_t cps = kGateBlock / kChunk;
+  g.Lp = kGateBlock;
+  g.split = nchunks > 0 ? (int)((nchunks + cps - 1) / cps) : 1;
+  return g;
+}
+
 struct GatedBwdWs {
-  size_t A, W, LD, Gs, SE, TOT, total;
+  size_t A, W, W2, LD, Gs, SE, TOT, total;
 };
-GatedBwdWs gated_bwd_ws(const Plan& p) {
+GatedBwdWs gated_bwd_ws(const Plan& p0) {
+  const Plan p = gated_bwd_plan(p0);
   GatedBwdWs w;
   auto up = [](size_t b) { return (b + 255) / 256 * 256; };
   const size_t DD4 = (size_t)p.D * p.D * sizeof(float);
   size_t o = 0;
   w.A = o;  o += up((size_t)p.nseq * DD4);
   w.W = o;  o += up(scan_ws_bytes(p));
+  w.W2 = o; o += up(scan_ws_bytes(p));
   w.LD = o; o += up((size_t)p.nseq * (size_t)(p.split > 1 ? p.split - 1 : 0) * sizeof(float));
   w.Gs = o; o += up((size_t)p.nseq * (size_t)p.Ls * sizeof(float));
   w.SE = o; o += up((size_t)p.nseq * DD4);
@@ -363,16 +382,21 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
                              const float* log_alpha, const float* S0, const void* dO,
                              const float* dS_end, void* dQ, void* dK, void* dV, float* dS0,
                              float* dlog_alpha, void* ws, size_t ws_bytes, void* stream) {
-  Plan pl;
-  la_status r = check_shape(s, &pl);
+  Plan pl0;
+  la_status r = check_shape(s, &pl0);
   if (r != LA_OK) return r;
+  if ((double)pl0.nseq * (double)((pl0.Ls + kGateBlock - 1) / kGateBlock) > 2.0e9)
+    return fail(LA_ERR_INVALID_ARG, "too many workgroups");
+  const Plan pl = gated_bwd_plan(pl0);  // forward sweep
+  Plan plr = pl;                        // reverse sweeps
+  plr.ragged_first = true;
   const bool has_tokens = pl.nseq > 0 && pl.Ls > 0;
   if (has_tokens && (!Q || !K || !V || !log_alpha || !dO || !dQ || !dK || !dV))
     return fail(LA_ERR_INVALID_ARG, "Q, K, V, log_alpha, dO, dQ, dK and dV are required");
   const void* ptrs[] = {Q, K, V, log_alpha, S0, dO, dS_end, dQ, dK, dV, dS0, dlog_alpha, ws};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return fail(LA_ERR_INVALID_ARG, "pointer %p is not 16-byte aligned", p);
-  const GatedBwdWs L = gated_bwd_ws(pl);
+  const GatedBwdWs L = gated_bwd_ws(pl0);
   if (L.total > 0 && (!ws || ws_bytes < L.total))
     return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
                 ws ? ws_bytes : (size_t)0);
@@ -380,7 +404,8 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);
   float* A = reinterpret_cast<float*>(base + L.A);
-  float* W = reinterpret_cast<float*>(base + L.W);
+  float* W = reinterpret_cast<float*>(base + L.W);    // forward sweep: S^T starts
+  float* W2 = reinterpret_cast<float*>(base + L.W2);  // reverse sweeps: G starts
   float* LDw = reinterpret_cast<float*>(base + L.LD);
   float* Gs = reinterpret_cast<float*>(base + L.Gs);
   float* SE = reinterpret_cast<float*>(base + L.SE);
@@ -416,7 +441,7 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
     return hip_fail(e, "gate shift launch");
   // dv_t = G_t^T k_t, G accumulating q dO^T from dS_end (the first reverse
   // step multiplies by 1); its final value G_1 gives dS0 = alpha_1 G_1
-  r = run_flow(pl, s->dtype, H, s->nseg, K, Q, dO, nullptr, dS_end, dV, dS0, W, 1, st, true, Gs,
+  r = run_flow(plr, s->dtype, H, s->nseg, K, Q, dO, nullptr, dS_end, dV, dS0, W2, 1, st, true, Gs,
                LDw);
   if (r != LA_OK) return r;
   if (dS0 && (e = la::launch_scale_first_gate(dS0, log_alpha, pl.nseq, pl.Ls, pl.D, st)) != hipSuccess)
@@ -424,7 +449,7 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
   // dk_t = G_t v_t: the same reverse recurrence for G^T, whose sub-segment
   // start states are the transposes of the ones just used
   if (pl.split > 1) {
-    e = la::launch_transpose(W, pl.nseq * (pl.split - 1), pl.D, st);
+    e = la::launch_transpose(W2, pl.nseq * (pl.split - 1), pl.D, st);
     if (e != hipSuccess) return hip_fail(e, "transpose launch");
   }
   start = nullptr;
@@ -436,11 +461,16 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
     if ((e = la::launch_prep(pa, st)) != hipSuccess) return hip_fail(e, "prep launch");
     start = A;
   }
-  r = run_main(pl, s->dtype, H, s->nseg, V, dO, Q, nullptr, start, dK, nullptr, W, 1, st, true, Gs);
+  r = run_main(plr, s->dtype, H, s->nseg, V, dO, Q, nullptr, start, dK, nullptr, W2, 1, st, true,
+               Gs);
   if (r != LA_OK) return r;
 
-  // d l / d log(alpha_t) = sum_{u >= t} (q_u . dq_u - k_u . dk_u) + <dS_end, S_end>
+  // d l / d log(alpha_t) = sum_{u >= t} (q_u . dq_u - k_u . dk_u) + <dS_end, S_end>, the sum
+  // anchored at every sub-segment boundary y by its exact value alpha_y <G_y, S_{y-1}>
   if (dlog_alpha) {
+    e = la::launch_gate_anchors(W, W2, log_alpha, dS_end, need_send ? SE : nullptr, TOT, pl.nseq,
+                                pl.Ls, pl.D, st);
+    if (e != hipSuccess) return hip_fail(e, "gate anchor launch");
     e = la::launch_gate_grad(s->dtype, pl.D, Q, dQ, K, dK, dlog_alpha, TOT, dS_end,
                              need_send ? SE : nullptr, pl.nseq, pl.Ls, st);
     if (e != hipSuccess) return hip_fail(e, "gate gradient launch");

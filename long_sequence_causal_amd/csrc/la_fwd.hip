@@ -28,8 +28,14 @@ __global__ __launch_bounds__((FwdLayout<T, D, WITH_O ? 3 : 2, GATED>::NT),
   const int64_t n = (int64_t)blockIdx.x / a.p_count;
   const int p = a.p_begin + (int)((int64_t)blockIdx.x % a.p_count);
   const int h = (int)((n / a.nseg) % a.H);
-  const int64_t t0 = (int64_t)p * a.Lp;
-  const int64_t t1 = (t0 + a.Lp < a.Ls) ? t0 + a.Lp : a.Ls;
+  int64_t t0, t1;  // positions of the sub-segment (the short one last, or first)
+  if (a.ragged_first) {
+    t1 = a.Ls - (int64_t)(a.split - 1 - p) * a.Lp;
+    t0 = (t1 - a.Lp > 0) ? t1 - a.Lp : 0;
+  } else {
+    t0 = (int64_t)p * a.Lp;
+    t1 = (t0 + a.Lp < a.Ls) ? t0 + a.Lp : a.Ls;
+  }
   const int64_t seq_elem0 = n * a.Ls * D;
   WalkJob jb;
   jb.Q = WITH_O ? (const void*)(reinterpret_cast<const T*>(a.Q) + seq_elem0) : nullptr;

@@ -8,13 +8,18 @@
 //   * the reverse sweeps step from token t+1 back to t with alpha_{t+1}:
 //     k_shift_gates writes g'_t = g_{t+1} (0 for a segment's last token);
 //   * dS0 = alpha_1 G_1: k_scale_first_gate;
-//   * d l / d log(alpha_t) = sum_{u >= t} (q_u . dq_u - k_u . dk_u)
-//     + <dS_end, S_end> within each segment (g_t enters only through the
-//     cumulative log-gates, which scale q_u by exp(c_u), k_u by exp(-c_u) and
-//     S_end by exp(c_L)): k_gate_grad_blocks forms r_u = q_u . dq_u - k_u . dk_u
-//     and its reverse cumulative sum inside blocks of 1024 tokens,
-//     k_gate_grad_totals the suffix sums of the block totals (plus the S_end
-//     term) per sequence, and k_gate_grad_finish adds them.
+//   * d l / d log(alpha_t) = alpha_t <G_t, S_{t-1}>
+//                          = sum_{u >= t} (q_u . dq_u - k_u . dk_u) + <dS_end, S_end>
+//     within each segment (g_t enters only through the cumulative log-gates,
+//     which scale q_u by exp(c_u), k_u by exp(-c_u) and S_end by exp(c_L)).
+//     The suffix sums run only inside blocks of 1024 tokens
+//     (k_gate_grad_blocks forms r_u = q_u . dq_u - k_u . dk_u and its reverse
+//     cumulative sum there); the value at the first token of the next block
+//     is taken exactly from the first form, with S and G the fp32 start states
+//     the two sweeps already hold at that row (k_gate_anchors), and
+//     k_gate_grad_finish adds it.  Summing r over a whole long segment
+//     instead would carry the rounding of dq and dk (and of the sweeps'
+//     bf16 operands) over every token: about 15 % at 256K tokens.
 #include "la_device.h"
 #include "la_internal.h"
 
@@ -52,7 +57,8 @@ __device__ inline float dot8(const T* a, const T* b) {
 // One workgroup per (sequence, block of GBLK tokens).  Sixteen lanes share a
 // token (8 features each, D / 8 lanes in use), reduce across the 16 with
 // shuffles, then the block's reverse cumulative sum is taken in LDS:
-// dG[t] = sum_{u >= t in block} r_u, and the block total goes to tot[n][b].
+// dG[t] = sum_{u >= t in block} r_u, and the block total goes to tot[n][b]
+// (when tot is not null).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_gate_grad_blocks(const T* Q, const T* dQ, const T* K,
                                                           const T* dK, float* dG, float* tot,
@@ -91,54 +97,48 @@ __global__ __launch_bounds__(256) void k_gate_grad_blocks(const T* Q, const T* d
     __syncthreads();
   }
   for (int i = threadIdx.x; i < len; i += 256) dG[n * Ls + t0 + i] = r[i];
-  if (threadIdx.x == 0) tot[n * nb + b] = r[0];
+  if (threadIdx.x == 0 && tot) tot[n * nb + b] = r[0];
 }
 
-// One workgroup per sequence: tot[n][b] <- sum of tot[n][b'] for b' > b, plus
-// <dS_end[n], S_end[n]> (S_end given transposed, as the dQ sweep ends with
-// S^T; either may be null: no such term).  Thread j owns the run of blocks
-// [j m, (j+1) m), m = ceil(nb / 256): run sums, a reverse exclusive scan of
-// the 256 run sums in LDS, then each run written back from its own end.
-__global__ __launch_bounds__(256) void k_gate_grad_totals(float* tot, int64_t nb, const float* dSe,
-                                                          const float* SendT, int D) {
-  __shared__ float red[256];
-  const int64_t n = blockIdx.x;
+// One workgroup per (sequence n, block b): tot[n][b] = the gate gradient at
+// the first token y = (b+1) GBLK of the next block, alpha_y <G_y, S_{y-1}>,
+// an elementwise dot of S^T (the forward sweep's start state of sub-segment
+// b + 1) and G^T (the reverse sweep's start state at row y, transposed; the
+// reverse sweep numbers its sub-segments from the end), or for the last block
+// <dS_end, S_end> (S_end given transposed; either null: 0).  Products in
+// fp32, sums in fp64 in a fixed order.
+__global__ __launch_bounds__(256) void k_gate_anchors(const float* WfT, const float* WrT,
+                                                      const float* G, const float* dSe,
+                                                      const float* SendT, float* tot, int64_t Ls,
+                                                      int64_t nb, int D) {
+  __shared__ double red[256];
+  const int64_t n = (int64_t)blockIdx.x / nb;
+  const int64_t b = (int64_t)blockIdx.x % nb;
   const int j = threadIdx.x;
+  const int64_t DD = (int64_t)D * D;
   float e = 0.0f;
-  if (dSe && SendT) {
-    const int64_t DD = (int64_t)D * D;
+  double scale = 1.0;
+  if (b < nb - 1) {
+    const f32x4* x = reinterpret_cast<const f32x4*>(WfT + (n * (nb - 1) + b) * DD);
+    const f32x4* y = reinterpret_cast<const f32x4*>(WrT + (n * (nb - 1) + (nb - 2 - b)) * DD);
+    for (int64_t i = j; i < DD / 4; i += 256) {
+      const f32x4 p = x[i] * y[i];
+      e += (p[0] + p[1]) + (p[2] + p[3]);
+    }
+    scale = exp((double)G[n * Ls + (b + 1) * GBLK]);
+  } else if (dSe && SendT) {
     for (int64_t i = j; i < DD; i += 256) {
       const int64_t kk = i / D, vv = i % D;
       e += dSe[n * DD + i] * SendT[n * DD + vv * D + kk];
     }
   }
-  red[j] = e;
+  red[j] = (double)e;
   __syncthreads();
   for (int s2 = 128; s2 > 0; s2 >>= 1) {
     if (j < s2) red[j] += red[j + s2];
     __syncthreads();
   }
-  const float end_term = red[0];
-  __syncthreads();
-  const int64_t m = (nb + 255) / 256;
-  const int64_t b0 = j * m, b1 = (b0 + m < nb) ? b0 + m : nb;
-  float run = 0.0f;
-  for (int64_t b = b0; b < b1; ++b) run += tot[n * nb + b];
-  red[j] = run;
-  __syncthreads();
-  // reverse exclusive scan over the runs: after = sum of runs j' > j
-  for (int d = 1; d < 256; d <<= 1) {
-    const float add = (j + d < 256) ? red[j + d] : 0.0f;
-    __syncthreads();
-    red[j] += add;
-    __syncthreads();
-  }
-  float acc = end_term + red[j] - run;  // sum of the runs after this one
-  for (int64_t b = b1 - 1; b >= b0; --b) {
-    const float x = tot[n * nb + b];
-    tot[n * nb + b] = acc;
-    acc += x;
-  }
+  if (j == 0) tot[n * nb + b] = (float)(red[0] * scale);
 }
 
 __global__ __launch_bounds__(256) void k_gate_grad_finish(float* dG, const float* tot, int64_t nseq,
@@ -166,18 +166,28 @@ hipError_t launch_scale_first_gate(float* X, const float* G, int64_t nseq, int64
   return hipGetLastError();
 }
 
+hipError_t launch_gate_anchors(const float* WfT, const float* WrT, const float* G,
+                               const float* dSe, const float* SendT, float* tot, int64_t nseq,
+                               int64_t Ls, int D, hipStream_t s) {
+  const int64_t nb = gate_grad_blocks(Ls);
+  if (nseq <= 0 || nb <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_gate_anchors, dim3((unsigned)(nseq * nb)), dim3(256), 0, s, WfT, WrT, G, dSe,
+                     SendT, tot, Ls, nb, D);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 static hipError_t gate_grad_t(const void* Q, const void* dQ, const void* K, const void* dK,
                               float* dG, float* tot, const float* dSe, const float* SendT,
                               int64_t nseq, int64_t Ls, hipStream_t s) {
+  (void)dSe;
+  (void)SendT;
   const int64_t nb = gate_grad_blocks(Ls);
+  // the block totals are not needed: tot already holds the anchors
   hipLaunchKernelGGL((k_gate_grad_blocks<T, D>), dim3((unsigned)(nseq * nb)), dim3(256), 0, s,
-                     (const T*)Q, (const T*)dQ, (const T*)K, (const T*)dK, dG, tot, Ls, nb);
+                     (const T*)Q, (const T*)dQ, (const T*)K, (const T*)dK, dG, nullptr, Ls, nb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_gate_grad_totals, dim3((unsigned)nseq), dim3(256), 0, s, tot, nb, dSe,
-                     SendT, D);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t all = nseq * Ls;
   hipLaunchKernelGGL(k_gate_grad_finish, dim3((unsigned)((all + 255) / 256)), dim3(256), 0, s, dG,
                      tot, nseq, Ls, nb);

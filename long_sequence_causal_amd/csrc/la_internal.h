@@ -37,6 +37,11 @@ struct FwdArgs {
   // reverse time order (token t of a sequence is read as token Ls-1-t); used
   // by the backward's reverse sweeps
   int reverse;
+  // sub-segment partition: 0 = [p Lp, min((p+1) Lp, Ls)) (a short last one);
+  // 1 = the short one first, [max(0, e - Lp), e) with e = Ls - (split-1-p) Lp,
+  // so that a reverse sweep cuts a sequence at the same rows m Lp as a
+  // forward one
+  int ragged_first;
   // gated recurrence (gated != 0): log-gates G [nseq*Ls], read only for the
   // chunks walked, and lam is never read; state-only launches write the total
   // log-gate of each sub-segment to LDout[n][p - sout_p0] beside Sout
@@ -130,6 +135,17 @@ hipError_t launch_shift_gates(const float* G, float* Gs, int64_t nseq, int64_t L
 hipError_t launch_scale_first_gate(float* X, const float* G, int64_t nseq, int64_t Ls, int D,
                                    hipStream_t s);
 int64_t gate_grad_blocks(int64_t Ls);
+// Per sequence n and block b of GBLK tokens, the gate gradient at the first
+// token of block b + 1: alpha_y <G_y, S_{y-1}> at y = (b+1) GBLK from the
+// forward sweep's start states WfT ([nseq][nb-1] of S^T) and the reverse
+// sweep's, transposed in place (WrT, [nseq][nb-1] of G^T, in reverse order);
+// for the last block <dS_end, S_end> (dSe, SendT may be null: 0).  Written
+// to tot[n][b] for launch_gate_grad_finish.  Requires 1024-token sub-segments.
+hipError_t launch_gate_anchors(const float* WfT, const float* WrT, const float* G,
+                               const float* dSe, const float* SendT, float* tot, int64_t nseq,
+                               int64_t Ls, int D, hipStream_t s);
+// dG[t] = the in-block suffix sum of r plus tot[n][t / GBLK] (launch_gate_grad
+// with anchors = true skips its own block-total scan)
 hipError_t launch_gate_grad(int dtype, int D, const void* Q, const void* dQ, const void* K,
                             const void* dK, float* dG, float* tot, const float* dSe,
                             const float* SendT, int64_t nseq, int64_t Ls, hipStream_t s);

@@ -179,6 +179,10 @@ BWD_CASES = [
     ("fp32", 64, 1, 2, 1024 + 17, 1, 0, 0.0, 0.0),
     ("fp32", 64, 2, 2, 130 * 2, 2, 2, 0.5, 0.5),
     ("fp32", 128, 1, 1, 70, 1, 0, 0.5, 0.5),
+    # several 1024-token sub-segments (ragged, segmented): anchored gate gradient
+    ("bf16", 128, 1, 2, 5000, 1, 0, 0.5, 0.5),
+    ("bf16", 64, 1, 2, 3 * 2100, 3, 0, 0.5, 0.5),
+    ("fp32", 64, 1, 2, 4096 + 64, 1, 0, 0.5, 0.5),
 ]
 
 
@@ -213,3 +217,38 @@ def test_gated_bwd_optional_outputs():
     assert part[3] is None and part[4] is None
     for a, b in zip(full[:3], part[:3]):
         assert bool(torch.equal(a, b))
+
+
+def test_gated_bwd_at_the_training_workload_on_sampled_heads():
+    """The 256K x 16 training workload with per-token gates, at full size in
+    the launch configuration the benchmark times; the oracle checks two whole
+    heads (every token), the log-gate gradient included.  The measure is the
+    tolerance's, max |X - ref| / max |ref| over the tensor, here over the two
+    sampled heads (a conservative stand-in for all 16: their max |ref| can
+    only be larger).  Each head's error on its own scale is logged too: the
+    short-window head's log-gate gradient is small next to the terms of its
+    suffix sums, about 1.8 % of its own maximum."""
+    from long_sequence_causal_amd.inputs import WORKLOADS
+    w = WORKLOADS["train_256k"]
+    inp = workload_inputs(w.name, device="cuda")
+    q, k, v, lam, dO = inp["q"], inp["k"], inp["v"], inp["lam"], inp["dO"]
+    G = gate_logs(lam, w.B, w.L, w.seed, device="cuda")
+    log(f"gated bwd full size: {w.name} B={w.B} H={w.H} L={w.L}")
+    got = la.la_chunk_bwd_gated(q, k, v, G, dO)
+    torch.cuda.synchronize()
+    heads = (0, w.H - 1)
+    gots, refs = [], []
+    for h in heads:
+        sl = lambda t: f64(t[:, h:h + 1])
+        ref = lao.bwd_gated(sl(q), sl(k), sl(v), sl(G), sl(dO))
+        gots.append([sl(x) for x in got])
+        refs.append(ref)
+        errs = [rel_err(a, r) for a, r in zip(gots[-1], ref)]
+        log("  head {} on its own scale: err dQ={:.3e} dK={:.3e} dV={:.3e} dS0={:.3e} "
+            "dlogalpha={:.3e}".format(h, *errs))
+    joint = [rel_err(np.concatenate([g[i] for g in gots], axis=1),
+                     np.concatenate([r[i] for r in refs], axis=1)) for i in range(5)]
+    log("  sampled heads jointly: err dQ={:.3e} dK={:.3e} dV={:.3e} dS0={:.3e} "
+        "dlogalpha={:.3e}".format(*joint))
+    assert max(joint) <= TOL["bf16"]
+    del q, k, v, dO, got
