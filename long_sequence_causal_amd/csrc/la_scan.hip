@@ -12,6 +12,7 @@
 
 namespace la {
 
+template <bool GATED>
 __global__ __launch_bounds__(256) void k_state_scan(ScanArgs a) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (gid >= a.nseq * a.E) return;
@@ -19,15 +20,39 @@ __global__ __launch_bounds__(256) void k_state_scan(ScanArgs a) {
   const int64_t e = gid - n * a.E;
   // lambda^seg_len = 2^(seg_len log2 lambda); underflow to 0 is intended
   const float dec =
-      a.gated ? 0.0f : exp2f((float)a.seg_len * log2f(a.lam[(int)((n / a.hdiv) % a.H)]));
+      GATED ? 0.0f : exp2f((float)a.seg_len * log2f(a.lam[(int)((n / a.hdiv) % a.H)]));
   float x = a.S0 ? a.S0[n * a.E + e] : 0.0f;
-  for (int it = 0; it < a.P; ++it) {
-    const int s = a.reverse ? (a.P - 1 - it) : it;
+  // Segments go in groups of PF whose inputs are all loaded before any of
+  // the group's outputs is stored: Sout may be dS itself, so the compiler
+  // cannot move a load above an earlier store, and one segment per memory
+  // round trip would make a long scan latency-bound.  Each output element is
+  // written only after its own input was read, so in place stays correct.
+  constexpr int PF = 16;
+  auto seg = [&](int it) { return a.reverse ? (a.P - 1 - it) : it; };
+  int it = 0;
+  for (; it + PF <= a.P; it += PF) {
+    float d[PF], f[PF];
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int s = seg(it + j);
+      d[j] = a.dS[(n * a.P + s) * a.E + e];
+      f[j] = GATED ? a.LD[n * a.P + s] : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < PF; ++j) {
+      const int64_t idx = (n * a.P + seg(it + j)) * a.E + e;
+      if (!a.inclusive) a.Sout[idx] = x;
+      // gated: the segment's own product of gates, exp(LD)
+      x = (GATED ? expf(f[j]) : dec) * x + d[j];
+      if (a.inclusive) a.Sout[idx] = x;
+    }
+  }
+  for (; it < a.P; ++it) {
+    const int s = seg(it);
     const int64_t idx = (n * a.P + s) * a.E + e;
     const float d = a.dS[idx];
     if (!a.inclusive) a.Sout[idx] = x;
-    // gated: the segment's own product of gates, exp(LD)
-    x = (a.gated ? expf(a.LD[n * a.P + s]) : dec) * x + d;
+    x = (GATED ? expf(a.LD[n * a.P + s]) : dec) * x + d;
     if (a.inclusive) a.Sout[idx] = x;
   }
   if (a.Send) a.Send[n * a.E + e] = x;
@@ -89,7 +114,10 @@ hipError_t launch_transpose(float* W, int64_t nmat, int D, hipStream_t s) {
 hipError_t launch_scan(const ScanArgs& a, hipStream_t s) {
   const int64_t tot = a.nseq * a.E;
   if (tot <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_state_scan, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, a);
+  if (a.gated)
+    hipLaunchKernelGGL(k_state_scan<true>, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_state_scan<false>, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
