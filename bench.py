@@ -49,26 +49,45 @@ def alg_flops(B, H, L, d):
 FWD_KERNEL_SOURCES = ("la_device.h", "la_fwd.hip", "la_internal.h", "la_walk.h")
 
 
-def measured_traffic():
-    """HBM bytes per launch of the main chunk kernel from the committed
-    FETCH_SIZE / WRITE_SIZE profile, or None once the kernel's sources differ
-    from the ones profiled (SHA-256 over FWD_KERNEL_SOURCES in that order,
-    each name followed by its bytes)."""
+def _fwd_kernel_sha():
     import hashlib
-    import re
-    prof = os.path.join(ROOT, "profiles", "k_chunk_fwd_segment_64k_hbm_bytes.md")
-    try:
-        m = re.search(r"```json\n(\{.*?\})\n```", open(prof).read(), re.S)
-        rec = json.loads(m.group(1))
-    except (OSError, AttributeError, ValueError):
-        return None
     src = os.path.join(ROOT, "long_sequence_causal_amd", "csrc")
     h = hashlib.sha256()
     for name in FWD_KERNEL_SOURCES:
         h.update(name.encode())
         with open(os.path.join(src, name), "rb") as f:
             h.update(f.read())
-    return rec["traffic_bytes"] if h.hexdigest() == rec.get("sources_sha256") else None
+    return h.hexdigest()
+
+
+def _profile_record(name):
+    """The JSON record of a committed profile summary, or None."""
+    import re
+    try:
+        text = open(os.path.join(ROOT, "profiles", name)).read()
+        return json.loads(re.search(r"```json\n(\{.*?\})\n```", text, re.S).group(1))
+    except (OSError, AttributeError, ValueError):
+        return None
+
+
+def measured_mfma():
+    """MFMA busy share (%) of the main chunk kernel from the committed
+    MfmaUtil profile, or None once the kernel's sources differ."""
+    rec = _profile_record("k_chunk_fwd_segment_64k_mfma.md")
+    if rec is None or rec.get("sources_sha256") != _fwd_kernel_sha():
+        return None
+    return rec["mfma_util_pct"]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the main chunk kernel from the committed
+    FETCH_SIZE / WRITE_SIZE profile, or None once the kernel's sources differ
+    from the ones profiled (SHA-256 over FWD_KERNEL_SOURCES in that order,
+    each name followed by its bytes)."""
+    rec = _profile_record("k_chunk_fwd_segment_64k_hbm_bytes.md")
+    if rec is None or rec.get("sources_sha256") != _fwd_kernel_sha():
+        return None
+    return rec["traffic_bytes"]
 
 
 def backward_leg(torch, la, workload_inputs, WORKLOADS, dev, iters):
@@ -345,7 +364,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "k_chunk_fwd<bf16,128,with O>",
-                     "alg_bytes_per_launch": nbytes, "kernel_us": main_ms * 1e3},
+                     "alg_bytes_per_launch": nbytes, "kernel_us": main_ms * 1e3,
+                     "mfma_util_pct": measured_mfma()},
     }
     if not args.no_gated:
         from long_sequence_causal_amd.inputs import gate_logs
