@@ -211,6 +211,20 @@ def decode_leg(torch, la, dev, iters):
             "achieved_GBs": nbytes / t / 1e9, "frac_hbm": nbytes / t / 1e9 / HBM_PEAK_GBS}
 
 
+def time_each(fn, iters, stream):
+    """Milliseconds of each of `iters` calls, each between its own events."""
+    import torch
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    evs[-1][1].synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
 def time_events(fn, iters, stream):
     import torch
 
@@ -310,6 +324,21 @@ def main():
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     eprint(f"[bench] whole op: {ms_ev * 1e3:.1f} us/step (events), {wall_ms * 1e3:.1f} us/step (wall)")
+    # the same calls timed one by one (an event pair around each), for the
+    # median and the minimum
+    per_call = sorted(time_each(step, args.steps, stream))
+    med_ms, min_ms = per_call[len(per_call) // 2], per_call[0]
+
+    # a device-to-device copy of 1 GiB (read 1 GiB, write 1 GiB): the
+    # bandwidth a plain copy reaches on this GPU
+    big = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    big2 = torch.empty_like(big)
+    big2.copy_(big)
+    copy_ms = time_events(lambda: big2.copy_(big), 5, stream)
+    copy_gbs = 2 * (1 << 30) / (copy_ms / 1e3) / 1e9
+    del big, big2
+    eprint(f"[bench] per call: median {med_ms * 1e3:.1f} us, min {min_ms * 1e3:.1f} us; "
+           f"1 GiB device copy {copy_gbs:.0f} GB/s")
 
     # The dominant kernel alone: with nseg = split and the scanned start
     # states, la_chunk_fwd launches exactly the main chunk kernel of the
@@ -361,6 +390,9 @@ def main():
                    "split": split, "S0": "N(0,0.02^2) fp32"},
         "tflops_alg": flops / t / 1e12,
         "frac_hbm_whole_op": nbytes / t / 1e9 / HBM_PEAK_GBS,
+        "per_call_us": {"median": med_ms * 1e3, "min": min_ms * 1e3},
+        "copy_GBs": copy_gbs,
+        "frac_of_copy_whole_op": nbytes / t / 1e9 / copy_gbs,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "k_chunk_fwd<bf16,128,with O>",
@@ -388,6 +420,7 @@ def main():
     if not args.no_cpu:
         eprint("[bench] CPU oracle baseline ...")
         rec["cpu_baseline"] = cpu_baseline(inp, H, L, d)
+        rec["cpu_baseline"]["gpu_over_cpu"] = tok_s / rec["cpu_baseline"]["value"]
     print(json.dumps(rec), flush=True)
 
 
