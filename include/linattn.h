@@ -216,7 +216,9 @@ la_status la_state_scan_gated(int64_t B, int64_t H, int32_t P, int32_t dk, int32
                               const float* dS, const float* log_decay, const float* S0,
                               float* S_start, float* S_end, int32_t reverse, void* stream);
 
-/* Workspace bytes la_chunk_bwd_gated needs for `shape`. */
+/* Workspace bytes la_chunk_bwd_gated needs for `shape`: about
+ * 2 * ceil(L/nseg / 1024) fp32 d x d states per sequence (the start states of
+ * both sweeps, 128 B per token-head at d = 128) plus the shifted gates. */
 size_t la_bwd_gated_workspace_bytes(const la_shape* shape);
 
 /*
@@ -236,6 +238,12 @@ size_t la_bwd_gated_workspace_bytes(const la_shape* shape);
  *   dS0 [B,H,nseg,dk,dv] fp32 output; NULL = not returned.
  *   dlog_alpha [B,H,L] fp32   output; NULL = not returned.
  *   ws, ws_bytes              workspace of la_bwd_gated_workspace_bytes().
+ * The sweeps always cut each segment into sub-segments of 1024 tokens
+ * (shape->split is ignored), the reverse ones with the short sub-segment
+ * first so that both cut at the same rows: at every such row y the gate
+ * gradient alpha_y <G_y, S_{y-1}> is formed exactly from the two sweeps' fp32
+ * states, so the suffix sums of the second form never span more than 1024
+ * tokens.
  * Errors as la_chunk_bwd.
  */
 la_status la_chunk_bwd_gated(const la_shape* shape, const void* Q, const void* K,
