@@ -212,9 +212,9 @@ la_status run_flow(const Plan& pl, int dtype, int H, int nseg, const void* Q, co
   return run_main(pl, dtype, H, nseg, Q, K, V, lam, start, O, Send, W, reverse, st, gated, G);
 }
 
-// gated forward workspace: the start states, then the sub-segment log-gates
-// Workspace of la_decay_grad: local, then start pairs (S, T) of sub-segments
-// 1..split-1 and one fp64 share per sub-segment.
+// Workspace of la_decay_grad: the local, then start, pairs (S, U) of
+// sub-segments 1..split-1 (S and U in separate blocks) and one fp64 share per
+// sub-segment.
 struct TangentWs {
   size_t WS = 0, WT = 0, part = 0, total = 0;
 };
@@ -229,6 +229,7 @@ TangentWs tangent_ws(const Plan& p) {
   return w;
 }
 
+// gated forward workspace: the start states, then the sub-segment log-gates
 size_t gated_ws_bytes(const Plan& p) {
   if (p.split <= 1) return 0;
   return scan_ws_bytes(p) + ((size_t)p.nseq * (size_t)(p.split - 1) * sizeof(float) + 255) / 256 * 256;
@@ -330,9 +331,6 @@ la_status la_chunk_fwd_gated(const la_shape* s, const void* Q, const void* K, co
                   static_cast<hipStream_t>(stream), true, log_alpha, LDw);
 }
 
-// gated backward workspace (in order): prepared start state [nseq][D][D],
-// start states and log-gates of the sweeps, shifted gates [nseq][Ls], the
-// final dQ-sweep state [nseq][D][D] and the gate-gradient block totals
 // The gated backward cuts every sequence into sub-segments of exactly 1024
 // tokens (whatever `split` asks for): the sweeps' start states at their
 // boundaries anchor the log-gate gradient (k_gate_anchors), so that its suffix
@@ -348,6 +346,11 @@ Plan gated_bwd_plan(const Plan& p) {
   return g;
 }
 
+// gated backward workspace (in order): prepared start state [nseq][D][D],
+// the forward sweep's start states W and the reverse sweeps' W2 (each
+// [nseq][split-1][D][D], kept side by side for the anchors), the sweeps'
+// sub-segment log-gates (reused), shifted gates [nseq][Ls], the final
+// dQ-sweep state [nseq][D][D] and one anchor per 1024-token block
 struct GatedBwdWs {
   size_t A, W, W2, LD, Gs, SE, TOT, total;
 };
