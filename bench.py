@@ -270,7 +270,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps first (the GPU clock takes tens of ms to ramp up)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--split", type=int, default=0, help="internal split (0 = library choice)")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward leg")

@@ -126,6 +126,31 @@ def _need(t, name, dtype=None):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
 
 
+def _expect_all(device, *specs):
+    """Each (tensor, name, shape, dtype) with a tensor given must have exactly
+    `shape` -- the kernels index every buffer by the sizes passed through the C
+    ABI, which cannot see tensor extents -- and be a contiguous `dtype` tensor
+    on `device`.  Every shape is checked before any dtype or device."""
+    for t, name, shape, _ in specs:
+        if t is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    for t, name, _, dtype in specs:
+        if t is None:
+            continue
+        _need(t, name, dtype)
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _out_specs(out, names, shapes, dtypes):
+    """_expect_all specs of a tuple of preallocated outputs (none if out is None)."""
+    if out is None:
+        return ()
+    if len(out) != len(names):
+        raise ValueError(f"out must hold {len(names)} tensors ({', '.join(names)})")
+    return tuple(zip(out, names, shapes, dtypes))
+
+
 def make_shape(B, H, L, dk, dv, nseg=1, dtype=LA_BF16, split=0) -> la_shape:
     return la_shape(int(B), int(H), int(L), int(dk), int(dv), int(nseg), int(dtype),
                     int(split), 0)
@@ -153,10 +178,16 @@ def la_chunk_fwd(q, k, v, lam, S0=None, nseg: int = 1, need_O: bool = True,
     B, H, L, dk = q.shape
     dv = v.shape[-1]
     dt = _dtype_code(q.dtype)
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n, q.dtype)
-    _need(lam, "lam", torch.float32)
-    _need(S0, "S0", torch.float32)
+    dev = q.device
+    _expect_all(
+        dev,
+        (q, "q", (B, H, L, dk), q.dtype),
+        (k, "k", (B, H, L, dk), q.dtype),
+        (v, "v", (B, H, L, dv), q.dtype),
+        (lam, "lam", (H,), torch.float32),
+        (S0, "S0", (B, H, nseg, dk, dv), torch.float32),
+        (out, "out", (B, H, L, dv), q.dtype),
+        (S_end_out, "S_end_out", (B, H, nseg, dk, dv), torch.float32))
     shape = make_shape(B, H, L, dk, dv, nseg, dt, split)
     O = None
     if need_O:
@@ -185,12 +216,16 @@ def la_chunk_fwd_gated(q, k, v, log_alpha, S0=None, nseg: int = 1, need_O: bool 
     B, H, L, dk = q.shape
     dv = v.shape[-1]
     dt = _dtype_code(q.dtype)
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n, q.dtype)
-    _need(log_alpha, "log_alpha", torch.float32)
-    if log_alpha.shape != (B, H, L):
-        raise ValueError(f"log_alpha has shape {tuple(log_alpha.shape)}, expected {(B, H, L)}")
-    _need(S0, "S0", torch.float32)
+    dev = q.device
+    _expect_all(
+        dev,
+        (q, "q", (B, H, L, dk), q.dtype),
+        (k, "k", (B, H, L, dk), q.dtype),
+        (v, "v", (B, H, L, dv), q.dtype),
+        (log_alpha, "log_alpha", (B, H, L), torch.float32),
+        (S0, "S0", (B, H, nseg, dk, dv), torch.float32),
+        (out, "out", (B, H, L, dv), q.dtype),
+        (S_end_out, "S_end_out", (B, H, nseg, dk, dv), torch.float32))
     shape = make_shape(B, H, L, dk, dv, nseg, dt, split)
     O = None
     if need_O:
@@ -212,9 +247,13 @@ def la_state_scan_gated(dS, log_decay, S0=None, reverse: bool = False, out=None,
     """Gated segment combine.  dS [B,H,P,dk,dv] fp32, log_decay [B,H,P] fp32,
     S0 [B,H,dk,dv] or None.  Returns (S_start, S_end or None)."""
     B, H, P, dk, dv = dS.shape
-    _need(dS, "dS", torch.float32)
-    _need(log_decay, "log_decay", torch.float32)
-    _need(S0, "S0", torch.float32)
+    dev = dS.device
+    _expect_all(
+        dev,
+        (dS, "dS", (B, H, P, dk, dv), torch.float32),
+        (log_decay, "log_decay", (B, H, P), torch.float32),
+        (S0, "S0", (B, H, dk, dv), torch.float32),
+        (out, "out", (B, H, P, dk, dv), torch.float32))
     S_start = out if out is not None else torch.empty_like(dS)
     S_end = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dS.device) if need_S_end else None
     _check(lib().la_state_scan_gated(B, H, P, dk, dv, _ptr(dS), _ptr(log_decay), _ptr(S0),
@@ -227,9 +266,13 @@ def la_state_scan(dS, lam, seg_len: int, S0=None, reverse: bool = False, out=Non
     """Segment scan.  dS [B,H,P,dk,dv] fp32, lam [H], S0 [B,H,dk,dv] or None.
     Returns (S_start [B,H,P,dk,dv], S_end [B,H,dk,dv] or None); ``out`` may be dS."""
     B, H, P, dk, dv = dS.shape
-    _need(dS, "dS", torch.float32)
-    _need(lam, "lam", torch.float32)
-    _need(S0, "S0", torch.float32)
+    dev = dS.device
+    _expect_all(
+        dev,
+        (dS, "dS", (B, H, P, dk, dv), torch.float32),
+        (lam, "lam", (H,), torch.float32),
+        (S0, "S0", (B, H, dk, dv), torch.float32),
+        (out, "out", (B, H, P, dk, dv), torch.float32))
     S_start = out if out is not None else torch.empty_like(dS)
     S_end = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dS.device) if need_S_end else None
     _check(lib().la_state_scan(B, H, P, dk, dv, _ptr(dS), _ptr(lam), int(seg_len), _ptr(S0),
@@ -244,19 +287,22 @@ def la_chunk_bwd(q, k, v, lam, dO, S0=None, dS_end=None, nseg: int = 1,
     B, H, L, dk = q.shape
     dv = v.shape[-1]
     dt = _dtype_code(q.dtype)
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (dO, "dO")):
-        _need(t, n, q.dtype)
-    _need(lam, "lam", torch.float32)
-    _need(S0, "S0", torch.float32)
-    _need(dS_end, "dS_end", torch.float32)
+    dev = q.device
+    _expect_all(
+        dev,
+        (q, "q", (B, H, L, dk), q.dtype),
+        (k, "k", (B, H, L, dk), q.dtype),
+        (v, "v", (B, H, L, dv), q.dtype),
+        (dO, "dO", (B, H, L, dv), q.dtype),
+        (lam, "lam", (H,), torch.float32),
+        (S0, "S0", (B, H, nseg, dk, dv), torch.float32),
+        (dS_end, "dS_end", (B, H, nseg, dk, dv), torch.float32),
+        *_out_specs(out, ("dQ", "dK", "dV", "dS0"),
+                    ((B, H, L, dk), (B, H, L, dk), (B, H, L, dv), (B, H, nseg, dk, dv)),
+                    (q.dtype, q.dtype, q.dtype, torch.float32)))
     shape = make_shape(B, H, L, dk, dv, nseg, dt, split)
     if out is not None:
         dQ, dK, dV, dS0 = out
-        for t, ref, n in ((dQ, q, "dQ"), (dK, k, "dK"), (dV, v, "dV")):
-            _need(t, n, q.dtype)
-            if t.shape != ref.shape:
-                raise ValueError(f"{n} has shape {tuple(t.shape)}, expected {tuple(ref.shape)}")
-        _need(dS0, "dS0", torch.float32)
     else:
         dQ = torch.empty_like(q)
         dK = torch.empty_like(k)
@@ -284,13 +330,19 @@ def la_chunk_bwd_gated(q, k, v, log_alpha, dO, S0=None, dS_end=None, nseg: int =
     B, H, L, dk = q.shape
     dv = v.shape[-1]
     dt = _dtype_code(q.dtype)
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (dO, "dO")):
-        _need(t, n, q.dtype)
-    _need(log_alpha, "log_alpha", torch.float32)
-    if log_alpha.shape != (B, H, L):
-        raise ValueError(f"log_alpha has shape {tuple(log_alpha.shape)}, expected {(B, H, L)}")
-    _need(S0, "S0", torch.float32)
-    _need(dS_end, "dS_end", torch.float32)
+    dev = q.device
+    _expect_all(
+        dev,
+        (q, "q", (B, H, L, dk), q.dtype),
+        (k, "k", (B, H, L, dk), q.dtype),
+        (v, "v", (B, H, L, dv), q.dtype),
+        (dO, "dO", (B, H, L, dv), q.dtype),
+        (log_alpha, "log_alpha", (B, H, L), torch.float32),
+        (S0, "S0", (B, H, nseg, dk, dv), torch.float32),
+        (dS_end, "dS_end", (B, H, nseg, dk, dv), torch.float32),
+        *_out_specs(out, ("dQ", "dK", "dV", "dS0", "dlog_alpha"),
+                    ((B, H, L, dk), (B, H, L, dk), (B, H, L, dv), (B, H, nseg, dk, dv), (B, H, L)),
+                    (q.dtype, q.dtype, q.dtype, torch.float32, torch.float32)))
     shape = make_shape(B, H, L, dk, dv, nseg, dt, split)
     if out is not None:
         dQ, dK, dV, dS0, dG = out
@@ -318,11 +370,17 @@ def la_decay_grad(q, k, v, lam, dO, S0=None, dS_end=None, nseg: int = 1, split: 
     B, H, L, dk = q.shape
     dv = v.shape[-1]
     dt = _dtype_code(q.dtype)
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (dO, "dO")):
-        _need(t, n, q.dtype)
-    _need(lam, "lam", torch.float32)
-    _need(S0, "S0", torch.float32)
-    _need(dS_end, "dS_end", torch.float32)
+    dev = q.device
+    _expect_all(
+        dev,
+        (q, "q", (B, H, L, dk), q.dtype),
+        (k, "k", (B, H, L, dk), q.dtype),
+        (v, "v", (B, H, L, dv), q.dtype),
+        (dO, "dO", (B, H, L, dv), q.dtype),
+        (lam, "lam", (H,), torch.float32),
+        (S0, "S0", (B, H, nseg, dk, dv), torch.float32),
+        (dS_end, "dS_end", (B, H, nseg, dk, dv), torch.float32),
+        (out, "out", (H,), torch.float32))
     shape = make_shape(B, H, L, dk, dv, nseg, dt, split)
     dlam = out if out is not None else torch.empty((H,), dtype=torch.float32, device=q.device)
     nbytes = la_decay_grad_workspace_bytes(shape)
@@ -340,13 +398,18 @@ def la_step(q, k, v, lam, S=None, out=None, S_out=None, need_o: bool = True):
     B, H, dk = q.shape
     dv = v.shape[-1]
     dt = _dtype_code(q.dtype)
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n, q.dtype)
-    _need(lam, "lam", torch.float32)
-    _need(S, "S", torch.float32)
+    dev = q.device
+    _expect_all(
+        dev,
+        (q, "q", (B, H, dk), q.dtype),
+        (k, "k", (B, H, dk), q.dtype),
+        (v, "v", (B, H, dv), q.dtype),
+        (lam, "lam", (H,), torch.float32),
+        (S, "S", (B, H, dk, dv), torch.float32),
+        (S_out, "S_out", (B, H, dk, dv), torch.float32),
+        (out, "out", (B, H, dv), q.dtype))
     if S_out is None:
         S_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
-    _need(S_out, "S_out", torch.float32)
     o = out if out is not None else (
         torch.empty((B, H, dv), dtype=q.dtype, device=q.device) if need_o else None)
     _check(lib().la_step(B, H, dk, dv, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(lam), _ptr(S),
