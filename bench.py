@@ -118,6 +118,23 @@ def backward_leg(torch, la, workload_inputs, WORKLOADS, dev, iters):
     rec = {"workload": w.name, "B": B, "H": H, "L": L, "d": d, "us_per_call": ms * 1e3,
            "tokens_per_s": B * L / t, "alg_bytes": nbytes, "achieved_GBs": nbytes / t / 1e9,
            "frac_hbm": nbytes / t / 1e9 / HBM_PEAK_GBS, "tflops_alg": flops / t / 1e12}
+    # the same backward taking the start states a forward call just left in
+    # its workspace (la_chunk_bwd_from_fwd), as a training step would
+    fws = torch.empty(max(la.la_fwd_workspace_bytes(shape), 1), dtype=torch.uint8, device=dev)
+    la.la_chunk_fwd(q, k, v, lam, S0=S0, need_O=False, workspace=fws)
+
+    def fcall():
+        la.la_chunk_bwd(q, k, v, lam, dO, S0=S0, dS_end=dSe, out=out, workspace=ws,
+                        fwd_workspace=fws)
+
+    for _ in range(2):
+        fcall()
+    torch.cuda.synchronize()
+    fms = time_events(fcall, iters, torch.cuda.current_stream())
+    ft = fms / 1e3
+    rec["from_fwd_states"] = {"us_per_call": fms * 1e3, "tokens_per_s": B * L / ft,
+                              "achieved_GBs": nbytes / ft / 1e9,
+                              "frac_hbm": nbytes / ft / 1e9 / HBM_PEAK_GBS}
     # the same with per-token gates: adds the gates read and their gradient
     # written (4 B each per token-head)
     from long_sequence_causal_amd.inputs import gate_logs
@@ -154,7 +171,7 @@ def backward_leg(torch, la, workload_inputs, WORKLOADS, dev, iters):
     rec["decay_grad"] = {"us_per_call": tms * 1e3, "tokens_per_s": B * L / tt, "alg_bytes": tbytes,
                          "achieved_GBs": tbytes / tt / 1e9,
                          "frac_hbm": tbytes / tt / 1e9 / HBM_PEAK_GBS}
-    del inp, q, k, v, dO, out, ws, G, dG, gout, gws, dlam, tws
+    del inp, q, k, v, dO, out, ws, G, dG, gout, gws, dlam, tws, fws
     return rec
 
 
@@ -410,7 +427,8 @@ def main():
         del O, ws
         bw = backward_leg(torch, la, workload_inputs, WORKLOADS, dev, max(3, args.steps // 5))
         eprint(f"[bench] backward ({bw['workload']}): {bw['us_per_call']:.1f} us/call, "
-               f"{bw['achieved_GBs']:.0f} GB/s algorithmic; gated {bw['gated']['us_per_call']:.1f} us/call; "
+               f"{bw['achieved_GBs']:.0f} GB/s algorithmic; from the forward's states "
+               f"{bw['from_fwd_states']['us_per_call']:.1f} us/call; gated {bw['gated']['us_per_call']:.1f} us/call; "
                f"decay gradient {bw['decay_grad']['us_per_call']:.1f} us/call")
         rec["backward"] = bw
     if not args.no_decode:

@@ -177,6 +177,28 @@ la_status la_chunk_bwd(const la_shape* shape, const void* Q, const void* K,
                        void* stream);
 
 /*
+ * la_chunk_bwd for a training step that has just run la_chunk_fwd on the same
+ * inputs: the dQ sweep takes the sub-segment start states that forward call
+ * left in its workspace instead of recomputing them (a state pre-pass over K
+ * and V and a scan: about one eighth of la_chunk_bwd's time at 256K tokens x
+ * 16 heads).  The intermediate memory states are what the LASP-2 page's
+ * abstract exchanges between ranks; keeping them from the forward is the
+ * single-GPU form of that reuse.
+ *   fwd_ws   the workspace of a la_chunk_fwd call with the same shape (split
+ *            included), Q, K, V, lambda and S0, not written since; read only.
+ *            Required when la_fwd_workspace_bytes(shape) > 0, else ignored.
+ *   other arguments and the workspace as for la_chunk_bwd.
+ * Results agree with la_chunk_bwd up to fp32 rounding (the forward forms the
+ * same states with K and V in the other operand roles).  Errors as
+ * la_chunk_bwd; a stale or foreign fwd_ws gives wrong numbers, not an error.
+ */
+la_status la_chunk_bwd_from_fwd(const la_shape* shape, const void* Q, const void* K,
+                                const void* V, const float* lambda, const float* S0,
+                                const void* dO, const float* dS_end, const void* fwd_ws,
+                                void* dQ, void* dK, void* dV, float* dS0, void* ws,
+                                size_t ws_bytes, void* stream);
+
+/*
  * Gated recurrence: the fixed decay becomes a per-token, per-head gate,
  *     S_t = alpha_t * S_{t-1} + k_t v_t^T        o_t = q_t^T S_t
  * the data-dependent gates of the "Gated Linear Attention Transformers with

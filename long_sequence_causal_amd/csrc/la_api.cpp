@@ -651,10 +651,14 @@ la_status la_state_scan(int64_t B, int64_t H, int32_t P, int32_t dk, int32_t dv,
   return LA_OK;
 }
 
-la_status la_chunk_bwd(const la_shape* s, const void* Q, const void* K, const void* V,
-                       const float* lambda, const float* S0, const void* dO, const float* dS_end,
-                       void* dQ, void* dK, void* dV, float* dS0, void* ws, size_t ws_bytes,
-                       void* stream) {
+// The backward of la_chunk_bwd; with fwd_starts (the sub-segment start states
+// S [nseq][split-1][D][D] a la_chunk_fwd call of the same shape left in its
+// workspace) the dQ sweep takes their transposes instead of recomputing them.
+static la_status chunk_bwd(const la_shape* s, const void* Q, const void* K, const void* V,
+                           const float* lambda, const float* S0, const void* dO,
+                           const float* dS_end, const float* fwd_starts, bool from_fwd, void* dQ,
+                           void* dK, void* dV, float* dS0, void* ws, size_t ws_bytes,
+                           void* stream) {
   Plan pl;
   la_status r = check_shape(s, &pl);
   if (r != LA_OK) return r;
@@ -662,7 +666,9 @@ la_status la_chunk_bwd(const la_shape* s, const void* Q, const void* K, const vo
   if (has_tokens && (!Q || !K || !V || !dO || !dQ || !dK || !dV))
     return fail(LA_ERR_INVALID_ARG, "Q, K, V, dO, dQ, dK and dV are required");
   if (pl.nseq > 0 && !lambda) return fail(LA_ERR_INVALID_ARG, "lambda is required");
-  const void* ptrs[] = {Q, K, V, lambda, S0, dO, dS_end, dQ, dK, dV, dS0, ws};
+  if (from_fwd && pl.nseq > 0 && pl.split > 1 && !fwd_starts)
+    return fail(LA_ERR_INVALID_ARG, "fwd_ws is required (this shape splits sequences)");
+  const void* ptrs[] = {Q, K, V, lambda, S0, dO, dS_end, dQ, dK, dV, dS0, ws, fwd_starts};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return fail(LA_ERR_INVALID_ARG, "pointer %p is not 16-byte aligned", p);
   const size_t need = (size_t)pl.nseq * pl.D * pl.D * sizeof(float) + scan_ws_bytes(pl);
@@ -694,7 +700,19 @@ la_status la_chunk_bwd(const la_shape* s, const void* Q, const void* K, const vo
     if ((e = la::launch_prep(pa, st)) != hipSuccess) return hip_fail(e, "prep launch");
     start = A;
   }
-  r = run_flow(pl, s->dtype, H, s->nseg, dO, V, K, lambda, start, dQ, nullptr, W, 0, st);
+  if (from_fwd && pl.split > 1) {
+    // the forward's start states, transposed: S^T starts of the dQ sweep
+    la::PrepArgs ta = pa;
+    ta.nseq = pl.nseq * (pl.split - 1);
+    ta.src = fwd_starts;
+    ta.dst = W;
+    ta.transpose = 1;
+    ta.mode = 0;
+    if ((e = la::launch_prep(ta, st)) != hipSuccess) return hip_fail(e, "prep launch");
+    r = run_main(pl, s->dtype, H, s->nseg, dO, V, K, lambda, start, dQ, nullptr, W, 0, st);
+  } else {
+    r = run_flow(pl, s->dtype, H, s->nseg, dO, V, K, lambda, start, dQ, nullptr, W, 0, st);
+  }
   if (r != LA_OK) return r;
 
   // dv_t = G_t^T k_t: in reverse time G accumulates q dO^T like a state,
@@ -737,6 +755,22 @@ la_status la_chunk_bwd(const la_shape* s, const void* Q, const void* K, const vo
     start = A;
   }
   return run_main(pl, s->dtype, H, s->nseg, V, dO, Q, lambda, start, dK, nullptr, W, 1, st);
+}
+
+la_status la_chunk_bwd(const la_shape* s, const void* Q, const void* K, const void* V,
+                       const float* lambda, const float* S0, const void* dO, const float* dS_end,
+                       void* dQ, void* dK, void* dV, float* dS0, void* ws, size_t ws_bytes,
+                       void* stream) {
+  return chunk_bwd(s, Q, K, V, lambda, S0, dO, dS_end, nullptr, false, dQ, dK, dV, dS0, ws,
+                   ws_bytes, stream);
+}
+
+la_status la_chunk_bwd_from_fwd(const la_shape* s, const void* Q, const void* K, const void* V,
+                                const float* lambda, const float* S0, const void* dO,
+                                const float* dS_end, const void* fwd_ws, void* dQ, void* dK,
+                                void* dV, float* dS0, void* ws, size_t ws_bytes, void* stream) {
+  return chunk_bwd(s, Q, K, V, lambda, S0, dO, dS_end, static_cast<const float*>(fwd_ws), true,
+                   dQ, dK, dV, dS0, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -24,7 +24,7 @@ EXPORTS = ("la_version", "la_status_str", "la_last_error", "la_fwd_workspace_byt
            "la_chunk_fwd", "la_state_scan", "la_bwd_workspace_bytes", "la_chunk_bwd",
            "la_fwd_gated_workspace_bytes", "la_chunk_fwd_gated", "la_state_scan_gated",
            "la_bwd_gated_workspace_bytes", "la_chunk_bwd_gated",
-           "la_decay_grad_workspace_bytes", "la_decay_grad", "la_step")
+           "la_decay_grad_workspace_bytes", "la_decay_grad", "la_step", "la_chunk_bwd_from_fwd")
 
 
 class LinAttnError(RuntimeError):
@@ -80,6 +80,8 @@ def lib():
     L.la_chunk_bwd_gated.argtypes = [sp] + [vp] * 13 + [sz, vp]
     L.la_state_scan_gated.restype = ctypes.c_int
     L.la_state_scan_gated.argtypes = [i64, i64, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp]
+    L.la_chunk_bwd_from_fwd.restype = ctypes.c_int
+    L.la_chunk_bwd_from_fwd.argtypes = [sp] + [vp] * 13 + [sz, vp]
     L.la_step.restype = ctypes.c_int
     L.la_step.argtypes = [i64, i64, i32, i32, i32] + [vp] * 7 + [vp]
     L.la_decay_grad_workspace_bytes.restype = sz
@@ -281,9 +283,13 @@ def la_state_scan(dS, lam, seg_len: int, S0=None, reverse: bool = False, out=Non
 
 
 def la_chunk_bwd(q, k, v, lam, dO, S0=None, dS_end=None, nseg: int = 1,
-                 need_dS0: bool = True, split: int = 0, workspace=None, out=None):
+                 need_dS0: bool = True, split: int = 0, workspace=None, out=None,
+                 fwd_workspace=None):
     """Backward pass.  Returns (dQ, dK, dV, dS0 or None).  `out`, if given, is
-    a (dQ, dK, dV, dS0-or-None) tuple of preallocated outputs."""
+    a (dQ, dK, dV, dS0-or-None) tuple of preallocated outputs.  With
+    `fwd_workspace` (the workspace tensor a la_chunk_fwd call with the same
+    shape and inputs just used) the call goes to la_chunk_bwd_from_fwd, which
+    reuses that call's sub-segment start states."""
     B, H, L, dk = q.shape
     dv = v.shape[-1]
     dt = _dtype_code(q.dtype)
@@ -310,10 +316,20 @@ def la_chunk_bwd(q, k, v, lam, dO, S0=None, dS_end=None, nseg: int = 1,
         dS0 = torch.empty((B, H, nseg, dk, dv), dtype=torch.float32, device=q.device) if need_dS0 else None
     nbytes = la_bwd_workspace_bytes(shape)
     ws = workspace if workspace is not None else _workspace(nbytes, q.device)
-    _check(lib().la_chunk_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(lam),
-                              _ptr(S0), _ptr(dO), _ptr(dS_end), _ptr(dQ), _ptr(dK), _ptr(dV),
-                              _ptr(dS0), _ptr(ws), ws.numel() if ws is not None else 0,
-                              _stream()))
+    nws = ws.numel() if ws is not None else 0
+    if fwd_workspace is not None:
+        need = la_fwd_workspace_bytes(shape)
+        if fwd_workspace.numel() * fwd_workspace.element_size() < need:
+            raise ValueError(f"fwd_workspace holds fewer than the {need} bytes of this shape's plan")
+        _need(fwd_workspace, "fwd_workspace")
+        _check(lib().la_chunk_bwd_from_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
+                                           _ptr(lam), _ptr(S0), _ptr(dO), _ptr(dS_end),
+                                           _ptr(fwd_workspace), _ptr(dQ), _ptr(dK), _ptr(dV),
+                                           _ptr(dS0), _ptr(ws), nws, _stream()))
+    else:
+        _check(lib().la_chunk_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(lam),
+                                  _ptr(S0), _ptr(dO), _ptr(dS_end), _ptr(dQ), _ptr(dK), _ptr(dV),
+                                  _ptr(dS0), _ptr(ws), nws, _stream()))
     return dQ, dK, dV, dS0
 
 

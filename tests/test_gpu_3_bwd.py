@@ -1,6 +1,8 @@
 """Backward parity of la_chunk_bwd (through the C ABI) against the CPU
 oracle's backward, on seeded inputs spanning several chunks, ragged tails,
 segments and internal splits.  Needs a gfx950 GPU."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -89,3 +91,51 @@ def test_bwd_euler_identities():
     assert abs(t_k + s0t - l) <= 1e-2 * (np.sum(np.abs(f64(dK) * K)) + abs(s0t))
     assert abs(t_v + s0t - l) <= 1e-2 * (np.sum(np.abs(f64(dV) * V)) + abs(s0t))
     assert scale > 0
+
+
+FROM_FWD_CASES = [
+    # dtype, D, B, H, L, nseg, split, S0 std, dS_end std
+    ("bf16", 128, 1, 4, 64 * 40 + 17, 1, 0, 0.5, 0.5),
+    ("bf16", 128, 2, 3, 64 * 12, 2, 3, 0.5, 0.0),
+    ("bf16", 64, 1, 2, 64 * 9, 1, 4, 0.0, 0.5),
+    ("fp32", 64, 1, 2, 64 * 10 + 5, 1, 3, 0.5, 0.5),
+]
+
+
+@pytest.mark.parametrize("dtype,D,B,H,L,nseg,split,s0,dse", FROM_FWD_CASES)
+def test_bwd_from_forward_states(dtype, D, B, H, L, nseg, split, s0, dse):
+    """la_chunk_bwd_from_fwd with the workspace of the forward call just made
+    matches the oracle and the plain backward."""
+    log(f"bwd from fwd states dtype={dtype} D={D} B={B} H={H} L={L} nseg={nseg} split={split}")
+    inp = make_inputs(B, H, L, D, D, dtype=dtype, s0_std=s0, nseg=nseg, need_dO=True,
+                      dS_end_std=dse, seed=700 + L + D, device="cuda")
+    q, k, v, lam, S0, dO, dSe = (inp[x] for x in ("q", "k", "v", "lam", "S0", "dO", "dS_end"))
+    shape = la.make_shape(B, H, L, D, D, nseg, la._dtype_code(q.dtype), split)
+    fws = torch.empty(max(la.la_fwd_workspace_bytes(shape), 16), dtype=torch.uint8, device="cuda")
+    la.la_chunk_fwd(q, k, v, lam, S0=S0, nseg=nseg, split=split, workspace=fws)
+    got = la.la_chunk_bwd(q, k, v, lam, dO, S0=S0, dS_end=dSe, nseg=nseg, split=split,
+                          fwd_workspace=fws)
+    plain = la.la_chunk_bwd(q, k, v, lam, dO, S0=S0, dS_end=dSe, nseg=nseg, split=split)
+    torch.cuda.synchronize()
+    ref = lao.bwd(f64(q), f64(k), f64(v), f64(lam), f64(dO), S0=f64(S0), dS_end=f64(dSe), nseg=nseg)
+    errs = [rel_err(f64(x), r) for x, r in zip(got, ref)]
+    diffs = [rel_err(f64(x), f64(y)) for x, y in zip(got, plain)]
+    log("  err dQ={:.3e} dK={:.3e} dV={:.3e} dS0={:.3e}".format(*errs))
+    log("  vs plain backward dQ={:.3e} dK={:.3e} dV={:.3e} dS0={:.3e}".format(*diffs))
+    assert max(errs) <= TOL[dtype]
+    # only dQ can differ (its start states); dK, dV, dS0 take the same path
+    assert all(bool(torch.equal(x, y)) for x, y in zip(got[1:], plain[1:]))
+
+
+def test_bwd_from_forward_states_requires_the_workspace():
+    B, H, L, D = 1, 2, 64 * 8, 64
+    inp = make_inputs(B, H, L, D, D, need_dO=True, seed=9, device="cuda")
+    q, k, v, lam, dO = inp["q"], inp["k"], inp["v"], inp["lam"], inp["dO"]
+    shape = la.make_shape(B, H, L, D, D, 1, la.LA_BF16, 4)
+    ws = torch.empty(la.la_bwd_workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+    out = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
+    st = la.lib().la_chunk_bwd_from_fwd(ctypes.byref(shape), la._ptr(q), la._ptr(k), la._ptr(v),
+                                        la._ptr(lam), None, la._ptr(dO), None, None,
+                                        la._ptr(out[0]), la._ptr(out[1]), la._ptr(out[2]), None,
+                                        la._ptr(ws), ws.numel(), None)
+    assert st == la.LA_ERR_INVALID_ARG
