@@ -104,6 +104,13 @@ size_t scan_ws_bytes(const Plan& p) {
   return (size_t)p.nseq * (size_t)(p.split - 1) * (size_t)p.D * (size_t)p.D * sizeof(float);
 }
 
+// la_chunk_bwd's workspace: two prepared start states per sequence and two
+// sets of sub-segment start states (the reverse sweeps for dV and dK run
+// together, each from its own)
+size_t bwd_ws_bytes(const Plan& p) {
+  return 2 * ((size_t)p.nseq * p.D * p.D * sizeof(float) + scan_ws_bytes(p));
+}
+
 la_status hip_fail(hipError_t e, const char* what) {
   return fail(LA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -172,11 +179,9 @@ la_status run_states(const Plan& pl, int dtype, int H, int nseg, const void* K, 
 // The chunk kernel over every sub-segment from its start state (`start` for
 // sub-segment 0, W for the others), writing O and/or Send.  With O null only
 // the last sub-segment runs (state only).
-la_status run_main(const Plan& pl, int dtype, int H, int nseg, const void* Q, const void* K,
-                   const void* V, const float* lam, const float* start, void* O, float* Send,
-                   const float* W, int reverse, hipStream_t st, bool gated = false,
-                   const float* G = nullptr) {
-  if (pl.nseq == 0 || (!O && !Send)) return LA_OK;
+la::FwdArgs main_args(const Plan& pl, int H, int nseg, const void* Q, const void* K,
+                      const void* V, const float* lam, const float* start, void* O, float* Send,
+                      const float* W, int reverse, bool gated, const float* G) {
   la::FwdArgs ma = flow_args(pl, H, nseg, Q, K, V, lam, reverse);
   ma.gated = gated;
   ma.G = G;
@@ -194,6 +199,15 @@ la_status run_main(const Plan& pl, int dtype, int H, int nseg, const void* Q, co
     ma.p_begin = pl.split - 1;
     ma.p_count = 1;
   }
+  return ma;
+}
+
+la_status run_main(const Plan& pl, int dtype, int H, int nseg, const void* Q, const void* K,
+                   const void* V, const float* lam, const float* start, void* O, float* Send,
+                   const float* W, int reverse, hipStream_t st, bool gated = false,
+                   const float* G = nullptr) {
+  if (pl.nseq == 0 || (!O && !Send)) return LA_OK;
+  const la::FwdArgs ma = main_args(pl, H, nseg, Q, K, V, lam, start, O, Send, W, reverse, gated, G);
   hipError_t e = la::launch_fwd(ma, dtype, pl.D, O != nullptr, pl.nseq * ma.p_count, st);
   if (e != hipSuccess) return hip_fail(e, "chunk kernel launch");
   return LA_OK;
@@ -271,8 +285,7 @@ size_t la_bwd_workspace_bytes(const la_shape* shape) {
     g_last_error = keep;
     return 0;
   }
-  // one prepared start state per sequence + the scan states of one pass
-  return (size_t)pl.nseq * pl.D * pl.D * sizeof(float) + scan_ws_bytes(pl);
+  return bwd_ws_bytes(pl);
 }
 
 la_status la_chunk_fwd(const la_shape* s, const void* Q, const void* K, const void* V,
@@ -671,14 +684,17 @@ static la_status chunk_bwd(const la_shape* s, const void* Q, const void* K, cons
   const void* ptrs[] = {Q, K, V, lambda, S0, dO, dS_end, dQ, dK, dV, dS0, ws, fwd_starts};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return fail(LA_ERR_INVALID_ARG, "pointer %p is not 16-byte aligned", p);
-  const size_t need = (size_t)pl.nseq * pl.D * pl.D * sizeof(float) + scan_ws_bytes(pl);
+  const size_t need = bwd_ws_bytes(pl);
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                 ws ? ws_bytes : (size_t)0);
   if (pl.nseq == 0) return LA_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  float* A = static_cast<float*>(ws);          // prepared start state
-  float* W = A + (size_t)pl.nseq * pl.D * pl.D;  // scan states
+  const size_t DDn = (size_t)pl.nseq * pl.D * pl.D;
+  float* A = static_cast<float*>(ws);             // prepared start state (dQ, then dV)
+  float* W = A + DDn;                             // sub-segment start states (dQ, then dV)
+  float* A2 = W + scan_ws_bytes(pl) / sizeof(float);  // prepared start state of dK
+  float* W2 = A2 + DDn;                           // sub-segment start states of dK
   const int H = (int)s->H;
   la::PrepArgs pa;
   std::memset(&pa, 0, sizeof(pa));
@@ -717,25 +733,43 @@ static la_status chunk_bwd(const la_shape* s, const void* Q, const void* K, cons
 
   // dv_t = G_t^T k_t: in reverse time G accumulates q dO^T like a state,
   // started from dS_end / lambda; its final value G_1 gives dS0 = lambda G_1.
-  start = nullptr;
+  // dk_t = G_t v_t: the same reverse recurrence for G^T = sum dO q^T over the
+  // same pairs (q_t, dO_t) with the roles swapped, seeded with the transposed
+  // seed, so its sub-segment start states are the transposes of the dV
+  // sweep's: one pre-pass and scan serve both.  The two sweeps then run as
+  // one paired launch, partners on one XCD walking the same rows, so that Q
+  // and dO, which both read, come from HBM about once.
+  const float* startV = nullptr;
+  const float* startK = nullptr;
   if (dS_end) {
     pa.src = dS_end;
     pa.dst = A;
     pa.transpose = 0;
     pa.mode = 2;
     if ((e = la::launch_prep(pa, st)) != hipSuccess) return hip_fail(e, "prep launch");
-    start = A;
+    pa.dst = A2;
+    pa.transpose = 1;
+    if ((e = la::launch_prep(pa, st)) != hipSuccess) return hip_fail(e, "prep launch");
+    startV = A;
+    startK = A2;
   }
-  r = run_flow(pl, s->dtype, H, s->nseg, K, Q, dO, lambda, start, dV, dS0, W, 1, st);
+  r = run_states(pl, s->dtype, H, s->nseg, Q, dO, lambda, startV, W, 1, st);
   if (r != LA_OK) return r;
-  // The dK recurrence below runs over the same pairs (q_t, dO_t) with the
-  // roles swapped and is seeded with the transposed seed, so its sub-segment
-  // start states are the transposes of the ones just used: transpose W in
-  // place instead of a second pre-pass and scan.
   if (pl.split > 1) {
-    e = la::launch_transpose(W, pl.nseq * (pl.split - 1), pl.D, st);
-    if (e != hipSuccess) return hip_fail(e, "transpose launch");
+    la::PrepArgs ta = pa;
+    ta.nseq = pl.nseq * (pl.split - 1);
+    ta.src = W;
+    ta.dst = W2;
+    ta.transpose = 1;
+    ta.mode = 0;
+    if ((e = la::launch_prep(ta, st)) != hipSuccess) return hip_fail(e, "prep launch");
   }
+  const la::FwdArgs av = main_args(pl, H, s->nseg, K, Q, dO, lambda, startV, dV, dS0, W, 1, false,
+                                   nullptr);
+  const la::FwdArgs ak = main_args(pl, H, s->nseg, V, dO, Q, lambda, startK, dK, nullptr, W2, 1,
+                                   false, nullptr);
+  if ((e = la::launch_fwd_pair(av, ak, s->dtype, pl.D, pl.nseq * pl.split, st)) != hipSuccess)
+    return hip_fail(e, "paired chunk kernel launch");
   if (dS0) {
     pa.src = dS0;
     pa.dst = dS0;
@@ -743,18 +777,7 @@ static la_status chunk_bwd(const la_shape* s, const void* Q, const void* K, cons
     pa.mode = 1;
     if ((e = la::launch_prep(pa, st)) != hipSuccess) return hip_fail(e, "prep launch");
   }
-
-  // dk_t = G_t v_t: the same reverse recurrence for G^T = sum dO q^T.
-  start = nullptr;
-  if (dS_end) {
-    pa.src = dS_end;
-    pa.dst = A;
-    pa.transpose = 1;
-    pa.mode = 2;
-    if ((e = la::launch_prep(pa, st)) != hipSuccess) return hip_fail(e, "prep launch");
-    start = A;
-  }
-  return run_main(pl, s->dtype, H, s->nseg, V, dO, Q, lambda, start, dK, nullptr, W, 1, st);
+  return LA_OK;
 }
 
 la_status la_chunk_bwd(const la_shape* s, const void* Q, const void* K, const void* V,

@@ -10,10 +10,10 @@
 
 namespace la {
 
+// Work item `wg` of a launch over a: sub-segment p_begin + wg % p_count of
+// sequence wg / p_count.
 template <typename T, int D, bool WITH_O, bool GATED>
-__global__ __launch_bounds__((FwdLayout<T, D, WITH_O ? 3 : 2, GATED>::NT),
-                             (FwdLayout<T, D, WITH_O ? 3 : 2, GATED>::WAVES_PER_EU)) void k_chunk_fwd(
-    FwdArgs a) {
+__device__ __forceinline__ void chunk_item(const FwdArgs& a, int64_t wg) {
   constexpr int NSLOT = WITH_O ? 3 : 2;
   typedef FwdLayout<T, D, NSLOT, GATED> LY;
   constexpr int NKT = D / 16;
@@ -25,8 +25,8 @@ __global__ __launch_bounds__((FwdLayout<T, D, WITH_O ? 3 : 2, GATED>::NT),
   const int col = 16 * __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
 
   // ---- work item: sub-segment p of sequence n
-  const int64_t n = (int64_t)blockIdx.x / a.p_count;
-  const int p = a.p_begin + (int)((int64_t)blockIdx.x % a.p_count);
+  const int64_t n = wg / a.p_count;
+  const int p = a.p_begin + (int)(wg % a.p_count);
   const int h = (int)((n / a.nseg) % a.H);
   int64_t t0, t1;  // positions of the sub-segment (the short one last, or first)
   if (a.ragged_first) {
@@ -83,6 +83,32 @@ __global__ __launch_bounds__((FwdLayout<T, D, WITH_O ? 3 : 2, GATED>::NT),
   }
 }
 
+template <typename T, int D, bool WITH_O, bool GATED>
+__global__ __launch_bounds__((FwdLayout<T, D, WITH_O ? 3 : 2, GATED>::NT),
+                             (FwdLayout<T, D, WITH_O ? 3 : 2, GATED>::WAVES_PER_EU)) void k_chunk_fwd(
+    FwdArgs a) {
+  chunk_item<T, D, WITH_O, GATED>(a, blockIdx.x);
+}
+
+// Two launches over the same number of work items in one grid, interleaved
+// in blocks of 8 workgroups: blocks 16 j + r and 16 j + 8 + r (r < 8) run
+// item 8 j + r of a and of b.  Workgroups are dealt to the 8 XCDs round-robin
+// by index, so the two partners share an XCD and its L2, and when a and b
+// walk the same rows (the backward's dV and dK sweeps, which both read Q and
+// dO) one partner's loads mostly find the other's lines there.
+template <typename T, int D, bool GATED>
+__global__ __launch_bounds__((FwdLayout<T, D, 3, GATED>::NT),
+                             (FwdLayout<T, D, 3, GATED>::WAVES_PER_EU)) void k_chunk_fwd_pair(
+    FwdArgs a, FwdArgs b, int64_t nitems) {
+  const int64_t blk = blockIdx.x;
+  const int64_t item = 8 * (blk / 16) + (blk % 8);
+  if (item >= nitems) return;
+  if ((blk & 8) == 0)
+    chunk_item<T, D, true, GATED>(a, item);
+  else
+    chunk_item<T, D, true, GATED>(b, item);
+}
+
 template <typename T, int D, bool GATED>
 static hipError_t launch_fwd_t(const FwdArgs& a, bool with_o, int64_t nwg, hipStream_t s) {
   if (with_o)
@@ -98,6 +124,32 @@ template <typename T, int D>
 static hipError_t launch_fwd_g(const FwdArgs& a, bool with_o, int64_t nwg, hipStream_t s) {
   return a.gated ? launch_fwd_t<T, D, true>(a, with_o, nwg, s)
                  : launch_fwd_t<T, D, false>(a, with_o, nwg, s);
+}
+
+template <typename T, int D>
+static hipError_t launch_pair_t(const FwdArgs& a, const FwdArgs& b, int64_t nitems, hipStream_t s) {
+  const unsigned grid = (unsigned)(16 * ((nitems + 7) / 8));
+  if (a.gated)
+    hipLaunchKernelGGL((k_chunk_fwd_pair<T, D, true>), dim3(grid), dim3(FwdLayout<T, D, 3, true>::NT),
+                       0, s, a, b, nitems);
+  else
+    hipLaunchKernelGGL((k_chunk_fwd_pair<T, D, false>), dim3(grid),
+                       dim3(FwdLayout<T, D, 3, false>::NT), 0, s, a, b, nitems);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_pair(const FwdArgs& a, const FwdArgs& b, int dtype, int D, int64_t nitems,
+                           hipStream_t s) {
+  if (nitems <= 0) return hipSuccess;
+  if (a.gated != b.gated) return hipErrorInvalidValue;
+  if (dtype == 0) {
+    if (D == 64) return launch_pair_t<__bf16, 64>(a, b, nitems, s);
+    if (D == 128) return launch_pair_t<__bf16, 128>(a, b, nitems, s);
+  } else {
+    if (D == 64) return launch_pair_t<float, 64>(a, b, nitems, s);
+    if (D == 128) return launch_pair_t<float, 128>(a, b, nitems, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, bool with_o, int64_t nwg,

@@ -123,6 +123,10 @@ struct StepArgs {
 };
 hipError_t launch_step(const StepArgs& a, int dtype, int D, int64_t nseq, hipStream_t stream);
 
+// Two chunk-kernel launches with outputs over nitems work items each, as one
+// grid whose partner workgroups share an XCD (la_fwd.hip); a.gated == b.gated.
+hipError_t launch_fwd_pair(const FwdArgs& a, const FwdArgs& b, int dtype, int D, int64_t nitems,
+                           hipStream_t stream);
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, bool with_o, int64_t nwg,
                       hipStream_t stream);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);

@@ -160,7 +160,11 @@ def test_bwd_rejects_bad_arguments():
     assert call(dK=None) == la.LA_ERR_INVALID_ARG
     assert call(dS0=FAKE + 2) == la.LA_ERR_INVALID_ARG
     need = la.la_bwd_workspace_bytes(s)
-    assert need == 2 * 64 * 64 * 4
+    # two prepared start states per sequence (the dV and dK sweeps run
+    # together), no sub-segment states at split 1
+    assert need == 2 * (2 * 64 * 64 * 4)
+    s4 = _shape(split=2)
+    assert la.la_bwd_workspace_bytes(s4) == 2 * (2 * 64 * 64 * 4 + 2 * 1 * 64 * 64 * 4)
     assert call(ws=None) == la.LA_ERR_WORKSPACE
     assert call(ws=FAKE, nb=need - 16) == la.LA_ERR_WORKSPACE
 
