@@ -239,8 +239,8 @@ la_status la_state_scan_gated(int64_t B, int64_t H, int32_t P, int32_t dk, int32
                               float* S_start, float* S_end, int32_t reverse, void* stream);
 
 /* Workspace bytes la_chunk_bwd_gated needs for `shape`: about
- * 2 * ceil(L/nseg / 1024) fp32 d x d states per sequence (the start states of
- * both sweeps, 128 B per token-head at d = 128) plus the shifted gates. */
+ * 3 * ceil(L/nseg / 1024) fp32 d x d states per sequence (the start states of
+ * the sweeps, 192 B per token-head at d = 128) plus the shifted gates. */
 size_t la_bwd_gated_workspace_bytes(const la_shape* shape);
 
 /*

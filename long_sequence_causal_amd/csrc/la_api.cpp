@@ -360,12 +360,13 @@ Plan gated_bwd_plan(const Plan& p) {
 }
 
 // gated backward workspace (in order): prepared start state [nseq][D][D],
-// the forward sweep's start states W and the reverse sweeps' W2 (each
-// [nseq][split-1][D][D], kept side by side for the anchors), the sweeps'
-// sub-segment log-gates (reused), shifted gates [nseq][Ls], the final
-// dQ-sweep state [nseq][D][D] and one anchor per 1024-token block
+// the forward sweep's start states W, the dV sweep's W2 and their transposes
+// W3 for the dK sweep (each [nseq][split-1][D][D]; W and W3 also feed the
+// anchors), the sweeps' sub-segment log-gates (reused), shifted gates
+// [nseq][Ls], the final dQ-sweep state [nseq][D][D] and one anchor per
+// 1024-token block
 struct GatedBwdWs {
-  size_t A, W, W2, LD, Gs, SE, TOT, total;
+  size_t A, W, W2, W3, LD, Gs, SE, TOT, total;
 };
 GatedBwdWs gated_bwd_ws(const Plan& p0) {
   const Plan p = gated_bwd_plan(p0);
@@ -376,6 +377,7 @@ GatedBwdWs gated_bwd_ws(const Plan& p0) {
   w.A = o;  o += up((size_t)p.nseq * DD4);
   w.W = o;  o += up(scan_ws_bytes(p));
   w.W2 = o; o += up(scan_ws_bytes(p));
+  w.W3 = o; o += up(scan_ws_bytes(p));
   w.LD = o; o += up((size_t)p.nseq * (size_t)(p.split > 1 ? p.split - 1 : 0) * sizeof(float));
   w.Gs = o; o += up((size_t)p.nseq * (size_t)p.Ls * sizeof(float));
   w.SE = o; o += up((size_t)p.nseq * DD4);
@@ -421,7 +423,8 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
   char* base = static_cast<char*>(ws);
   float* A = reinterpret_cast<float*>(base + L.A);
   float* W = reinterpret_cast<float*>(base + L.W);    // forward sweep: S^T starts
-  float* W2 = reinterpret_cast<float*>(base + L.W2);  // reverse sweeps: G starts
+  float* W2 = reinterpret_cast<float*>(base + L.W2);  // dV sweep: G starts
+  float* W3 = reinterpret_cast<float*>(base + L.W3);  // dK sweep: G^T starts
   float* LDw = reinterpret_cast<float*>(base + L.LD);
   float* Gs = reinterpret_cast<float*>(base + L.Gs);
   float* SE = reinterpret_cast<float*>(base + L.SE);
@@ -456,16 +459,15 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
   if ((e = la::launch_shift_gates(log_alpha, Gs, pl.nseq, pl.Ls, st)) != hipSuccess)
     return hip_fail(e, "gate shift launch");
   // dv_t = G_t^T k_t, G accumulating q dO^T from dS_end (the first reverse
-  // step multiplies by 1); its final value G_1 gives dS0 = alpha_1 G_1
-  r = run_flow(plr, s->dtype, H, s->nseg, K, Q, dO, nullptr, dS_end, dV, dS0, W2, 1, st, true, Gs,
-               LDw);
-  if (r != LA_OK) return r;
-  if (dS0 && (e = la::launch_scale_first_gate(dS0, log_alpha, pl.nseq, pl.Ls, pl.D, st)) != hipSuccess)
-    return hip_fail(e, "dS0 scale launch");
+  // step multiplies by 1); its final value G_1 gives dS0 = alpha_1 G_1.
   // dk_t = G_t v_t: the same reverse recurrence for G^T, whose sub-segment
-  // start states are the transposes of the ones just used
+  // start states are the transposes of the dV sweep's.  One pre-pass and scan
+  // serve both, and the two sweeps run as one paired launch (partners share
+  // an XCD and walk the same rows, so Q and dO come from HBM about once).
+  r = run_states(plr, s->dtype, H, s->nseg, Q, dO, nullptr, dS_end, W2, 1, st, true, Gs, LDw);
+  if (r != LA_OK) return r;
   if (pl.split > 1) {
-    e = la::launch_transpose(W2, pl.nseq * (pl.split - 1), pl.D, st);
+    e = la::launch_transpose_copy(W2, W3, pl.nseq * (pl.split - 1), pl.D, st);
     if (e != hipSuccess) return hip_fail(e, "transpose launch");
   }
   start = nullptr;
@@ -477,14 +479,21 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
     if ((e = la::launch_prep(pa, st)) != hipSuccess) return hip_fail(e, "prep launch");
     start = A;
   }
-  r = run_main(plr, s->dtype, H, s->nseg, V, dO, Q, nullptr, start, dK, nullptr, W2, 1, st, true,
-               Gs);
-  if (r != LA_OK) return r;
+  {
+    const la::FwdArgs av = main_args(plr, H, s->nseg, K, Q, dO, nullptr, dS_end, dV, dS0, W2, 1,
+                                     true, Gs);
+    const la::FwdArgs ak = main_args(plr, H, s->nseg, V, dO, Q, nullptr, start, dK, nullptr, W3, 1,
+                                     true, Gs);
+    if ((e = la::launch_fwd_pair(av, ak, s->dtype, pl.D, pl.nseq * pl.split, st)) != hipSuccess)
+      return hip_fail(e, "paired chunk kernel launch");
+  }
+  if (dS0 && (e = la::launch_scale_first_gate(dS0, log_alpha, pl.nseq, pl.Ls, pl.D, st)) != hipSuccess)
+    return hip_fail(e, "dS0 scale launch");
 
   // d l / d log(alpha_t) = sum_{u >= t} (q_u . dq_u - k_u . dk_u) + <dS_end, S_end>, the sum
   // anchored at every sub-segment boundary y by its exact value alpha_y <G_y, S_{y-1}>
   if (dlog_alpha) {
-    e = la::launch_gate_anchors(W, W2, log_alpha, dS_end, need_send ? SE : nullptr, TOT, pl.nseq,
+    e = la::launch_gate_anchors(W, W3, log_alpha, dS_end, need_send ? SE : nullptr, TOT, pl.nseq,
                                 pl.Ls, pl.D, st);
     if (e != hipSuccess) return hip_fail(e, "gate anchor launch");
     e = la::launch_gate_grad(s->dtype, pl.D, Q, dQ, K, dK, dlog_alpha, TOT, dS_end,
@@ -718,13 +727,8 @@ static la_status chunk_bwd(const la_shape* s, const void* Q, const void* K, cons
   }
   if (from_fwd && pl.split > 1) {
     // the forward's start states, transposed: S^T starts of the dQ sweep
-    la::PrepArgs ta = pa;
-    ta.nseq = pl.nseq * (pl.split - 1);
-    ta.src = fwd_starts;
-    ta.dst = W;
-    ta.transpose = 1;
-    ta.mode = 0;
-    if ((e = la::launch_prep(ta, st)) != hipSuccess) return hip_fail(e, "prep launch");
+    e = la::launch_transpose_copy(fwd_starts, W, pl.nseq * (pl.split - 1), pl.D, st);
+    if (e != hipSuccess) return hip_fail(e, "transpose launch");
     r = run_main(pl, s->dtype, H, s->nseg, dO, V, K, lambda, start, dQ, nullptr, W, 0, st);
   } else {
     r = run_flow(pl, s->dtype, H, s->nseg, dO, V, K, lambda, start, dQ, nullptr, W, 0, st);
@@ -756,13 +760,8 @@ static la_status chunk_bwd(const la_shape* s, const void* Q, const void* K, cons
   r = run_states(pl, s->dtype, H, s->nseg, Q, dO, lambda, startV, W, 1, st);
   if (r != LA_OK) return r;
   if (pl.split > 1) {
-    la::PrepArgs ta = pa;
-    ta.nseq = pl.nseq * (pl.split - 1);
-    ta.src = W;
-    ta.dst = W2;
-    ta.transpose = 1;
-    ta.mode = 0;
-    if ((e = la::launch_prep(ta, st)) != hipSuccess) return hip_fail(e, "prep launch");
+    e = la::launch_transpose_copy(W, W2, pl.nseq * (pl.split - 1), pl.D, st);
+    if (e != hipSuccess) return hip_fail(e, "transpose launch");
   }
   const la::FwdArgs av = main_args(pl, H, s->nseg, K, Q, dO, lambda, startV, dV, dS0, W, 1, false,
                                    nullptr);

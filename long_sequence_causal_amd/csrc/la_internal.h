@@ -130,6 +130,9 @@ hipError_t launch_fwd_pair(const FwdArgs& a, const FwdArgs& b, int dtype, int D,
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, bool with_o, int64_t nwg,
                       hipStream_t stream);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
+// dst[m] = src[m]^T for nmat consecutive D x D fp32 matrices (no overlap).
+hipError_t launch_transpose_copy(const float* src, float* dst, int64_t nmat, int D,
+                                 hipStream_t stream);
 hipError_t launch_prep(const PrepArgs& a, hipStream_t stream);
 // Gated backward helpers (la_gate.hip): shifted gates for the reverse
 // sweeps, dS0 scaled by the first gate of each sequence, and the log-gate
@@ -142,7 +145,7 @@ int64_t gate_grad_blocks(int64_t Ls);
 // Per sequence n and block b of GBLK tokens, the gate gradient at the first
 // token of block b + 1: alpha_y <G_y, S_{y-1}> at y = (b+1) GBLK from the
 // forward sweep's start states WfT ([nseq][nb-1] of S^T) and the reverse
-// sweep's, transposed in place (WrT, [nseq][nb-1] of G^T, in reverse order);
+// sweep's, transposed (WrT, [nseq][nb-1] of G^T, in reverse order);
 // for the last block <dS_end, S_end> (dSe, SendT may be null: 0).  Written
 // to tot[n][b] for launch_gate_grad_finish.  Requires 1024-token sub-segments.
 hipError_t launch_gate_anchors(const float* WfT, const float* WrT, const float* G,
@@ -153,7 +156,5 @@ hipError_t launch_gate_anchors(const float* WfT, const float* WrT, const float* 
 hipError_t launch_gate_grad(int dtype, int D, const void* Q, const void* dQ, const void* K,
                             const void* dK, float* dG, float* tot, const float* dSe,
                             const float* SendT, int64_t nseq, int64_t Ls, hipStream_t s);
-// In-place transpose of nmat consecutive D x D fp32 matrices.
-hipError_t launch_transpose(float* W, int64_t nmat, int D, hipStream_t stream);
 
 }  // namespace la

@@ -74,40 +74,33 @@ __global__ __launch_bounds__(256) void k_prep_state(PrepArgs a) {
   a.dst[gid] = x;
 }
 
-// In-place transpose of D x D matrices (D a multiple of 32) in 32 x 32
-// tiles: workgroup (m, pair) reads tiles (bi, bj) and (bj, bi), bi <= bj, of
-// matrix m into LDS and writes each back transposed into the other's place,
-// with every global access a coalesced row segment.
-__global__ __launch_bounds__(256) void k_transpose_inplace(float* W, int D) {
-  __shared__ float ta[32][33], tb[32][33];
+// dst[m] = src[m]^T for nmat D x D matrices (D a multiple of 32), in
+// 32 x 32 tiles through LDS so that every global read and write is a
+// coalesced row segment: workgroup (m, bi, bj) reads tile (bi, bj) of src[m]
+// and writes it transposed as tile (bj, bi) of dst[m].  src and dst must not
+// overlap.
+__global__ __launch_bounds__(256) void k_transpose_copy(const float* src, float* dst, int D) {
+  __shared__ float t[32][33];
   const int nt = D / 32;
-  const int npair = nt * (nt + 1) / 2;
-  const int64_t m = blockIdx.x / npair;
-  int pr = (int)(blockIdx.x % npair);
-  int bi = 0;
-  while (pr >= nt - bi) {
-    pr -= nt - bi;
-    ++bi;
-  }
-  const int bj = bi + pr;
-  float* M = W + m * (int64_t)D * D;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-  for (int r = ty; r < 32; r += 8) {
-    ta[r][tx] = M[(int64_t)(32 * bi + r) * D + 32 * bj + tx];
-    tb[r][tx] = M[(int64_t)(32 * bj + r) * D + 32 * bi + tx];
-  }
+  const int64_t m = blockIdx.x / (nt * nt);
+  const int bi = (int)(blockIdx.x % (nt * nt)) / nt, bj = (int)(blockIdx.x % nt);
+  const int64_t DD = (int64_t)D * D;
+  const float* sm = src + m * DD;
+  float* dm = dst + m * DD;
+  const int c = threadIdx.x & 31, r0 = threadIdx.x >> 5;  // 8 rows per pass
+#pragma unroll
+  for (int r = r0; r < 32; r += 8) t[r][c] = sm[(int64_t)(32 * bi + r) * D + 32 * bj + c];
   __syncthreads();
-  for (int r = ty; r < 32; r += 8) {
-    M[(int64_t)(32 * bj + r) * D + 32 * bi + tx] = ta[tx][r];
-    M[(int64_t)(32 * bi + r) * D + 32 * bj + tx] = tb[tx][r];
-  }
+#pragma unroll
+  for (int r = r0; r < 32; r += 8) dm[(int64_t)(32 * bj + r) * D + 32 * bi + c] = t[c][r];
 }
 
-hipError_t launch_transpose(float* W, int64_t nmat, int D, hipStream_t s) {
+hipError_t launch_transpose_copy(const float* src, float* dst, int64_t nmat, int D, hipStream_t s) {
   const int nt = D / 32;
-  const int64_t nwg = nmat * (nt * (nt + 1) / 2);
-  if (nwg <= 0 || D % 32 != 0) return nwg <= 0 ? hipSuccess : hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_transpose_inplace, dim3((unsigned)nwg), dim3(256), 0, s, W, D);
+  if (nmat <= 0) return hipSuccess;
+  if (D % 32 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_transpose_copy, dim3((unsigned)(nmat * nt * nt)), dim3(256), 0, s, src, dst,
+                     D);
   return hipGetLastError();
 }
 

@@ -194,11 +194,11 @@ def test_gated_entry_points_validate_on_the_host():
 def test_gated_backward_workspace_follows_the_1024_token_plan():
     # L = 5000 -> 79 chunks -> 5 sub-segments of 1024 tokens whatever split asks;
     # d = 64: a state is 16 KiB.  Blocks (256-byte aligned): prepared start
-    # state, both sweeps' start states (4 each), their log-gates, the shifted
-    # gates, S_end and one anchor per block.
+    # state, the sweeps' start states (4 each: forward, dV, dV transposed for
+    # dK), their log-gates, the shifted gates, S_end and one anchor per block.
     DD4, nseq, Ls = 64 * 64 * 4, 2, 5000
     up = lambda x: -(-x // 256) * 256
-    want = (up(nseq * DD4) + 2 * up(nseq * 4 * DD4) + up(nseq * 4 * 4) + up(nseq * Ls * 4)
+    want = (up(nseq * DD4) + 3 * up(nseq * 4 * DD4) + up(nseq * 4 * 4) + up(nseq * Ls * 4)
             + up(nseq * DD4) + up(nseq * 5 * 4))
     for split in (0, 1, 3, 40):
         assert la.la_bwd_gated_workspace_bytes(_shape(L=Ls, split=split)) == want
