@@ -204,8 +204,9 @@ def gated_leg(torch, la, inp, dev, iters, gate_logs):
 
 def decode_leg(torch, la, dev, iters):
     """la_step on the decode batch (64 sequences x 32 heads, d = 128, bf16,
-    state updated in place): time per step, against its algorithmic bytes
-    (the fp32 state read and written once, q, k, v read and o written)."""
+    state updated in place): the median of per-call event times, against its
+    algorithmic bytes (the fp32 state read and written once, q, k, v read
+    and o written)."""
     from long_sequence_causal_amd.inputs import DECODE, decode_inputs
     w = DECODE["decode_b64"]
     inp = decode_inputs("decode_b64", device=dev)
@@ -219,12 +220,14 @@ def decode_leg(torch, la, dev, iters):
     for _ in range(5):
         call()
     torch.cuda.synchronize()
-    ms = time_events(call, iters, torch.cuda.current_stream())
+    each = sorted(time_each(call, iters, torch.cuda.current_stream()))
+    ms = each[len(each) // 2]  # median: a step is short enough for one stall to swamp a mean
     nbytes = B * H * (2 * d * d * 4 + 4 * d * 2)
     t = ms / 1e3
     del inp, q, k, v, S, o
     return {"workload": "decode_b64", "B": B, "H": H, "d": d, "dtype": w["dtype"],
-            "us_per_call": ms * 1e3, "tokens_per_s": B / t, "alg_bytes": nbytes,
+            "us_per_call": ms * 1e3, "us_min": each[0] * 1e3, "us_max": each[-1] * 1e3,
+            "calls": iters, "tokens_per_s": B / t, "alg_bytes": nbytes,
             "achieved_GBs": nbytes / t / 1e9, "frac_hbm": nbytes / t / 1e9 / HBM_PEAK_GBS}
 
 
@@ -432,8 +435,9 @@ def main():
                f"decay gradient {bw['decay_grad']['us_per_call']:.1f} us/call")
         rec["backward"] = bw
     if not args.no_decode:
-        dl = decode_leg(torch, la, dev, max(20, args.steps))
-        eprint(f"[bench] decode step ({dl['workload']}): {dl['us_per_call']:.1f} us/call, "
+        dl = decode_leg(torch, la, dev, max(200, args.steps))
+        eprint(f"[bench] decode step ({dl['workload']}): {dl['us_per_call']:.1f} us/call median "
+               f"(min {dl['us_min']:.1f}, max {dl['us_max']:.1f} over {dl['calls']}), "
                f"{dl['achieved_GBs']:.0f} GB/s algorithmic")
         rec["decode"] = dl
     if not args.no_cpu:
