@@ -154,6 +154,11 @@ __device__ inline float lane_value(float x, int lane) {  // x of a wave-uniform 
 }
 
 // ---------------------------------------------------------------- small helpers
+// 2^x for x <= 0 (a decay factor): the hardware exponential alone.  Results
+// below 2^-126, which the denormal-safe exp2f would keep, flush to zero;
+// such a factor weighs nothing next to the terms of size 1 it is summed with.
+__device__ inline float exp2_np(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ inline float pow_lam(float lg2, float n) {
   // lambda^n = 2^(n log2 lambda); only non-negative n are formed.
   return exp2f(n * lg2);

@@ -54,9 +54,29 @@ __device__ inline void score_tile(int idx, int& jb, int& ib) {
 
 constexpr int LDS_MAX = 160 * 1024;  // per workgroup on gfx950
 
+// Position of token t (0..63) in a gated walk's per-chunk factor tables
+// (cumulative log-gate c_t, update weight exp(c_last - c_t)), chosen so that
+// the values a lane needs sit together: the 16 update-weight slots of MFMA
+// lane group g (tokens slot_token) are entries 16 g .. 16 g + 15 in slot
+// order, and the 4 keys of group g in key block jb (score tile rows) are
+// entries 16 g + 4 jb .. + 3.
+template <typename T>
+__device__ inline int tab_pos(int t) {
+  if constexpr (sizeof(T) == 2) {
+    // group of t: t mod 8 in {0, 2} -> 0, {4, 6} -> 1, {5, 7} -> 2, {1, 3} -> 3
+    // (the token sets tr_row gives lane groups 0..3); slot order inside
+    const int grp = (0x2130 >> (4 * (((t >> 2) & 1) * 2 + (t & 1)))) & 3;
+    return 16 * grp + 2 * (t >> 3) + ((t >> 1) & 1);
+  } else {
+    return 16 * (t & 3) + (t >> 2);  // group g = t mod 4, slot js = t / 4
+  }
+}
+
 // LDS of a workgroup: STAGES stages of NSLOT token-major tiles (Q, K, V when
 // NSLOT = 3, K, V when NSLOT = 2), plus P when NSLOT = 3, plus (gated walks)
-// the 64 log-gates of each stage's chunk.
+// a ring of STAGES + 1 slots of 64 log-gates (a chunk's gates travel with
+// the previous chunk's tiles, one chunk ahead of them) and two buffers of the
+// chunk factor tables (GateTab).
 template <typename T, int D, int NSLOT, bool GATED = false>
 struct FwdLayout {
   typedef PadTile<T, CH, D> TN;                // Q, K, V token-major [token][d]
@@ -67,11 +87,14 @@ struct FwdLayout {
   static constexpr int PBYTES = NSLOT == 3 ? TP::BYTES : 0;
   static constexpr int SMAX = NSLOT == 3 ? 3 : 5;
   static constexpr int GB = GATED ? CH * 4 : 0;  // log-gates of one chunk
-  static constexpr int SFIT = (LDS_MAX - PBYTES) / (STAGE + GB);
+  static constexpr int TBL = GATED ? 2 * 2 * CH * 4 : 0;  // 2 x (cumulative gate, update weight)
+  static constexpr int SFIT = (LDS_MAX - PBYTES - GB - TBL) / (STAGE + GB);
   static constexpr int STAGES = SFIT < SMAX ? SFIT : SMAX;
   static constexpr int OFF_P = STAGES * STAGE;
   static constexpr int OFF_G = OFF_P + PBYTES;
-  static constexpr int BYTES = OFF_G + STAGES * GB;
+  static constexpr int GSLOTS = STAGES + 1;  // gate ring (gated walks)
+  static constexpr int OFF_T = OFF_G + GSLOTS * GB;
+  static constexpr int BYTES = OFF_T + TBL;
   static constexpr int NW = D / 16;  // waves: one per 16 state columns
   static constexpr int NT = 64 * NW;
   // bf16 keeps two waves per SIMD (256 registers per lane)
@@ -133,9 +156,13 @@ struct WalkJob {
 // With c_i = g_0 + .. + g_i the chunk-local cumulative log-gate, every
 // factor above becomes a difference of c: lambda^(i-j) -> exp(c_i - c_j),
 // lambda^(i+1) -> exp(c_i), lambda^(cl-1-j) -> exp(c_{cl-1} - c_j),
-// lambda^cl -> exp(c_{cl-1}); all are <= 1.  Wave NW-1 brings the chunk's 64
-// gates to LDS with the tiles; every wave forms c with a wave-wide prefix sum
-// (lane = token).  Returns the range's total log-gate (0 if not GATED).
+// lambda^cl -> exp(c_{cl-1}); all are <= 1.  Wave NW-1 brings each chunk's
+// 64 gates to LDS together with the previous chunk's tiles, forms c with a
+// wave-wide prefix sum (lane = token) and writes c and the update weights
+// exp(c_{cl-1} - c_j) to a table (tab_pos order) while chunk c - 1's update
+// runs; after the next barrier every wave reads the factors it needs with a
+// few vector LDS reads instead of gathering them lane by lane.  Returns the
+// range's total log-gate (0 if not GATED).
 template <typename T, int D, bool OUT, int NSLOT, bool GATED = false>
 __device__ __forceinline__ float walk(char* smem, const WalkJob& jb, f32x4 (&accS)[D / 16]) {
   typedef Elt<T> X;
@@ -190,7 +217,10 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob& jb, f32x4 (&acc
   // the end to the last valid token.
   // The gate load rides with wave NW-1, which otherwise issues one load fewer
   // than the busiest wave (NBLK is never a multiple of NW here), so every
-  // wave's per-chunk count stays LPC_HI or LPC_HI - 1.
+  // wave's per-chunk count stays LPC_HI or LPC_HI - 1.  Chunk c's group
+  // carries the gates of chunk c + 1 (of the last chunk again at the end, so
+  // the count never changes); chunk 0's gates are one extra load issued
+  // before any tile, older than everything the waits count.
   static_assert(!GATED || NBLK % NW != 0, "the gate load needs a wave with a spare slot");
   const bool gwave = GATED && (w == NW - 1);
   const bool lpc_hi = (w < NBLK - (LPC_HI - 1) * NW);  // issues LPC_HI tile loads
@@ -219,6 +249,13 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob& jb, f32x4 (&acc
     src_of[q] = tensor_base(bb / G);
     dst_of[q] = smem_lds + (unsigned)((SLOT0 + bb / G) * TB + (bb % G) * 1024);
   }
+  // gates of chunk cg into the gate slot of chunk number `slot_of`
+  auto gate_slot = [&](int cc) -> int { return cc % LY::GSLOTS; };
+  auto issue_gates = [&](int cg, int slot_of) {
+    const int tt = (cg * CH + lane < len) ? cg * CH + lane : len - 1;
+    dma4(jb.G, (unsigned)(relrow(tt) * 4),
+         smem_lds + (unsigned)(LY::OFF_G + gate_slot(slot_of) * LY::GB));
+  };
   // chunk c into stage `stage`; offsets wrap modulo 2^32 like the byte
   // offsets they stand for (the host keeps one sequence below 4 GiB)
   auto issue = [&](int c, int stage) {
@@ -241,13 +278,11 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob& jb, f32x4 (&acc
         dma16(src_of[q], voff, dst_of[q] + sb);
       }
     }
-    if (GATED && gwave) {
-      const int tt = (c * CH + lane < len) ? c * CH + lane : len - 1;
-      dma4(jb.G, (unsigned)(relrow(tt) * 4), smem_lds + (unsigned)(LY::OFF_G + stage * LY::GB));
-    }
+    if (GATED && gwave) issue_gates(c + 1 < nch ? c + 1 : nch - 1, c + 1);
   };
 
   // first chunks in flight while the factors are computed
+  if (GATED && gwave && nch > 0) issue_gates(0, 0);
   for (int pc = 0; pc < S - 1; ++pc)
     if (pc < nch) issue(pc, pc);
 
@@ -292,6 +327,77 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob& jb, f32x4 (&acc
   };
   if (!GATED) set_wv(CH);
   float gsum2 = 0.0f;  // total log2-gate of the chunks walked (GATED)
+  float dc = GATED ? 0.0f : lamC;  // decay of the state over the current chunk
+
+  // GATED, wave NW-1: the factor tables of chunk cc (its gates are in LDS
+  // and visible) into buffer cc % 2
+  auto write_tables = [&](int cc) {
+    const int cl = (len - cc * CH < CH) ? (len - cc * CH) : CH;
+    // chunk-local cumulative log-gate in log2 units, lane = token
+    const float c2 = wave_prefix_sum(
+        *reinterpret_cast<const float*>(smem + LY::OFF_G + gate_slot(cc) * LY::GB + 4 * lane) *
+        1.4426950408889634f);
+    const float clast = lane_value(c2, cl - 1);
+    const float ew = (lane < cl) ? exp2_np(clast - c2) : 0.0f;  // update weight
+    float* tab = reinterpret_cast<float*>(smem + LY::OFF_T + (cc & 1) * 2 * CH * 4);
+    const int pos = tab_pos<T>(lane);
+    tab[pos] = c2;
+    tab[CH + pos] = ew;
+  };
+  // GATED, every wave: the factors of chunk cc from its tables
+  auto read_factors = [&](int cc) {
+    const int cl = (len - cc * CH < CH) ? (len - cc * CH) : CH;
+    const float* tab = reinterpret_cast<const float*>(smem + LY::OFF_T + (cc & 1) * 2 * CH * 4);
+    const float clast = tab[tab_pos<T>(cl - 1)];
+    gsum2 += clast;
+    dc = exp2_np(clast);
+    // update weights of the lane's contraction slots
+    if constexpr (E == 8) {
+#pragma unroll
+      for (int js = 0; js < NJS; ++js) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(tab + CH + 16 * g + 8 * js);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(tab + CH + 16 * g + 8 * js + 4);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          wv[js][x] = a[x];
+          wv[js][4 + x] = b[x];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int js = 0; js < NJS; js += 4) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(tab + CH + 16 * g + js);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) wv[js + x][0] = a[x];
+      }
+    }
+    if (OUT) {
+#pragma unroll
+      for (int it = 0; it < 4; ++it) qf[it] = exp2_np(tab[tab_pos<T>(16 * it + l16)]);
+#pragma unroll
+      for (int sti = 0; sti < NST; ++sti) {
+        const int idx = w + NW * sti;
+        int jb_ = 0, ib_ = 0;
+        if (idx < 10) score_tile(idx, jb_, ib_);
+        const int i = 16 * ib_ + perm16<T>(l16);
+        const float ci = tab[tab_pos<T>(i)];
+        float cj[4];
+        if constexpr (sizeof(T) == 2) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(tab + 16 * g + 4 * jb_);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) cj[r] = a[r];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) cj[r] = tab[tab_pos<T>(16 * jb_ + perm16<T>(4 * g + r))];
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = 16 * jb_ + perm16<T>(4 * g + r);
+          pf[sti][r] = (idx < 10 && j <= i && j < cl) ? exp2_np(ci - cj[r]) : 0.0f;
+        }
+      }
+    }
+  };
 
   int st = 0;             // stage holding chunk c
   int st_next = S - 1;    // stage for chunk c + S - 1 (the one chunk c - 1 used)
@@ -307,40 +413,12 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob& jb, f32x4 (&acc
       if (c + S - 1 < nch) issue(c + S - 1, st_next);
       st_next = (st_next + 1 == S) ? 0 : st_next + 1;
     }
-    float dc;  // decay of the state over the chunk
     if constexpr (GATED) {
-      // chunk-local cumulative log-gate in log2 units, lane = token
-      const float c2 = wave_prefix_sum(
-          *reinterpret_cast<const float*>(smem + LY::OFF_G + st * LY::GB + 4 * lane) *
-          1.4426950408889634f);
-      const float clast = lane_value(c2, cl - 1);
-      gsum2 += clast;
-      dc = exp2f(clast);
-      // factors of this lane's own token, gathered by the slots that need them
-      const float ew = (lane < cl) ? exp2f(clast - c2) : 0.0f;  // update weight
-#pragma unroll
-      for (int js = 0; js < NJS; ++js)
-#pragma unroll
-        for (int x = 0; x < E; ++x) wv[js][x] = __shfl(ew, slot_token<T>(js * KS, g, x), 64);
-      if (OUT) {
-        const float eq = exp2f(c2);  // inter-chunk factor of query token i
-#pragma unroll
-        for (int it = 0; it < 4; ++it) qf[it] = __shfl(eq, 16 * it + l16, 64);
-#pragma unroll
-        for (int sti = 0; sti < NST; ++sti) {
-          const int idx = w + NW * sti;
-          int jb_ = 0, ib_ = 0;
-          if (idx < 10) score_tile(idx, jb_, ib_);
-          const int i = 16 * ib_ + perm16<T>(l16);
-          const float ci = __shfl(c2, i, 64);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int j = 16 * jb_ + perm16<T>(4 * g + r);
-            const float cj = __shfl(c2, j, 64);
-            pf[sti][r] = (idx < 10 && j <= i && j < cl) ? exp2f(ci - cj) : 0.0f;
-          }
-        }
+      if (c == 0) {  // later chunks' tables are written one chunk ahead
+        if (gwave) write_tables(0);
+        lds_barrier();
       }
+      read_factors(c);
     } else {
       if (cl != CH) {
         set_wv(cl);
@@ -490,6 +568,12 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob& jb, f32x4 (&acc
           const op_t Ak = tr_op<T, TN>(sK, js * KS, 16 * tk, lane);
           accS[tk] = X::mfma(Ak, Bv[js], accS[tk]);
         }
+    }
+    // GATED: the next chunk's tables (its gates came with this chunk's
+    // tiles), while the update runs on the matrix cores; the next barrier
+    // publishes them
+    if constexpr (GATED) {
+      if (gwave && c + 1 < nch) write_tables(c + 1);
     }
   }
 
