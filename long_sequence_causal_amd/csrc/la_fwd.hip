@@ -48,6 +48,7 @@ __device__ __forceinline__ void chunk_item(const FwdArgs& a, int64_t wg) {
   jb.reverse = a.reverse;
   jb.lg = GATED ? 0.0f : log2f(a.lam[h]);
   jb.G = GATED ? a.G + n * a.Ls : nullptr;
+  jb.last_chunk_first = a.last_chunk_first;
 
   // ---- start state -> accumulators (wave w: columns [16 w, 16 w + 16))
   f32x4 accS[NKT];

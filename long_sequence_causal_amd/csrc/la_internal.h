@@ -48,6 +48,10 @@ struct FwdArgs {
   int gated;
   const float* G;
   float* LDout;
+  // state-only fixed-decay launches: walk each sub-segment's chunks last
+  // first (the state a sub-segment ends with is the same sum, so only the
+  // rounding order changes); a sub-segment with a ragged chunk walks in order
+  int last_chunk_first;
 };
 
 // dst[n] = f(src[n]) for nseq D x D fp32 states: optional transpose, then a

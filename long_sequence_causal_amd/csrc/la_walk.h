@@ -141,6 +141,7 @@ struct WalkJob {
   int reverse;
   float lg;       // log2 lambda (fixed-decay walks)
   const float* G; // log-gates of the sequence, [Ls] (gated walks)
+  int last_chunk_first;  // state-only fixed-decay walks over whole chunks: chunks in reverse order
 };
 
 // Walk the range with the state in accS (wave w: columns [16 w, 16 w + 16),
@@ -208,6 +209,10 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob& jb, f32x4 (&acc
   // `dir * CH` rows apart.
   auto relrow = [&](int64_t tt) -> int64_t { return jb.reverse ? (jb.Ls - 1 - (t0 + tt)) : (t0 + tt); };
   const int cstride_b = (jb.reverse ? -1 : 1) * CH * D * (int)sizeof(T);  // bytes per chunk
+  // last chunk first (state-only fixed-decay walks over whole chunks): step c
+  // takes chunk nch-1-c, and its update weights carry the decay of the c
+  // chunks after it, lambda^(cl-1-j + CH c), instead of decaying the state
+  const bool lcf = !OUT && !GATED && jb.last_chunk_first && len % CH == 0;
 
   // ---- chunk loads: HBM -> LDS, 1 KiB (64 lanes x 16 B) per instruction.
   // Load b of a chunk fills granules 64 (b % G) .. + 63 of tensor b / G's
@@ -260,6 +265,7 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob& jb, f32x4 (&acc
   // offsets they stand for (the host keeps one sequence below 4 GiB)
   auto issue = [&](int c, int stage) {
     const unsigned sb = (unsigned)(stage * LY::STAGE);
+    if (lcf) c = nch - 1 - c;
     const bool full = (c + 1) * CH <= len;
 #pragma unroll
     for (int q = 0; q < LPC_HI; ++q) {
@@ -424,7 +430,7 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob& jb, f32x4 (&acc
         set_wv(cl);
         if (OUT) set_pf(cl);
       }
-      dc = (cl == CH) ? lamC : pow_lam(lg, (float)cl);
+      dc = lcf ? 1.0f : ((cl == CH) ? lamC : pow_lam(lg, (float)cl));
     }
     const char* const stage = smem + st * LY::STAGE;
     st = (st + 1 == S) ? 0 : st + 1;
@@ -568,6 +574,12 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob& jb, f32x4 (&acc
           const op_t Ak = tr_op<T, TN>(sK, js * KS, 16 * tk, lane);
           accS[tk] = X::mfma(Ak, Bv[js], accS[tk]);
         }
+      if (lcf) {
+#pragma unroll
+        for (int js = 0; js < NJS; ++js)
+#pragma unroll
+          for (int x = 0; x < E; ++x) wv[js][x] *= lamC;
+      }
     }
     // GATED: the next chunk's tables (its gates came with this chunk's
     // tiles), while the update runs on the matrix cores; the next barrier
