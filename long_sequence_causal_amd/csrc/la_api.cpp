@@ -154,7 +154,7 @@ la_status run_states(const Plan& pl, int dtype, int H, int nseg, const void* K, 
   pa.sout_np = pl.split - 1;
   // last chunk first: the chunks this pass reads last are the ones the main
   // pass reads first, so those are still in the last-level cache then
-  pa.last_chunk_first = gated ? 0 : 1;
+  pa.last_chunk_first = 1;
   hipError_t e = la::launch_fwd(pa, dtype, pl.D, false, pl.nseq * (pl.split - 1), st);
   if (e != hipSuccess) return hip_fail(e, "state pre-pass launch");
   la::ScanArgs sa;

@@ -48,7 +48,7 @@ struct FwdArgs {
   int gated;
   const float* G;
   float* LDout;
-  // state-only fixed-decay launches: walk each sub-segment's chunks last
+  // state-only launches: walk each sub-segment's chunks last
   // first (the state a sub-segment ends with is the same sum, so only the
   // rounding order changes); a sub-segment with a ragged chunk walks in order
   int last_chunk_first;

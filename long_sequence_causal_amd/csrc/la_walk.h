@@ -141,7 +141,7 @@ struct WalkJob {
   int reverse;
   float lg;       // log2 lambda (fixed-decay walks)
   const float* G; // log-gates of the sequence, [Ls] (gated walks)
-  int last_chunk_first;  // state-only fixed-decay walks over whole chunks: chunks in reverse order
+  int last_chunk_first;  // state-only walks over whole chunks: chunks in reverse order
 };
 
 // Walk the range with the state in accS (wave w: columns [16 w, 16 w + 16),
@@ -209,10 +209,12 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob& jb, f32x4 (&acc
   // `dir * CH` rows apart.
   auto relrow = [&](int64_t tt) -> int64_t { return jb.reverse ? (jb.Ls - 1 - (t0 + tt)) : (t0 + tt); };
   const int cstride_b = (jb.reverse ? -1 : 1) * CH * D * (int)sizeof(T);  // bytes per chunk
-  // last chunk first (state-only fixed-decay walks over whole chunks): step c
-  // takes chunk nch-1-c, and its update weights carry the decay of the c
-  // chunks after it, lambda^(cl-1-j + CH c), instead of decaying the state
-  const bool lcf = !OUT && !GATED && jb.last_chunk_first && len % CH == 0;
+  // last chunk first (state-only walks over whole chunks): step c takes chunk
+  // nch-1-c, and its update weights carry the decay of the c chunks after it
+  // (lambda^(cl-1-j + CH c); gated: exp(c_last - c_j) times the gates of the
+  // chunks already walked) instead of decaying the state
+  const bool lcf = !OUT && jb.last_chunk_first && len % CH == 0;
+  auto phys = [&](int c) { return lcf ? nch - 1 - c : c; };
 
   // ---- chunk loads: HBM -> LDS, 1 KiB (64 lanes x 16 B) per instruction.
   // Load b of a chunk fills granules 64 (b % G) .. + 63 of tensor b / G's
@@ -257,15 +259,16 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob& jb, f32x4 (&acc
   // gates of chunk cg into the gate slot of chunk number `slot_of`
   auto gate_slot = [&](int cc) -> int { return cc % LY::GSLOTS; };
   auto issue_gates = [&](int cg, int slot_of) {
-    const int tt = (cg * CH + lane < len) ? cg * CH + lane : len - 1;
+    const int pg = phys(cg);
+    const int tt = (pg * CH + lane < len) ? pg * CH + lane : len - 1;
     dma4(jb.G, (unsigned)(relrow(tt) * 4),
          smem_lds + (unsigned)(LY::OFF_G + gate_slot(slot_of) * LY::GB));
   };
   // chunk c into stage `stage`; offsets wrap modulo 2^32 like the byte
   // offsets they stand for (the host keeps one sequence below 4 GiB)
-  auto issue = [&](int c, int stage) {
+  auto issue = [&](int cs, int stage) {
     const unsigned sb = (unsigned)(stage * LY::STAGE);
-    if (lcf) c = nch - 1 - c;
+    const int c = phys(cs);
     const bool full = (c + 1) * CH <= len;
 #pragma unroll
     for (int q = 0; q < LPC_HI; ++q) {
@@ -284,7 +287,7 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob& jb, f32x4 (&acc
         dma16(src_of[q], voff, dst_of[q] + sb);
       }
     }
-    if (GATED && gwave) issue_gates(c + 1 < nch ? c + 1 : nch - 1, c + 1);
+    if (GATED && gwave) issue_gates(cs + 1 < nch ? cs + 1 : nch - 1, cs + 1);
   };
 
   // first chunks in flight while the factors are computed
@@ -337,6 +340,7 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob& jb, f32x4 (&acc
 
   // GATED, wave NW-1: the factor tables of chunk cc (its gates are in LDS
   // and visible) into buffer cc % 2
+  float gwalked2 = 0.0f;  // (lcf) total log2-gate of the chunks walked, wave NW-1
   auto write_tables = [&](int cc) {
     const int cl = (len - cc * CH < CH) ? (len - cc * CH) : CH;
     // chunk-local cumulative log-gate in log2 units, lane = token
@@ -344,7 +348,8 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob& jb, f32x4 (&acc
         *reinterpret_cast<const float*>(smem + LY::OFF_G + gate_slot(cc) * LY::GB + 4 * lane) *
         1.4426950408889634f);
     const float clast = lane_value(c2, cl - 1);
-    const float ew = (lane < cl) ? exp2_np(clast - c2) : 0.0f;  // update weight
+    const float ew = (lane < cl) ? exp2_np(clast - c2 + gwalked2) : 0.0f;  // update weight
+    if (lcf) gwalked2 += clast;
     float* tab = reinterpret_cast<float*>(smem + LY::OFF_T + (cc & 1) * 2 * CH * 4);
     const int pos = tab_pos<T>(lane);
     tab[pos] = c2;
@@ -356,7 +361,7 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob& jb, f32x4 (&acc
     const float* tab = reinterpret_cast<const float*>(smem + LY::OFF_T + (cc & 1) * 2 * CH * 4);
     const float clast = tab[tab_pos<T>(cl - 1)];
     gsum2 += clast;
-    dc = exp2_np(clast);
+    dc = lcf ? 1.0f : exp2_np(clast);
     // update weights of the lane's contraction slots
     if constexpr (E == 8) {
 #pragma unroll
