@@ -33,6 +33,9 @@ namespace {
 constexpr int kChunk = 64;
 // Workgroups the plan aims for: one per compute unit of an MI355X.
 constexpr int64_t kTargetWG = 256;
+// Chunks per sub-segment at or above which the chunk walks prefer two
+// rounds of workgroups to one (see check_shape).
+constexpr int64_t kTwoRoundChunks = 128;
 
 thread_local std::string g_last_error;
 
@@ -58,7 +61,12 @@ struct Plan {
 };
 
 // Shape checks shared by forward and backward.  No HIP call.
-la_status check_shape(const la_shape* s, Plan* plan) {
+// two_rounds: the automatic split may double so that the chunk walks fill
+// the chip twice (measured faster for the fixed-decay forward and backward
+// when each sub-segment still spans at least kTwoRoundChunks chunks, e.g.
+// 16 sequences of 256K tokens: 512 walks of 8K tokens beat 256 of 16K; the
+// tangent walks of la_decay_grad, bound by their arithmetic, do not gain).
+la_status check_shape(const la_shape* s, Plan* plan, bool two_rounds = true) {
   if (!s) return fail(LA_ERR_INVALID_ARG, "shape is NULL");
   if (s->B < 0 || s->H < 0 || s->L < 0)
     return fail(LA_ERR_INVALID_ARG, "negative size (B=%lld H=%lld L=%lld)", (long long)s->B,
@@ -90,6 +98,9 @@ la_status check_shape(const la_shape* s, Plan* plan) {
   const int64_t nchunks = (plan->Ls + kChunk - 1) / kChunk;
   int64_t want = s->split > 0 ? s->split
                               : (plan->nseq > 0 ? (kTargetWG + plan->nseq - 1) / plan->nseq : 1);
+  if (s->split == 0 && two_rounds && plan->nseq * 2 * want <= 2 * kTargetWG &&
+      nchunks >= 2 * want * kTwoRoundChunks)
+    want *= 2;
   if (want > nchunks) want = nchunks;
   if (want < 1) want = 1;
   const int64_t cps = nchunks > 0 ? (nchunks + want - 1) / want : 1;  // chunks per sub-segment
@@ -509,7 +520,7 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
 size_t la_decay_grad_workspace_bytes(const la_shape* shape) {
   Plan pl;
   std::string keep = g_last_error;
-  if (check_shape(shape, &pl) != LA_OK) {
+  if (check_shape(shape, &pl, false) != LA_OK) {
     g_last_error = keep;
     return 0;
   }
@@ -521,7 +532,7 @@ la_status la_decay_grad(const la_shape* s, const void* Q, const void* K, const v
                         const float* dS_end, float* dlambda, void* ws, size_t ws_bytes,
                         void* stream) {
   Plan pl;
-  la_status r = check_shape(s, &pl);
+  la_status r = check_shape(s, &pl, false);
   if (r != LA_OK) return r;
   const bool has_tokens = pl.nseq > 0 && pl.Ls > 0;
   if (has_tokens && (!Q || !K || !V || !dO))
