@@ -142,6 +142,8 @@ la::FwdArgs flow_args(const Plan& pl, int H, int nseg, const void* Q, const void
   fa.split = pl.split;
   fa.reverse = reverse;
   fa.ragged_first = pl.ragged_first;
+  fa.sws_nper = pl.split - 1;
+  fa.sws_step = 1;
   return fa;
 }
 
@@ -373,6 +375,38 @@ Plan gated_bwd_plan(const Plan& p) {
   return g;
 }
 
+// The gated sweeps themselves walk coarser sub-segments: the automatic
+// plan's (p0), rounded up to whole 1024-token blocks, i.e. `step` blocks
+// each, and take their start states from every step-th entry of the
+// 1024-token states (short walks measured slower).  Cut the same way as the
+// fine plan, so every coarse boundary is a fine one.
+Plan gated_sweep_plan(const Plan& p0, const Plan& fine, int64_t* step) {
+  Plan c = fine;
+  const int64_t blocks = (p0.Lp + kGateBlock - 1) / kGateBlock;
+  *step = blocks > 0 ? blocks : 1;
+  c.Lp = *step * kGateBlock;
+  const int64_t nchunks = (p0.Ls + kChunk - 1) / kChunk;
+  const int64_t cps = c.Lp / kChunk;
+  c.split = nchunks > 0 ? (int)((nchunks + cps - 1) / cps) : 1;
+  return c;
+}
+
+// Every sub-segment p >= 1 of the coarse plan c starts on a boundary of the
+// fine plan f, whose start state sits in slot [0, f.split - 2] (the slot
+// rule of the chunk kernel, sws_slot).
+bool sweep_slots_valid(const Plan& c, const Plan& f, int64_t step) {
+  const int64_t nper = f.split - 1;
+  for (int64_t p = 1; p < c.split; ++p) {
+    const int64_t slot = c.ragged_first ? nper - (c.split - p) * step : p * step - 1;
+    if (slot < 0 || slot >= nper) return false;
+    const int64_t fp = slot + 1;  // fine sub-segment starting there
+    const int64_t fstart = f.ragged_first ? f.Ls - (f.split - fp) * f.Lp : fp * f.Lp;
+    const int64_t cstart = c.ragged_first ? c.Ls - (c.split - p) * c.Lp : p * c.Lp;
+    if (fstart != cstart) return false;
+  }
+  return true;
+}
+
 // gated backward workspace (in order): prepared start state [nseq][D][D],
 // the forward sweep's start states W, the dV sweep's W2 and their transposes
 // W3 for the dK sweep (each [nseq][split-1][D][D]; W and W3 also feed the
@@ -419,9 +453,15 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
   if (r != LA_OK) return r;
   if ((double)pl0.nseq * (double)((pl0.Ls + kGateBlock - 1) / kGateBlock) > 2.0e9)
     return fail(LA_ERR_INVALID_ARG, "too many workgroups");
-  const Plan pl = gated_bwd_plan(pl0);  // forward sweep
-  Plan plr = pl;                        // reverse sweeps
+  const Plan pl = gated_bwd_plan(pl0);  // forward sweep's 1024-token states
+  Plan plr = pl;                        // reverse sweeps'
   plr.ragged_first = true;
+  int64_t step = 1;
+  const Plan plc = gated_sweep_plan(pl0, pl, &step);  // the sweeps' own walks
+  Plan plrc = plc;
+  plrc.ragged_first = true;
+  if (!sweep_slots_valid(plc, pl, step) || !sweep_slots_valid(plrc, plr, step))
+    return fail(LA_ERR_UNSUPPORTED, "sweep plan does not align with the 1024-token states");
   const bool has_tokens = pl.nseq > 0 && pl.Ls > 0;
   if (has_tokens && (!Q || !K || !V || !log_alpha || !dO || !dQ || !dK || !dV))
     return fail(LA_ERR_INVALID_ARG, "Q, K, V, log_alpha, dO, dQ, dK and dV are required");
@@ -465,9 +505,16 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
     start = A;
   }
   const bool need_send = dlog_alpha && dS_end;
-  r = run_flow(pl, s->dtype, H, s->nseg, dO, V, K, nullptr, start, dQ, need_send ? SE : nullptr,
-               W, 0, st, true, log_alpha, LDw);
+  r = run_states(pl, s->dtype, H, s->nseg, V, K, nullptr, start, W, 0, st, true, log_alpha, LDw);
   if (r != LA_OK) return r;
+  {
+    la::FwdArgs ma = main_args(plc, H, s->nseg, dO, V, K, nullptr, start, dQ,
+                               need_send ? SE : nullptr, W, 0, true, log_alpha);
+    ma.sws_nper = pl.split - 1;
+    ma.sws_step = (int)step;
+    if ((e = la::launch_fwd(ma, s->dtype, pl.D, true, plc.nseq * ma.p_count, st)) != hipSuccess)
+      return hip_fail(e, "chunk kernel launch");
+  }
 
   // reverse sweeps: from token t+1 back to t with alpha_{t+1}
   if ((e = la::launch_shift_gates(log_alpha, Gs, pl.nseq, pl.Ls, st)) != hipSuccess)
@@ -494,11 +541,13 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
     start = A;
   }
   {
-    const la::FwdArgs av = main_args(plr, H, s->nseg, K, Q, dO, nullptr, dS_end, dV, dS0, W2, 1,
-                                     true, Gs);
-    const la::FwdArgs ak = main_args(plr, H, s->nseg, V, dO, Q, nullptr, start, dK, nullptr, W3, 1,
-                                     true, Gs);
-    if ((e = la::launch_fwd_pair(av, ak, s->dtype, pl.D, pl.nseq * pl.split, st)) != hipSuccess)
+    la::FwdArgs av = main_args(plrc, H, s->nseg, K, Q, dO, nullptr, dS_end, dV, dS0, W2, 1,
+                               true, Gs);
+    la::FwdArgs ak = main_args(plrc, H, s->nseg, V, dO, Q, nullptr, start, dK, nullptr, W3, 1,
+                               true, Gs);
+    av.sws_nper = ak.sws_nper = plr.split - 1;
+    av.sws_step = ak.sws_step = (int)step;
+    if ((e = la::launch_fwd_pair(av, ak, s->dtype, pl.D, plc.nseq * plc.split, st)) != hipSuccess)
       return hip_fail(e, "paired chunk kernel launch");
   }
   if (dS0 && (e = la::launch_scale_first_gate(dS0, log_alpha, pl.nseq, pl.Ls, pl.D, st)) != hipSuccess)

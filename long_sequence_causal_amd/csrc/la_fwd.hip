@@ -10,6 +10,14 @@
 
 namespace la {
 
+// Slot in a.Sws of the start state of sub-segment p >= 1: the finer
+// partition's sub-segment that starts on the same row (counted from the
+// sequence's start, or from its end when the short sub-segment comes first).
+__device__ inline int64_t sws_slot(const FwdArgs& a, int p) {
+  return a.ragged_first ? a.sws_nper - (int64_t)(a.split - p) * a.sws_step
+                        : (int64_t)p * a.sws_step - 1;
+}
+
 // Work item `wg` of a launch over a: sub-segment p_begin + wg % p_count of
 // sequence wg / p_count.
 template <typename T, int D, bool WITH_O, bool GATED>
@@ -58,7 +66,7 @@ __device__ __forceinline__ void chunk_item(const FwdArgs& a, int64_t wg) {
       if (p == 0)
         sp = a.S0 ? a.S0 + n * D * D : nullptr;
       else
-        sp = a.Sws + (n * (a.split - 1) + (p - 1)) * (int64_t)D * D;
+        sp = a.Sws + (n * a.sws_nper + sws_slot(a, p)) * (int64_t)D * D;
     }
 #pragma unroll
     for (int tk = 0; tk < NKT; ++tk)

@@ -27,7 +27,13 @@ struct FwdArgs {
   // Sws[n][p-1] for p > 0
   int start_from_state;
   const float* S0;   // [nseq][D][D]
-  const float* Sws;  // [nseq][split-1][D][D]
+  const float* Sws;  // [nseq][sws_nper][D][D]
+  // Sws holds the start states of a finer partition of each sequence into
+  // sub-segments of Lp / sws_step tokens, cut the same way (ragged_first
+  // alike): sws_nper = its sub-segment count - 1.  sws_step = 1 and
+  // sws_nper = split - 1 is this launch's own partition.
+  int64_t sws_nper;
+  int sws_step;
   void* O;           // [nseq*Ls][D], null in state-only launches
   // the final state of sub-segment p is written to Sout[n][p - sout_p0] when
   // p is in [sout_p0, sout_p0 + sout_np)

@@ -183,6 +183,11 @@ BWD_CASES = [
     ("bf16", 128, 1, 2, 5000, 1, 0, 0.5, 0.5),
     ("bf16", 64, 1, 2, 3 * 2100, 3, 0, 0.5, 0.5),
     ("fp32", 64, 1, 2, 4096 + 64, 1, 0, 0.5, 0.5),
+    # sweeps walking several 1024-token blocks each from every step-th block
+    # state (step 9, 5, 3), ragged in blocks and in chunks, forward and reverse
+    ("bf16", 64, 1, 2, 3 * 8192 + 1037, 1, 3, 0.5, 0.5),
+    ("bf16", 128, 1, 2, 2 * (2 * 4096 + 700), 2, 2, 0.5, 1.0),
+    ("fp32", 64, 1, 1, 5000, 1, 2, 0.5, 0.5),
 ]
 
 
