@@ -260,12 +260,13 @@ size_t la_bwd_gated_workspace_bytes(const la_shape* shape);
  *   dS0 [B,H,nseg,dk,dv] fp32 output; NULL = not returned.
  *   dlog_alpha [B,H,L] fp32   output; NULL = not returned.
  *   ws, ws_bytes              workspace of la_bwd_gated_workspace_bytes().
- * The sweeps always cut each segment into sub-segments of 1024 tokens
- * (shape->split is ignored), the reverse ones with the short sub-segment
- * first so that both cut at the same rows: at every such row y the gate
- * gradient alpha_y <G_y, S_{y-1}> is formed exactly from the two sweeps' fp32
- * states, so the suffix sums of the second form never span more than 1024
- * tokens.
+ * The sweeps' start states are always formed at every 1024th row of each
+ * segment (whatever shape->split asks for), the reverse ones counted from the
+ * segment's end so that both fall on the same rows: at every such row y the
+ * gate gradient alpha_y <G_y, S_{y-1}> is formed exactly from the two
+ * sweeps' fp32 states, so the suffix sums of the second form never span more
+ * than 1024 tokens.  The sweeps themselves walk whole multiples of 1024 tokens
+ * (shape->split, rounded up; 0 = the library's choice).
  * Errors as la_chunk_bwd.
  */
 la_status la_chunk_bwd_gated(const la_shape* shape, const void* Q, const void* K,
