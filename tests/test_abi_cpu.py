@@ -129,6 +129,35 @@ def test_plan_split_normalisation():
     assert la.la_fwd_workspace_bytes(s) == 32 * 7 * 128 * 128 * 4
 
 
+def test_automatic_plan_takes_a_second_round_only_for_long_walks():
+    # the workspace holds the start states of sub-segments 1..split-1, so its
+    # size gives the split the library chose
+    state = 128 * 128 * 4
+
+    def ws(B, H, L, nseg=1, split=0):
+        return la.la_fwd_workspace_bytes(la.make_shape(B, H, L, 128, 128, nseg, la.LA_BF16, split))
+
+    # 32 sequences of 64K tokens: 8 walks of 128 chunks each, one round of 256
+    assert ws(1, 32, 65536) == 32 * 7 * state
+    # 32 sequences of 16K tokens (walks of 32 chunks): one round
+    assert ws(2, 16, 16384) == 32 * 7 * state
+    # 16 sequences of 256K tokens: walks of 256 chunks at split 16 become
+    # two rounds of 512 walks of 128 chunks
+    assert ws(1, 16, 262144) == 16 * 31 * state
+    # 16 sequences of 1M tokens: two rounds at most (512 walks)
+    assert ws(1, 16, 1 << 20) == 16 * 31 * state
+    # 1024 segments of 16K tokens fill the chip without a split
+    assert ws(1, 16, 1 << 20, nseg=64) == 0
+    # an explicit split is taken as given
+    assert ws(1, 16, 262144, split=16) == 16 * 15 * state
+    # the backward follows the same plan: two prepared states and two sets of starts
+    s = la.make_shape(1, 16, 262144, 128, 128, 1, la.LA_BF16, 0)
+    assert la.la_bwd_workspace_bytes(s) == 2 * (16 * state + 16 * 31 * state)
+    # the decay gradient's tangent walks keep one round: (S, U) starts and one
+    # fp64 share per sub-segment
+    assert la.la_decay_grad_workspace_bytes(s) == 2 * 16 * 15 * state + 16 * 16 * 8
+
+
 def test_scan_rejects_bad_arguments():
     L = la.lib()
     v = ctypes.c_void_p
