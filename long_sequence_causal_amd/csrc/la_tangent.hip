@@ -50,6 +50,20 @@ namespace la {
 
 namespace {
 
+// bf16 hi + lo of a pair of fp32 values, each packed as two bf16 (element
+// 0 in the low half), returned as {hi, lo}: hi = round-to-nearest-even(x),
+// lo = the same rounding of the residual x - hi, which is exact in fp32.
+// One conversion serves both values of a pair.
+__device__ inline u32x2 split_hi_lo(float x0, float x1) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const f32x2 x = {x0, x1};
+  const unsigned hi = __builtin_bit_cast(unsigned, __builtin_convertvector(x, bf16x2));
+  const f32x2 h = {__builtin_bit_cast(float, hi << 16), __builtin_bit_cast(float, hi & 0xffff0000u)};
+  const unsigned lo = __builtin_bit_cast(unsigned, __builtin_convertvector(x - h, bf16x2));
+  return u32x2{hi, lo};
+}
+
 template <typename T, int D, bool MAIN>
 struct TanLayout {
   typedef PadTile<T, CH, D> TN;
@@ -255,20 +269,23 @@ k_tangent(TanArgs a) {
         for (int js = 0; js < NJS; ++js) {
           const op_t Dop = tr_op<T, TN>(sD, js * KS, col, lane);
           if constexpr (E == 8) {
-            bf16x8 h1, l1, h2, l2;
+            u32x4 h1, l1, h2, l2;
 #pragma unroll
-            for (int x = 0; x < 8; ++x) {
-              const float a1 = (float)Dop[x] * tq[8 * js + x];
-              const float a2 = a1 * (float)(1 + slot_token<T>(js * KS, g, x));
-              h1[x] = (__bf16)a1;
-              l1[x] = (__bf16)(a1 - (float)h1[x]);
-              h2[x] = (__bf16)a2;
-              l2[x] = (__bf16)(a2 - (float)h2[x]);
+            for (int x = 0; x < 8; x += 2) {
+              const float a10 = (float)Dop[x] * tq[8 * js + x];
+              const float a11 = (float)Dop[x + 1] * tq[8 * js + x + 1];
+              const float a20 = a10 * (float)(1 + slot_token<T>(js * KS, g, x));
+              const float a21 = a11 * (float)(1 + slot_token<T>(js * KS, g, x + 1));
+              const u32x2 s1 = split_hi_lo(a10, a11), s2 = split_hi_lo(a20, a21);
+              h1[x / 2] = s1[0];
+              l1[x / 2] = s1[1];
+              h2[x / 2] = s2[0];
+              l2[x / 2] = s2[1];
             }
-            D1[js] = h1;
-            D1l[js] = l1;
-            D2[js] = h2;
-            D2l[js] = l2;
+            D1[js] = __builtin_bit_cast(bf16x8, h1);
+            D1l[js] = __builtin_bit_cast(bf16x8, l1);
+            D2[js] = __builtin_bit_cast(bf16x8, h2);
+            D2l[js] = __builtin_bit_cast(bf16x8, l2);
           } else {
             D1[js] = Dop * tq[js];
             D2[js] = D1[js] * (float)(1 + slot_token<T>(js * KS, g, 0));
@@ -312,20 +329,23 @@ k_tangent(TanArgs a) {
       for (int js = 0; js < NJS; ++js) {
         const op_t Vop = tr_op<T, TN>(sV, js * KS, col, lane);
         if constexpr (E == 8) {
-          bf16x8 b1, b1l, b2, b2l;
+          u32x4 b1, b1l, b2, b2l;
 #pragma unroll
-          for (int x = 0; x < 8; ++x) {
-            const float vw = (float)Vop[x] * tw[8 * js + x];
-            const float vu = vw * (float)(clf - 1 - slot_token<T>(js * KS, g, x));
-            b1[x] = (__bf16)vw;
-            b1l[x] = (__bf16)(vw - (float)b1[x]);
-            b2[x] = (__bf16)vu;
-            b2l[x] = (__bf16)(vu - (float)b2[x]);
+          for (int x = 0; x < 8; x += 2) {
+            const float vw0 = (float)Vop[x] * tw[8 * js + x];
+            const float vw1 = (float)Vop[x + 1] * tw[8 * js + x + 1];
+            const float vu0 = vw0 * (float)(clf - 1 - slot_token<T>(js * KS, g, x));
+            const float vu1 = vw1 * (float)(clf - 1 - slot_token<T>(js * KS, g, x + 1));
+            const u32x2 s1 = split_hi_lo(vw0, vw1), s2 = split_hi_lo(vu0, vu1);
+            b1[x / 2] = s1[0];
+            b1l[x / 2] = s1[1];
+            b2[x / 2] = s2[0];
+            b2l[x / 2] = s2[1];
           }
-          B1[js] = b1;
-          B1l[js] = b1l;
-          B2[js] = b2;
-          B2l[js] = b2l;
+          B1[js] = __builtin_bit_cast(bf16x8, b1);
+          B1l[js] = __builtin_bit_cast(bf16x8, b1l);
+          B2[js] = __builtin_bit_cast(bf16x8, b2);
+          B2l[js] = __builtin_bit_cast(bf16x8, b2l);
         } else {
           B1[js] = Vop * tw[js];
           B2[js] = B1[js] * (float)(clf - 1 - slot_token<T>(js * KS, g, 0));
