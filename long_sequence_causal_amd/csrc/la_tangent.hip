@@ -214,6 +214,10 @@ k_tangent(TanArgs a) {
   set_factors(CH);  // tabW is complete at the loop's first barrier
 
   double dsum = 0.0;  // this lane's share of lambda * gradient (main pass)
+  // The token of a contraction slot is a lane-group term plus a
+  // compile-time one (slot_token(j0, g, x) = slot_token(j0, 0, x) + fB);
+  // small integers, so the factors below are exact in fp32 either way.
+  const float fB = (float)slot_token<T>(0, g, 0);
   if (S > 1 && nch > 0) issue(0, 0);
   for (int c = 0; c < nch; ++c) {
     const int cl = (len - c * CH < CH) ? (len - c * CH) : CH;
@@ -274,8 +278,8 @@ k_tangent(TanArgs a) {
             for (int x = 0; x < 8; x += 2) {
               const float a10 = (float)Dop[x] * tq[8 * js + x];
               const float a11 = (float)Dop[x + 1] * tq[8 * js + x + 1];
-              const float a20 = a10 * (float)(1 + slot_token<T>(js * KS, g, x));
-              const float a21 = a11 * (float)(1 + slot_token<T>(js * KS, g, x + 1));
+              const float a20 = a10 * (fB + (float)(1 + slot_token<T>(js * KS, 0, x)));
+              const float a21 = a11 * (fB + (float)(1 + slot_token<T>(js * KS, 0, x + 1)));
               const u32x2 s1 = split_hi_lo(a10, a11), s2 = split_hi_lo(a20, a21);
               h1[x / 2] = s1[0];
               l1[x / 2] = s1[1];
@@ -324,6 +328,7 @@ k_tangent(TanArgs a) {
       }
       // V^T operands of this wave's columns, scaled per token (hi + lo in bf16)
       const float* tw = tabW + 16 * g;
+      const float cB = (float)(clf - 1) - fB;  // clf - 1 - slot_token = cB - slot_token(., 0, .)
       op_t B1[NJS], B1l[NJS], B2[NJS], B2l[NJS];
 #pragma unroll
       for (int js = 0; js < NJS; ++js) {
@@ -334,8 +339,8 @@ k_tangent(TanArgs a) {
           for (int x = 0; x < 8; x += 2) {
             const float vw0 = (float)Vop[x] * tw[8 * js + x];
             const float vw1 = (float)Vop[x + 1] * tw[8 * js + x + 1];
-            const float vu0 = vw0 * (float)(clf - 1 - slot_token<T>(js * KS, g, x));
-            const float vu1 = vw1 * (float)(clf - 1 - slot_token<T>(js * KS, g, x + 1));
+            const float vu0 = vw0 * (cB - (float)slot_token<T>(js * KS, 0, x));
+            const float vu1 = vw1 * (cB - (float)slot_token<T>(js * KS, 0, x + 1));
             const u32x2 s1 = split_hi_lo(vw0, vw1), s2 = split_hi_lo(vu0, vu1);
             b1[x / 2] = s1[0];
             b1l[x / 2] = s1[1];
