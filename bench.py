@@ -202,14 +202,15 @@ def gated_leg(torch, la, inp, dev, iters, gate_logs):
             "frac_hbm": nbytes / t / 1e9 / HBM_PEAK_GBS}
 
 
-def decode_leg(torch, la, dev, iters):
-    """la_step on the decode batch (64 sequences x 32 heads, d = 128, bf16,
-    state updated in place): the median of per-call event times, against its
-    algorithmic bytes (the fp32 state read and written once, q, k, v read
-    and o written)."""
+def decode_leg(torch, la, dev, iters, name="decode_b64"):
+    """la_step on a decode batch (decode_b64: 64 sequences x 32 heads, d = 128,
+    bf16, state updated in place; decode_b512: 512 sequences, whose 1 GiB of
+    state cannot stay in the last-level cache between steps): the median of
+    per-call event times, against its algorithmic bytes (the fp32 state read
+    and written once, q, k, v read and o written)."""
     from long_sequence_causal_amd.inputs import DECODE, decode_inputs
-    w = DECODE["decode_b64"]
-    inp = decode_inputs("decode_b64", device=dev)
+    w = DECODE[name]
+    inp = decode_inputs(name, device=dev)
     q, k, v, lam, S = inp["q"], inp["k"], inp["v"], inp["lam"], inp["S"]
     B, H, d = q.shape
     o = torch.empty_like(v)
@@ -225,7 +226,7 @@ def decode_leg(torch, la, dev, iters):
     nbytes = B * H * (2 * d * d * 4 + 4 * d * 2)
     t = ms / 1e3
     del inp, q, k, v, S, o
-    return {"workload": "decode_b64", "B": B, "H": H, "d": d, "dtype": w["dtype"],
+    return {"workload": name, "B": B, "H": H, "d": d, "dtype": w["dtype"],
             "us_per_call": ms * 1e3, "us_min": each[0] * 1e3, "us_max": each[-1] * 1e3,
             "calls": iters, "tokens_per_s": B / t, "alg_bytes": nbytes,
             "achieved_GBs": nbytes / t / 1e9, "frac_hbm": nbytes / t / 1e9 / HBM_PEAK_GBS}
@@ -444,6 +445,10 @@ def main():
         eprint(f"[bench] decode step ({dl['workload']}): {dl['us_per_call']:.1f} us/call median "
                f"(min {dl['us_min']:.1f}, max {dl['us_max']:.1f} over {dl['calls']}), "
                f"{dl['achieved_GBs']:.0f} GB/s algorithmic")
+        dx = decode_leg(torch, la, dev, 50, "decode_b512")
+        eprint(f"[bench] decode step ({dx['workload']}, state beyond the last-level cache): "
+               f"{dx['us_per_call']:.1f} us/call median, {dx['achieved_GBs']:.0f} GB/s algorithmic")
+        dl["beyond_cache"] = dx
         rec["decode"] = dl
     if not args.no_cpu:
         eprint("[bench] CPU oracle baseline ...")

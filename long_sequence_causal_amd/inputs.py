@@ -139,6 +139,10 @@ def gate_logs(lam: torch.Tensor, B: int, L: int, seed: int, device="cpu") -> tor
 DECODE = {
     "decode_b64": dict(B=64, H=32, d=128, dtype="bf16", s_std=0.02, seed=5,
                        note="one decode step of 64 sequences x 32 heads, d = 128"),
+    # 1 GiB of fp32 state, four times the 256 MB last-level cache: a step
+    # streams its state from HBM however often it is repeated
+    "decode_b512": dict(B=512, H=32, d=128, dtype="bf16", s_std=0.02, seed=6,
+                        note="one decode step of 512 sequences x 32 heads, d = 128"),
 }
 
 

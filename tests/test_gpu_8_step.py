@@ -99,3 +99,20 @@ def test_step_at_the_decode_batch():
     eo, es = rel_err(f64(o), o_r), rel_err(f64(S1), S1_r)
     log(f"  err o={eo:.3e} S'={es:.3e}")
     assert eo <= TOL["bf16"] and es <= TOL["fp32"]
+
+
+def test_step_at_the_large_decode_batch_on_sampled_sequences():
+    """The 512-sequence decode batch (1 GiB of state, beyond the last-level
+    cache) run whole as the bench runs it; three sequences, all heads,
+    checked against the oracle."""
+    inp = decode_inputs("decode_b512", device="cuda")
+    q, k, v, lam, S = inp["q"], inp["k"], inp["v"], inp["lam"], inp["S"]
+    log(f"step large decode batch {tuple(q.shape)}")
+    o, S1 = la.la_step(q, k, v, lam, S)
+    torch.cuda.synchronize()
+    rows = [0, 255, 511]
+    o_r, S1_r = lao.step(f64(q[rows]), f64(k[rows]), f64(v[rows]), f64(lam), f64(S[rows]))
+    eo, es = rel_err(f64(o[rows]), o_r), rel_err(f64(S1[rows]), S1_r)
+    log(f"  err o={eo:.3e} S'={es:.3e} (sequences {rows})")
+    assert eo <= TOL["bf16"] and es <= TOL["fp32"]
+
