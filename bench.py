@@ -232,6 +232,24 @@ def decode_leg(torch, la, dev, iters, name="decode_b64"):
             "achieved_GBs": nbytes / t / 1e9, "frac_hbm": nbytes / t / 1e9 / HBM_PEAK_GBS}
 
 
+def ramp(fn, min_ms):
+    """Untimed calls, in batches of 10, until at least min_ms of wall time has
+    passed (the GPU clock takes tens of ms to settle under load).  Returns
+    (milliseconds spent, calls made)."""
+    import torch
+
+    t0 = time.perf_counter()
+    calls = 0
+    while True:
+        for _ in range(10):
+            fn()
+        calls += 10
+        torch.cuda.synchronize()
+        el = (time.perf_counter() - t0) * 1e3
+        if el >= min_ms:
+            return el, calls
+
+
 def time_each(fn, iters, stream):
     """Milliseconds of each of `iters` calls, each between its own events."""
     import torch
@@ -283,16 +301,67 @@ def cpu_baseline(inp, H, L, d):
     dt = time.perf_counter() - t0
     tok_s = T / dt  # all H heads of T tokens
     return {"value": tok_s, "unit": "tokens/s", "cores": lao.threads(), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"all {H} heads x first {T} of {L} tokens, d={d}, S0 given, fp64 recurrence; "
                       f"{dt:.2f} s wall"}
+
+
+def cpu_model():
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_single_thread(dev, heads=4):
+    """The oracle on ONE thread over a bounded sample of the 16K-token decay
+    workload (B=2, H=16, L=16384, d=128, bf16 inputs): batch 0, heads
+    0..heads-1, every token.  Reported per token-head and as tokens/s of the
+    whole workload (a token counts once across its 16 heads)."""
+    import numpy as np
+    from long_sequence_causal_amd.inputs import WORKLOADS, workload_inputs
+    from oracle import lao
+
+    w = WORKLOADS["decay_16k"]
+    inp = workload_inputs(w.name, device=dev)
+
+    def f64(t):
+        return t[:1, :heads].float().cpu().numpy().astype(np.float64)
+
+    q, k, v = f64(inp["q"]), f64(inp["k"]), f64(inp["v"])
+    lam = inp["lam"][:heads].double().cpu().numpy()
+    del inp
+    before = lao.threads()
+    lao.set_threads(1)
+    try:
+        lao.fwd(q[:, :1, :64], k[:, :1, :64], v[:, :1, :64], lam[:1])
+        t0 = time.perf_counter()
+        lao.fwd(q, k, v, lam)
+        dt = time.perf_counter() - t0
+        used = lao.threads()
+    finally:
+        lao.set_threads(before)
+    th = heads * w.L / dt
+    return {"value": th / w.H, "unit": "tokens/s", "token_heads_per_s": th, "cores": used,
+            "kind": "oracle",
+            "sample": f"{w.name}: batch 0, heads 0..{heads - 1} of {w.H}, all {w.L} tokens, d={w.d}, "
+                      f"fp64 recurrence on one thread; {dt:.2f} s wall"}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=100,
-                    help="untimed steps first (the GPU clock takes tens of ms to ramp up)")
+    ap.add_argument("--warmup", type=int, default=100, help="untimed steps before the timed ones")
+    ap.add_argument("--ramp-ms", type=float, default=500.0,
+                    help="untimed calls for at least this long before the warm-up steps, so "
+                         "that the GPU clock has settled whatever --warmup is")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--split", type=int, default=0, help="internal split (0 = library choice)")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward leg")
@@ -338,6 +407,8 @@ def main():
         la.la_chunk_fwd(q, k, v, lam, S0=S0, split=args.split, out=O, S_end_out=S_end,
                         workspace=ws)
 
+    ramp_ms, ramp_calls = ramp(step, args.ramp_ms)
+    eprint(f"[bench] clock ramp: {ramp_calls} untimed calls in {ramp_ms:.0f} ms")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -418,6 +489,7 @@ def main():
         "tflops_alg": flops / t / 1e12,
         "frac_hbm_whole_op": nbytes / t / 1e9 / HBM_PEAK_GBS,
         "per_call_us": {"median": med_ms * 1e3, "min": min_ms * 1e3},
+        "ramp": {"ms": ramp_ms, "calls": ramp_calls},
         "copy_GBs": copy_gbs,
         "frac_of_copy_whole_op": nbytes / t / 1e9 / copy_gbs,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -454,6 +526,7 @@ def main():
         eprint("[bench] CPU oracle baseline ...")
         rec["cpu_baseline"] = cpu_baseline(inp, H, L, d)
         rec["cpu_baseline"]["gpu_over_cpu"] = tok_s / rec["cpu_baseline"]["value"]
+        rec["cpu_baseline"]["single_thread"] = cpu_single_thread(dev)
     print(json.dumps(rec), flush=True)
 
 

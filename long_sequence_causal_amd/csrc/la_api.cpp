@@ -51,6 +51,12 @@ la_status fail(la_status st, const char* fmt, ...) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// A launch covers at most 2^32 - 1 work-items (blocks x threads per block).
+// Every launch of a plan is sized by one of these counts, checked on the host
+// before anything is launched.
+constexpr double kMaxItems = 4294967295.0;
+bool fits_grid(double items) { return items <= kMaxItems; }
+
 struct Plan {
   int64_t nseq = 0;  // B * H * nseg independent sequences
   int64_t Ls = 0;    // tokens per sequence
@@ -106,8 +112,15 @@ la_status check_shape(const la_shape* s, Plan* plan, bool two_rounds = true) {
   const int64_t cps = nchunks > 0 ? (nchunks + want - 1) / want : 1;  // chunks per sub-segment
   plan->Lp = cps * kChunk;
   plan->split = nchunks > 0 ? (int)((nchunks + cps - 1) / cps) : 1;
-  if (plan->nseq * plan->split > 2000000000LL)
-    return fail(LA_ERR_INVALID_ARG, "too many workgroups");
+  // launch sizes: paired chunk walks (D/16 waves per workgroup), one thread
+  // per state element (scans, transposes, prepared states) and per token
+  // (gates)
+  const double walks = (double)plan->nseq * plan->split;
+  if (!fits_grid(2.0 * walks * 4.0 * plan->D) ||
+      !fits_grid(walks * (double)plan->D * plan->D) ||
+      !fits_grid((double)plan->nseq * ((double)plan->Ls + 1024.0)))
+    return fail(LA_ERR_UNSUPPORTED, "%lld sequences of %lld tokens exceed one launch's grid",
+                (long long)plan->nseq, (long long)plan->Ls);
   return LA_OK;
 }
 
@@ -153,7 +166,8 @@ la::FwdArgs flow_args(const Plan& pl, int H, int nseg, const void* Q, const void
 // zero).  Nothing to do when split == 1.
 la_status run_states(const Plan& pl, int dtype, int H, int nseg, const void* K, const void* V,
                      const float* lam, const float* start, float* W, int reverse, hipStream_t st,
-                     bool gated = false, const float* G = nullptr, float* LDw = nullptr) {
+                     bool gated = false, const float* G = nullptr, float* LDw = nullptr,
+                     bool start_undecayed = false) {
   if (pl.nseq == 0 || pl.split <= 1) return LA_OK;
   la::FwdArgs pa = flow_args(pl, H, nseg, nullptr, K, V, lam, reverse);
   pa.gated = gated;  // gated: sub-segment log-gates to LDw for the combine
@@ -185,6 +199,7 @@ la_status run_states(const Plan& pl, int dtype, int H, int nseg, const void* K, 
   sa.Send = nullptr;
   sa.reverse = 0;
   sa.inclusive = 1;
+  sa.s0_undecayed = start_undecayed;
   sa.gated = gated;
   sa.LD = LDw;
   e = la::launch_scan(sa, st);
@@ -451,8 +466,12 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
   Plan pl0;
   la_status r = check_shape(s, &pl0);
   if (r != LA_OK) return r;
-  if ((double)pl0.nseq * (double)((pl0.Ls + kGateBlock - 1) / kGateBlock) > 2.0e9)
-    return fail(LA_ERR_INVALID_ARG, "too many workgroups");
+  // 1024-token blocks: one workgroup of 256 each (anchors, gate gradient),
+  // their start states one thread per element
+  const double gblocks = (double)pl0.nseq * (double)((pl0.Ls + kGateBlock - 1) / kGateBlock + 1);
+  if (!fits_grid(gblocks * 256.0) || !fits_grid(gblocks * (double)pl0.D * pl0.D) ||
+      !fits_grid(gblocks * 2.0 * 4.0 * pl0.D))
+    return fail(LA_ERR_UNSUPPORTED, "too many 1024-token blocks for one launch");
   const Plan pl = gated_bwd_plan(pl0);  // forward sweep's 1024-token states
   Plan plr = pl;                        // reverse sweeps'
   plr.ragged_first = true;
@@ -595,9 +614,6 @@ la_status la_decay_grad(const la_shape* s, const void* Q, const void* K, const v
   if (L.total > 0 && (!ws || ws_bytes < L.total))
     return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", L.total,
                 ws ? ws_bytes : (size_t)0);
-  // the scan runs one thread per state element of every sequence
-  if (pl.split > 1 && (double)pl.nseq * pl.D * pl.D / 256.0 >= 2147483648.0)
-    return fail(LA_ERR_UNSUPPORTED, "too many sequences for a split plan");
   if (s->H == 0) return LA_OK;
   char* base = static_cast<char*>(ws);
   la::TanArgs ta;
@@ -632,8 +648,9 @@ la_status la_step(int64_t B, int64_t H, int32_t dk, int32_t dv, int32_t dtype, c
   if (dtype != LA_BF16 && dtype != LA_FP32) return fail(LA_ERR_INVALID_ARG, "unknown dtype %d", dtype);
   if (dk != dv) return fail(LA_ERR_UNSUPPORTED, "dk != dv (%d, %d)", dk, dv);
   if (dk != 64 && dk != 128) return fail(LA_ERR_UNSUPPORTED, "d=%d not in {64, 128}", dk);
-  if ((double)B * (double)H * (dk / 32) >= 2147483648.0)
-    return fail(LA_ERR_INVALID_ARG, "too many sequences");
+  // one workgroup of 256 per 32-column slab of every state
+  if (!fits_grid((double)B * (double)H * (dk / 32) * 256.0))
+    return fail(LA_ERR_UNSUPPORTED, "too many sequences for one launch");
   const int64_t nseq = B * H;
   if (nseq == 0) return LA_OK;
   if (!q || !k || !v || !lambda || !S_out)
@@ -670,6 +687,8 @@ la_status la_state_scan_gated(int64_t B, int64_t H, int32_t P, int32_t dk, int32
   if (dk <= 0 || dv <= 0) return fail(LA_ERR_INVALID_ARG, "dk and dv must be positive");
   if ((double)B * H * ((double)P + 1) * dk * dv > 4.0e18)
     return fail(LA_ERR_INVALID_ARG, "tensor too large");
+  if (!fits_grid((double)B * H * dk * dv + 256.0))
+    return fail(LA_ERR_UNSUPPORTED, "too many state elements for one launch");
   const int64_t nseq = B * H;
   if (nseq > 0 && P > 0 && (!dS || !S_start || !log_decay))
     return fail(LA_ERR_INVALID_ARG, "dS, log_decay and S_start are required");
@@ -707,6 +726,8 @@ la_status la_state_scan(int64_t B, int64_t H, int32_t P, int32_t dk, int32_t dv,
   if (dk <= 0 || dv <= 0) return fail(LA_ERR_INVALID_ARG, "dk and dv must be positive");
   if ((double)B * H * ((double)P + 1) * dk * dv > 4.0e18)
     return fail(LA_ERR_INVALID_ARG, "tensor too large");
+  if (!fits_grid((double)B * H * dk * dv + 256.0))
+    return fail(LA_ERR_UNSUPPORTED, "too many state elements for one launch");
   const int64_t nseq = B * H;
   if (nseq > 0 && !lambda) return fail(LA_ERR_INVALID_ARG, "lambda is required");
   if (nseq > 0 && P > 0 && (!dS || !S_start))
@@ -798,41 +819,41 @@ static la_status chunk_bwd(const la_shape* s, const void* Q, const void* K, cons
   }
   if (r != LA_OK) return r;
 
-  // dv_t = G_t^T k_t: in reverse time G accumulates q dO^T like a state,
-  // started from dS_end / lambda; its final value G_1 gives dS0 = lambda G_1.
-  // dk_t = G_t v_t: the same reverse recurrence for G^T = sum dO q^T over the
-  // same pairs (q_t, dO_t) with the roles swapped, seeded with the transposed
-  // seed, so its sub-segment start states are the transposes of the dV
-  // sweep's: one pre-pass and scan serve both.  The two sweeps then run as
-  // one paired launch, partners on one XCD walking the same rows, so that Q
-  // and dO, which both read, come from HBM about once.
-  const float* startV = nullptr;
+  // dv_t = G_t^T k_t: in reverse time G accumulates q dO^T like a state.
+  // Its seed dS_end = lambda G_{L+1} already carries the decay of the first
+  // reverse step, so the sweeps and the scan take it undecayed (G_L = dS_end +
+  // q_L dO_L^T; no division by lambda anywhere); its final value G_1 gives
+  // dS0 = lambda G_1.  dk_t = G_t v_t: the same reverse recurrence for G^T =
+  // sum dO q^T over the same pairs (q_t, dO_t) with the roles swapped, seeded
+  // with the transposed seed, so its sub-segment start states are the
+  // transposes of the dV sweep's: one pre-pass and scan serve both.  The two
+  // sweeps then run as one paired launch, partners on one XCD walking the
+  // same rows, so that Q and dO, which both read, come from HBM about once.
   const float* startK = nullptr;
   if (dS_end) {
     pa.src = dS_end;
-    pa.dst = A;
-    pa.transpose = 0;
-    pa.mode = 2;
-    if ((e = la::launch_prep(pa, st)) != hipSuccess) return hip_fail(e, "prep launch");
     pa.dst = A2;
     pa.transpose = 1;
+    pa.mode = 0;
     if ((e = la::launch_prep(pa, st)) != hipSuccess) return hip_fail(e, "prep launch");
-    startV = A;
     startK = A2;
   }
-  r = run_states(pl, s->dtype, H, s->nseg, Q, dO, lambda, startV, W, 1, st);
+  r = run_states(pl, s->dtype, H, s->nseg, Q, dO, lambda, dS_end, W, 1, st, false, nullptr,
+                 nullptr, true);
   if (r != LA_OK) return r;
   if (pl.split > 1) {
     e = la::launch_transpose_copy(W, W2, pl.nseq * (pl.split - 1), pl.D, st);
     if (e != hipSuccess) return hip_fail(e, "transpose launch");
   }
-  const la::FwdArgs av = main_args(pl, H, s->nseg, K, Q, dO, lambda, startV, dV, dS0, W, 1, false,
-                                   nullptr);
-  const la::FwdArgs ak = main_args(pl, H, s->nseg, V, dO, Q, lambda, startK, dK, nullptr, W2, 1,
-                                   false, nullptr);
+  la::FwdArgs av = main_args(pl, H, s->nseg, K, Q, dO, lambda, dS_end, dV, dS0, W, 1, false,
+                             nullptr);
+  la::FwdArgs ak = main_args(pl, H, s->nseg, V, dO, Q, lambda, startK, dK, nullptr, W2, 1,
+                             false, nullptr);
+  av.s0_undecayed = ak.s0_undecayed = 1;
   if ((e = la::launch_fwd_pair(av, ak, s->dtype, pl.D, pl.nseq * pl.split, st)) != hipSuccess)
     return hip_fail(e, "paired chunk kernel launch");
-  if (dS0) {
+  // (with no tokens the sweep's final state is its seed, dS0 = dS_end: no factor)
+  if (dS0 && pl.Ls > 0) {
     pa.src = dS0;
     pa.dst = dS0;
     pa.transpose = 0;

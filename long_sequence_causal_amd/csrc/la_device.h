@@ -160,8 +160,9 @@ __device__ inline float lane_value(float x, int lane) {  // x of a wave-uniform 
 __device__ inline float exp2_np(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ inline float pow_lam(float lg2, float n) {
-  // lambda^n = 2^(n log2 lambda); only non-negative n are formed.
-  return exp2f(n * lg2);
+  // lambda^n = 2^(n log2 lambda); only non-negative n are formed.  n = 0 is
+  // exactly 1 for every lambda, 0 included (log2 0 = -inf would give NaN).
+  return n == 0.0f ? 1.0f : exp2f(n * lg2);
 }
 
 template <typename T>

@@ -57,6 +57,7 @@ __device__ __forceinline__ void chunk_item(const FwdArgs& a, int64_t wg) {
   jb.lg = GATED ? 0.0f : log2f(a.lam[h]);
   jb.G = GATED ? a.G + n * a.Ls : nullptr;
   jb.last_chunk_first = a.last_chunk_first;
+  jb.first_undecayed = !GATED && a.s0_undecayed && a.start_from_state && p == 0;
 
   // ---- start state -> accumulators (wave w: columns [16 w, 16 w + 16))
   f32x4 accS[NKT];

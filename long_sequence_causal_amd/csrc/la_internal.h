@@ -1,5 +1,6 @@
 // la_internal.h -- host-side interface between the C ABI layer (la_api.cpp)
-// and the kernel launchers (la_fwd.hip, la_bwd.hip, la_scan.hip).
+// and the kernel launchers (la_fwd.hip, la_scan.hip, la_gate.hip,
+// la_tangent.hip, la_step.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -54,6 +55,11 @@ struct FwdArgs {
   int gated;
   const float* G;
   float* LDout;
+  // fixed decay, sub-segment 0 from S0: S0 is the state after the first
+  // token's decay (S_1 = S0 + k_1 v_1^T instead of lambda S0 + k_1 v_1^T).
+  // The backward's reverse sweeps start from dS_end this way, which spares
+  // them a division by lambda.
+  int s0_undecayed;
   // state-only launches: walk each sub-segment's chunks last
   // first (the state a sub-segment ends with is the same sum, so only the
   // rounding order changes); a sub-segment with a ragged chunk walks in order
@@ -61,7 +67,7 @@ struct FwdArgs {
 };
 
 // dst[n] = f(src[n]) for nseq D x D fp32 states: optional transpose, then a
-// per-head factor (mode 0: none, 1: * lambda_h, 2: / lambda_h).
+// per-head factor (mode 0: none, 1: * lambda_h).
 struct PrepArgs {
   int64_t nseq;
   int D;
@@ -89,6 +95,9 @@ struct ScanArgs {
   float* Send;       // [nseq][E] or null
   int reverse;
   int inclusive;     // 0: Sout[s] = state before adding dS[s]; 1: after
+  // the first segment decays S0 by lambda^(seg_len - 1) instead of
+  // lambda^seg_len (S0 already carries the first token's decay; fixed decay)
+  int s0_undecayed;
   // gated != 0: segment s of sequence n decays by exp(LD[n][s]) instead of
   // lambda^seg_len (lam is then never read, LD only for s < P)
   int gated;

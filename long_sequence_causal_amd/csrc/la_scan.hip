@@ -19,8 +19,11 @@ __global__ __launch_bounds__(256) void k_state_scan(ScanArgs a) {
   const int64_t n = gid / a.E;
   const int64_t e = gid - n * a.E;
   // lambda^seg_len = 2^(seg_len log2 lambda); underflow to 0 is intended
-  const float dec =
-      GATED ? 0.0f : exp2f((float)a.seg_len * log2f(a.lam[(int)((n / a.hdiv) % a.H)]));
+  const float lg = GATED ? 0.0f : log2f(a.lam[(int)((n / a.hdiv) % a.H)]);
+  const float dec = GATED ? 0.0f : pow_lam(lg, (float)a.seg_len);
+  // decay of the first segment: a seed that already carries the first
+  // token's decay takes one power fewer
+  float dcur = (!GATED && a.s0_undecayed && a.seg_len > 0) ? pow_lam(lg, (float)(a.seg_len - 1)) : dec;
   float x = a.S0 ? a.S0[n * a.E + e] : 0.0f;
   // Segments go in groups of PF whose inputs are all loaded before any of
   // the group's outputs is stored: Sout may be dS itself, so the compiler
@@ -43,7 +46,8 @@ __global__ __launch_bounds__(256) void k_state_scan(ScanArgs a) {
       const int64_t idx = (n * a.P + seg(it + j)) * a.E + e;
       if (!a.inclusive) a.Sout[idx] = x;
       // gated: the segment's own product of gates, exp(LD)
-      x = (GATED ? expf(f[j]) : dec) * x + d[j];
+      x = (GATED ? expf(f[j]) : dcur) * x + d[j];
+      dcur = dec;
       if (a.inclusive) a.Sout[idx] = x;
     }
   }
@@ -52,7 +56,8 @@ __global__ __launch_bounds__(256) void k_state_scan(ScanArgs a) {
     const int64_t idx = (n * a.P + s) * a.E + e;
     const float d = a.dS[idx];
     if (!a.inclusive) a.Sout[idx] = x;
-    x = (GATED ? expf(a.LD[n * a.P + s]) : dec) * x + d;
+    x = (GATED ? expf(a.LD[n * a.P + s]) : dcur) * x + d;
+    dcur = dec;
     if (a.inclusive) a.Sout[idx] = x;
   }
   if (a.Send) a.Send[n * a.E + e] = x;
@@ -67,10 +72,7 @@ __global__ __launch_bounds__(256) void k_prep_state(PrepArgs a) {
   const int r = (int)(e / a.D), c = (int)(e % a.D);
   const int64_t se = a.transpose ? ((int64_t)c * a.D + r) : e;
   float x = a.src[n * DD + se];
-  if (a.mode != 0) {
-    const float l = a.lam[(n / a.hdiv) % a.H];
-    x = (a.mode == 1) ? x * l : x / l;
-  }
+  if (a.mode == 1) x *= a.lam[(n / a.hdiv) % a.H];
   a.dst[gid] = x;
 }
 

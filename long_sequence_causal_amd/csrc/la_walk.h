@@ -142,6 +142,10 @@ struct WalkJob {
   float lg;       // log2 lambda (fixed-decay walks)
   const float* G; // log-gates of the sequence, [Ls] (gated walks)
   int last_chunk_first;  // state-only walks over whole chunks: chunks in reverse order
+  // fixed decay: the start state already carries the first token's decay,
+  // so the first chunk decays it by lambda^(i) and lambda^(cl-1) instead of
+  // lambda^(i+1) and lambda^cl
+  int first_undecayed;
 };
 
 // Walk the range with the state in accS (wave w: columns [16 w, 16 w + 16),
@@ -314,13 +318,20 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob& jb, f32x4 (&acc
   };
   T* const Oseq = reinterpret_cast<T*>(jb.O);  // sequence base of O
   unsigned ooff0[4];  // element offset (chunk 0) of the lane's outputs in each 16-row block
+  const bool und = !GATED && jb.first_undecayed;  // wave-uniform
+  // lambda^(i+1) (or lambda^i for a start state that already carries the
+  // first token's decay) for the lane's query i of each 16-row block
+  auto set_qf = [&](int shift) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) qf[it] = pow_lam(lg, (float)(16 * it + l16 + shift));
+  };
   if (OUT) {
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      if (!GATED) qf[it] = pow_lam(lg, (float)(16 * it + l16 + 1));
-      ooff0[it] = (unsigned)(relrow(16 * it + l16) * D + col + 4 * g);
+    for (int it = 0; it < 4; ++it) ooff0[it] = (unsigned)(relrow(16 * it + l16) * D + col + 4 * g);
+    if (!GATED) {
+      set_qf(und ? 0 : 1);
+      set_pf(CH);
     }
-    if (!GATED) set_pf(CH);
   }
   const float lamC = GATED ? 0.0f : pow_lam(lg, (float)CH);
   // lambda^(cl-1-j) (0 past the tail) for the lane's contraction slots j of the update
@@ -436,6 +447,10 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob& jb, f32x4 (&acc
         if (OUT) set_pf(cl);
       }
       dc = lcf ? 1.0f : ((cl == CH) ? lamC : pow_lam(lg, (float)cl));
+      if (und) {
+        if (c == 0) dc = pow_lam(lg, (float)(cl - 1));
+        if (OUT && c == 1) set_qf(1);
+      }
     }
     const char* const stage = smem + st * LY::STAGE;
     st = (st + 1 == S) ? 0 : st + 1;

@@ -245,7 +245,7 @@ def la_chunk_fwd_gated(q, k, v, log_alpha, S0=None, nseg: int = 1, need_O: bool 
 
 
 def la_state_scan_gated(dS, log_decay, S0=None, reverse: bool = False, out=None,
-                        need_S_end: bool = True):
+                        need_S_end: bool = True, S_end_out=None):
     """Gated segment combine.  dS [B,H,P,dk,dv] fp32, log_decay [B,H,P] fp32,
     S0 [B,H,dk,dv] or None.  Returns (S_start, S_end or None)."""
     B, H, P, dk, dv = dS.shape
@@ -255,16 +255,20 @@ def la_state_scan_gated(dS, log_decay, S0=None, reverse: bool = False, out=None,
         (dS, "dS", (B, H, P, dk, dv), torch.float32),
         (log_decay, "log_decay", (B, H, P), torch.float32),
         (S0, "S0", (B, H, dk, dv), torch.float32),
-        (out, "out", (B, H, P, dk, dv), torch.float32))
+        (out, "out", (B, H, P, dk, dv), torch.float32),
+        (S_end_out, "S_end_out", (B, H, dk, dv), torch.float32))
     S_start = out if out is not None else torch.empty_like(dS)
-    S_end = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dS.device) if need_S_end else None
+    if S_end_out is not None:
+        S_end = S_end_out
+    else:
+        S_end = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dS.device) if need_S_end else None
     _check(lib().la_state_scan_gated(B, H, P, dk, dv, _ptr(dS), _ptr(log_decay), _ptr(S0),
                                      _ptr(S_start), _ptr(S_end), int(bool(reverse)), _stream()))
     return S_start, S_end
 
 
 def la_state_scan(dS, lam, seg_len: int, S0=None, reverse: bool = False, out=None,
-                  need_S_end: bool = True):
+                  need_S_end: bool = True, S_end_out=None):
     """Segment scan.  dS [B,H,P,dk,dv] fp32, lam [H], S0 [B,H,dk,dv] or None.
     Returns (S_start [B,H,P,dk,dv], S_end [B,H,dk,dv] or None); ``out`` may be dS."""
     B, H, P, dk, dv = dS.shape
@@ -274,9 +278,13 @@ def la_state_scan(dS, lam, seg_len: int, S0=None, reverse: bool = False, out=Non
         (dS, "dS", (B, H, P, dk, dv), torch.float32),
         (lam, "lam", (H,), torch.float32),
         (S0, "S0", (B, H, dk, dv), torch.float32),
-        (out, "out", (B, H, P, dk, dv), torch.float32))
+        (out, "out", (B, H, P, dk, dv), torch.float32),
+        (S_end_out, "S_end_out", (B, H, dk, dv), torch.float32))
     S_start = out if out is not None else torch.empty_like(dS)
-    S_end = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dS.device) if need_S_end else None
+    if S_end_out is not None:
+        S_end = S_end_out
+    else:
+        S_end = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dS.device) if need_S_end else None
     _check(lib().la_state_scan(B, H, P, dk, dv, _ptr(dS), _ptr(lam), int(seg_len), _ptr(S0),
                                _ptr(S_start), _ptr(S_end), int(bool(reverse)), _stream()))
     return S_start, S_end

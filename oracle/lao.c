@@ -642,3 +642,11 @@ int lao_threads(void) {
   }
   return n;
 }
+
+/* Run later calls on n OpenMP threads (n >= 1); returns the count now in
+ * force.  Changes no arithmetic: every thread's share is a fixed set of
+ * independent columns or rows. */
+int lao_set_threads(int n) {
+  if (n >= 1) omp_set_num_threads(n);
+  return lao_threads();
+}

@@ -63,12 +63,19 @@ def bind(lib):
     lib.lao_bwd_gated.restype = ctypes.c_int
     lib.lao_threads.restype = ctypes.c_int
     lib.lao_threads.argtypes = []
+    lib.lao_set_threads.restype = ctypes.c_int
+    lib.lao_set_threads.argtypes = [ctypes.c_int]
     return lib
 
 
 def threads() -> int:
     """OpenMP threads the oracle runs on."""
     return int(_load().lao_threads())
+
+
+def set_threads(n: int) -> int:
+    """Run later oracle calls on n threads; returns the count in force."""
+    return int(_load().lao_set_threads(int(n)))
 
 
 def _f64(x):

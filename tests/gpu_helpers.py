@@ -27,10 +27,45 @@ def rel_err(x, ref):
     return num / den if den > 0 else num
 
 
-def per_head_err(x, ref):
-    """Relative error of each (b, h) slice, for reporting."""
-    B, H = ref.shape[:2]
-    return np.array([[rel_err(x[b, h], ref[b, h]) for h in range(H)] for b in range(B)])
+class WholeTensorErr:
+    """The graded measure max |X - X_ref| / max |X_ref| over whole tensors that
+    are compared a slice of heads at a time: running maxima of the numerator
+    and denominator per output name, and each head's own error for the log
+    (a fast-decaying head's outputs are small next to the slow heads', so its
+    error on its own scale is worth seeing even though it is not graded)."""
+
+    def __init__(self):
+        self.num, self.den, self.heads = {}, {}, {}
+
+    def add(self, name, got, ref, heads):
+        """got, ref: fp64 arrays [B, len(heads), ...] of the heads listed."""
+        got = np.asarray(got, dtype=np.float64)
+        ref = np.asarray(ref, dtype=np.float64)
+        assert got.shape == ref.shape, (name, got.shape, ref.shape)
+        for i, h in enumerate(heads):
+            d = float(np.max(np.abs(got[:, i] - ref[:, i]))) if ref[:, i].size else 0.0
+            r = float(np.max(np.abs(ref[:, i]))) if ref[:, i].size else 0.0
+            self.num[name] = max(self.num.get(name, 0.0), d)
+            self.den[name] = max(self.den.get(name, 0.0), r)
+            self.heads.setdefault(name, {})[h] = d / r if r > 0 else d
+
+    def err(self, name):
+        n, d = self.num[name], self.den[name]
+        return n / d if d > 0 else n
+
+    def report(self, label):
+        """Log the whole-tensor error of every output and each head's own
+        error; return {name: whole-tensor error}."""
+        out = {}
+        for name in self.num:
+            out[name] = self.err(name)
+            ph = self.heads[name]
+            worst = max(ph, key=ph.get)
+            log(f"{label}: {name} whole-tensor err {out[name]:.3e} over {len(ph)} heads "
+                f"(max |ref| {self.den[name]:.4g}); per head on its own scale: "
+                + " ".join(f"h{h}={e:.2e}" for h, e in sorted(ph.items()))
+                + f"; worst h{worst}")
+        return out
 
 
 def log(msg):

@@ -289,3 +289,37 @@ def test_product_path_has_no_oracle_dependency():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
                 assert "liblao" not in text and "lao_" not in text and "lao.c" not in text, f
+
+
+def test_launch_grids_stay_within_32_bit_work_item_counts():
+    """A launch covers at most 2^32 - 1 work-items.  Shapes whose launches
+    would exceed that (one thread per state element of 2^18 states of
+    128 x 128; one workgroup of 256 per 32-column slab of a decode state; a
+    walk per 64-token sub-segment) are rejected on the host, before any HIP
+    call, with LA_ERR_UNSUPPORTED -- never half-run."""
+    L = la.lib()
+    v = lambda x: None if x is None else ctypes.c_void_p(x)
+    # 2^18 sequences of 128 x 128 states: 2^32 state elements
+    big = _shape(B=1 << 12, H=64, L=64, dk=128, dv=128, split=0)
+    assert _fwd(big) == la.LA_ERR_UNSUPPORTED
+    assert la.la_fwd_workspace_bytes(big) == 0
+    assert la.la_bwd_workspace_bytes(big) == 0
+    assert la.la_decay_grad_workspace_bytes(big) == 0
+    ok = _shape(B=1 << 11, H=64, L=64, dk=128, dv=128, split=0)  # 2^17 sequences: fits
+    assert la.la_decay_grad_workspace_bytes(ok) > 0  # a valid plan (its fp64 shares)
+    assert L.la_state_scan(1 << 12, 64, 2, 128, 128, v(FAKE), v(FAKE), 64, None, v(FAKE), None,
+                           0, None) == la.LA_ERR_UNSUPPORTED
+    assert L.la_state_scan_gated(1 << 12, 64, 2, 128, 128, v(FAKE), v(FAKE), None, v(FAKE), None,
+                                 0, None) == la.LA_ERR_UNSUPPORTED
+    # decode: 2^21 sequences x 4 slabs x 256 threads = 2^31 fits; 2^22 x 4 x 256 does not
+    step = lambda B: L.la_step(B, 1, 128, 128, la.LA_BF16, v(FAKE), v(FAKE), v(FAKE), v(FAKE),
+                               None, v(FAKE), v(FAKE), None)
+    assert step(1 << 23) == la.LA_ERR_UNSUPPORTED
+    # many short sequences: 2^26 sequences of one chunk -> 2^26 walks x 512 threads
+    many = _shape(B=1 << 20, H=64, L=64, dk=128, dv=128, split=1)
+    assert _fwd(many) == la.LA_ERR_UNSUPPORTED
+    # the gated backward's 1024-token blocks
+    s = _shape(B=1 << 10, H=64, L=1 << 14, dk=128, dv=128, split=0)
+    assert L.la_chunk_bwd_gated(ctypes.byref(s), v(FAKE), v(FAKE), v(FAKE), v(FAKE), None, v(FAKE),
+                                None, v(FAKE), v(FAKE), v(FAKE), None, None, v(FAKE), 1 << 40,
+                                None) == la.LA_ERR_UNSUPPORTED

@@ -78,3 +78,21 @@ def test_lost_segment_recomputed_from_its_start_state():
                                v[:, :, sl].contiguous(), lam, S0=S_start[:, :, s:s + 1].contiguous())
     torch.cuda.synchronize()
     assert rel_err(f64(O_one), f64(O_all[:, :, sl])) <= 1e-3
+
+
+@pytest.mark.parametrize("seg_len", [0, 1, 64])
+def test_scan_with_zero_decay(seg_len):
+    """lambda = 0 next to lambda = 1: lambda^0 = 1 exactly (seg_len = 0 makes
+    the scan a plain prefix sum for every head), lambda^n = 0 for n > 0."""
+    B, H, P, d = 1, 2, 5, 64
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7 + seg_len)
+    dS = torch.randn(B, H, P, d, d, generator=g, device="cuda")
+    S0 = torch.randn(B, H, d, d, generator=g, device="cuda")
+    lam = torch.tensor([0.0, 1.0], device="cuda")
+    st, en = la.la_state_scan(dS, lam, seg_len, S0=S0)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(st).all()) and bool(torch.isfinite(en).all())
+    st_ref, en_ref = lao.scan(f64(dS), f64(lam), seg_len, S0=f64(S0))
+    assert rel_err(f64(st), st_ref) <= 1e-5
+    assert rel_err(f64(en), en_ref) <= 1e-5

@@ -139,3 +139,34 @@ def test_bwd_from_forward_states_requires_the_workspace():
                                         la._ptr(out[0]), la._ptr(out[1]), la._ptr(out[2]), None,
                                         la._ptr(ws), ws.numel(), None)
     assert st == la.LA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("lam0", [0.0, 1e-38, 1e-30])
+@pytest.mark.parametrize("dtype,D,split", [("bf16", 128, 0), ("bf16", 128, 3), ("fp32", 64, 2)])
+def test_tiny_and_zero_decay_forward_and_backward(lam0, dtype, D, split):
+    """lambda = 0 (each token sees only itself; 0^0 = 1), a denormal fp32
+    lambda (1e-38) and 1e-30, next to a slow head, with S0 and dS_end given:
+    forward and backward match the oracle and stay finite.  The backward
+    seeds its reverse sweeps with dS_end itself (never dS_end / lambda)."""
+    B, H, L = 1, 2, 64 * 5 + 17
+    lam = torch.tensor([lam0, 0.97], dtype=torch.float32)
+    log(f"tiny decay case lambda0={float(lam[0]):.3e} dtype={dtype} D={D} split={split}")
+    inp = make_inputs(B, H, L, D, D, dtype=dtype, s0_std=0.5, need_dO=True, dS_end_std=0.5,
+                      seed=91, device="cuda", lam=lam)
+    q, k, v, lam, S0, dO, dSe = (inp[x] for x in ("q", "k", "v", "lam", "S0", "dO", "dS_end"))
+    O, S_end = la.la_chunk_fwd(q, k, v, lam, S0=S0, split=split)
+    dQ, dK, dV, dS0 = la.la_chunk_bwd(q, k, v, lam, dO, S0=S0, dS_end=dSe, split=split)
+    torch.cuda.synchronize()
+    for t in (O, S_end, dQ, dK, dV, dS0):
+        assert bool(torch.isfinite(t.float()).all())
+    O_r, S_r = lao.fwd(f64(q), f64(k), f64(v), f64(lam), S0=f64(S0))
+    ref = lao.bwd(f64(q), f64(k), f64(v), f64(lam), f64(dO), S0=f64(S0), dS_end=f64(dSe))
+    errs = [rel_err(f64(O), O_r), rel_err(f64(S_end), S_r)]
+    errs += [rel_err(f64(x), r) for x, r in zip((dQ, dK, dV, dS0), ref)]
+    # the fast head on its own (its outputs are small next to the slow head's)
+    own = [rel_err(f64(O[:, :1]), O_r[:, :1]), rel_err(f64(dK[:, :1]), ref[1][:, :1]),
+           rel_err(f64(dS0[:, :1]), ref[3][:, :1])]
+    log("  err O={:.3e} S_end={:.3e} dQ={:.3e} dK={:.3e} dV={:.3e} dS0={:.3e}".format(*errs)
+        + "; fast head alone O={:.3e} dK={:.3e} dS0={:.3e}".format(*own))
+    assert max(errs) <= TOL[dtype]
+    assert max(own) <= TOL[dtype]

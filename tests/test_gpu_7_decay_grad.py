@@ -80,21 +80,27 @@ def test_decay_grad_of_empty_problem_is_zero(B, L):
     assert torch.equal(out, torch.zeros_like(out))
 
 
-@pytest.mark.parametrize("name,heads,dse", [("segment_64k", (0, 13, 31), 0.02),
-                                            ("train_256k", (0, 15), 0.0)])
-def test_decay_grad_at_full_size_on_sampled_heads(name, heads, dse):
+@pytest.mark.parametrize("name,dse", [("segment_64k", 0.02), ("train_256k", 0.0)])
+def test_decay_grad_at_full_size_every_head(name, dse):
     """The workloads at full size in the launch configuration the benchmark
-    times; the oracle checks whole heads (every token of a sampled head)."""
-    log(f"decay grad full size: {name}, heads {heads}")
+    times; the oracle computes every head's gradient (every token), and the
+    measure is taken over the whole [H] vector, with each head's own error
+    logged."""
     inp = workload_inputs(name, device="cuda", need_dO=True, dS_end_std=dse)
     q, k, v, lam, S0, dO, dSe = (inp[x] for x in ("q", "k", "v", "lam", "S0", "dO", "dS_end"))
+    H = q.shape[1]
+    log(f"decay grad full size: {name}, {H} heads")
     got = f64(la.la_decay_grad(q, k, v, lam, dO, S0=S0, dS_end=dSe))
     torch.cuda.synchronize()
-    for h in heads:
-        sl = lambda t: None if t is None else f64(t[:, h:h + 1])
-        ref = lao.dlambda(sl(q), sl(k), sl(v), f64(lam[h:h + 1]), sl(dO), S0=sl(S0),
-                          dS_end=sl(dSe))
-        e = rel_err(got[h:h + 1], ref)
-        log(f"  head {h}: {got[h]:.6e} ref {ref[0]:.6e} err {e:.3e}")
-        assert e <= TOL["bf16"]
+    ref = np.empty(H)
+    for h0 in range(0, H, 8):
+        hs = slice(h0, min(H, h0 + 8))
+        sl = lambda t: None if t is None else f64(t[:, hs])
+        ref[hs] = lao.dlambda(sl(q), sl(k), sl(v), f64(lam[hs]), sl(dO), S0=sl(S0),
+                              dS_end=sl(dSe))
+    e = rel_err(got, ref)
+    own = np.abs(got - ref) / np.abs(ref)
+    log(f"  whole-vector err {e:.3e}; per head on its own scale: "
+        + " ".join(f"h{h}={x:.1e}" for h, x in enumerate(own)))
+    assert e <= TOL["bf16"]
     del q, k, v, dO
