@@ -29,7 +29,8 @@
  * Conventions shared by every entry point
  *  - All tensor pointers are DEVICE pointers (including lambda), contiguous,
  *    row-major, 16-byte aligned.  The caller owns every buffer; the library
- *    allocates and frees nothing and keeps no device state.
+ *    allocates and frees nothing and keeps no device state, except the fixed
+ *    array of la_chunk_fwd_noalloc (below).
  *  - Token tensors: Q, K, dQ, dK are [B, H, L, dk]; V, O, dO, dV are
  *    [B, H, L, dv], all of element type `dtype`.  States (S0, S_end, dS_end,
  *    dS0) are fp32 [B, H, nseg, dk, dv] with the state row-major as [dk][dv].
@@ -322,6 +323,28 @@ la_status la_decay_grad(const la_shape* shape, const void* Q, const void* K,
 la_status la_step(int64_t B, int64_t H, int32_t dk, int32_t dv, int32_t dtype,
                   const void* q, const void* k, const void* v, const float* lambda,
                   const float* S, float* S_out, void* o, void* stream);
+
+/*
+ * la_chunk_fwd without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, results and checks as la_chunk_fwd (the
+ * same kernels, bit for bit), minus ws and ws_bytes: the start states of the
+ * split plan live in a fixed device array of the library,
+ * LA_NOALLOC_SCRATCH_BYTES per GPU, held from the library's load on that GPU
+ * until the process ends.  The call allocates and frees nothing.
+ *  - A shape whose plan needs more than LA_NOALLOC_SCRATCH_BYTES
+ *    (la_fwd_workspace_bytes) is rejected with LA_ERR_WORKSPACE before any
+ *    HIP call, and nothing is written.  32 MiB covers, e.g., 32 heads of 64K
+ *    tokens (14 MiB) and 16 heads of 256K tokens (31 MiB) at d = 128.
+ *  - `stream` must belong to the current device (the array is per device).
+ *  - Every call on one GPU shares that GPU's array: two calls that overlap in
+ *    time on one GPU (on different streams or host threads) race and give
+ *    wrong numbers.  Calls in one stream's order are safe.
+ */
+#define LA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+la_status la_chunk_fwd_noalloc(const la_shape* shape, const void* Q, const void* K,
+                               const void* V, const float* lambda, const float* S0,
+                               void* O, float* S_end, void* stream);
 
 #ifdef __cplusplus
 }

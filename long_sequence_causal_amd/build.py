@@ -22,7 +22,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblinattn.so")
 ARCH = "gfx950"
 
-SOURCES = ["la_fwd.hip", "la_scan.hip", "la_gate.hip", "la_tangent.hip", "la_step.hip", "la_api.cpp"]
+SOURCES = ["la_fwd.hip", "la_scan.hip", "la_gate.hip", "la_tangent.hip", "la_step.hip",
+           "la_noalloc.hip", "la_api.cpp"]
 
 
 def hipcc() -> str:

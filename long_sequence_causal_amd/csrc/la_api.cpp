@@ -39,14 +39,19 @@ constexpr int64_t kTwoRoundChunks = 128;
 
 thread_local std::string g_last_error;
 
-la_status fail(la_status st, const char* fmt, ...) {
+la_status vfail(la_status st, const char* fmt, va_list ap) {
   char buf[512];
-  va_list ap;
-  va_start(ap, fmt);
   vsnprintf(buf, sizeof(buf), fmt, ap);
-  va_end(ap);
   g_last_error = std::string(la_status_str(st)) + ": " + buf;
   return st;
+}
+
+la_status fail(la_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  const la_status r = vfail(st, fmt, ap);
+  va_end(ap);
+  return r;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -282,6 +287,14 @@ size_t gated_ws_bytes(const Plan& p) {
 
 }  // namespace
 
+la_status la::record_error(la_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  const la_status r = vfail(st, fmt, ap);
+  va_end(ap);
+  return r;
+}
+
 extern "C" {
 
 int la_version(void) { return 1; }
@@ -319,9 +332,12 @@ size_t la_bwd_workspace_bytes(const la_shape* shape) {
   return bwd_ws_bytes(pl);
 }
 
-la_status la_chunk_fwd(const la_shape* s, const void* Q, const void* K, const void* V,
-                       const float* lambda, const float* S0, void* O, float* S_end, void* ws,
-                       size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+// Every check of la_chunk_fwd but the workspace's (host only, no HIP call).
+la_status la::check_fwd_args(const la_shape* s, const void* Q, const void* K, const void* V,
+                             const float* lambda, const float* S0, const void* O,
+                             const float* S_end) {
   Plan pl;
   la_status r = check_shape(s, &pl);
   if (r != LA_OK) return r;
@@ -329,9 +345,22 @@ la_status la_chunk_fwd(const la_shape* s, const void* Q, const void* K, const vo
   if (has_tokens && (!Q || !K || !V)) return fail(LA_ERR_INVALID_ARG, "Q, K and V are required");
   if (pl.nseq > 0 && !lambda) return fail(LA_ERR_INVALID_ARG, "lambda is required");
   if (!O && !S_end) return fail(LA_ERR_INVALID_ARG, "O and S_end are both NULL");
-  const void* ptrs[] = {Q, K, V, lambda, S0, O, S_end, ws};
+  const void* ptrs[] = {Q, K, V, lambda, S0, O, S_end};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return fail(LA_ERR_INVALID_ARG, "pointer %p is not 16-byte aligned", p);
+  return LA_OK;
+}
+
+extern "C" {
+
+la_status la_chunk_fwd(const la_shape* s, const void* Q, const void* K, const void* V,
+                       const float* lambda, const float* S0, void* O, float* S_end, void* ws,
+                       size_t ws_bytes, void* stream) {
+  la_status r = la::check_fwd_args(s, Q, K, V, lambda, S0, O, S_end);
+  if (r != LA_OK) return r;
+  Plan pl;
+  check_shape(s, &pl);
+  if (ws && !aligned16(ws)) return fail(LA_ERR_INVALID_ARG, "pointer %p is not 16-byte aligned", ws);
   const size_t need = scan_ws_bytes(pl);
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(LA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,

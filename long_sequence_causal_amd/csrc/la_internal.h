@@ -6,7 +6,18 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "linattn.h"
+
 namespace la {
+
+// Record the message la_last_error() returns on this thread (printf format)
+// and return st.
+la_status record_error(la_status st, const char* fmt, ...);
+
+// Every check la_chunk_fwd makes except the workspace's: host only, no HIP
+// call; LA_OK or the failing status (with la_last_error() set).
+la_status check_fwd_args(const la_shape* s, const void* Q, const void* K, const void* V,
+                         const float* lambda, const float* S0, const void* O, const float* S_end);
 
 // One launch of the chunk kernel over sub-segments [p_begin, p_begin+p_count)
 // of every one of nseq sequences.  Sequence n occupies token rows

@@ -24,7 +24,8 @@ EXPORTS = ("la_version", "la_status_str", "la_last_error", "la_fwd_workspace_byt
            "la_chunk_fwd", "la_state_scan", "la_bwd_workspace_bytes", "la_chunk_bwd",
            "la_fwd_gated_workspace_bytes", "la_chunk_fwd_gated", "la_state_scan_gated",
            "la_bwd_gated_workspace_bytes", "la_chunk_bwd_gated",
-           "la_decay_grad_workspace_bytes", "la_decay_grad", "la_step", "la_chunk_bwd_from_fwd")
+           "la_decay_grad_workspace_bytes", "la_decay_grad", "la_step", "la_chunk_bwd_from_fwd",
+           "la_chunk_fwd_noalloc")
 
 
 class LinAttnError(RuntimeError):
@@ -88,6 +89,8 @@ def lib():
     L.la_decay_grad_workspace_bytes.argtypes = [sp]
     L.la_decay_grad.restype = ctypes.c_int
     L.la_decay_grad.argtypes = [sp] + [vp] * 9 + [sz, vp]
+    L.la_chunk_fwd_noalloc.restype = ctypes.c_int
+    L.la_chunk_fwd_noalloc.argtypes = [sp] + [vp] * 8
     _lib = L
     return L
 
@@ -203,6 +206,28 @@ def la_chunk_fwd(q, k, v, lam, S0=None, nseg: int = 1, need_O: bool = True,
     _check(lib().la_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(lam),
                               _ptr(S0), _ptr(O), _ptr(S_end), _ptr(ws),
                               ws.numel() if ws is not None else 0, _stream()))
+    return O, S_end
+
+
+def la_chunk_fwd_noalloc(q, k, v, lam, O, S_end, S0=None, nseg: int = 1, split: int = 0):
+    """la_chunk_fwd into preallocated O and/or S_end (either may be None, not
+    both) with the library's fixed scratch array instead of a workspace: no
+    device memory is allocated by this call."""
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q.dtype)
+    _expect_all(
+        q.device,
+        (q, "q", (B, H, L, dk), q.dtype),
+        (k, "k", (B, H, L, dk), q.dtype),
+        (v, "v", (B, H, L, dv), q.dtype),
+        (lam, "lam", (H,), torch.float32),
+        (S0, "S0", (B, H, nseg, dk, dv), torch.float32),
+        (O, "O", (B, H, L, dv), q.dtype),
+        (S_end, "S_end", (B, H, nseg, dk, dv), torch.float32))
+    shape = make_shape(B, H, L, dk, dv, nseg, dt, split)
+    _check(lib().la_chunk_fwd_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(lam),
+                                      _ptr(S0), _ptr(O), _ptr(S_end), _stream()))
     return O, S_end
 
 
