@@ -9,8 +9,8 @@
  *     o_t = q_t^T S_t                             (output row, length d_v)
  *
  * for t = 1..L starting from the initial state S_0 and returns S_end = S_L.
- *  - The state is the "intermediate memory state whose size is independent of
- *    the sequence length" and the evaluation is right-product-first: LASP-2
+ *  - The state is the per-sequence memory state, whose size does not grow
+ *    with the sequence, and the evaluation is right-product-first: LASP-2
  *    (Rethinking Sequence Parallelism for Linear Attention and Its Hybrid),
  *    abstract.
  *  - Work is tiled into 64-token chunks: exact causal attention inside a
@@ -45,7 +45,9 @@
  *    returns LA_ERR_HIP.  la_last_error() describes the last failure of the
  *    calling thread.  No C++ exception crosses this interface.
  *  - Preconditions that are not checked (device data is not read on the
- *    host): 0 < lambda[h] <= 1.  Other values give undefined numbers (but no
+ *    host): 0 <= lambda[h] <= 1 (lambda = 0 gives lambda^0 = 1 and every
+ *    higher power 0; no entry point divides by lambda except la_decay_grad,
+ *    which needs lambda[h] > 0).  Other values give undefined numbers (but no
  *    out-of-bounds access).  NaN and Inf inputs propagate.
  *  - Outputs are fully overwritten, never accumulated into.  No input may
  *    overlap an output except where stated.
@@ -290,7 +292,10 @@ size_t la_decay_grad_workspace_bytes(const la_shape* shape);
  *     d l / d lambda = sum_t dO_t . (q_t^T T_t) + <dS_end, T_end>
  *                    = sum_t <G_t, S_{t-1}>     (G_t as in la_chunk_bwd).
  * The tangent walk is chunked like la_chunk_fwd (state and tangent fp32,
- * per-workgroup shares summed in fp64 in a fixed order).
+ * per-workgroup shares summed in fp64 in a fixed order).  It carries
+ * lambda T and divides the final sum by lambda_h, so it needs lambda_h > 0
+ * (and loses precision for lambda_h far below 1e-38, where lambda T falls
+ * into the fp32 denormals).
  *   Q, K, V, lambda, S0, shape   as for la_chunk_fwd (S0 NULL = zero).
  *   dO [B,H,L,dv]                upstream gradient of O, required.
  *   dS_end [B,H,nseg,dk,dv] fp32 upstream gradient of S_end; NULL = zero.
