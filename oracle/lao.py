@@ -18,13 +18,17 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "lao.c")
-_LIB = os.path.join(_HERE, "liblao.so")
+# LAO_LIB names another build of lao.c to load instead (e.g. one made with
+# the host sanitizers by the tests); build() never writes over it
+_LIB = os.environ.get("LAO_LIB") or os.path.join(_HERE, "liblao.so")
 
 _lib = None
 
 
 def build(force: bool = True) -> str:
     """Compile the oracle with gcc (fp64, OpenMP, no fast-math)."""
+    if os.environ.get("LAO_LIB"):
+        return _LIB
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
