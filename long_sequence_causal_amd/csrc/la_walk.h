@@ -54,6 +54,7 @@ __device__ inline void score_tile(int idx, int& jb, int& ib) {
 
 constexpr int LDS_MAX = 160 * 1024;  // per workgroup on gfx950
 
+
 // Position of token t (0..63) in a gated walk's per-chunk factor tables
 // (cumulative log-gate c_t, update weight exp(c_last - c_t)), chosen so that
 // the values a lane needs sit together: the 16 update-weight slots of MFMA
@@ -88,6 +89,7 @@ struct FwdLayout {
   static constexpr int SMAX = NSLOT == 3 ? 3 : 5;
   static constexpr int GB = GATED ? CH * 4 : 0;  // log-gates of one chunk
   static constexpr int TBL = GATED ? 2 * 2 * CH * 4 : 0;  // 2 x (cumulative gate, update weight)
+  static constexpr int NW = D / 16;  // waves: one per 16 state columns
   static constexpr int SFIT = (LDS_MAX - PBYTES - GB - TBL) / (STAGE + GB);
   static constexpr int STAGES = SFIT < SMAX ? SFIT : SMAX;
   static constexpr int OFF_P = STAGES * STAGE;
@@ -95,7 +97,6 @@ struct FwdLayout {
   static constexpr int GSLOTS = STAGES + 1;  // gate ring (gated walks)
   static constexpr int OFF_T = OFF_G + GSLOTS * GB;
   static constexpr int BYTES = OFF_T + TBL;
-  static constexpr int NW = D / 16;  // waves: one per 16 state columns
   static constexpr int NT = 64 * NW;
   // bf16 keeps two waves per SIMD (256 registers per lane)
   static constexpr int WAVES_PER_EU = sizeof(T) == 2 ? 2 : 1;
@@ -317,6 +318,15 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob& jb, f32x4 (&acc
     }
   };
   T* const Oseq = reinterpret_cast<T*>(jb.O);  // sequence base of O
+  // bf16 at d = 128 (8 waves x 16 columns, 256-byte rows): a chunk's outputs
+  // are staged in LDS and stored as whole rows with non-temporal stores (the
+  // rows are written once and never read here, so they do not displace the
+  // K, V lines the state pre-pass left in the last-level cache); storing each
+  // lane's 8-byte piece directly sends every 128-byte line to L2 in four
+  // pieces from four waves.  Measured at 64K tokens x 32 heads: whole call
+  // 582.7 -> 564.1 us (plain whole-row stores: no gain).
+  constexpr bool OSTAGE = OUT && sizeof(T) == 2 && D == 128;
+  T ohold[4][4];
   unsigned ooff0[4];  // element offset (chunk 0) of the lane's outputs in each 16-row block
   const bool und = !GATED && jb.first_undecayed;  // wave-uniform
   // lambda^(i+1) (or lambda^i for a start state that already carries the
@@ -555,18 +565,41 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob& jb, f32x4 (&acc
           }
         }
         // store: lane holds O[token i][v0 .. v0+3]
-        if (c * CH + i < len) {
+        if constexpr (OSTAGE) {
+          // held until every wave is done with the chunk's Q tile
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ohold[it][r] = X::from_f(o[r]);
+        } else if (c * CH + i < len) {
           T* orow = Oseq + (ooff0[it] + (unsigned)c * (unsigned)(cstride_b / (int)sizeof(T)));
           T ov[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) ov[r] = X::from_f(o[r]);
           if (sizeof(T) == 2)
-            // (a plain store: each instruction writes 32-byte pieces of 16
-            // rows whose other pieces come from the other waves, and L2 merges
-            // them; non-temporal stores measured far slower here)
+            // (bf16 at d = 64: 32-byte pieces of 16 rows, merged in L2)
             *reinterpret_cast<u32x2*>(orow) = *reinterpret_cast<u32x2*>(ov);
           else
             *reinterpret_cast<u32x4*>(orow) = *reinterpret_cast<u32x4*>(ov);
+        }
+      }
+      if constexpr (OSTAGE) {
+        // the chunk's O tile through the Q slot: each wave writes its 16
+        // columns of every token, then stores 8 whole rows, 16 bytes per lane
+        lds_barrier();  // every wave is done reading Q
+        char* const sO = const_cast<char*>(sQ);
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+          *reinterpret_cast<u32x2*>(sO + TN::off(16 * it + l16, col + 4 * g)) =
+              *reinterpret_cast<const u32x2*>(ohold[it]);
+        lds_barrier();
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int row = 8 * w + 4 * h + (lane >> 4);  // 16 lanes per 256-byte row
+          const int piece = lane & 15;
+          if (c * CH + row < len) {
+            const u32x4 val = *reinterpret_cast<const u32x4*>(sO + TN::off(row, 8 * piece));
+            T* orow = Oseq + (unsigned)((relrow(c * CH + row)) * D + 8 * piece);
+            __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(orow));
+          }
         }
       }
     }
