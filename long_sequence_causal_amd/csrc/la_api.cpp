@@ -133,11 +133,11 @@ size_t scan_ws_bytes(const Plan& p) {
   return (size_t)p.nseq * (size_t)(p.split - 1) * (size_t)p.D * (size_t)p.D * sizeof(float);
 }
 
-// la_chunk_bwd's workspace: two prepared start states per sequence and two
-// sets of sub-segment start states (the reverse sweeps for dV and dK run
-// together, each from its own)
+// la_chunk_bwd's workspace: two prepared start states per sequence and three
+// sets of sub-segment start states (the dQ, dV and dK sweeps run in one
+// launch, each from its own)
 size_t bwd_ws_bytes(const Plan& p) {
-  return 2 * ((size_t)p.nseq * p.D * p.D * sizeof(float) + scan_ws_bytes(p));
+  return 2 * (size_t)p.nseq * p.D * p.D * sizeof(float) + 3 * scan_ws_bytes(p);
 }
 
 la_status hip_fail(hipError_t e, const char* what) {
@@ -451,14 +451,14 @@ bool sweep_slots_valid(const Plan& c, const Plan& f, int64_t step) {
   return true;
 }
 
-// gated backward workspace (in order): prepared start state [nseq][D][D],
-// the forward sweep's start states W, the dV sweep's W2 and their transposes
-// W3 for the dK sweep (each [nseq][split-1][D][D]; W and W3 also feed the
-// anchors), the sweeps' sub-segment log-gates (reused), shifted gates
-// [nseq][Ls], the final dQ-sweep state [nseq][D][D] and one anchor per
-// 1024-token block
+// gated backward workspace (in order): the prepared start states of the dQ
+// sweep (S0^T) and of the dK sweep (dS_end^T) [nseq][D][D] each, the forward
+// sweep's start states W, the dV sweep's W2 and their transposes W3 for the
+// dK sweep (each [nseq][split-1][D][D]; W and W3 also feed the anchors), the
+// sweeps' sub-segment log-gates (reused), shifted gates [nseq][Ls], the final
+// dQ-sweep state [nseq][D][D] and one anchor per 1024-token block
 struct GatedBwdWs {
-  size_t A, W, W2, W3, LD, Gs, SE, TOT, total;
+  size_t A, A2, W, W2, W3, LD, Gs, SE, TOT, total;
 };
 GatedBwdWs gated_bwd_ws(const Plan& p0) {
   const Plan p = gated_bwd_plan(p0);
@@ -467,6 +467,7 @@ GatedBwdWs gated_bwd_ws(const Plan& p0) {
   const size_t DD4 = (size_t)p.D * p.D * sizeof(float);
   size_t o = 0;
   w.A = o;  o += up((size_t)p.nseq * DD4);
+  w.A2 = o; o += up((size_t)p.nseq * DD4);
   w.W = o;  o += up(scan_ws_bytes(p));
   w.W2 = o; o += up(scan_ws_bytes(p));
   w.W3 = o; o += up(scan_ws_bytes(p));
@@ -523,7 +524,8 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
   if (pl.nseq == 0) return LA_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);
-  float* A = reinterpret_cast<float*>(base + L.A);
+  float* A = reinterpret_cast<float*>(base + L.A);    // S0^T (dQ sweep)
+  float* A2 = reinterpret_cast<float*>(base + L.A2);  // dS_end^T (dK sweep)
   float* W = reinterpret_cast<float*>(base + L.W);    // forward sweep: S^T starts
   float* W2 = reinterpret_cast<float*>(base + L.W2);  // dV sweep: G starts
   float* W3 = reinterpret_cast<float*>(base + L.W3);  // dK sweep: G^T starts
@@ -555,14 +557,10 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
   const bool need_send = dlog_alpha && dS_end;
   r = run_states(pl, s->dtype, H, s->nseg, V, K, nullptr, start, W, 0, st, true, log_alpha, LDw);
   if (r != LA_OK) return r;
-  {
-    la::FwdArgs ma = main_args(plc, H, s->nseg, dO, V, K, nullptr, start, dQ,
-                               need_send ? SE : nullptr, W, 0, true, log_alpha);
-    ma.sws_nper = pl.split - 1;
-    ma.sws_step = (int)step;
-    if ((e = la::launch_fwd(ma, s->dtype, pl.D, true, plc.nseq * ma.p_count, st)) != hipSuccess)
-      return hip_fail(e, "chunk kernel launch");
-  }
+  la::FwdArgs aq = main_args(plc, H, s->nseg, dO, V, K, nullptr, start, dQ,
+                             need_send ? SE : nullptr, W, 0, true, log_alpha);
+  aq.sws_nper = pl.split - 1;
+  aq.sws_step = (int)step;
 
   // reverse sweeps: from token t+1 back to t with alpha_{t+1}
   if ((e = la::launch_shift_gates(log_alpha, Gs, pl.nseq, pl.Ls, st)) != hipSuccess)
@@ -571,32 +569,36 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
   // step multiplies by 1); its final value G_1 gives dS0 = alpha_1 G_1.
   // dk_t = G_t v_t: the same reverse recurrence for G^T, whose sub-segment
   // start states are the transposes of the dV sweep's.  One pre-pass and scan
-  // serve both, and the two sweeps run as one paired launch (partners share
-  // an XCD and walk the same rows, so Q and dO come from HBM about once).
+  // serve both, and the two sweeps run as partners in one launch (sharing an
+  // XCD and walking the same rows, so Q and dO come from HBM about once).
   r = run_states(plr, s->dtype, H, s->nseg, Q, dO, nullptr, dS_end, W2, 1, st, true, Gs, LDw);
   if (r != LA_OK) return r;
   if (pl.split > 1) {
     e = la::launch_transpose_copy(W2, W3, pl.nseq * (pl.split - 1), pl.D, st);
     if (e != hipSuccess) return hip_fail(e, "transpose launch");
   }
-  start = nullptr;
+  const float* startK = nullptr;
   if (dS_end) {
     pa.src = dS_end;
-    pa.dst = A;
+    pa.dst = A2;
     pa.transpose = 1;
     pa.mode = 0;
     if ((e = la::launch_prep(pa, st)) != hipSuccess) return hip_fail(e, "prep launch");
-    start = A;
+    startK = A2;
   }
   {
+    // the dQ sweep (aq) and the paired dV and dK sweeps in one launch: the
+    // start states of all three are ready, and both plans have plc.split
+    // walks per sequence
     la::FwdArgs av = main_args(plrc, H, s->nseg, K, Q, dO, nullptr, dS_end, dV, dS0, W2, 1,
                                true, Gs);
-    la::FwdArgs ak = main_args(plrc, H, s->nseg, V, dO, Q, nullptr, start, dK, nullptr, W3, 1,
+    la::FwdArgs ak = main_args(plrc, H, s->nseg, V, dO, Q, nullptr, startK, dK, nullptr, W3, 1,
                                true, Gs);
     av.sws_nper = ak.sws_nper = plr.split - 1;
     av.sws_step = ak.sws_step = (int)step;
-    if ((e = la::launch_fwd_pair(av, ak, s->dtype, pl.D, plc.nseq * plc.split, st)) != hipSuccess)
-      return hip_fail(e, "paired chunk kernel launch");
+    if ((e = la::launch_fwd_triple(aq, av, ak, s->dtype, pl.D, plc.nseq * plc.split, st)) !=
+        hipSuccess)
+      return hip_fail(e, "sweep launch");
   }
   if (dS0 && (e = la::launch_scale_first_gate(dS0, log_alpha, pl.nseq, pl.Ls, pl.D, st)) != hipSuccess)
     return hip_fail(e, "dS0 scale launch");
@@ -813,10 +815,12 @@ static la_status chunk_bwd(const la_shape* s, const void* Q, const void* K, cons
   if (pl.nseq == 0) return LA_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const size_t DDn = (size_t)pl.nseq * pl.D * pl.D;
-  float* A = static_cast<float*>(ws);             // prepared start state (dQ, then dV)
-  float* W = A + DDn;                             // sub-segment start states (dQ, then dV)
-  float* A2 = W + scan_ws_bytes(pl) / sizeof(float);  // prepared start state of dK
-  float* W2 = A2 + DDn;                           // sub-segment start states of dK
+  const size_t Wn = scan_ws_bytes(pl) / sizeof(float);
+  float* A = static_cast<float*>(ws);  // prepared start state of the dQ sweep (S0^T)
+  float* A2 = A + DDn;                 // prepared start state of the dK sweep (dS_end^T)
+  float* W = A2 + DDn;                 // sub-segment start states: dQ sweep
+  float* Wv = W + Wn;                  // dV sweep
+  float* Wk = Wv + Wn;                 // dK sweep (the dV sweep's, transposed)
   const int H = (int)s->H;
   la::PrepArgs pa;
   std::memset(&pa, 0, sizeof(pa));
@@ -828,7 +832,8 @@ static la_status chunk_bwd(const la_shape* s, const void* Q, const void* K, cons
   hipError_t e;
 
   // dq_t = S_t dO_t: the forward recurrence of S^T = sum v k^T read by dO,
-  // started from S0^T.
+  // started from S0^T; its sub-segment start states from a pre-pass and scan
+  // over (V, K), or the transposes of the ones a forward call left.
   const float* start = nullptr;
   if (S0) {
     pa.src = S0;
@@ -839,14 +844,12 @@ static la_status chunk_bwd(const la_shape* s, const void* Q, const void* K, cons
     start = A;
   }
   if (from_fwd && pl.split > 1) {
-    // the forward's start states, transposed: S^T starts of the dQ sweep
     e = la::launch_transpose_copy(fwd_starts, W, pl.nseq * (pl.split - 1), pl.D, st);
     if (e != hipSuccess) return hip_fail(e, "transpose launch");
-    r = run_main(pl, s->dtype, H, s->nseg, dO, V, K, lambda, start, dQ, nullptr, W, 0, st);
   } else {
-    r = run_flow(pl, s->dtype, H, s->nseg, dO, V, K, lambda, start, dQ, nullptr, W, 0, st);
+    r = run_states(pl, s->dtype, H, s->nseg, V, K, lambda, start, W, 0, st);
+    if (r != LA_OK) return r;
   }
-  if (r != LA_OK) return r;
 
   // dv_t = G_t^T k_t: in reverse time G accumulates q dO^T like a state.
   // Its seed dS_end = lambda G_{L+1} already carries the decay of the first
@@ -855,9 +858,7 @@ static la_status chunk_bwd(const la_shape* s, const void* Q, const void* K, cons
   // dS0 = lambda G_1.  dk_t = G_t v_t: the same reverse recurrence for G^T =
   // sum dO q^T over the same pairs (q_t, dO_t) with the roles swapped, seeded
   // with the transposed seed, so its sub-segment start states are the
-  // transposes of the dV sweep's: one pre-pass and scan serve both.  The two
-  // sweeps then run as one paired launch, partners on one XCD walking the
-  // same rows, so that Q and dO, which both read, come from HBM about once.
+  // transposes of the dV sweep's: one pre-pass and scan serve both.
   const float* startK = nullptr;
   if (dS_end) {
     pa.src = dS_end;
@@ -867,20 +868,27 @@ static la_status chunk_bwd(const la_shape* s, const void* Q, const void* K, cons
     if ((e = la::launch_prep(pa, st)) != hipSuccess) return hip_fail(e, "prep launch");
     startK = A2;
   }
-  r = run_states(pl, s->dtype, H, s->nseg, Q, dO, lambda, dS_end, W, 1, st, false, nullptr,
+  r = run_states(pl, s->dtype, H, s->nseg, Q, dO, lambda, dS_end, Wv, 1, st, false, nullptr,
                  nullptr, true);
   if (r != LA_OK) return r;
   if (pl.split > 1) {
-    e = la::launch_transpose_copy(W, W2, pl.nseq * (pl.split - 1), pl.D, st);
+    e = la::launch_transpose_copy(Wv, Wk, pl.nseq * (pl.split - 1), pl.D, st);
     if (e != hipSuccess) return hip_fail(e, "transpose launch");
   }
-  la::FwdArgs av = main_args(pl, H, s->nseg, K, Q, dO, lambda, dS_end, dV, dS0, W, 1, false,
+
+  // The three sweeps as one launch: the dV and dK sweeps walk the same rows
+  // and both read Q and dO, so they run as XCD partners (Q and dO come from
+  // HBM about once); the dQ sweep's walks run beside them.
+  const la::FwdArgs aq = main_args(pl, H, s->nseg, dO, V, K, lambda, start, dQ, nullptr, W, 0,
+                                   false, nullptr);
+  la::FwdArgs av = main_args(pl, H, s->nseg, K, Q, dO, lambda, dS_end, dV, dS0, Wv, 1, false,
                              nullptr);
-  la::FwdArgs ak = main_args(pl, H, s->nseg, V, dO, Q, lambda, startK, dK, nullptr, W2, 1,
+  la::FwdArgs ak = main_args(pl, H, s->nseg, V, dO, Q, lambda, startK, dK, nullptr, Wk, 1,
                              false, nullptr);
   av.s0_undecayed = ak.s0_undecayed = 1;
-  if ((e = la::launch_fwd_pair(av, ak, s->dtype, pl.D, pl.nseq * pl.split, st)) != hipSuccess)
-    return hip_fail(e, "paired chunk kernel launch");
+  if ((e = la::launch_fwd_triple(aq, av, ak, s->dtype, pl.D, pl.nseq * pl.split, st)) !=
+      hipSuccess)
+    return hip_fail(e, "sweep launch");
   // (with no tokens the sweep's final state is its seed, dS0 = dS_end: no factor)
   if (dS0 && pl.Ls > 0) {
     pa.src = dS0;

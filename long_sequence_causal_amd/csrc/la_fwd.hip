@@ -119,6 +119,57 @@ __global__ __launch_bounds__((FwdLayout<T, D, 3, GATED>::NT),
     chunk_item<T, D, true, GATED>(b, item);
 }
 
+// Three launches with outputs over nitems work items each as one grid, in
+// groups of 24 workgroups: blocks 24 j + r run item 8 j + r of a (r < 8), of
+// b (8 <= r < 16) and of c (r >= 16), so b's and c's items keep the pair
+// kernel's XCD sharing (blocks 8 apart) while a's walks run beside them.  The
+// backward uses it for its dQ sweep (a) and the dV and dK sweeps (b, c): the
+// paired sweeps are bound by the latency of their walks rather than by HBM,
+// the dQ sweep by HBM, so side by side they share the chip's time better than
+// one after the other.
+template <typename T, int D, bool GATED>
+__global__ __launch_bounds__((FwdLayout<T, D, 3, GATED>::NT),
+                             (FwdLayout<T, D, 3, GATED>::WAVES_PER_EU)) void k_chunk_fwd_triple(
+    FwdArgs a, FwdArgs b, FwdArgs c, int64_t nitems) {
+  const int64_t blk = blockIdx.x;
+  const int r = (int)(blk % 24);
+  const int64_t item = 8 * (blk / 24) + (r % 8);
+  if (item >= nitems) return;
+  if (r < 8)
+    chunk_item<T, D, true, GATED>(a, item);
+  else if (r < 16)
+    chunk_item<T, D, true, GATED>(b, item);
+  else
+    chunk_item<T, D, true, GATED>(c, item);
+}
+
+template <typename T, int D>
+static hipError_t launch_triple_t(const FwdArgs& a, const FwdArgs& b, const FwdArgs& c,
+                                  int64_t nitems, hipStream_t s) {
+  const unsigned grid = (unsigned)(24 * ((nitems + 7) / 8));
+  if (a.gated)
+    hipLaunchKernelGGL((k_chunk_fwd_triple<T, D, true>), dim3(grid),
+                       dim3(FwdLayout<T, D, 3, true>::NT), 0, s, a, b, c, nitems);
+  else
+    hipLaunchKernelGGL((k_chunk_fwd_triple<T, D, false>), dim3(grid),
+                       dim3(FwdLayout<T, D, 3, false>::NT), 0, s, a, b, c, nitems);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_triple(const FwdArgs& a, const FwdArgs& b, const FwdArgs& c, int dtype,
+                             int D, int64_t nitems, hipStream_t s) {
+  if (nitems <= 0) return hipSuccess;
+  if (a.gated != b.gated || a.gated != c.gated) return hipErrorInvalidValue;
+  if (dtype == 0) {
+    if (D == 64) return launch_triple_t<__bf16, 64>(a, b, c, nitems, s);
+    if (D == 128) return launch_triple_t<__bf16, 128>(a, b, c, nitems, s);
+  } else {
+    if (D == 64) return launch_triple_t<float, 64>(a, b, c, nitems, s);
+    if (D == 128) return launch_triple_t<float, 128>(a, b, c, nitems, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <typename T, int D, bool GATED>
 static hipError_t launch_fwd_t(const FwdArgs& a, bool with_o, int64_t nwg, hipStream_t s) {
   if (with_o)

@@ -159,6 +159,11 @@ hipError_t launch_fwd_pair(const FwdArgs& a, const FwdArgs& b, int dtype, int D,
                            hipStream_t stream);
 hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, bool with_o, int64_t nwg,
                       hipStream_t stream);
+// Three chunk-kernel launches with outputs over nitems work items each as one
+// grid (la_fwd.hip): a's items beside the XCD-paired items of b and c;
+// a.gated == b.gated == c.gated.
+hipError_t launch_fwd_triple(const FwdArgs& a, const FwdArgs& b, const FwdArgs& c, int dtype,
+                             int D, int64_t nitems, hipStream_t stream);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
 // dst[m] = src[m]^T for nmat consecutive D x D fp32 matrices (no overlap).
 hipError_t launch_transpose_copy(const float* src, float* dst, int64_t nmat, int D,

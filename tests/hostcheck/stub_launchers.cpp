@@ -52,6 +52,18 @@ hipError_t launch_fwd_pair(const FwdArgs& a, const FwdArgs& b, int, int, int64_t
   return hipSuccess;
 }
 
+hipError_t launch_fwd_triple(const FwdArgs& a, const FwdArgs& b, const FwdArgs& c, int, int,
+                             int64_t nitems, hipStream_t) {
+  if (nitems <= 0) return hipSuccess;
+  check_fwd(a, nitems);
+  check_fwd(b, nitems);
+  check_fwd(c, nitems);
+  expect(a.gated == b.gated && a.gated == c.gated, "triple of one kind");
+  expect(a.Q && a.O && b.Q && b.O && c.Q && c.O, "outputs of all three");
+  ++g_launches;
+  return hipSuccess;
+}
+
 hipError_t launch_scan(const ScanArgs& a, hipStream_t) {
   expect(a.nseq >= 0 && a.P >= 0 && a.E > 0, "scan sizes");
   if (a.P > 0) expect(a.dS && a.Sout, "scan buffers");

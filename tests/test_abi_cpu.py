@@ -150,9 +150,10 @@ def test_automatic_plan_takes_a_second_round_only_for_long_walks():
     assert ws(1, 16, 1 << 20, nseg=64) == 0
     # an explicit split is taken as given
     assert ws(1, 16, 262144, split=16) == 16 * 15 * state
-    # the backward follows the same plan: two prepared states and two sets of starts
+    # the backward follows the same plan: two prepared states and three sets
+    # of starts (dQ, dV and dK sweeps)
     s = la.make_shape(1, 16, 262144, 128, 128, 1, la.LA_BF16, 0)
-    assert la.la_bwd_workspace_bytes(s) == 2 * (16 * state + 16 * 31 * state)
+    assert la.la_bwd_workspace_bytes(s) == 2 * 16 * state + 3 * 16 * 31 * state
     # the decay gradient's tangent walks keep one round: (S, U) starts and one
     # fp64 share per sub-segment
     assert la.la_decay_grad_workspace_bytes(s) == 2 * 16 * 15 * state + 16 * 16 * 8
@@ -193,7 +194,9 @@ def test_bwd_rejects_bad_arguments():
     # together), no sub-segment states at split 1
     assert need == 2 * (2 * 64 * 64 * 4)
     s4 = _shape(split=2)
-    assert la.la_bwd_workspace_bytes(s4) == 2 * (2 * 64 * 64 * 4 + 2 * 1 * 64 * 64 * 4)
+    # ... and three sets of sub-segment start states (dQ, dV and dK sweeps,
+    # which run in one launch)
+    assert la.la_bwd_workspace_bytes(s4) == 2 * (2 * 64 * 64 * 4) + 3 * (2 * 1 * 64 * 64 * 4)
     assert call(ws=None) == la.LA_ERR_WORKSPACE
     assert call(ws=FAKE, nb=need - 16) == la.LA_ERR_WORKSPACE
 
@@ -222,12 +225,12 @@ def test_gated_entry_points_validate_on_the_host():
 
 def test_gated_backward_workspace_follows_the_1024_token_plan():
     # L = 5000 -> 79 chunks -> 5 sub-segments of 1024 tokens whatever split asks;
-    # d = 64: a state is 16 KiB.  Blocks (256-byte aligned): prepared start
-    # state, the sweeps' start states (4 each: forward, dV, dV transposed for
+    # d = 64: a state is 16 KiB.  Blocks (256-byte aligned): two prepared start
+    # states, the sweeps' start states (4 each: forward, dV, dV transposed for
     # dK), their log-gates, the shifted gates, S_end and one anchor per block.
     DD4, nseq, Ls = 64 * 64 * 4, 2, 5000
     up = lambda x: -(-x // 256) * 256
-    want = (up(nseq * DD4) + 3 * up(nseq * 4 * DD4) + up(nseq * 4 * 4) + up(nseq * Ls * 4)
+    want = (2 * up(nseq * DD4) + 3 * up(nseq * 4 * DD4) + up(nseq * 4 * 4) + up(nseq * Ls * 4)
             + up(nseq * DD4) + up(nseq * 5 * 4))
     for split in (0, 1, 3, 40):
         assert la.la_bwd_gated_workspace_bytes(_shape(L=Ls, split=split)) == want
