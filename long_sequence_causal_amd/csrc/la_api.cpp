@@ -262,6 +262,23 @@ la_status run_flow(const Plan& pl, int dtype, int H, int nseg, const void* Q, co
   return run_main(pl, dtype, H, nseg, Q, K, V, lam, start, O, Send, W, reverse, st, gated, G);
 }
 
+// The backward's three sweeps from their start states (aq: dQ; av, ak: dV
+// and dK, whose keys and values are crosswise the same Q and dO).  bf16: the
+// dQ sweep, then one workgroup per item walking both dV and dK over one
+// stream of Q, K, V, dO tiles (4 tile loads per chunk instead of 6, one set
+// of barriers and decay factors for two walks).  fp32, and gated d = 64
+// (whose joint walk has no spare load slot for the gates): one launch of
+// the three, the paired dV and dK workgroups on one XCD beside the dQ walks.
+hipError_t launch_sweeps(const la::FwdArgs& aq, const la::FwdArgs& av, const la::FwdArgs& ak,
+                         int dtype, int D, int64_t nitems, hipStream_t st) {
+  if (dtype == LA_BF16 && !(aq.gated && D == 64)) {
+    hipError_t e = la::launch_fwd(aq, dtype, D, true, nitems, st);
+    if (e != hipSuccess) return e;
+    return la::launch_fwd_duo(av, ak, dtype, D, nitems, st);
+  }
+  return la::launch_fwd_triple(aq, av, ak, dtype, D, nitems, st);
+}
+
 // Workspace of la_decay_grad: the local, then start, pairs (S, U) of
 // sub-segments 1..split-1 (S and U in separate blocks) and one fp64 share per
 // sub-segment.
@@ -569,8 +586,8 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
   // step multiplies by 1); its final value G_1 gives dS0 = alpha_1 G_1.
   // dk_t = G_t v_t: the same reverse recurrence for G^T, whose sub-segment
   // start states are the transposes of the dV sweep's.  One pre-pass and scan
-  // serve both, and the two sweeps run as partners in one launch (sharing an
-  // XCD and walking the same rows, so Q and dO come from HBM about once).
+  // serve both, and the two sweeps share their Q and dO reads
+  // (launch_sweeps).
   r = run_states(plr, s->dtype, H, s->nseg, Q, dO, nullptr, dS_end, W2, 1, st, true, Gs, LDw);
   if (r != LA_OK) return r;
   if (pl.split > 1) {
@@ -587,17 +604,16 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
     startK = A2;
   }
   {
-    // the dQ sweep (aq) and the paired dV and dK sweeps in one launch: the
-    // start states of all three are ready, and both plans have plc.split
-    // walks per sequence
+    // the dQ sweep (aq) and the dV and dK sweeps (launch_sweeps): the start
+    // states of all three are ready, and both plans have plc.split walks
+    // per sequence
     la::FwdArgs av = main_args(plrc, H, s->nseg, K, Q, dO, nullptr, dS_end, dV, dS0, W2, 1,
                                true, Gs);
     la::FwdArgs ak = main_args(plrc, H, s->nseg, V, dO, Q, nullptr, startK, dK, nullptr, W3, 1,
                                true, Gs);
     av.sws_nper = ak.sws_nper = plr.split - 1;
     av.sws_step = ak.sws_step = (int)step;
-    if ((e = la::launch_fwd_triple(aq, av, ak, s->dtype, pl.D, plc.nseq * plc.split, st)) !=
-        hipSuccess)
+    if ((e = launch_sweeps(aq, av, ak, s->dtype, pl.D, plc.nseq * plc.split, st)) != hipSuccess)
       return hip_fail(e, "sweep launch");
   }
   if (dS0 && (e = la::launch_scale_first_gate(dS0, log_alpha, pl.nseq, pl.Ls, pl.D, st)) != hipSuccess)
@@ -858,7 +874,8 @@ static la_status chunk_bwd(const la_shape* s, const void* Q, const void* K, cons
   // dS0 = lambda G_1.  dk_t = G_t v_t: the same reverse recurrence for G^T =
   // sum dO q^T over the same pairs (q_t, dO_t) with the roles swapped, seeded
   // with the transposed seed, so its sub-segment start states are the
-  // transposes of the dV sweep's: one pre-pass and scan serve both.
+  // transposes of the dV sweep's: one set of local states and one scan serve
+  // both.
   const float* startK = nullptr;
   if (dS_end) {
     pa.src = dS_end;
@@ -868,27 +885,68 @@ static la_status chunk_bwd(const la_shape* s, const void* Q, const void* K, cons
     if ((e = la::launch_prep(pa, st)) != hipSuccess) return hip_fail(e, "prep launch");
     startK = A2;
   }
-  r = run_states(pl, s->dtype, H, s->nseg, Q, dO, lambda, dS_end, Wv, 1, st, false, nullptr,
-                 nullptr, true);
-  if (r != LA_OK) return r;
-  if (pl.split > 1) {
-    e = la::launch_transpose_copy(Wv, Wk, pl.nseq * (pl.split - 1), pl.D, st);
-    if (e != hipSuccess) return hip_fail(e, "transpose launch");
+  const la::FwdArgs aq0 = main_args(pl, H, s->nseg, dO, V, K, lambda, start, dQ, nullptr, W, 0,
+                                    false, nullptr);
+  if (s->dtype == LA_BF16) {
+    // The reverse sweeps cut each sequence at the forward one's rows (the
+    // short sub-segment first in reverse time), and the dQ sweep, which
+    // streams dO anyway, forms their local states U = sum_t lambda^(t - t0)
+    // q_t dO_t^T on its way (four tiles a stage: dO, V, K, Q); then the
+    // reverse scan, and the dV and dK sweeps as one workgroup per item.
+    Plan plr = pl;
+    plr.ragged_first = true;
+    if (pl.split > 1) {
+      la::FwdArgs aq = aq0;
+      aq.Q2 = Q;
+      aq.Uout = Wv;
+      if ((e = la::launch_fwd_u(aq, s->dtype, pl.D, pl.nseq * pl.split, st)) != hipSuccess)
+        return hip_fail(e, "dQ sweep launch");
+      la::ScanArgs sa;
+      std::memset(&sa, 0, sizeof(sa));
+      sa.nseq = pl.nseq;
+      sa.P = pl.split - 1;
+      sa.E = (int64_t)pl.D * pl.D;
+      sa.dS = Wv;
+      sa.lam = lambda;
+      sa.H = H;
+      sa.hdiv = s->nseg;
+      sa.seg_len = pl.Lp;
+      sa.first_len = pl.Ls - (int64_t)(pl.split - 1) * pl.Lp;
+      sa.S0 = dS_end;
+      sa.Sout = Wv;
+      sa.inclusive = 1;
+      sa.s0_undecayed = 1;
+      if ((e = la::launch_scan(sa, st)) != hipSuccess) return hip_fail(e, "state scan launch");
+      e = la::launch_transpose_copy(Wv, Wk, pl.nseq * (pl.split - 1), pl.D, st);
+      if (e != hipSuccess) return hip_fail(e, "transpose launch");
+    } else if ((e = la::launch_fwd(aq0, s->dtype, pl.D, true, pl.nseq, st)) != hipSuccess) {
+      return hip_fail(e, "dQ sweep launch");
+    }
+    la::FwdArgs av = main_args(plr, H, s->nseg, K, Q, dO, lambda, dS_end, dV, dS0, Wv, 1, false,
+                               nullptr);
+    la::FwdArgs ak = main_args(plr, H, s->nseg, V, dO, Q, lambda, startK, dK, nullptr, Wk, 1,
+                               false, nullptr);
+    av.s0_undecayed = ak.s0_undecayed = 1;
+    if ((e = la::launch_fwd_duo(av, ak, s->dtype, pl.D, pl.nseq * pl.split, st)) != hipSuccess)
+      return hip_fail(e, "dV/dK sweep launch");
+  } else {
+    // fp32: a pre-pass over (Q, dO) and the scan give the reverse start
+    // states, then the three sweeps in one launch
+    r = run_states(pl, s->dtype, H, s->nseg, Q, dO, lambda, dS_end, Wv, 1, st, false, nullptr,
+                   nullptr, true);
+    if (r != LA_OK) return r;
+    if (pl.split > 1) {
+      e = la::launch_transpose_copy(Wv, Wk, pl.nseq * (pl.split - 1), pl.D, st);
+      if (e != hipSuccess) return hip_fail(e, "transpose launch");
+    }
+    la::FwdArgs av = main_args(pl, H, s->nseg, K, Q, dO, lambda, dS_end, dV, dS0, Wv, 1, false,
+                               nullptr);
+    la::FwdArgs ak = main_args(pl, H, s->nseg, V, dO, Q, lambda, startK, dK, nullptr, Wk, 1,
+                               false, nullptr);
+    av.s0_undecayed = ak.s0_undecayed = 1;
+    if ((e = launch_sweeps(aq0, av, ak, s->dtype, pl.D, pl.nseq * pl.split, st)) != hipSuccess)
+      return hip_fail(e, "sweep launch");
   }
-
-  // The three sweeps as one launch: the dV and dK sweeps walk the same rows
-  // and both read Q and dO, so they run as XCD partners (Q and dO come from
-  // HBM about once); the dQ sweep's walks run beside them.
-  const la::FwdArgs aq = main_args(pl, H, s->nseg, dO, V, K, lambda, start, dQ, nullptr, W, 0,
-                                   false, nullptr);
-  la::FwdArgs av = main_args(pl, H, s->nseg, K, Q, dO, lambda, dS_end, dV, dS0, Wv, 1, false,
-                             nullptr);
-  la::FwdArgs ak = main_args(pl, H, s->nseg, V, dO, Q, lambda, startK, dK, nullptr, Wk, 1,
-                             false, nullptr);
-  av.s0_undecayed = ak.s0_undecayed = 1;
-  if ((e = la::launch_fwd_triple(aq, av, ak, s->dtype, pl.D, pl.nseq * pl.split, st)) !=
-      hipSuccess)
-    return hip_fail(e, "sweep launch");
   // (with no tokens the sweep's final state is its seed, dS0 = dS_end: no factor)
   if (dS0 && pl.Ls > 0) {
     pa.src = dS0;

@@ -18,12 +18,14 @@ __device__ inline int64_t sws_slot(const FwdArgs& a, int p) {
                         : (int64_t)p * a.sws_step - 1;
 }
 
-// Work item `wg` of a launch over a: sub-segment p_begin + wg % p_count of
-// sequence wg / p_count.
-template <typename T, int D, bool WITH_O, bool GATED>
-__device__ __forceinline__ void chunk_item(const FwdArgs& a, int64_t wg) {
-  constexpr int NSLOT = WITH_O ? 3 : 2;
-  typedef FwdLayout<T, D, NSLOT, GATED> LY;
+// Work item `wg` of a launch over a0: sub-segment p_begin + wg % p_count of
+// sequence wg / p_count.  NH = 2: the same item of a1 as well, walked by
+// the same waves beside it (a1 has a0's plan, positions and decay, and a0's
+// values and keys as its keys and values).
+template <typename T, int D, bool WITH_O, bool GATED, int NH = 1, bool ACCU = false>
+__device__ __forceinline__ void chunk_item(const FwdArgs& a0, const FwdArgs& a1, int64_t wg) {
+  constexpr int NSLOT = (NH == 2 || ACCU) ? 4 : (WITH_O ? 3 : 2);
+  typedef FwdLayout<T, D, NSLOT, GATED, NH> LY;
   constexpr int NKT = D / 16;
   __shared__ __attribute__((aligned(1024))) char smem[LY::BYTES];
 
@@ -33,6 +35,7 @@ __device__ __forceinline__ void chunk_item(const FwdArgs& a, int64_t wg) {
   const int col = 16 * __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
 
   // ---- work item: sub-segment p of sequence n
+  const FwdArgs& a = a0;  // the plan (shared by a1)
   const int64_t n = wg / a.p_count;
   const int p = a.p_begin + (int)(wg % a.p_count);
   const int h = (int)((n / a.nseg) % a.H);
@@ -45,51 +48,78 @@ __device__ __forceinline__ void chunk_item(const FwdArgs& a, int64_t wg) {
     t1 = (t0 + a.Lp < a.Ls) ? t0 + a.Lp : a.Ls;
   }
   const int64_t seq_elem0 = n * a.Ls * D;
-  WalkJob jb;
-  jb.Q = WITH_O ? (const void*)(reinterpret_cast<const T*>(a.Q) + seq_elem0) : nullptr;
-  jb.K = reinterpret_cast<const T*>(a.K) + seq_elem0;
-  jb.V = reinterpret_cast<const T*>(a.V) + seq_elem0;
-  jb.O = WITH_O ? (void*)(reinterpret_cast<T*>(a.O) + seq_elem0) : nullptr;
-  jb.t0 = t0;
-  jb.len = (int)((t1 > t0) ? t1 - t0 : 0);
-  jb.Ls = a.Ls;
-  jb.reverse = a.reverse;
-  jb.lg = GATED ? 0.0f : log2f(a.lam[h]);
-  jb.G = GATED ? a.G + n * a.Ls : nullptr;
-  jb.last_chunk_first = a.last_chunk_first;
-  jb.first_undecayed = !GATED && a.s0_undecayed && a.start_from_state && p == 0;
+  WalkJob jb[NH];
+  f32x4 accS[NH][NKT];
+#pragma unroll
+  for (int u = 0; u < NH; ++u) {
+    const FwdArgs& x = u ? a1 : a0;
+    jb[u].Q = WITH_O ? (const void*)(reinterpret_cast<const T*>(x.Q) + seq_elem0) : nullptr;
+    jb[u].K = reinterpret_cast<const T*>(x.K) + seq_elem0;
+    jb[u].V = reinterpret_cast<const T*>(x.V) + seq_elem0;
+    jb[u].O = WITH_O ? (void*)(reinterpret_cast<T*>(x.O) + seq_elem0) : nullptr;
+    jb[u].t0 = t0;
+    jb[u].len = (int)((t1 > t0) ? t1 - t0 : 0);
+    jb[u].Ls = a.Ls;
+    jb[u].reverse = a.reverse;
+    jb[u].lg = GATED ? 0.0f : log2f(a.lam[h]);
+    jb[u].G = GATED ? a.G + n * a.Ls : nullptr;
+    jb[u].last_chunk_first = a.last_chunk_first;
+    jb[u].first_undecayed = !GATED && x.s0_undecayed && x.start_from_state && p == 0;
 
-  // ---- start state -> accumulators (wave w: columns [16 w, 16 w + 16))
-  f32x4 accS[NKT];
-  {
+    // ---- start state -> accumulators (wave w: columns [16 w, 16 w + 16))
     const float* sp = nullptr;
-    if (a.start_from_state) {
+    if (x.start_from_state) {
       if (p == 0)
-        sp = a.S0 ? a.S0 + n * D * D : nullptr;
+        sp = x.S0 ? x.S0 + n * D * D : nullptr;
       else
-        sp = a.Sws + (n * a.sws_nper + sws_slot(a, p)) * (int64_t)D * D;
+        sp = x.Sws + (n * x.sws_nper + sws_slot(x, p)) * (int64_t)D * D;
     }
 #pragma unroll
     for (int tk = 0; tk < NKT; ++tk)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        accS[tk][r] = sp ? sp[(16 * tk + 4 * g + r) * D + col + l16] : 0.0f;
-    // Retire these loads here, visibly to the compiler (vmcnt(0) only):
-    // otherwise it waits for them at their first use inside the chunk loop,
-    // i.e. on every chunk, which would also drain the chunk prefetches.
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+        accS[u][tk][r] = sp ? sp[(16 * tk + 4 * g + r) * D + col + l16] : 0.0f;
+  }
+  f32x4 accU[NKT];
+  if constexpr (ACCU) {
+    jb[0].Q2 = reinterpret_cast<const T*>(a.Q2) + seq_elem0;
+#pragma unroll
+    for (int tk = 0; tk < NKT; ++tk) accU[tk] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  if constexpr (NH == 2) {
+    jb[0].src4[0] = jb[0].Q;
+    jb[0].src4[1] = jb[1].Q;
+    jb[0].src4[2] = jb[0].K;
+    jb[0].src4[3] = jb[0].V;
+  }
+  // Retire the start-state loads here, visibly to the compiler (vmcnt(0)
+  // only): otherwise it waits for them at their first use inside the chunk
+  // loop, i.e. on every chunk, which would also drain the chunk prefetches.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
+  const float lgate = walk<T, D, WITH_O, NSLOT, GATED, NH>(smem, jb, accS, accU);
+  if constexpr (ACCU) {
+    if (p >= 1) {
+      float* dst = a.Uout + (n * (a.split - 1) + (a.split - 1 - p)) * (int64_t)D * D;
+#pragma unroll
+      for (int tk = 0; tk < NKT; ++tk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[(16 * tk + 4 * g + r) * D + col + l16] = accU[tk][r];
+    }
   }
 
-  const float lgate = walk<T, D, WITH_O, NSLOT, GATED>(smem, jb, accS);
-
   // ---- final state of this sub-segment (and its total log-gate)
-  if (a.Sout && p >= a.sout_p0 && p < a.sout_p0 + a.sout_np) {
-    if (GATED && a.LDout && threadIdx.x == 0) a.LDout[n * a.sout_np + (p - a.sout_p0)] = lgate;
-    float* dst = a.Sout + (n * a.sout_np + (p - a.sout_p0)) * (int64_t)D * D;
 #pragma unroll
-    for (int tk = 0; tk < NKT; ++tk)
+  for (int u = 0; u < NH; ++u) {
+    const FwdArgs& x = u ? a1 : a0;
+    if (x.Sout && p >= x.sout_p0 && p < x.sout_p0 + x.sout_np) {
+      if (GATED && x.LDout && threadIdx.x == 0) x.LDout[n * x.sout_np + (p - x.sout_p0)] = lgate;
+      float* dst = x.Sout + (n * x.sout_np + (p - x.sout_p0)) * (int64_t)D * D;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dst[(16 * tk + 4 * g + r) * D + col + l16] = accS[tk][r];
+      for (int tk = 0; tk < NKT; ++tk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dst[(16 * tk + 4 * g + r) * D + col + l16] = accS[u][tk][r];
+    }
   }
 }
 
@@ -97,7 +127,7 @@ template <typename T, int D, bool WITH_O, bool GATED>
 __global__ __launch_bounds__((FwdLayout<T, D, WITH_O ? 3 : 2, GATED>::NT),
                              (FwdLayout<T, D, WITH_O ? 3 : 2, GATED>::WAVES_PER_EU)) void k_chunk_fwd(
     FwdArgs a) {
-  chunk_item<T, D, WITH_O, GATED>(a, blockIdx.x);
+  chunk_item<T, D, WITH_O, GATED>(a, a, blockIdx.x);
 }
 
 // Two launches over the same number of work items in one grid, interleaved
@@ -114,9 +144,9 @@ __global__ __launch_bounds__((FwdLayout<T, D, 3, GATED>::NT),
   const int64_t item = 8 * (blk / 16) + (blk % 8);
   if (item >= nitems) return;
   if ((blk & 8) == 0)
-    chunk_item<T, D, true, GATED>(a, item);
+    chunk_item<T, D, true, GATED>(a, a, item);
   else
-    chunk_item<T, D, true, GATED>(b, item);
+    chunk_item<T, D, true, GATED>(b, b, item);
 }
 
 // Three launches with outputs over nitems work items each as one grid, in
@@ -136,11 +166,11 @@ __global__ __launch_bounds__((FwdLayout<T, D, 3, GATED>::NT),
   const int64_t item = 8 * (blk / 24) + (r % 8);
   if (item >= nitems) return;
   if (r < 8)
-    chunk_item<T, D, true, GATED>(a, item);
+    chunk_item<T, D, true, GATED>(a, a, item);
   else if (r < 16)
-    chunk_item<T, D, true, GATED>(b, item);
+    chunk_item<T, D, true, GATED>(b, b, item);
   else
-    chunk_item<T, D, true, GATED>(c, item);
+    chunk_item<T, D, true, GATED>(c, c, item);
 }
 
 template <typename T, int D>
@@ -168,6 +198,69 @@ hipError_t launch_fwd_triple(const FwdArgs& a, const FwdArgs& b, const FwdArgs& 
     if (D == 128) return launch_triple_t<float, 128>(a, b, c, nitems, s);
   }
   return hipErrorInvalidValue;
+}
+
+// Two launches with outputs over the same work items whose recurrences have
+// crosswise keys and values (b.K = a.V, b.V = a.K: the backward's dV and dK
+// sweeps, both over q dO^T) as one workgroup per item, every wave walking
+// its columns of both: one stream of four tiles per chunk feeds both.
+template <typename T, int D, bool GATED>
+__global__ __launch_bounds__((FwdLayout<T, D, 4, GATED, 2>::NT),
+                             (FwdLayout<T, D, 4, GATED, 2>::WAVES_PER_EU)) void k_chunk_fwd_duo(
+    FwdArgs a, FwdArgs b) {
+  chunk_item<T, D, true, GATED, 2>(a, b, blockIdx.x);
+}
+
+template <typename T, int D>
+static hipError_t launch_duo_t(const FwdArgs& a, const FwdArgs& b, int64_t nitems, hipStream_t s) {
+  if (a.gated) {
+    // (d = 64: 36 tile loads over 4 waves leave no wave a spare slot for
+    // the gates' load; those sweeps keep their own workgroups)
+    if constexpr (D == 64) return hipErrorInvalidValue;
+    else
+      hipLaunchKernelGGL((k_chunk_fwd_duo<T, D, true>), dim3((unsigned)nitems),
+                         dim3(FwdLayout<T, D, 4, true, 2>::NT), 0, s, a, b);
+  } else
+    hipLaunchKernelGGL((k_chunk_fwd_duo<T, D, false>), dim3((unsigned)nitems),
+                       dim3(FwdLayout<T, D, 4, false, 2>::NT), 0, s, a, b);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_duo(const FwdArgs& a, const FwdArgs& b, int dtype, int D, int64_t nitems,
+                          hipStream_t s) {
+  if (nitems <= 0) return hipSuccess;
+  // one plan and decay, crosswise keys and values
+  if (a.gated != b.gated || a.G != b.G || a.K != b.V || a.V != b.K || a.lam != b.lam ||
+      a.H != b.H || a.nseg != b.nseg || a.Ls != b.Ls || a.Lp != b.Lp || a.split != b.split ||
+      a.p_begin != b.p_begin || a.p_count != b.p_count || a.reverse != b.reverse ||
+      a.ragged_first != b.ragged_first || a.last_chunk_first != b.last_chunk_first)
+    return hipErrorInvalidValue;
+  if (dtype != 0) return hipErrorInvalidValue;  // bf16 only
+  if (D == 64) return launch_duo_t<__bf16, 64>(a, b, nitems, s);
+  if (D == 128) return launch_duo_t<__bf16, 128>(a, b, nitems, s);
+  return hipErrorInvalidValue;
+}
+
+// The chunk kernel with outputs whose walks also form each sub-segment's U
+// (fixed decay; four tiles a stage: Q, K, V and Q2).
+template <typename T, int D>
+__global__ __launch_bounds__((FwdLayout<T, D, 4, false>::NT),
+                             (FwdLayout<T, D, 4, false>::WAVES_PER_EU)) void k_chunk_fwd_u(FwdArgs a) {
+  chunk_item<T, D, true, false, 1, true>(a, a, blockIdx.x);
+}
+
+hipError_t launch_fwd_u(const FwdArgs& a, int dtype, int D, int64_t nitems, hipStream_t s) {
+  if (nitems <= 0) return hipSuccess;
+  if (a.gated || !a.Q2 || !a.Uout || !a.O) return hipErrorInvalidValue;
+  if (dtype == 0 && D == 64)
+    hipLaunchKernelGGL((k_chunk_fwd_u<__bf16, 64>), dim3((unsigned)nitems),
+                       dim3(FwdLayout<__bf16, 64, 4, false>::NT), 0, s, a);
+  else if (dtype == 0 && D == 128)
+    hipLaunchKernelGGL((k_chunk_fwd_u<__bf16, 128>), dim3((unsigned)nitems),
+                       dim3(FwdLayout<__bf16, 128, 4, false>::NT), 0, s, a);
+  else
+    return hipErrorInvalidValue;  // bf16 only
+  return hipGetLastError();
 }
 
 template <typename T, int D, bool GATED>

@@ -75,6 +75,12 @@ struct FwdArgs {
   // first (the state a sub-segment ends with is the same sum, so only the
   // rounding order changes); a sub-segment with a ragged chunk walks in order
   int last_chunk_first;
+  // launch_fwd_u only: each sub-segment p >= 1 also forms
+  // U = sum_t lambda^(t - t0) Q2_t Q_t^T over its tokens (t0 its first) and
+  // writes it to Uout[n][split - 1 - p] ([nseq][split-1][D][D], the
+  // numbering of a reverse sweep whose sub-segments end where these start)
+  const void* Q2;
+  float* Uout;
 };
 
 // dst[n] = f(src[n]) for nseq D x D fp32 states: optional transpose, then a
@@ -109,6 +115,10 @@ struct ScanArgs {
   // the first segment decays S0 by lambda^(seg_len - 1) instead of
   // lambda^seg_len (S0 already carries the first token's decay; fixed decay)
   int s0_undecayed;
+  // fixed decay: the first segment in scan order spans first_len tokens
+  // (0: seg_len like the others), the short one of a partition cut from the
+  // sequence's other end
+  int64_t first_len;
   // gated != 0: segment s of sequence n decays by exp(LD[n][s]) instead of
   // lambda^seg_len (lam is then never read, LD only for s < P)
   int gated;
@@ -164,6 +174,14 @@ hipError_t launch_fwd(const FwdArgs& a, int dtype, int D, bool with_o, int64_t n
 // a.gated == b.gated == c.gated.
 hipError_t launch_fwd_triple(const FwdArgs& a, const FwdArgs& b, const FwdArgs& c, int dtype,
                              int D, int64_t nitems, hipStream_t stream);
+// Two chunk-kernel launches with outputs over nitems work items each whose
+// recurrences have crosswise keys and values (b.K == a.V, b.V == a.K; same
+// plan, decay and gates) as one workgroup per item (la_fwd.hip); bf16 only.
+hipError_t launch_fwd_duo(const FwdArgs& a, const FwdArgs& b, int dtype, int D, int64_t nitems,
+                          hipStream_t stream);
+// The chunk kernel with outputs over nitems work items of a (fixed decay,
+// a.Q2 and a.Uout set), every sub-segment also forming its U (la_fwd.hip).
+hipError_t launch_fwd_u(const FwdArgs& a, int dtype, int D, int64_t nitems, hipStream_t stream);
 hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
 // dst[m] = src[m]^T for nmat consecutive D x D fp32 matrices (no overlap).
 hipError_t launch_transpose_copy(const float* src, float* dst, int64_t nmat, int D,

@@ -21,9 +21,12 @@ __global__ __launch_bounds__(256) void k_state_scan(ScanArgs a) {
   // lambda^seg_len = 2^(seg_len log2 lambda); underflow to 0 is intended
   const float lg = GATED ? 0.0f : log2f(a.lam[(int)((n / a.hdiv) % a.H)]);
   const float dec = GATED ? 0.0f : pow_lam(lg, (float)a.seg_len);
-  // decay of the first segment: a seed that already carries the first
-  // token's decay takes one power fewer
-  float dcur = (!GATED && a.s0_undecayed && a.seg_len > 0) ? pow_lam(lg, (float)(a.seg_len - 1)) : dec;
+  // decay of the first segment (first_len tokens when it is the short
+  // one): a seed that already carries the first token's decay takes one
+  // power fewer
+  const int64_t len0 = a.first_len > 0 ? a.first_len : a.seg_len;
+  float dcur = GATED ? 0.0f
+                     : pow_lam(lg, (float)((a.s0_undecayed && len0 > 0) ? len0 - 1 : len0));
   float x = a.S0 ? a.S0[n * a.E + e] : 0.0f;
   // Segments go in groups of PF whose inputs are all loaded before any of
   // the group's outputs is stored: Sout may be dS itself, so the compiler

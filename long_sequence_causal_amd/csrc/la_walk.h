@@ -74,29 +74,35 @@ __device__ inline int tab_pos(int t) {
 }
 
 // LDS of a workgroup: STAGES stages of NSLOT token-major tiles (Q, K, V when
-// NSLOT = 3, K, V when NSLOT = 2), plus P when NSLOT = 3, plus (gated walks)
+// NSLOT = 3, K, V when NSLOT = 2, the four tensors of NH = 2 walks that share
+// their keys and values crosswise when NSLOT = 4, or of one walk that also
+// accumulates a second state (Q, K, V, Q2) when NSLOT = 4 and NH = 1), plus
+// one P per walk when NSLOT >= 3, plus (gated walks)
 // a ring of STAGES + 1 slots of 64 log-gates (a chunk's gates travel with
 // the previous chunk's tiles, one chunk ahead of them) and two buffers of the
 // chunk factor tables (GateTab).
-template <typename T, int D, int NSLOT, bool GATED = false>
+template <typename T, int D, int NSLOT, bool GATED = false, int NH = 1>
 struct FwdLayout {
   typedef PadTile<T, CH, D> TN;                // Q, K, V token-major [token][d]
   typedef PBlocks<T> TP;                       // P, its 10 nonzero 16x16 blocks
+  static_assert(NH == 1 || NSLOT == 4, "two walks share a stage of four tiles");
   static constexpr int NTEN = NSLOT;           // tensor tiles per stage
   static constexpr int TB = TN::BYTES;         // one tensor tile
   static constexpr int STAGE = NTEN * TB;
-  static constexpr int PBYTES = NSLOT == 3 ? TP::BYTES : 0;
-  static constexpr int SMAX = NSLOT == 3 ? 3 : 5;
+  static constexpr int PBYTES = NSLOT >= 3 ? NH * TP::BYTES : 0;  // one P per walk
+  static constexpr int SMAX = NSLOT >= 3 ? 3 : 5;
   static constexpr int GB = GATED ? CH * 4 : 0;  // log-gates of one chunk
   static constexpr int TBL = GATED ? 2 * 2 * CH * 4 : 0;  // 2 x (cumulative gate, update weight)
   static constexpr int NW = D / 16;  // waves: one per 16 state columns
-  static constexpr int SFIT = (LDS_MAX - PBYTES - GB - TBL) / (STAGE + GB);
+  static constexpr int UB = (NSLOT == 4 && NH == 1) ? CH * 4 : 0;
+  static constexpr int SFIT = (LDS_MAX - PBYTES - GB - TBL - UB) / (STAGE + GB);
   static constexpr int STAGES = SFIT < SMAX ? SFIT : SMAX;
   static constexpr int OFF_P = STAGES * STAGE;
   static constexpr int OFF_G = OFF_P + PBYTES;
   static constexpr int GSLOTS = STAGES + 1;  // gate ring (gated walks)
   static constexpr int OFF_T = OFF_G + GSLOTS * GB;
-  static constexpr int BYTES = OFF_T + TBL;
+  static constexpr int OFF_U = OFF_T + TBL;  // (one walk of four tiles) weights of its second state
+  static constexpr int BYTES = OFF_U + UB;
   static constexpr int NT = 64 * NW;
   // bf16 keeps two waves per SIMD (256 registers per lane)
   static constexpr int WAVES_PER_EU = sizeof(T) == 2 ? 2 : 1;
@@ -147,6 +153,13 @@ struct WalkJob {
   // so the first chunk decays it by lambda^(i) and lambda^(cl-1) instead of
   // lambda^(i+1) and lambda^cl
   int first_undecayed;
+  // NH = 2 walks: the four tensors a stage holds (slots 0..3: the first
+  // walk's Q, the second's Q, the first's K, the first's V; the second walk's
+  // K and V are the first's V and K).  Set in the first job.
+  const void* src4[4];
+  // one walk of four tiles (NSLOT = 4, NH = 1): the keys of its second state
+  // U = sum_t lambda^(t - t0) Q2_t Q_t^T (its values are this walk's queries)
+  const void* Q2;
 };
 
 // Walk the range with the state in accS (wave w: columns [16 w, 16 w + 16),
@@ -169,12 +182,34 @@ struct WalkJob {
 // runs; after the next barrier every wave reads the factors it needs with a
 // few vector LDS reads instead of gathering them lane by lane.  Returns the
 // range's total log-gate (0 if not GATED).
-template <typename T, int D, bool OUT, int NSLOT, bool GATED = false>
-__device__ __forceinline__ float walk(char* smem, const WalkJob& jb, f32x4 (&accS)[D / 16]) {
+//
+// NH = 2: every wave walks two recurrences side by side over the same
+// positions with the same decay (jbs[0], jbs[1]; state h in accS[h]) whose
+// keys and values are crosswise the same tensors: the backward's dV and dK
+// sweeps, both over q dO^T (keys Q, values dO, queried by K; keys dO, values
+// Q, queried by V).  A stage then holds four tiles instead of six, the two
+// share every load, barrier and decay factor, and each wave has two
+// independent streams of matrix products to interleave.
+//
+// NSLOT = 4 with NH = 1 (fixed decay, outputs): the walk also accumulates
+// U = sum_t lambda^(t - t0) q2_t q_t^T over its positions from zero into
+// accU (same column split as the state; keys Q2 = jb.Q2, values this walk's
+// queries), the weights growing with the position instead of decaying a
+// state.  The backward's dQ sweep (queries dO) takes Q2 = Q: U is then the
+// local state of each sub-segment for the reverse dV and dK sweeps, formed
+// from the dO tiles the dQ sweep reads anyway instead of by a pre-pass that
+// reads Q and dO again.
+template <typename T, int D, bool OUT, int NSLOT, bool GATED = false, int NH = 1>
+__device__ __forceinline__ float walk(char* smem, const WalkJob (&jbs)[NH],
+                                      f32x4 (&accS)[NH][D / 16], f32x4* accU = nullptr) {
   typedef Elt<T> X;
   typedef typename X::op_t op_t;
-  typedef FwdLayout<T, D, NSLOT, GATED> LY;
-  static_assert(NSLOT == 3 || !OUT, "outputs need the Q slot and P");
+  typedef FwdLayout<T, D, NSLOT, GATED, NH> LY;
+  constexpr bool ACCU = NSLOT == 4 && NH == 1;
+  static_assert(NSLOT >= 3 || !OUT, "outputs need the Q slot and P");
+  static_assert(NH == 1 || (OUT && NSLOT == 4), "two walks form outputs from four tiles");
+  static_assert(!ACCU || (OUT && !GATED), "the second state rides on a fixed-decay output walk");
+  const WalkJob& jb = jbs[0];  // positions, direction, decay: shared
   typedef typename LY::TN TN;
   typedef typename LY::TP TP;
   constexpr int E = X::E;           // operand elements per lane
@@ -190,11 +225,14 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob& jb, f32x4 (&acc
   constexpr int G = TN::G;
   // one chunk is NLOAD * G loads of 1 KiB (64 lanes x 16 B) into slots
   // SLOT0..; wave w issues loads w, w + NW, ...: LPC_HI or LPC_HI - 1 of them
-  constexpr int NLOAD = OUT ? 3 : 2;
+  constexpr int NLOAD = (NH == 2 || ACCU) ? 4 : (OUT ? 3 : 2);
   constexpr int SLOT0 = NSLOT - NLOAD;
   constexpr int NBLK = NLOAD * G;
   constexpr int LPC_HI = (NBLK + NW - 1) / NW;
-  char* const sP = smem + LY::OFF_P;
+  // stage slots of walk h's Q, K, V tiles
+  auto qslot = [](int h) { return NH == 2 ? h : 0; };
+  auto kslot = [](int h) { return NH == 2 ? 2 + h : (NSLOT >= 3 ? 1 : 0); };
+  auto vslot = [](int h) { return NH == 2 ? 3 - h : (NSLOT >= 3 ? 2 : 1); };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -239,7 +277,12 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob& jb, f32x4 (&acc
   const bool wait_hi = lpc_hi || gwave;                // LPC_HI loads in all
   auto blk_of = [&](int q) { const int bq = w + NW * q; return bq < NBLK ? bq : 0; };
   auto tensor_base = [&](int ten) -> const T* {
-    const void* bp = OUT ? (ten == 0 ? jb.Q : (ten == 1 ? jb.K : jb.V)) : (ten == 0 ? jb.K : jb.V);
+    // (selects, not an indexed array: the base must stay wave-uniform)
+    const void* bp =
+        NH == 2 ? (ten == 0 ? jb.src4[0] : ten == 1 ? jb.src4[1] : ten == 2 ? jb.src4[2] : jb.src4[3])
+        : ACCU  ? (ten == 0 ? jb.Q : ten == 1 ? jb.K : ten == 2 ? jb.V : jb.Q2)
+        : OUT   ? (ten == 0 ? jb.Q : (ten == 1 ? jb.K : jb.V))
+                : (ten == 0 ? jb.K : jb.V);
     return reinterpret_cast<const T*>(bp);
   };
   unsigned voff0[LPC_HI];  // chunk-0 byte offset of this lane's piece, per load
@@ -317,7 +360,9 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob& jb, f32x4 (&acc
       }
     }
   };
-  T* const Oseq = reinterpret_cast<T*>(jb.O);  // sequence base of O
+  T* Oseq[NH];  // sequence base of each walk's O
+#pragma unroll
+  for (int h = 0; h < NH; ++h) Oseq[h] = reinterpret_cast<T*>(jbs[h].O);
   // bf16 at d = 128 (8 waves x 16 columns, 256-byte rows): a chunk's outputs
   // are staged in LDS and stored as whole rows with non-temporal stores (the
   // rows are written once and never read here, so they do not displace the
@@ -326,7 +371,7 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob& jb, f32x4 (&acc
   // pieces from four waves.  Measured at 64K tokens x 32 heads: whole call
   // 582.7 -> 564.1 us (plain whole-row stores: no gain).
   constexpr bool OSTAGE = OUT && sizeof(T) == 2 && D == 128;
-  T ohold[4][4];
+  T ohold[NH][4][4];
   unsigned ooff0[4];  // element offset (chunk 0) of the lane's outputs in each 16-row block
   const bool und = !GATED && jb.first_undecayed;  // wave-uniform
   // lambda^(i+1) (or lambda^i for a start state that already carries the
@@ -356,6 +401,15 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob& jb, f32x4 (&acc
       }
   };
   if (!GATED) set_wv(CH);
+  // ACCU: lambda^j for the lane's contraction slots j of a chunk, in slot
+  // order (entry 16 g + E js + x), visible after the loop's first barrier
+  float* const tabU = reinterpret_cast<float*>(smem + LY::OFF_U);
+  if constexpr (ACCU) {
+    if (tid < 64) {
+      const int js = (tid & 15) / E, x = (tid & 15) % E;
+      tabU[tid] = pow_lam(lg, (float)slot_token<T>(js * KS, tid >> 4, x));
+    }
+  }
   float gsum2 = 0.0f;  // total log2-gate of the chunks walked (GATED)
   float dc = GATED ? 0.0f : lamC;  // decay of the state over the current chunk
 
@@ -464,141 +518,202 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob& jb, f32x4 (&acc
     }
     const char* const stage = smem + st * LY::STAGE;
     st = (st + 1 == S) ? 0 : st + 1;
-    const char* const sQ = stage;
-    const char* const sK = stage + (NSLOT == 3 ? TB : 0);
-    const char* const sV = sK + TB;
 
     // V^T operands of this wave's columns (intra A operand; scaled: update B operand)
-    op_t Vop[NJS];
+    op_t Vop[NH][NJS];
 #pragma unroll
-    for (int js = 0; js < NJS; ++js) Vop[js] = tr_op<T, TN>(sV, js * KS, col, lane);
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int js = 0; js < NJS; ++js)
+        Vop[h][js] = tr_op<T, TN>(stage + vslot(h) * TB, js * KS, col, lane);
 
+    // ---- ACCU: U += Q2^T (diag(lambda^(64 c + j)) Q), 0 past the tail (before
+    // the outputs are staged in the Q tile)
+    if constexpr (ACCU) {
+      const char* const sQ = stage + qslot(0) * TB;
+      const char* const sU = stage + 3 * TB;
+      float wu[NJS][E];
+      if (cl == CH) {
+        const float fu = pow_lam(lg, (float)(CH * c));  // lambda^(64 c)
+#pragma unroll
+        for (int js = 0; js < NJS; ++js)
+#pragma unroll
+          for (int x = 0; x < E; ++x) wu[js][x] = tabU[16 * g + E * js + x] * fu;
+      } else {
+#pragma unroll
+        for (int js = 0; js < NJS; ++js)
+#pragma unroll
+          for (int x = 0; x < E; ++x) {
+            const int j = slot_token<T>(js * KS, g, x);
+            wu[js][x] = j < cl ? pow_lam(lg, (float)(CH * c + j)) : 0.0f;
+          }
+      }
+      op_t Bu[NJS];
+#pragma unroll
+      for (int js = 0; js < NJS; ++js) {
+        const op_t Qop = tr_op<T, TN>(sQ, js * KS, col, lane);
+        if constexpr (E == 8) {
+          bf16x8 b;
+#pragma unroll
+          for (int x = 0; x < 8; ++x) b[x] = (__bf16)((float)Qop[x] * wu[js][x]);
+          Bu[js] = b;
+        } else {
+          Bu[js] = Qop * wu[js][0];
+        }
+      }
+#pragma unroll
+      for (int tk = 0; tk < NKT; ++tk)
+#pragma unroll
+        for (int js = 0; js < NJS; ++js) {
+          const op_t Au = tr_op<T, TN>(sU, js * KS, 16 * tk, lane);
+          accU[tk] = X::mfma(Au, Bu[js], accU[tk]);
+        }
+    }
     if (OUT) {
       // ---- intra scores: P^T tiles = K Q^T, masked and decayed, to LDS as P[i][j]
 #pragma unroll
-      for (int st = 0; st < NST; ++st) {
-        const int idx = w + NW * st;
-        if (idx < 10) {
-          int jb, ib;
-          score_tile(idx, jb, ib);
-          // operand row l16 is token perm16(l16) of the block; the
-          // contraction over d visits features in score_granule order
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-          const int rk = 16 * jb + perm16<T>(l16), rq = 16 * ib + perm16<T>(l16);
+      for (int h = 0; h < NH; ++h) {
+        const char* const sQ = stage + qslot(h) * TB;
+        const char* const sK = stage + kslot(h) * TB;
+        char* const sP = smem + LY::OFF_P + h * TP::BYTES;
 #pragma unroll
-          for (int ks = 0; ks < NKS; ++ks) {
-            const int f = (E == 8) ? 8 * score_granule<D>(ks, g) : ks * KS + g;
-            const op_t A = lds_op<T>(sK, TN::off(rk, f));
-            const op_t B = lds_op<T>(sQ, TN::off(rq, f));
-            acc = X::mfma(A, B, acc);
+        for (int st = 0; st < NST; ++st) {
+          const int idx = w + NW * st;
+          if (idx < 10) {
+            int jb, ib;
+            score_tile(idx, jb, ib);
+            // operand row l16 is token perm16(l16) of the block; the
+            // contraction over d visits features in score_granule order
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            const int rk = 16 * jb + perm16<T>(l16), rq = 16 * ib + perm16<T>(l16);
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+              const int f = (E == 8) ? 8 * score_granule<D>(ks, g) : ks * KS + g;
+              const op_t A = lds_op<T>(sK, TN::off(rk, f));
+              const op_t B = lds_op<T>(sQ, TN::off(rq, f));
+              acc = X::mfma(A, B, acc);
+            }
+            T pv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pv[r] = X::from_f(acc[r] * pf[st][r]);
+            // keys perm16(4 g + r), r = 0..3, form slab g; query row perm16(l16)
+            char* dst = sP + TP::at(ib, jb, g, perm16<T>(l16));
+            if (sizeof(T) == 2)
+              *reinterpret_cast<u32x2*>(dst) = *reinterpret_cast<u32x2*>(pv);
+            else
+              *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<u32x4*>(pv);
           }
-          T pv[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) pv[r] = X::from_f(acc[r] * pf[st][r]);
-          // keys perm16(4 g + r), r = 0..3, form slab g; query row perm16(l16)
-          char* dst = sP + TP::at(ib, jb, g, perm16<T>(l16));
-          if (sizeof(T) == 2)
-            *reinterpret_cast<u32x2*>(dst) = *reinterpret_cast<u32x2*>(pv);
-          else
-            *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<u32x4*>(pv);
         }
       }
       lds_barrier();  // P complete
 
-      // ---- state before this chunk as the A operand of O^T = S^T Q^T
-      op_t Sop[NKS];
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        if constexpr (E == 8) {
-          bf16x8 o;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            o[r] = (__bf16)accS[2 * ks][r];
-            o[4 + r] = (__bf16)accS[2 * ks + 1][r];
-          }
-          Sop[ks] = o;
-        } else {
-          Sop[ks] = accS[ks / 4][ks % 4];
-        }
-      }
-
-      // ---- outputs, one 16-token block at a time
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int i = 16 * it + l16;
-        f32x4 o = {0.f, 0.f, 0.f, 0.f};
-        // inter: sum_k S[k][v] q_i[k], with Q read in the permuted slot order
+      for (int h = 0; h < NH; ++h) {
+        const char* const sQ = stage + qslot(h) * TB;
+        const char* const sP = smem + LY::OFF_P + h * TP::BYTES;
+        // ---- state before this chunk as the A operand of O^T = S^T Q^T
+        op_t Sop[NKS];
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-          op_t B;
           if constexpr (E == 8) {
-            const u32x2 lo = lds_read8(sQ + TN::off(i, 32 * ks + 4 * g));
-            const u32x2 hi = lds_read8(sQ + TN::off(i, 32 * ks + 16 + 4 * g));
-            const u32x4 both = {lo[0], lo[1], hi[0], hi[1]};
-            B = __builtin_bit_cast(bf16x8, both);
-          } else {
-            B = *reinterpret_cast<const float*>(sQ + TN::off(i, 16 * (ks / 4) + 4 * g + (ks % 4)));
-          }
-          o = X::mfma(Sop[ks], B, o);
-        }
-        o *= qf[it];
-        // intra: sum_j V^T[v][j] P[i][j] over key blocks jb <= it; slab g of
-        // a block holds exactly the keys of lane group g's slots
+            bf16x8 o;
 #pragma unroll
-        for (int js = 0; js < NJS; ++js) {
-          if (js * KS < 16 * (it + 1)) {
-            op_t Bp;
-            if constexpr (E == 8) {
-              const u32x2 z = {0u, 0u};
-              const u32x2 lo = lds_read8(sP + TP::at(it, 2 * js, g, l16));
-              const u32x2 hi = (2 * js + 1 <= it) ? lds_read8(sP + TP::at(it, 2 * js + 1, g, l16)) : z;
-              const u32x4 both = {lo[0], lo[1], hi[0], hi[1]};
-              Bp = __builtin_bit_cast(bf16x8, both);
-            } else {
-              const int j = js * KS + g;
-              Bp = ((j >> 4) <= it)
-                       ? *reinterpret_cast<const float*>(sP + TP::at(it, j >> 4, (j & 15) >> 2, l16) +
-                                                         (j & 3) * (int)sizeof(T))
-                       : 0.0f;
+            for (int r = 0; r < 4; ++r) {
+              o[r] = (__bf16)accS[h][2 * ks][r];
+              o[4 + r] = (__bf16)accS[h][2 * ks + 1][r];
             }
-            o = X::mfma(Vop[js], Bp, o);
+            Sop[ks] = o;
+          } else {
+            Sop[ks] = accS[h][ks / 4][ks % 4];
           }
         }
-        // store: lane holds O[token i][v0 .. v0+3]
-        if constexpr (OSTAGE) {
-          // held until every wave is done with the chunk's Q tile
+
+        // ---- outputs, one 16-token block at a time
 #pragma unroll
-          for (int r = 0; r < 4; ++r) ohold[it][r] = X::from_f(o[r]);
-        } else if (c * CH + i < len) {
-          T* orow = Oseq + (ooff0[it] + (unsigned)c * (unsigned)(cstride_b / (int)sizeof(T)));
-          T ov[4];
+        for (int it = 0; it < 4; ++it) {
+          const int i = 16 * it + l16;
+          f32x4 o = {0.f, 0.f, 0.f, 0.f};
+          // inter: sum_k S[k][v] q_i[k], with Q read in the permuted slot order
 #pragma unroll
-          for (int r = 0; r < 4; ++r) ov[r] = X::from_f(o[r]);
-          if (sizeof(T) == 2)
-            // (bf16 at d = 64: 32-byte pieces of 16 rows, merged in L2)
-            *reinterpret_cast<u32x2*>(orow) = *reinterpret_cast<u32x2*>(ov);
-          else
-            *reinterpret_cast<u32x4*>(orow) = *reinterpret_cast<u32x4*>(ov);
+          for (int ks = 0; ks < NKS; ++ks) {
+            op_t B;
+            if constexpr (E == 8) {
+              const u32x2 lo = lds_read8(sQ + TN::off(i, 32 * ks + 4 * g));
+              const u32x2 hi = lds_read8(sQ + TN::off(i, 32 * ks + 16 + 4 * g));
+              const u32x4 both = {lo[0], lo[1], hi[0], hi[1]};
+              B = __builtin_bit_cast(bf16x8, both);
+            } else {
+              B = *reinterpret_cast<const float*>(sQ + TN::off(i, 16 * (ks / 4) + 4 * g + (ks % 4)));
+            }
+            o = X::mfma(Sop[ks], B, o);
+          }
+          o *= qf[it];
+          // intra: sum_j V^T[v][j] P[i][j] over key blocks jb <= it; slab g of
+          // a block holds exactly the keys of lane group g's slots
+#pragma unroll
+          for (int js = 0; js < NJS; ++js) {
+            if (js * KS < 16 * (it + 1)) {
+              op_t Bp;
+              if constexpr (E == 8) {
+                const u32x2 z = {0u, 0u};
+                const u32x2 lo = lds_read8(sP + TP::at(it, 2 * js, g, l16));
+                const u32x2 hi =
+                    (2 * js + 1 <= it) ? lds_read8(sP + TP::at(it, 2 * js + 1, g, l16)) : z;
+                const u32x4 both = {lo[0], lo[1], hi[0], hi[1]};
+                Bp = __builtin_bit_cast(bf16x8, both);
+              } else {
+                const int j = js * KS + g;
+                Bp = ((j >> 4) <= it)
+                         ? *reinterpret_cast<const float*>(
+                               sP + TP::at(it, j >> 4, (j & 15) >> 2, l16) + (j & 3) * (int)sizeof(T))
+                         : 0.0f;
+              }
+              o = X::mfma(Vop[h][js], Bp, o);
+            }
+          }
+          // store: lane holds O[token i][v0 .. v0+3]
+          if constexpr (OSTAGE) {
+            // held until every wave is done with the chunk's Q tile
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ohold[h][it][r] = X::from_f(o[r]);
+          } else if (c * CH + i < len) {
+            T* orow = Oseq[h] + (ooff0[it] + (unsigned)c * (unsigned)(cstride_b / (int)sizeof(T)));
+            T ov[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ov[r] = X::from_f(o[r]);
+            if (sizeof(T) == 2)
+              // (bf16 at d = 64: 32-byte pieces of 16 rows, merged in L2)
+              *reinterpret_cast<u32x2*>(orow) = *reinterpret_cast<u32x2*>(ov);
+            else
+              *reinterpret_cast<u32x4*>(orow) = *reinterpret_cast<u32x4*>(ov);
+          }
         }
       }
       if constexpr (OSTAGE) {
         // the chunk's O tile through the Q slot: each wave writes its 16
         // columns of every token, then stores 8 whole rows, 16 bytes per lane
         lds_barrier();  // every wave is done reading Q
-        char* const sO = const_cast<char*>(sQ);
 #pragma unroll
-        for (int it = 0; it < 4; ++it)
-          *reinterpret_cast<u32x2*>(sO + TN::off(16 * it + l16, col + 4 * g)) =
-              *reinterpret_cast<const u32x2*>(ohold[it]);
+        for (int h = 0; h < NH; ++h) {
+          char* const sO = const_cast<char*>(stage + qslot(h) * TB);
+#pragma unroll
+          for (int it = 0; it < 4; ++it)
+            *reinterpret_cast<u32x2*>(sO + TN::off(16 * it + l16, col + 4 * g)) =
+                *reinterpret_cast<const u32x2*>(ohold[h][it]);
+        }
         lds_barrier();
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int row = 8 * w + 4 * h + (lane >> 4);  // 16 lanes per 256-byte row
-          const int piece = lane & 15;
-          if (c * CH + row < len) {
-            const u32x4 val = *reinterpret_cast<const u32x4*>(sO + TN::off(row, 8 * piece));
-            T* orow = Oseq + (unsigned)((relrow(c * CH + row)) * D + 8 * piece);
-            __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(orow));
+        for (int h = 0; h < NH; ++h) {
+          const char* const sO = stage + qslot(h) * TB;
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int row = 8 * w + 4 * hh + (lane >> 4);  // 16 lanes per 256-byte row
+            const int piece = lane & 15;
+            if (c * CH + row < len) {
+              const u32x4 val = *reinterpret_cast<const u32x4*>(sO + TN::off(row, 8 * piece));
+              T* orow = Oseq[h] + (unsigned)((relrow(c * CH + row)) * D + 8 * piece);
+              __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(orow));
+            }
           }
         }
       }
@@ -607,26 +722,30 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob& jb, f32x4 (&acc
     // ---- state update: S = lambda^cl S + K^T (diag(lambda^(cl-1-j)) V)
     {
 #pragma unroll
-      for (int tk = 0; tk < NKT; ++tk) accS[tk] *= dc;
-      op_t Bv[NJS];
+      for (int h = 0; h < NH; ++h) {
+        const char* const sK = stage + kslot(h) * TB;
 #pragma unroll
-      for (int js = 0; js < NJS; ++js) {
-        if constexpr (E == 8) {
-          bf16x8 b;
-#pragma unroll
-          for (int x = 0; x < 8; ++x) b[x] = (__bf16)((float)Vop[js][x] * wv[js][x]);
-          Bv[js] = b;
-        } else {
-          Bv[js] = Vop[js] * wv[js][0];
-        }
-      }
-#pragma unroll
-      for (int tk = 0; tk < NKT; ++tk)
+        for (int tk = 0; tk < NKT; ++tk) accS[h][tk] *= dc;
+        op_t Bv[NJS];
 #pragma unroll
         for (int js = 0; js < NJS; ++js) {
-          const op_t Ak = tr_op<T, TN>(sK, js * KS, 16 * tk, lane);
-          accS[tk] = X::mfma(Ak, Bv[js], accS[tk]);
+          if constexpr (E == 8) {
+            bf16x8 b;
+#pragma unroll
+            for (int x = 0; x < 8; ++x) b[x] = (__bf16)((float)Vop[h][js][x] * wv[js][x]);
+            Bv[js] = b;
+          } else {
+            Bv[js] = Vop[h][js] * wv[js][0];
+          }
         }
+#pragma unroll
+        for (int tk = 0; tk < NKT; ++tk)
+#pragma unroll
+          for (int js = 0; js < NJS; ++js) {
+            const op_t Ak = tr_op<T, TN>(sK, js * KS, 16 * tk, lane);
+            accS[h][tk] = X::mfma(Ak, Bv[js], accS[h][tk]);
+          }
+      }
       if (lcf) {
 #pragma unroll
         for (int js = 0; js < NJS; ++js)

@@ -64,6 +64,31 @@ hipError_t launch_fwd_triple(const FwdArgs& a, const FwdArgs& b, const FwdArgs& 
   return hipSuccess;
 }
 
+hipError_t launch_fwd_u(const FwdArgs& a, int dtype, int, int64_t nitems, hipStream_t) {
+  if (nitems <= 0) return hipSuccess;
+  check_fwd(a, nitems);
+  expect(dtype == 0 && !a.gated, "U-forming walk is bf16 fixed decay");
+  expect(a.Q && a.O && a.Q2 && a.Uout && a.split > 1, "outputs and U");
+  ++g_launches;
+  return hipSuccess;
+}
+
+hipError_t launch_fwd_duo(const FwdArgs& a, const FwdArgs& b, int dtype, int, int64_t nitems,
+                          hipStream_t) {
+  if (nitems <= 0) return hipSuccess;
+  check_fwd(a, nitems);
+  check_fwd(b, nitems);
+  expect(dtype == 0, "joint dV/dK walk is bf16 only");
+  expect(a.gated == b.gated && a.G == b.G, "one gate sequence");
+  expect(a.K == b.V && a.V == b.K, "crosswise keys and values");
+  expect(a.Ls == b.Ls && a.Lp == b.Lp && a.split == b.split && a.reverse == b.reverse &&
+             a.ragged_first == b.ragged_first && a.p_begin == b.p_begin && a.p_count == b.p_count,
+         "one plan");
+  expect(a.Q && a.O && b.Q && b.O, "outputs of both");
+  ++g_launches;
+  return hipSuccess;
+}
+
 hipError_t launch_scan(const ScanArgs& a, hipStream_t) {
   expect(a.nseq >= 0 && a.P >= 0 && a.E > 0, "scan sizes");
   if (a.P > 0) expect(a.dS && a.Sout, "scan buffers");

@@ -33,6 +33,10 @@ CASES = [
     ("fp32", 64, 1, 2, 1024, 1, 0, 0.0, 0.0, False),
     ("fp32", 64, 2, 2, 130 * 2, 2, 2, 0.5, 0.5, True),
     ("fp32", 128, 1, 1, 70, 1, 0, 0.5, 0.5, True),
+    # a short last sub-segment ending in a partial chunk (the reverse sweeps
+    # then start with it), fixed decay fast and slow
+    ("bf16", 128, 1, 2, 64 * 7 + 5, 1, 3, 0.5, 0.5, True),
+    ("bf16", 64, 2, 1, 64 * 10 + 40, 2, 4, 0.5, 1.0, False),
     # 32 sequences of 72 chunks: 8 sub-segments of 9 chunks in all three sweeps
     ("bf16", 128, 2, 16, 64 * 72, 1, 0, 0.5, 0.5, False),
 ]
