@@ -603,6 +603,7 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
     if ((e = la::launch_prep(pa, st)) != hipSuccess) return hip_fail(e, "prep launch");
     startK = A2;
   }
+  const bool rk_from_walk = dlog_alpha && s->dtype == LA_BF16 && pl.D == 128;
   {
     // the dQ sweep (aq) and the dV and dK sweeps (launch_sweeps): the start
     // states of all three are ready, and both plans have plc.split walks
@@ -613,6 +614,9 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
                                true, Gs);
     av.sws_nper = ak.sws_nper = plr.split - 1;
     av.sws_step = ak.sws_step = (int)step;
+    // the joint dV/dK walk (bf16, d = 128) also leaves k_t . dk_t per token
+    // in dlog_alpha for the log-gate gradient below
+    if (rk_from_walk) ak.rk = dlog_alpha;
     if ((e = launch_sweeps(aq, av, ak, s->dtype, pl.D, plc.nseq * plc.split, st)) != hipSuccess)
       return hip_fail(e, "sweep launch");
   }
@@ -625,7 +629,8 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
     e = la::launch_gate_anchors(W, W3, log_alpha, dS_end, need_send ? SE : nullptr, TOT, pl.nseq,
                                 pl.Ls, pl.D, st);
     if (e != hipSuccess) return hip_fail(e, "gate anchor launch");
-    e = la::launch_gate_grad(s->dtype, pl.D, Q, dQ, K, dK, dlog_alpha, TOT, dS_end,
+    e = la::launch_gate_grad(s->dtype, pl.D, Q, dQ, rk_from_walk ? nullptr : K,
+                             rk_from_walk ? nullptr : dK, dlog_alpha, TOT, dS_end,
                              need_send ? SE : nullptr, pl.nseq, pl.Ls, st);
     if (e != hipSuccess) return hip_fail(e, "gate gradient launch");
   }

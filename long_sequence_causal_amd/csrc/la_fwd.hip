@@ -22,7 +22,7 @@ __device__ inline int64_t sws_slot(const FwdArgs& a, int p) {
 // sequence wg / p_count.  NH = 2: the same item of a1 as well, walked by
 // the same waves beside it (a1 has a0's plan, positions and decay, and a0's
 // values and keys as its keys and values).
-template <typename T, int D, bool WITH_O, bool GATED, int NH = 1, bool ACCU = false>
+template <typename T, int D, bool WITH_O, bool GATED, int NH = 1, bool ACCU = false, bool RK = false>
 __device__ __forceinline__ void chunk_item(const FwdArgs& a0, const FwdArgs& a1, int64_t wg) {
   constexpr int NSLOT = (NH == 2 || ACCU) ? 4 : (WITH_O ? 3 : 2);
   typedef FwdLayout<T, D, NSLOT, GATED, NH> LY;
@@ -65,6 +65,7 @@ __device__ __forceinline__ void chunk_item(const FwdArgs& a0, const FwdArgs& a1,
     jb[u].G = GATED ? a.G + n * a.Ls : nullptr;
     jb[u].last_chunk_first = a.last_chunk_first;
     jb[u].first_undecayed = !GATED && x.s0_undecayed && x.start_from_state && p == 0;
+    jb[u].rk = (RK && u == 1) ? x.rk + n * a.Ls : nullptr;
 
     // ---- start state -> accumulators (wave w: columns [16 w, 16 w + 16))
     const float* sp = nullptr;
@@ -97,7 +98,7 @@ __device__ __forceinline__ void chunk_item(const FwdArgs& a0, const FwdArgs& a1,
   // loop, i.e. on every chunk, which would also drain the chunk prefetches.
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
-  const float lgate = walk<T, D, WITH_O, NSLOT, GATED, NH>(smem, jb, accS, accU);
+  const float lgate = walk<T, D, WITH_O, NSLOT, GATED, NH, RK>(smem, jb, accS, accU);
   if constexpr (ACCU) {
     if (p >= 1) {
       float* dst = a.Uout + (n * (a.split - 1) + (a.split - 1 - p)) * (int64_t)D * D;
@@ -204,11 +205,11 @@ hipError_t launch_fwd_triple(const FwdArgs& a, const FwdArgs& b, const FwdArgs& 
 // crosswise keys and values (b.K = a.V, b.V = a.K: the backward's dV and dK
 // sweeps, both over q dO^T) as one workgroup per item, every wave walking
 // its columns of both: one stream of four tiles per chunk feeds both.
-template <typename T, int D, bool GATED>
+template <typename T, int D, bool GATED, bool RK>
 __global__ __launch_bounds__((FwdLayout<T, D, 4, GATED, 2>::NT),
                              (FwdLayout<T, D, 4, GATED, 2>::WAVES_PER_EU)) void k_chunk_fwd_duo(
     FwdArgs a, FwdArgs b) {
-  chunk_item<T, D, true, GATED, 2>(a, b, blockIdx.x);
+  chunk_item<T, D, true, GATED, 2, false, RK>(a, b, blockIdx.x);
 }
 
 template <typename T, int D>
@@ -216,13 +217,21 @@ static hipError_t launch_duo_t(const FwdArgs& a, const FwdArgs& b, int64_t nitem
   if (a.gated) {
     // (d = 64: 36 tile loads over 4 waves leave no wave a spare slot for
     // the gates' load; those sweeps keep their own workgroups)
-    if constexpr (D == 64) return hipErrorInvalidValue;
-    else
-      hipLaunchKernelGGL((k_chunk_fwd_duo<T, D, true>), dim3((unsigned)nitems),
-                         dim3(FwdLayout<T, D, 4, true, 2>::NT), 0, s, a, b);
-  } else
-    hipLaunchKernelGGL((k_chunk_fwd_duo<T, D, false>), dim3((unsigned)nitems),
+    if constexpr (D == 64) {
+      return hipErrorInvalidValue;
+    } else {
+      if (b.rk)
+        hipLaunchKernelGGL((k_chunk_fwd_duo<T, D, true, true>), dim3((unsigned)nitems),
+                           dim3(FwdLayout<T, D, 4, true, 2>::NT), 0, s, a, b);
+      else
+        hipLaunchKernelGGL((k_chunk_fwd_duo<T, D, true, false>), dim3((unsigned)nitems),
+                           dim3(FwdLayout<T, D, 4, true, 2>::NT), 0, s, a, b);
+    }
+  } else {
+    if (b.rk) return hipErrorInvalidValue;  // (only the gated backward asks for the row dots)
+    hipLaunchKernelGGL((k_chunk_fwd_duo<T, D, false, false>), dim3((unsigned)nitems),
                        dim3(FwdLayout<T, D, 4, false, 2>::NT), 0, s, a, b);
+  }
   return hipGetLastError();
 }
 
@@ -236,6 +245,7 @@ hipError_t launch_fwd_duo(const FwdArgs& a, const FwdArgs& b, int dtype, int D, 
       a.ragged_first != b.ragged_first || a.last_chunk_first != b.last_chunk_first)
     return hipErrorInvalidValue;
   if (dtype != 0) return hipErrorInvalidValue;  // bf16 only
+  if (a.rk || (b.rk && D != 128)) return hipErrorInvalidValue;  // row dots: b, d = 128
   if (D == 64) return launch_duo_t<__bf16, 64>(a, b, nitems, s);
   if (D == 128) return launch_duo_t<__bf16, 128>(a, b, nitems, s);
   return hipErrorInvalidValue;

@@ -58,8 +58,9 @@ __device__ inline float dot8(const T* a, const T* b) {
 // token (8 features each, D / 8 lanes in use), reduce across the 16 with
 // shuffles, then the block's reverse cumulative sum is taken in LDS:
 // dG[t] = sum_{u >= t in block} r_u, and the block total goes to tot[n][b]
-// (when tot is not null).
-template <typename T, int D>
+// (when tot is not null).  RK: k_u . dk_u comes from dG itself (formed by
+// the joint dV/dK walk), read before the block's values are written.
+template <typename T, int D, bool RK>
 __global__ __launch_bounds__(256) void k_gate_grad_blocks(const T* Q, const T* dQ, const T* K,
                                                           const T* dK, float* dG, float* tot,
                                                           int64_t Ls, int64_t nb) {
@@ -75,10 +76,11 @@ __global__ __launch_bounds__(256) void k_gate_grad_blocks(const T* Q, const T* d
     float s = 0.0f;
     if (i < len && sub < D / 8) {
       const int64_t row = (n * Ls + t0 + i) * D + 8 * sub;
-      s = dot8(Q + row, dQ + row) - dot8(K + row, dK + row);
+      s = RK ? dot8(Q + row, dQ + row) : dot8(Q + row, dQ + row) - dot8(K + row, dK + row);
     }
 #pragma unroll
     for (int m = 8; m >= 1; m >>= 1) s += __shfl_xor(s, m, 16);
+    if (RK && i < len) s -= dG[n * Ls + t0 + i];
     if (sub == 0) r[i] = s;  // tokens past the end hold 0
   }
   __syncthreads();
@@ -184,8 +186,12 @@ static hipError_t gate_grad_t(const void* Q, const void* dQ, const void* K, cons
   (void)SendT;
   const int64_t nb = gate_grad_blocks(Ls);
   // the block totals are not needed: tot already holds the anchors
-  hipLaunchKernelGGL((k_gate_grad_blocks<T, D>), dim3((unsigned)(nseq * nb)), dim3(256), 0, s,
-                     (const T*)Q, (const T*)dQ, (const T*)K, (const T*)dK, dG, nullptr, Ls, nb);
+  if (K && dK)
+    hipLaunchKernelGGL((k_gate_grad_blocks<T, D, false>), dim3((unsigned)(nseq * nb)), dim3(256), 0,
+                       s, (const T*)Q, (const T*)dQ, (const T*)K, (const T*)dK, dG, nullptr, Ls, nb);
+  else
+    hipLaunchKernelGGL((k_gate_grad_blocks<T, D, true>), dim3((unsigned)(nseq * nb)), dim3(256), 0,
+                       s, (const T*)Q, (const T*)dQ, nullptr, nullptr, dG, nullptr, Ls, nb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t all = nseq * Ls;

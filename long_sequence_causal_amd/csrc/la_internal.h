@@ -81,6 +81,11 @@ struct FwdArgs {
   // numbering of a reverse sweep whose sub-segments end where these start)
   const void* Q2;
   float* Uout;
+  // launch_fwd_duo only, in the second argument set (bf16, d = 128; may be
+  // null): rk[n][row] = (first set's Q row) . (second set's output row),
+  // [nseq][Ls] floats, over the bf16 outputs in fp32 (the gated backward's
+  // k_t . dk_t)
+  float* rk;
 };
 
 // dst[n] = f(src[n]) for nseq D x D fp32 states: optional transpose, then a
@@ -204,8 +209,9 @@ int64_t gate_grad_blocks(int64_t Ls);
 hipError_t launch_gate_anchors(const float* WfT, const float* WrT, const float* G,
                                const float* dSe, const float* SendT, float* tot, int64_t nseq,
                                int64_t Ls, int D, hipStream_t s);
-// dG[t] = the in-block suffix sum of r plus tot[n][t / GBLK] (launch_gate_grad
-// with anchors = true skips its own block-total scan)
+// dG[t] = the in-block suffix sum of r_u = q_u . dq_u - k_u . dk_u plus
+// tot[n][t / GBLK].  With K and dK null, dG must already hold k_t . dk_t per
+// token (the joint dV/dK walk's row dots) and is overwritten in place.
 hipError_t launch_gate_grad(int dtype, int D, const void* Q, const void* dQ, const void* K,
                             const void* dK, float* dG, float* tot, const float* dSe,
                             const float* SendT, int64_t nseq, int64_t Ls, hipStream_t s);

@@ -125,12 +125,16 @@ __device__ inline void wait_chunk_n(int later) {
   }
   wait_vm_barrier<0>();
 }
-template <int LPC_HI, int MAXLATER>
-__device__ inline void wait_chunk(bool hi, int later) {
-  if (hi || LPC_HI == 1)
-    wait_chunk_n<LPC_HI, MAXLATER>(later);
+// the same for a wave in load-count class cls (0, 1, 2: L0, L1 or L2 loads
+// per chunk)
+template <int L0, int L1, int L2, int MAXLATER>
+__device__ inline void wait_chunk3(int cls, int later) {
+  if (cls == 0)
+    wait_chunk_n<L0, MAXLATER>(later);
+  else if (cls == 1)
+    wait_chunk_n<L1, MAXLATER>(later);
   else
-    wait_chunk_n<(LPC_HI > 1 ? LPC_HI - 1 : 1), MAXLATER>(later);
+    wait_chunk_n<L2, MAXLATER>(later);
 }
 
 
@@ -160,6 +164,10 @@ struct WalkJob {
   // one walk of four tiles (NSLOT = 4, NH = 1): the keys of its second state
   // U = sum_t lambda^(t - t0) Q2_t Q_t^T (its values are this walk's queries)
   const void* Q2;
+  // NH = 2 with RK, second job (bf16 at d = 128): per position,
+  // rk[row] = (the first walk's query row) . (this walk's output row) over
+  // the bf16 outputs, in fp32; sequence base like the tensors
+  float* rk;
 };
 
 // Walk the range with the state in accS (wave w: columns [16 w, 16 w + 16),
@@ -199,7 +207,7 @@ struct WalkJob {
 // local state of each sub-segment for the reverse dV and dK sweeps, formed
 // from the dO tiles the dQ sweep reads anyway instead of by a pre-pass that
 // reads Q and dO again.
-template <typename T, int D, bool OUT, int NSLOT, bool GATED = false, int NH = 1>
+template <typename T, int D, bool OUT, int NSLOT, bool GATED = false, int NH = 1, bool RK = false>
 __device__ __forceinline__ float walk(char* smem, const WalkJob (&jbs)[NH],
                                       f32x4 (&accS)[NH][D / 16], f32x4* accU = nullptr) {
   typedef Elt<T> X;
@@ -224,11 +232,9 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob (&jbs)[NH],
   constexpr int TB = LY::TB;
   constexpr int G = TN::G;
   // one chunk is NLOAD * G loads of 1 KiB (64 lanes x 16 B) into slots
-  // SLOT0..; wave w issues loads w, w + NW, ...: LPC_HI or LPC_HI - 1 of them
+  // SLOT0.. (see the chunk loads below)
   constexpr int NLOAD = (NH == 2 || ACCU) ? 4 : (OUT ? 3 : 2);
   constexpr int SLOT0 = NSLOT - NLOAD;
-  constexpr int NBLK = NLOAD * G;
-  constexpr int LPC_HI = (NBLK + NW - 1) / NW;
   // stage slots of walk h's Q, K, V tiles
   auto qslot = [](int h) { return NH == 2 ? h : 0; };
   auto kslot = [](int h) { return NH == 2 ? 2 + h : (NSLOT >= 3 ? 1 : 0); };
@@ -260,22 +266,25 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob (&jbs)[NH],
   auto phys = [&](int c) { return lcf ? nch - 1 - c : c; };
 
   // ---- chunk loads: HBM -> LDS, 1 KiB (64 lanes x 16 B) per instruction.
-  // Load b of a chunk fills granules 64 (b % G) .. + 63 of tensor b / G's
-  // tile; lane l's granule is (row, piece) = divmod(64 (b % G) + l, G), the
-  // last piece of a row being padding (it loads the row's first piece).
-  // Offsets of chunk 0 are precomputed; a ragged last chunk clamps rows past
-  // the end to the last valid token.
-  // The gate load rides with wave NW-1, which otherwise issues one load fewer
-  // than the busiest wave (NBLK is never a multiple of NW here), so every
-  // wave's per-chunk count stays LPC_HI or LPC_HI - 1.  Chunk c's group
-  // carries the gates of chunk c + 1 (of the last chunk again at the end, so
-  // the count never changes); chunk 0's gates are one extra load issued
-  // before any tile, older than everything the waits count.
-  static_assert(!GATED || NBLK % NW != 0, "the gate load needs a wave with a spare slot");
+  // Block blk (0..G-1) of a tile is granules 64 blk .. + 63; lane l's granule
+  // is (row, piece) = divmod(64 blk + l, G), the last piece of a row being
+  // padding (it loads the row's first piece).  Wave w takes blocks w, w + NW,
+  // ... and loads each of them for all NLOAD tiles, whose offsets within a
+  // tile agree: NBW offsets per lane, those of chunk 0 precomputed; a ragged
+  // last chunk clamps rows past the end to the last valid token.
+  // Per chunk a wave issues nbw * NLOAD tile loads (nbw = NBW or NBW - 1),
+  // wave NW-1 one more for the gates: chunk c's group carries the gates of
+  // chunk c + 1 (of the last chunk again at the end, so the count never
+  // changes); chunk 0's gates are one extra load issued before any tile,
+  // older than everything the waits count.
+  constexpr int NBW = (G + NW - 1) / NW;  // blocks of the busiest wave
+  static_assert(G > NW, "every wave loads at least one block");
+  constexpr int NBW_LAST = (G - (NW - 1) + NW - 1) / NW;  // blocks of wave NW-1
+  const int nbw = (G - w + NW - 1) / NW;                  // this wave's (wave-uniform)
   const bool gwave = GATED && (w == NW - 1);
-  const bool lpc_hi = (w < NBLK - (LPC_HI - 1) * NW);  // issues LPC_HI tile loads
-  const bool wait_hi = lpc_hi || gwave;                // LPC_HI loads in all
-  auto blk_of = [&](int q) { const int bq = w + NW * q; return bq < NBLK ? bq : 0; };
+  // per-wave load count class for the waits: NBW blocks, NBW - 1, or the
+  // gate wave's blocks plus its gate load
+  const int wcls = gwave ? 2 : (nbw == NBW ? 0 : 1);
   auto tensor_base = [&](int ten) -> const T* {
     // (selects, not an indexed array: the base must stay wave-uniform)
     const void* bp =
@@ -285,25 +294,21 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob (&jbs)[NH],
                 : (ten == 0 ? jb.K : jb.V);
     return reinterpret_cast<const T*>(bp);
   };
-  unsigned voff0[LPC_HI];  // chunk-0 byte offset of this lane's piece, per load
+  auto piece_off = [&](int blk, int& row) -> int {  // lane's row and piece offset (elements)
+    const int pos = 64 * blk + lane;
+    row = pos / G;
+    const int pc = pos % G;
+    return ((pc == G - 1) ? 0 : pc) * EP;
+  };
+  unsigned voff0[NBW];  // chunk-0 byte offset of this lane's piece, per block
 #pragma unroll
-  for (int q = 0; q < LPC_HI; ++q) {
-    const int bb = blk_of(q);
-    const int pos = 64 * (bb % G) + lane;
-    const int row = pos / G, pc = pos % G;
-    const int piece = (pc == G - 1) ? 0 : pc;
-    voff0[q] = (unsigned)((relrow(row) * D + piece * EP) * (int64_t)sizeof(T));
+  for (int k = 0; k < NBW; ++k) {
+    const int blk = (w + NW * k < G) ? w + NW * k : 0;
+    int row;
+    const int po = piece_off(blk, row);
+    voff0[k] = (unsigned)((relrow(row) * D + po) * (int64_t)sizeof(T));
   }
-  // wave-uniform per load: source tensor and LDS destination within a stage
-  const T* src_of[LPC_HI];
-  unsigned dst_of[LPC_HI];
   const unsigned smem_lds = lds_address(smem);
-#pragma unroll
-  for (int q = 0; q < LPC_HI; ++q) {
-    const int bb = blk_of(q);
-    src_of[q] = tensor_base(bb / G);
-    dst_of[q] = smem_lds + (unsigned)((SLOT0 + bb / G) * TB + (bb % G) * 1024);
-  }
   // gates of chunk cg into the gate slot of chunk number `slot_of`
   auto gate_slot = [&](int cc) -> int { return cc % LY::GSLOTS; };
   auto issue_gates = [&](int cg, int slot_of) {
@@ -315,24 +320,25 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob (&jbs)[NH],
   // chunk c into stage `stage`; offsets wrap modulo 2^32 like the byte
   // offsets they stand for (the host keeps one sequence below 4 GiB)
   auto issue = [&](int cs, int stage) {
-    const unsigned sb = (unsigned)(stage * LY::STAGE);
+    const unsigned sb = smem_lds + (unsigned)(stage * LY::STAGE);
     const int c = phys(cs);
     const bool full = (c + 1) * CH <= len;
 #pragma unroll
-    for (int q = 0; q < LPC_HI; ++q) {
-      if (q < LPC_HI - 1 || lpc_hi) {
+    for (int k = 0; k < NBW; ++k) {
+      if (k < NBW - 1 || nbw == NBW) {
+        const int blk = w + NW * k;
         unsigned voff;
         if (full) {
-          voff = voff0[q] + (unsigned)c * (unsigned)cstride_b;
+          voff = voff0[k] + (unsigned)c * (unsigned)cstride_b;
         } else {
-          const int bb = blk_of(q);
-          const int pos = 64 * (bb % G) + lane;
-          const int row = pos / G, pc = pos % G;
-          const int piece = (pc == G - 1) ? 0 : pc;
+          int row;
+          const int po = piece_off(blk, row);
           const int tt = (c * CH + row < len) ? c * CH + row : len - 1;
-          voff = (unsigned)((relrow(tt) * D + piece * EP) * (int64_t)sizeof(T));
+          voff = (unsigned)((relrow(tt) * D + po) * (int64_t)sizeof(T));
         }
-        dma16(src_of[q], voff, dst_of[q] + sb);
+#pragma unroll
+        for (int ten = 0; ten < NLOAD; ++ten)
+          dma16(tensor_base(ten), voff, sb + (unsigned)((SLOT0 + ten) * TB + blk * 1024));
       }
     }
     if (GATED && gwave) issue_gates(cs + 1 < nch ? cs + 1 : nch - 1, cs + 1);
@@ -372,6 +378,9 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob (&jbs)[NH],
   // 582.7 -> 564.1 us (plain whole-row stores: no gain).
   constexpr bool OSTAGE = OUT && sizeof(T) == 2 && D == 128;
   T ohold[NH][4][4];
+  // NH = 2: row dots of the first walk's queries with the second's outputs
+  constexpr bool rkw = RK && NH == 2 && OSTAGE;
+  static_assert(!RK || rkw, "row dots: two walks, bf16 at d = 128");
   unsigned ooff0[4];  // element offset (chunk 0) of the lane's outputs in each 16-row block
   const bool und = !GATED && jb.first_undecayed;  // wave-uniform
   // lambda^(i+1) (or lambda^i for a start state that already carries the
@@ -495,7 +504,8 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob (&jbs)[NH],
       wait_vm_barrier<0>();
     } else {
       const int later = (nch - 1 - c < S - 2) ? nch - 1 - c : S - 2;
-      wait_chunk<LPC_HI, S - 2>(wait_hi, later);  // chunk c landed; chunk c-1 consumed
+      // chunk c landed; chunk c-1 consumed
+      wait_chunk3<NBW * NLOAD, (NBW - 1) * NLOAD, NBW_LAST * NLOAD + 1, S - 2>(wcls, later);
       if (c + S - 1 < nch) issue(c + S - 1, st_next);
       st_next = (st_next + 1 == S) ? 0 : st_next + 1;
     }
@@ -689,35 +699,60 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob (&jbs)[NH],
           }
         }
       }
-      if constexpr (OSTAGE) {
-        // the chunk's O tile through the Q slot: each wave writes its 16
-        // columns of every token, then stores 8 whole rows, 16 bytes per lane
-        lds_barrier();  // every wave is done reading Q
+    }
+
+    // ---- the chunk's O tile through LDS: each wave writes its 16 columns of
+    // every token, then stores 8 whole rows, 16 bytes per lane.  One walk:
+    // through its Q tile, right after the outputs.  Two walks (NH = 2): after
+    // the state updates, through the tiles no longer read then (the first
+    // walk's keys, the second walk's queries), so that the first walk's
+    // queries stay in place; RK dots them with the second walk's output rows
+    // on the way out.
+    auto flush_o = [&]() {
+      auto oslot = [](int h) { return NH == 2 ? (h == 0 ? 2 : 1) : 0; };
+      lds_barrier();  // every wave is done reading the tiles written below
 #pragma unroll
-        for (int h = 0; h < NH; ++h) {
-          char* const sO = const_cast<char*>(stage + qslot(h) * TB);
+      for (int h = 0; h < NH; ++h) {
+        char* const sO = const_cast<char*>(stage + oslot(h) * TB);
 #pragma unroll
-          for (int it = 0; it < 4; ++it)
-            *reinterpret_cast<u32x2*>(sO + TN::off(16 * it + l16, col + 4 * g)) =
-                *reinterpret_cast<const u32x2*>(ohold[h][it]);
-        }
-        lds_barrier();
+        for (int it = 0; it < 4; ++it)
+          *reinterpret_cast<u32x2*>(sO + TN::off(16 * it + l16, col + 4 * g)) =
+              *reinterpret_cast<const u32x2*>(ohold[h][it]);
+      }
+      lds_barrier();
 #pragma unroll
-        for (int h = 0; h < NH; ++h) {
-          const char* const sO = stage + qslot(h) * TB;
+      for (int h = 0; h < NH; ++h) {
+        const char* const sO = stage + oslot(h) * TB;
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int row = 8 * w + 4 * hh + (lane >> 4);  // 16 lanes per 256-byte row
-            const int piece = lane & 15;
-            if (c * CH + row < len) {
-              const u32x4 val = *reinterpret_cast<const u32x4*>(sO + TN::off(row, 8 * piece));
+        for (int hh = 0; hh < 2; ++hh) {
+          const int row = 8 * w + 4 * hh + (lane >> 4);  // 16 lanes per 256-byte row
+          const int piece = lane & 15;
+          const bool valid = c * CH + row < len;
+          if (rkw && h == 1) {
+            const u32x4 val = *reinterpret_cast<const u32x4*>(sO + TN::off(row, 8 * piece));
+            const u32x4 kq =
+                *reinterpret_cast<const u32x4*>(stage + qslot(0) * TB + TN::off(row, 8 * piece));
+            const T* a8 = reinterpret_cast<const T*>(&kq);
+            const T* b8 = reinterpret_cast<const T*>(&val);
+            float d = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) d += X::to_f(a8[e]) * X::to_f(b8[e]);
+#pragma unroll
+            for (int m = 8; m >= 1; m >>= 1) d += __shfl_xor(d, m, 16);
+            if (valid) {
+              if (piece == 0) jbs[NH - 1].rk[relrow(c * CH + row)] = d;
               T* orow = Oseq[h] + (unsigned)((relrow(c * CH + row)) * D + 8 * piece);
               __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(orow));
             }
+          } else if (valid) {
+            const u32x4 val = *reinterpret_cast<const u32x4*>(sO + TN::off(row, 8 * piece));
+            T* orow = Oseq[h] + (unsigned)((relrow(c * CH + row)) * D + 8 * piece);
+            __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(orow));
           }
         }
       }
-    }
+    };
+    if constexpr (OSTAGE && NH == 1) flush_o();
 
     // ---- state update: S = lambda^cl S + K^T (diag(lambda^(cl-1-j)) V)
     {
@@ -753,6 +788,7 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob (&jbs)[NH],
           for (int x = 0; x < E; ++x) wv[js][x] *= lamC;
       }
     }
+    if constexpr (OSTAGE && NH == 2) flush_o();
     // GATED: the next chunk's tables (its gates came with this chunk's
     // tiles), while the update runs on the matrix cores; the next barrier
     // publishes them

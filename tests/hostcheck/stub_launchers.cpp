@@ -73,9 +73,10 @@ hipError_t launch_fwd_u(const FwdArgs& a, int dtype, int, int64_t nitems, hipStr
   return hipSuccess;
 }
 
-hipError_t launch_fwd_duo(const FwdArgs& a, const FwdArgs& b, int dtype, int, int64_t nitems,
+hipError_t launch_fwd_duo(const FwdArgs& a, const FwdArgs& b, int dtype, int D, int64_t nitems,
                           hipStream_t) {
   if (nitems <= 0) return hipSuccess;
+  expect(!a.rk && (!b.rk || (b.gated && D == 128)), "row dots: gated, d = 128, second set");
   check_fwd(a, nitems);
   check_fwd(b, nitems);
   expect(dtype == 0, "joint dV/dK walk is bf16 only");
@@ -136,7 +137,8 @@ hipError_t launch_gate_anchors(const float* WfT, const float* WrT, const float* 
 hipError_t launch_gate_grad(int, int, const void* Q, const void* dQ, const void* K, const void* dK,
                             float* dG, float* tot, const float*, const float*, int64_t, int64_t,
                             hipStream_t) {
-  expect(Q && dQ && K && dK && dG && tot, "gate gradient");
+  // K, dK null: dG holds k . dk from the joint dV/dK walk
+  expect(Q && dQ && dG && tot && ((K == nullptr) == (dK == nullptr)), "gate gradient");
   ++g_launches;
   return hipSuccess;
 }
