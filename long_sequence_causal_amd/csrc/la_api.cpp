@@ -475,19 +475,24 @@ bool sweep_slots_valid(const Plan& c, const Plan& f, int64_t step) {
 // sweeps' sub-segment log-gates (reused), shifted gates [nseq][Ls], the final
 // dQ-sweep state [nseq][D][D] and one anchor per 1024-token block
 struct GatedBwdWs {
-  size_t A, A2, W, W2, W3, LD, Gs, SE, TOT, total;
+  size_t A, A2, W, W2, W3, Wc, W2c, W3c, LD, Gs, SE, TOT, total;
 };
 GatedBwdWs gated_bwd_ws(const Plan& p0) {
   const Plan p = gated_bwd_plan(p0);
+  int64_t step = 1;
+  const Plan pc = gated_sweep_plan(p0, p, &step);
   GatedBwdWs w;
   auto up = [](size_t b) { return (b + 255) / 256 * 256; };
   const size_t DD4 = (size_t)p.D * p.D * sizeof(float);
   size_t o = 0;
   w.A = o;  o += up((size_t)p.nseq * DD4);
   w.A2 = o; o += up((size_t)p.nseq * DD4);
-  w.W = o;  o += up(scan_ws_bytes(p));
+  w.W = o;  o += up(scan_ws_bytes(p));   // 1024-row states (forward)
   w.W2 = o; o += up(scan_ws_bytes(p));
-  w.W3 = o; o += up(scan_ws_bytes(p));
+  w.W3 = o; o += up(scan_ws_bytes(p));   // (reverse, transposed)
+  w.Wc = o;  o += up(scan_ws_bytes(pc));  // the sweeps' own start states
+  w.W2c = o; o += up(scan_ws_bytes(pc));
+  w.W3c = o; o += up(scan_ws_bytes(pc));
   w.LD = o; o += up((size_t)p.nseq * (size_t)(p.split > 1 ? p.split - 1 : 0) * sizeof(float));
   w.Gs = o; o += up((size_t)p.nseq * (size_t)p.Ls * sizeof(float));
   w.SE = o; o += up((size_t)p.nseq * DD4);
@@ -546,6 +551,9 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
   float* W = reinterpret_cast<float*>(base + L.W);    // forward sweep: S^T starts
   float* W2 = reinterpret_cast<float*>(base + L.W2);  // dV sweep: G starts
   float* W3 = reinterpret_cast<float*>(base + L.W3);  // dK sweep: G^T starts
+  float* Wc = reinterpret_cast<float*>(base + L.Wc);  // the same on the sweeps' plan
+  float* W2c = reinterpret_cast<float*>(base + L.W2c);
+  float* W3c = reinterpret_cast<float*>(base + L.W3c);
   float* LDw = reinterpret_cast<float*>(base + L.LD);
   float* Gs = reinterpret_cast<float*>(base + L.Gs);
   float* SE = reinterpret_cast<float*>(base + L.SE);
@@ -571,13 +579,33 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
     if ((e = la::launch_prep(pa, st)) != hipSuccess) return hip_fail(e, "prep launch");
     start = A;
   }
+  // The sweeps walk plc (sub-segments of step x 1024 tokens) from start
+  // states formed on that plan, and write the 1024-row states the log-gate
+  // anchors need (W and W3) themselves as they pass those rows; every such
+  // row then has to end a chunk of the reverse sweeps too, which holds when
+  // Ls % 64 == 0.  Otherwise (with the log-gate gradient asked for) the
+  // pre-passes and scans run on the 1024-token plan, which gives those
+  // states directly, and the sweeps start from every step-th of them.
+  const bool fine = dlog_alpha && pl.Ls % kChunk != 0;
+  const Plan& pf = fine ? pl : plc;    // plan of the forward start states
+  const Plan& prf = fine ? plr : plrc;  // and of the reverse ones
+  float* const Wf = fine ? W : Wc;
+  float* const W2f = fine ? W2 : W2c;
+  float* const W3f = fine ? W3 : W3c;
+  const int sstep = fine ? (int)step : 1;
+  const bool dumps = dlog_alpha && !fine;
   const bool need_send = dlog_alpha && dS_end;
-  r = run_states(pl, s->dtype, H, s->nseg, V, K, nullptr, start, W, 0, st, true, log_alpha, LDw);
+  r = run_states(pf, s->dtype, H, s->nseg, V, K, nullptr, start, Wf, 0, st, true, log_alpha, LDw);
   if (r != LA_OK) return r;
   la::FwdArgs aq = main_args(plc, H, s->nseg, dO, V, K, nullptr, start, dQ,
-                             need_send ? SE : nullptr, W, 0, true, log_alpha);
-  aq.sws_nper = pl.split - 1;
-  aq.sws_step = (int)step;
+                             need_send ? SE : nullptr, Wf, 0, true, log_alpha);
+  aq.sws_nper = pf.split - 1;
+  aq.sws_step = sstep;
+  if (dumps) {
+    aq.dump = W;
+    aq.dump_rows = (int)kGateBlock;
+    aq.dump_rev = 0;
+  }
 
   // reverse sweeps: from token t+1 back to t with alpha_{t+1}
   if ((e = la::launch_shift_gates(log_alpha, Gs, pl.nseq, pl.Ls, st)) != hipSuccess)
@@ -588,10 +616,10 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
   // start states are the transposes of the dV sweep's.  One pre-pass and scan
   // serve both, and the two sweeps share their Q and dO reads
   // (launch_sweeps).
-  r = run_states(plr, s->dtype, H, s->nseg, Q, dO, nullptr, dS_end, W2, 1, st, true, Gs, LDw);
+  r = run_states(prf, s->dtype, H, s->nseg, Q, dO, nullptr, dS_end, W2f, 1, st, true, Gs, LDw);
   if (r != LA_OK) return r;
-  if (pl.split > 1) {
-    e = la::launch_transpose_copy(W2, W3, pl.nseq * (pl.split - 1), pl.D, st);
+  if (prf.split > 1) {
+    e = la::launch_transpose_copy(W2f, W3f, prf.nseq * (prf.split - 1), prf.D, st);
     if (e != hipSuccess) return hip_fail(e, "transpose launch");
   }
   const float* startK = nullptr;
@@ -608,12 +636,17 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
     // the dQ sweep (aq) and the dV and dK sweeps (launch_sweeps): the start
     // states of all three are ready, and both plans have plc.split walks
     // per sequence
-    la::FwdArgs av = main_args(plrc, H, s->nseg, K, Q, dO, nullptr, dS_end, dV, dS0, W2, 1,
+    la::FwdArgs av = main_args(plrc, H, s->nseg, K, Q, dO, nullptr, dS_end, dV, dS0, W2f, 1,
                                true, Gs);
-    la::FwdArgs ak = main_args(plrc, H, s->nseg, V, dO, Q, nullptr, startK, dK, nullptr, W3, 1,
+    la::FwdArgs ak = main_args(plrc, H, s->nseg, V, dO, Q, nullptr, startK, dK, nullptr, W3f, 1,
                                true, Gs);
-    av.sws_nper = ak.sws_nper = plr.split - 1;
-    av.sws_step = ak.sws_step = (int)step;
+    av.sws_nper = ak.sws_nper = prf.split - 1;
+    av.sws_step = ak.sws_step = sstep;
+    if (dumps) {
+      ak.dump = W3;  // G^T at the 1024-token rows, numbered from the end
+      ak.dump_rows = (int)kGateBlock;
+      ak.dump_rev = 1;
+    }
     // the joint dV/dK walk (bf16, d = 128) also leaves k_t . dk_t per token
     // in dlog_alpha for the log-gate gradient below
     if (rk_from_walk) ak.rk = dlog_alpha;

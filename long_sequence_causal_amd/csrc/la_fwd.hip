@@ -22,7 +22,8 @@ __device__ inline int64_t sws_slot(const FwdArgs& a, int p) {
 // sequence wg / p_count.  NH = 2: the same item of a1 as well, walked by
 // the same waves beside it (a1 has a0's plan, positions and decay, and a0's
 // values and keys as its keys and values).
-template <typename T, int D, bool WITH_O, bool GATED, int NH = 1, bool ACCU = false, bool RK = false>
+template <typename T, int D, bool WITH_O, bool GATED, int NH = 1, bool ACCU = false, bool RK = false,
+          bool DUMP = false>
 __device__ __forceinline__ void chunk_item(const FwdArgs& a0, const FwdArgs& a1, int64_t wg) {
   constexpr int NSLOT = (NH == 2 || ACCU) ? 4 : (WITH_O ? 3 : 2);
   typedef FwdLayout<T, D, NSLOT, GATED, NH> LY;
@@ -66,6 +67,13 @@ __device__ __forceinline__ void chunk_item(const FwdArgs& a0, const FwdArgs& a1,
     jb[u].last_chunk_first = a.last_chunk_first;
     jb[u].first_undecayed = !GATED && x.s0_undecayed && x.start_from_state && p == 0;
     jb[u].rk = (RK && u == 1) ? x.rk + n * a.Ls : nullptr;
+    jb[u].dump = nullptr;
+    if (DUMP && WITH_O && x.dump) {
+      jb[u].dump_rows = x.dump_rows;
+      jb[u].ndump = (int)((a.Ls + x.dump_rows - 1) / x.dump_rows - 1);
+      jb[u].dump_rev = x.dump_rev;
+      jb[u].dump = x.dump + n * (int64_t)jb[u].ndump * D * D;
+    }
 
     // ---- start state -> accumulators (wave w: columns [16 w, 16 w + 16))
     const float* sp = nullptr;
@@ -98,7 +106,7 @@ __device__ __forceinline__ void chunk_item(const FwdArgs& a0, const FwdArgs& a1,
   // loop, i.e. on every chunk, which would also drain the chunk prefetches.
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
-  const float lgate = walk<T, D, WITH_O, NSLOT, GATED, NH, RK>(smem, jb, accS, accU);
+  const float lgate = walk<T, D, WITH_O, NSLOT, GATED, NH, RK, DUMP>(smem, jb, accS, accU);
   if constexpr (ACCU) {
     if (p >= 1) {
       float* dst = a.Uout + (n * (a.split - 1) + (a.split - 1 - p)) * (int64_t)D * D;
@@ -166,12 +174,13 @@ __global__ __launch_bounds__((FwdLayout<T, D, 3, GATED>::NT),
   const int r = (int)(blk % 24);
   const int64_t item = 8 * (blk / 24) + (r % 8);
   if (item >= nitems) return;
+  // (the gated backward asks its dQ and dK walks for their 1024-row states)
   if (r < 8)
-    chunk_item<T, D, true, GATED>(a, a, item);
+    chunk_item<T, D, true, GATED, 1, false, false, GATED>(a, a, item);
   else if (r < 16)
-    chunk_item<T, D, true, GATED>(b, b, item);
+    chunk_item<T, D, true, GATED, 1, false, false, GATED>(b, b, item);
   else
-    chunk_item<T, D, true, GATED>(c, c, item);
+    chunk_item<T, D, true, GATED, 1, false, false, GATED>(c, c, item);
 }
 
 template <typename T, int D>
@@ -209,7 +218,7 @@ template <typename T, int D, bool GATED, bool RK>
 __global__ __launch_bounds__((FwdLayout<T, D, 4, GATED, 2>::NT),
                              (FwdLayout<T, D, 4, GATED, 2>::WAVES_PER_EU)) void k_chunk_fwd_duo(
     FwdArgs a, FwdArgs b) {
-  chunk_item<T, D, true, GATED, 2, false, RK>(a, b, blockIdx.x);
+  chunk_item<T, D, true, GATED, 2, false, RK, GATED>(a, b, blockIdx.x);
 }
 
 template <typename T, int D>
@@ -251,6 +260,14 @@ hipError_t launch_fwd_duo(const FwdArgs& a, const FwdArgs& b, int dtype, int D, 
   return hipErrorInvalidValue;
 }
 
+// The gated chunk kernel with outputs that also writes the state at the
+// boundary rows a.dump asks for (the gated backward's dQ sweep).
+template <typename T, int D>
+__global__ __launch_bounds__((FwdLayout<T, D, 3, true>::NT),
+                             (FwdLayout<T, D, 3, true>::WAVES_PER_EU)) void k_chunk_fwd_dump(FwdArgs a) {
+  chunk_item<T, D, true, true, 1, false, false, true>(a, a, blockIdx.x);
+}
+
 // The chunk kernel with outputs whose walks also form each sub-segment's U
 // (fixed decay; four tiles a stage: Q, K, V and Q2).
 template <typename T, int D>
@@ -275,7 +292,11 @@ hipError_t launch_fwd_u(const FwdArgs& a, int dtype, int D, int64_t nitems, hipS
 
 template <typename T, int D, bool GATED>
 static hipError_t launch_fwd_t(const FwdArgs& a, bool with_o, int64_t nwg, hipStream_t s) {
-  if (with_o)
+  if (a.dump) {
+    if (!GATED || !with_o) return hipErrorInvalidValue;  // (built for the gated dQ sweep only)
+    hipLaunchKernelGGL((k_chunk_fwd_dump<T, D>), dim3((unsigned)nwg),
+                       dim3(FwdLayout<T, D, 3, true>::NT), 0, s, a);
+  } else if (with_o)
     hipLaunchKernelGGL((k_chunk_fwd<T, D, true, GATED>), dim3((unsigned)nwg),
                        dim3(FwdLayout<T, D, 3, GATED>::NT), 0, s, a);
   else

@@ -86,6 +86,15 @@ struct FwdArgs {
   // [nseq][Ls] floats, over the bf16 outputs in fp32 (the gated backward's
   // k_t . dk_t)
   float* rk;
+  // launches with outputs (may be null): the state at every boundary row
+  // y = m * dump_rows (0 < y < Ls) of each sequence, to
+  // dump[n][m - 1] ([nseq][ceil(Ls / dump_rows) - 1][D][D]), or to
+  // dump[n][ceil(Ls / dump_rows) - 1 - m] when dump_rev; written by the walk
+  // whose chunk ends there (reverse sweeps: at Ls % 64 == 0 every such row
+  // ends a chunk)
+  float* dump;
+  int dump_rows;
+  int dump_rev;
 };
 
 // dst[n] = f(src[n]) for nseq D x D fp32 states: optional transpose, then a

@@ -168,6 +168,12 @@ struct WalkJob {
   // rk[row] = (the first walk's query row) . (this walk's output row) over
   // the bf16 outputs, in fp32; sequence base like the tensors
   float* rk;
+  // output walks built with DUMP (may be null): after every chunk that ends on a boundary
+  // row y = m * dump_rows (0 < y < Ls) of the sequence, this walk's state
+  // goes to dump[slot] ([ndump][D][D], the sequence's own), slot y / dump_rows
+  // - 1, or ndump - y / dump_rows when dump_rev (numbered from the end)
+  float* dump;
+  int dump_rows, ndump, dump_rev;
 };
 
 // Walk the range with the state in accS (wave w: columns [16 w, 16 w + 16),
@@ -207,7 +213,8 @@ struct WalkJob {
 // local state of each sub-segment for the reverse dV and dK sweeps, formed
 // from the dO tiles the dQ sweep reads anyway instead of by a pre-pass that
 // reads Q and dO again.
-template <typename T, int D, bool OUT, int NSLOT, bool GATED = false, int NH = 1, bool RK = false>
+template <typename T, int D, bool OUT, int NSLOT, bool GATED = false, int NH = 1, bool RK = false,
+          bool DUMP = false>
 __device__ __forceinline__ float walk(char* smem, const WalkJob (&jbs)[NH],
                                       f32x4 (&accS)[NH][D / 16], f32x4* accU = nullptr) {
   typedef Elt<T> X;
@@ -789,6 +796,30 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob (&jbs)[NH],
       }
     }
     if constexpr (OSTAGE && NH == 2) flush_o();
+    // ---- DUMP: the state at a boundary row, for callers that need it there
+    // (compiled into the walks that may be asked for it only: its mere
+    // presence slowed the other walks' chunk loop by a tenth)
+    if constexpr (OUT && DUMP) {
+      const int64_t pe = t0 + (int64_t)c * CH + cl;  // position after the chunk
+      const int64_t y = jb.reverse ? jb.Ls - pe : pe;
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const WalkJob& jh = jbs[h];
+        if (jh.dump && y > 0 && y < jb.Ls && y % jh.dump_rows == 0) {
+          const int m = (int)(y / jh.dump_rows);
+          float* dst = jh.dump + (int64_t)(jh.dump_rev ? jh.ndump - m : m - 1) * D * D;
+          // the lane's element offset, formed here: without the empty asm the
+          // compiler hoists all NKT x 4 store addresses out of the chunk loop
+          // and keeps them in registers the walk needs
+          unsigned lo = (unsigned)(4 * g * D + col + l16);
+          asm volatile("" : "+v"(lo));
+#pragma unroll
+          for (int tk = 0; tk < NKT; ++tk)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[lo + (unsigned)((16 * tk + r) * D)] = accS[h][tk][r];
+        }
+      }
+    }
     // GATED: the next chunk's tables (its gates came with this chunk's
     // tiles), while the update runs on the matrix cores; the next barrier
     // publishes them
