@@ -266,12 +266,11 @@ la_status run_flow(const Plan& pl, int dtype, int H, int nseg, const void* Q, co
 // and dK, whose keys and values are crosswise the same Q and dO).  bf16: the
 // dQ sweep, then one workgroup per item walking both dV and dK over one
 // stream of Q, K, V, dO tiles (4 tile loads per chunk instead of 6, one set
-// of barriers and decay factors for two walks).  fp32, and gated d = 64
-// (whose joint walk has no spare load slot for the gates): one launch of
-// the three, the paired dV and dK workgroups on one XCD beside the dQ walks.
+// of barriers and decay factors for two walks).  fp32: one launch of the
+// three, the paired dV and dK workgroups on one XCD beside the dQ walks.
 hipError_t launch_sweeps(const la::FwdArgs& aq, const la::FwdArgs& av, const la::FwdArgs& ak,
                          int dtype, int D, int64_t nitems, hipStream_t st) {
-  if (dtype == LA_BF16 && !(aq.gated && D == 64)) {
+  if (dtype == LA_BF16) {
     hipError_t e = la::launch_fwd(aq, dtype, D, true, nitems, st);
     if (e != hipSuccess) return e;
     return la::launch_fwd_duo(av, ak, dtype, D, nitems, st);
@@ -475,7 +474,7 @@ bool sweep_slots_valid(const Plan& c, const Plan& f, int64_t step) {
 // sweeps' sub-segment log-gates (reused), shifted gates [nseq][Ls], the final
 // dQ-sweep state [nseq][D][D] and one anchor per 1024-token block
 struct GatedBwdWs {
-  size_t A, A2, W, W2, W3, Wc, W2c, W3c, LD, Gs, SE, TOT, total;
+  size_t A, A2, W, W2, W3, Wc, W2c, W3c, LD, LDr, Gs, RQ, SE, TOT, total;
 };
 GatedBwdWs gated_bwd_ws(const Plan& p0) {
   const Plan p = gated_bwd_plan(p0);
@@ -494,7 +493,9 @@ GatedBwdWs gated_bwd_ws(const Plan& p0) {
   w.W2c = o; o += up(scan_ws_bytes(pc));
   w.W3c = o; o += up(scan_ws_bytes(pc));
   w.LD = o; o += up((size_t)p.nseq * (size_t)(p.split > 1 ? p.split - 1 : 0) * sizeof(float));
+  w.LDr = o; o += up((size_t)pc.nseq * (size_t)(pc.split > 1 ? pc.split - 1 : 0) * sizeof(float));
   w.Gs = o; o += up((size_t)p.nseq * (size_t)p.Ls * sizeof(float));
+  w.RQ = o; o += up((size_t)p.nseq * (size_t)p.Ls * sizeof(float));  // q_t . dq_t
   w.SE = o; o += up((size_t)p.nseq * DD4);
   w.TOT = o; o += up((size_t)p.nseq * (size_t)la::gate_grad_blocks(p.Ls) * sizeof(float));
   w.total = o;
@@ -555,6 +556,8 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
   float* W2c = reinterpret_cast<float*>(base + L.W2c);
   float* W3c = reinterpret_cast<float*>(base + L.W3c);
   float* LDw = reinterpret_cast<float*>(base + L.LD);
+  float* LDr = reinterpret_cast<float*>(base + L.LDr);
+  float* RQ = reinterpret_cast<float*>(base + L.RQ);
   float* Gs = reinterpret_cast<float*>(base + L.Gs);
   float* SE = reinterpret_cast<float*>(base + L.SE);
   float* TOT = reinterpret_cast<float*>(base + L.TOT);
@@ -613,11 +616,46 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
   // dv_t = G_t^T k_t, G accumulating q dO^T from dS_end (the first reverse
   // step multiplies by 1); its final value G_1 gives dS0 = alpha_1 G_1.
   // dk_t = G_t v_t: the same reverse recurrence for G^T, whose sub-segment
-  // start states are the transposes of the dV sweep's.  One pre-pass and scan
-  // serve both, and the two sweeps share their Q and dO reads
-  // (launch_sweeps).
-  r = run_states(prf, s->dtype, H, s->nseg, Q, dO, nullptr, dS_end, W2f, 1, st, true, Gs, LDw);
-  if (r != LA_OK) return r;
+  // start states are the transposes of the dV sweep's.  One set of local
+  // states and one scan serve both, and the two sweeps share their Q and dO
+  // reads (launch_sweeps).
+  //
+  // bf16 on the sweeps' plan: the dQ walk (four tiles: dO, V, K, Q) forms the
+  // reverse sweeps' local states U = sum_t (gates of t0+1 .. t) q_t dO_t^T
+  // and their reverse log-gates itself, instead of a pre-pass reading Q and
+  // dO again, and at d = 128 leaves q_t . dq_t per token for the log-gate
+  // gradient.
+  const bool fused = s->dtype == LA_BF16 && !fine;
+  const bool rk_from_walk = dlog_alpha && s->dtype == LA_BF16 && pl.D == 128;
+  const bool rq_from_walk = rk_from_walk && fused;
+  if (fused) {
+    aq.Q2 = Q;
+    aq.Uout = W2f;
+    aq.LDrev = LDr;
+    if (rq_from_walk) aq.rk = RQ;
+    if ((e = la::launch_fwd_u(aq, s->dtype, pl.D, plc.nseq * plc.split, st)) != hipSuccess)
+      return hip_fail(e, "dQ sweep launch");
+    if (plc.split > 1) {
+      la::ScanArgs sa;
+      std::memset(&sa, 0, sizeof(sa));
+      sa.nseq = plc.nseq;
+      sa.P = plc.split - 1;
+      sa.E = (int64_t)plc.D * plc.D;
+      sa.dS = W2f;
+      sa.H = H;
+      sa.hdiv = s->nseg;
+      sa.seg_len = plc.Lp;
+      sa.S0 = dS_end;
+      sa.Sout = W2f;
+      sa.inclusive = 1;
+      sa.gated = 1;
+      sa.LD = LDr;
+      if ((e = la::launch_scan(sa, st)) != hipSuccess) return hip_fail(e, "state scan launch");
+    }
+  } else {
+    r = run_states(prf, s->dtype, H, s->nseg, Q, dO, nullptr, dS_end, W2f, 1, st, true, Gs, LDw);
+    if (r != LA_OK) return r;
+  }
   if (prf.split > 1) {
     e = la::launch_transpose_copy(W2f, W3f, prf.nseq * (prf.split - 1), prf.D, st);
     if (e != hipSuccess) return hip_fail(e, "transpose launch");
@@ -631,11 +669,9 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
     if ((e = la::launch_prep(pa, st)) != hipSuccess) return hip_fail(e, "prep launch");
     startK = A2;
   }
-  const bool rk_from_walk = dlog_alpha && s->dtype == LA_BF16 && pl.D == 128;
   {
-    // the dQ sweep (aq) and the dV and dK sweeps (launch_sweeps): the start
-    // states of all three are ready, and both plans have plc.split walks
-    // per sequence
+    // the dV and dK sweeps (with the dQ sweep unless it ran above): the start
+    // states are ready, and both plans have plc.split walks per sequence
     la::FwdArgs av = main_args(plrc, H, s->nseg, K, Q, dO, nullptr, dS_end, dV, dS0, W2f, 1,
                                true, Gs);
     la::FwdArgs ak = main_args(plrc, H, s->nseg, V, dO, Q, nullptr, startK, dK, nullptr, W3f, 1,
@@ -650,8 +686,11 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
     // the joint dV/dK walk (bf16, d = 128) also leaves k_t . dk_t per token
     // in dlog_alpha for the log-gate gradient below
     if (rk_from_walk) ak.rk = dlog_alpha;
-    if ((e = launch_sweeps(aq, av, ak, s->dtype, pl.D, plc.nseq * plc.split, st)) != hipSuccess)
-      return hip_fail(e, "sweep launch");
+    if (fused)
+      e = la::launch_fwd_duo(av, ak, s->dtype, pl.D, plc.nseq * plc.split, st);
+    else
+      e = launch_sweeps(aq, av, ak, s->dtype, pl.D, plc.nseq * plc.split, st);
+    if (e != hipSuccess) return hip_fail(e, "sweep launch");
   }
   if (dS0 && (e = la::launch_scale_first_gate(dS0, log_alpha, pl.nseq, pl.Ls, pl.D, st)) != hipSuccess)
     return hip_fail(e, "dS0 scale launch");
@@ -663,8 +702,8 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
                                 pl.Ls, pl.D, st);
     if (e != hipSuccess) return hip_fail(e, "gate anchor launch");
     e = la::launch_gate_grad(s->dtype, pl.D, Q, dQ, rk_from_walk ? nullptr : K,
-                             rk_from_walk ? nullptr : dK, dlog_alpha, TOT, dS_end,
-                             need_send ? SE : nullptr, pl.nseq, pl.Ls, st);
+                             rk_from_walk ? nullptr : dK, rq_from_walk ? RQ : nullptr, dlog_alpha,
+                             TOT, dS_end, need_send ? SE : nullptr, pl.nseq, pl.Ls, st);
     if (e != hipSuccess) return hip_fail(e, "gate gradient launch");
   }
   return LA_OK;

@@ -66,7 +66,7 @@ __device__ __forceinline__ void chunk_item(const FwdArgs& a0, const FwdArgs& a1,
     jb[u].G = GATED ? a.G + n * a.Ls : nullptr;
     jb[u].last_chunk_first = a.last_chunk_first;
     jb[u].first_undecayed = !GATED && x.s0_undecayed && x.start_from_state && p == 0;
-    jb[u].rk = (RK && u == 1) ? x.rk + n * a.Ls : nullptr;
+    jb[u].rk = (RK && u == NH - 1) ? x.rk + n * a.Ls : nullptr;
     jb[u].dump = nullptr;
     if (DUMP && WITH_O && x.dump) {
       jb[u].dump_rows = x.dump_rows;
@@ -109,11 +109,18 @@ __device__ __forceinline__ void chunk_item(const FwdArgs& a0, const FwdArgs& a1,
   const float lgate = walk<T, D, WITH_O, NSLOT, GATED, NH, RK, DUMP>(smem, jb, accS, accU);
   if constexpr (ACCU) {
     if (p >= 1) {
-      float* dst = a.Uout + (n * (a.split - 1) + (a.split - 1 - p)) * (int64_t)D * D;
+      const int64_t slot = n * (a.split - 1) + (a.split - 1 - p);
+      float* dst = a.Uout + slot * (int64_t)D * D;
 #pragma unroll
       for (int tk = 0; tk < NKT; ++tk)
 #pragma unroll
         for (int r = 0; r < 4; ++r) dst[(16 * tk + 4 * g + r) * D + col + l16] = accU[tk][r];
+      // gated: the sub-segment's total log-gate as the reverse sweep steps
+      // through it (token t takes g_{t+1}; the sequence's last token 0)
+      if (GATED && threadIdx.x == 0) {
+        const float* gs = a.G + n * a.Ls;
+        a.LDrev[slot] = lgate - gs[t0] + (t1 < a.Ls ? gs[t1] : 0.0f);
+      }
     }
   }
 
@@ -224,18 +231,14 @@ __global__ __launch_bounds__((FwdLayout<T, D, 4, GATED, 2>::NT),
 template <typename T, int D>
 static hipError_t launch_duo_t(const FwdArgs& a, const FwdArgs& b, int64_t nitems, hipStream_t s) {
   if (a.gated) {
-    // (d = 64: 36 tile loads over 4 waves leave no wave a spare slot for
-    // the gates' load; those sweeps keep their own workgroups)
-    if constexpr (D == 64) {
-      return hipErrorInvalidValue;
-    } else {
-      if (b.rk)
-        hipLaunchKernelGGL((k_chunk_fwd_duo<T, D, true, true>), dim3((unsigned)nitems),
-                           dim3(FwdLayout<T, D, 4, true, 2>::NT), 0, s, a, b);
-      else
-        hipLaunchKernelGGL((k_chunk_fwd_duo<T, D, true, false>), dim3((unsigned)nitems),
-                           dim3(FwdLayout<T, D, 4, true, 2>::NT), 0, s, a, b);
-    }
+    if (!b.rk)
+      hipLaunchKernelGGL((k_chunk_fwd_duo<T, D, true, false>), dim3((unsigned)nitems),
+                         dim3(FwdLayout<T, D, 4, true, 2>::NT), 0, s, a, b);
+    else if constexpr (D == 128)
+      hipLaunchKernelGGL((k_chunk_fwd_duo<T, D, true, true>), dim3((unsigned)nitems),
+                         dim3(FwdLayout<T, D, 4, true, 2>::NT), 0, s, a, b);
+    else
+      return hipErrorInvalidValue;  // row dots: d = 128
   } else {
     if (b.rk) return hipErrorInvalidValue;  // (only the gated backward asks for the row dots)
     hipLaunchKernelGGL((k_chunk_fwd_duo<T, D, false, false>), dim3((unsigned)nitems),
@@ -269,25 +272,41 @@ __global__ __launch_bounds__((FwdLayout<T, D, 3, true>::NT),
 }
 
 // The chunk kernel with outputs whose walks also form each sub-segment's U
-// (fixed decay; four tiles a stage: Q, K, V and Q2).
-template <typename T, int D>
-__global__ __launch_bounds__((FwdLayout<T, D, 4, false>::NT),
-                             (FwdLayout<T, D, 4, false>::WAVES_PER_EU)) void k_chunk_fwd_u(FwdArgs a) {
-  chunk_item<T, D, true, false, 1, true>(a, a, blockIdx.x);
+// (four tiles a stage: Q, K, V and Q2).  Gated: also the sub-segments'
+// reverse log-gates (LDrev), the states at a.dump's rows, and with RK the
+// row dots of the outputs with Q2 (a.rk).
+template <typename T, int D, bool GATED, bool RK>
+__global__ __launch_bounds__((FwdLayout<T, D, 4, GATED>::NT),
+                             (FwdLayout<T, D, 4, GATED>::WAVES_PER_EU)) void k_chunk_fwd_u(FwdArgs a) {
+  chunk_item<T, D, true, GATED, 1, true, RK, GATED>(a, a, blockIdx.x);
+}
+
+template <int D>
+static hipError_t launch_u_t(const FwdArgs& a, int64_t nitems, hipStream_t s) {
+  typedef __bf16 T;
+  const dim3 grid((unsigned)nitems);
+  if (!a.gated)
+    hipLaunchKernelGGL((k_chunk_fwd_u<T, D, false, false>), grid,
+                       dim3(FwdLayout<T, D, 4, false>::NT), 0, s, a);
+  else if (!a.rk)
+    hipLaunchKernelGGL((k_chunk_fwd_u<T, D, true, false>), grid,
+                       dim3(FwdLayout<T, D, 4, true>::NT), 0, s, a);
+  else if constexpr (D == 128)
+    hipLaunchKernelGGL((k_chunk_fwd_u<T, D, true, true>), grid,
+                       dim3(FwdLayout<T, D, 4, true>::NT), 0, s, a);
+  else
+    return hipErrorInvalidValue;  // row dots: d = 128
+  return hipGetLastError();
 }
 
 hipError_t launch_fwd_u(const FwdArgs& a, int dtype, int D, int64_t nitems, hipStream_t s) {
   if (nitems <= 0) return hipSuccess;
-  if (a.gated || !a.Q2 || !a.Uout || !a.O) return hipErrorInvalidValue;
-  if (dtype == 0 && D == 64)
-    hipLaunchKernelGGL((k_chunk_fwd_u<__bf16, 64>), dim3((unsigned)nitems),
-                       dim3(FwdLayout<__bf16, 64, 4, false>::NT), 0, s, a);
-  else if (dtype == 0 && D == 128)
-    hipLaunchKernelGGL((k_chunk_fwd_u<__bf16, 128>), dim3((unsigned)nitems),
-                       dim3(FwdLayout<__bf16, 128, 4, false>::NT), 0, s, a);
-  else
-    return hipErrorInvalidValue;  // bf16 only
-  return hipGetLastError();
+  if (!a.Q2 || !a.Uout || !a.O || (a.gated && (!a.G || !a.LDrev)) || (a.rk && !a.gated))
+    return hipErrorInvalidValue;
+  if (dtype != 0) return hipErrorInvalidValue;  // bf16 only
+  if (D == 64) return launch_u_t<64>(a, nitems, s);
+  if (D == 128) return launch_u_t<128>(a, nitems, s);
+  return hipErrorInvalidValue;
 }
 
 template <typename T, int D, bool GATED>

@@ -58,12 +58,14 @@ __device__ inline float dot8(const T* a, const T* b) {
 // token (8 features each, D / 8 lanes in use), reduce across the 16 with
 // shuffles, then the block's reverse cumulative sum is taken in LDS:
 // dG[t] = sum_{u >= t in block} r_u, and the block total goes to tot[n][b]
-// (when tot is not null).  RK: k_u . dk_u comes from dG itself (formed by
-// the joint dV/dK walk), read before the block's values are written.
-template <typename T, int D, bool RK>
+// (when tot is not null).  MODE 1: k_u . dk_u comes from dG itself (formed
+// by the joint dV/dK walk), read before the block's values are written;
+// MODE 2: q_u . dq_u comes from rq too (formed by the dQ walk), so no
+// token tensor is read.
+template <typename T, int D, int MODE>
 __global__ __launch_bounds__(256) void k_gate_grad_blocks(const T* Q, const T* dQ, const T* K,
-                                                          const T* dK, float* dG, float* tot,
-                                                          int64_t Ls, int64_t nb) {
+                                                          const T* dK, const float* rq, float* dG,
+                                                          float* tot, int64_t Ls, int64_t nb) {
   static_assert(D / 8 <= 16, "16 lanes of 8 features cover a row");
   __shared__ float r[GBLK];
   const int64_t n = blockIdx.x / nb;
@@ -74,13 +76,17 @@ __global__ __launch_bounds__(256) void k_gate_grad_blocks(const T* Q, const T* d
   const int tok = threadIdx.x >> 4;   // 16 tokens per pass
   for (int i = tok; i < GBLK; i += 16) {
     float s = 0.0f;
-    if (i < len && sub < D / 8) {
-      const int64_t row = (n * Ls + t0 + i) * D + 8 * sub;
-      s = RK ? dot8(Q + row, dQ + row) : dot8(Q + row, dQ + row) - dot8(K + row, dK + row);
-    }
+    if constexpr (MODE == 2) {
+      if (sub == 0 && i < len) s = rq[n * Ls + t0 + i] - dG[n * Ls + t0 + i];
+    } else {
+      if (i < len && sub < D / 8) {
+        const int64_t row = (n * Ls + t0 + i) * D + 8 * sub;
+        s = MODE == 1 ? dot8(Q + row, dQ + row) : dot8(Q + row, dQ + row) - dot8(K + row, dK + row);
+      }
 #pragma unroll
-    for (int m = 8; m >= 1; m >>= 1) s += __shfl_xor(s, m, 16);
-    if (RK && i < len) s -= dG[n * Ls + t0 + i];
+      for (int m = 8; m >= 1; m >>= 1) s += __shfl_xor(s, m, 16);
+      if (MODE == 1 && i < len) s -= dG[n * Ls + t0 + i];
+    }
     if (sub == 0) r[i] = s;  // tokens past the end hold 0
   }
   __syncthreads();
@@ -180,18 +186,22 @@ hipError_t launch_gate_anchors(const float* WfT, const float* WrT, const float* 
 
 template <typename T, int D>
 static hipError_t gate_grad_t(const void* Q, const void* dQ, const void* K, const void* dK,
-                              float* dG, float* tot, const float* dSe, const float* SendT,
-                              int64_t nseq, int64_t Ls, hipStream_t s) {
+                              const float* rq, float* dG, float* tot, const float* dSe,
+                              const float* SendT, int64_t nseq, int64_t Ls, hipStream_t s) {
   (void)dSe;
   (void)SendT;
   const int64_t nb = gate_grad_blocks(Ls);
+  const dim3 grid((unsigned)(nseq * nb));
   // the block totals are not needed: tot already holds the anchors
-  if (K && dK)
-    hipLaunchKernelGGL((k_gate_grad_blocks<T, D, false>), dim3((unsigned)(nseq * nb)), dim3(256), 0,
-                       s, (const T*)Q, (const T*)dQ, (const T*)K, (const T*)dK, dG, nullptr, Ls, nb);
+  if (rq)
+    hipLaunchKernelGGL((k_gate_grad_blocks<T, D, 2>), grid, dim3(256), 0, s, nullptr, nullptr,
+                       nullptr, nullptr, rq, dG, nullptr, Ls, nb);
+  else if (K && dK)
+    hipLaunchKernelGGL((k_gate_grad_blocks<T, D, 0>), grid, dim3(256), 0, s, (const T*)Q,
+                       (const T*)dQ, (const T*)K, (const T*)dK, nullptr, dG, nullptr, Ls, nb);
   else
-    hipLaunchKernelGGL((k_gate_grad_blocks<T, D, true>), dim3((unsigned)(nseq * nb)), dim3(256), 0,
-                       s, (const T*)Q, (const T*)dQ, nullptr, nullptr, dG, nullptr, Ls, nb);
+    hipLaunchKernelGGL((k_gate_grad_blocks<T, D, 1>), grid, dim3(256), 0, s, (const T*)Q,
+                       (const T*)dQ, nullptr, nullptr, nullptr, dG, nullptr, Ls, nb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t all = nseq * Ls;
@@ -201,15 +211,16 @@ static hipError_t gate_grad_t(const void* Q, const void* dQ, const void* K, cons
 }
 
 hipError_t launch_gate_grad(int dtype, int D, const void* Q, const void* dQ, const void* K,
-                            const void* dK, float* dG, float* tot, const float* dSe,
-                            const float* SendT, int64_t nseq, int64_t Ls, hipStream_t s) {
+                            const void* dK, const float* rq, float* dG, float* tot,
+                            const float* dSe, const float* SendT, int64_t nseq, int64_t Ls,
+                            hipStream_t s) {
   if (nseq <= 0 || Ls <= 0) return hipSuccess;
   if (dtype == 0) {
-    if (D == 64) return gate_grad_t<__bf16, 64>(Q, dQ, K, dK, dG, tot, dSe, SendT, nseq, Ls, s);
-    if (D == 128) return gate_grad_t<__bf16, 128>(Q, dQ, K, dK, dG, tot, dSe, SendT, nseq, Ls, s);
+    if (D == 64) return gate_grad_t<__bf16, 64>(Q, dQ, K, dK, rq, dG, tot, dSe, SendT, nseq, Ls, s);
+    if (D == 128) return gate_grad_t<__bf16, 128>(Q, dQ, K, dK, rq, dG, tot, dSe, SendT, nseq, Ls, s);
   } else {
-    if (D == 64) return gate_grad_t<float, 64>(Q, dQ, K, dK, dG, tot, dSe, SendT, nseq, Ls, s);
-    if (D == 128) return gate_grad_t<float, 128>(Q, dQ, K, dK, dG, tot, dSe, SendT, nseq, Ls, s);
+    if (D == 64) return gate_grad_t<float, 64>(Q, dQ, K, dK, rq, dG, tot, dSe, SendT, nseq, Ls, s);
+    if (D == 128) return gate_grad_t<float, 128>(Q, dQ, K, dK, rq, dG, tot, dSe, SendT, nseq, Ls, s);
   }
   return hipErrorInvalidValue;
 }

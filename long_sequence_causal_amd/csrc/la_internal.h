@@ -76,15 +76,19 @@ struct FwdArgs {
   // rounding order changes); a sub-segment with a ragged chunk walks in order
   int last_chunk_first;
   // launch_fwd_u only: each sub-segment p >= 1 also forms
-  // U = sum_t lambda^(t - t0) Q2_t Q_t^T over its tokens (t0 its first) and
-  // writes it to Uout[n][split - 1 - p] ([nseq][split-1][D][D], the
-  // numbering of a reverse sweep whose sub-segments end where these start)
+  // U = sum_t w_t Q2_t Q_t^T over its tokens and writes it to
+  // Uout[n][split - 1 - p] ([nseq][split-1][D][D], the numbering of a
+  // reverse sweep whose sub-segments end where these start); w_t =
+  // lambda^(t - t0) (t0 the first token), gated the product of the gates of
+  // tokens t0+1 .. t; gated, the sub-segment's log-gate sum as that reverse
+  // sweep sees it (gates shifted by one token) goes to LDrev[n][split - 1 - p]
   const void* Q2;
   float* Uout;
-  // launch_fwd_duo only, in the second argument set (bf16, d = 128; may be
-  // null): rk[n][row] = (first set's Q row) . (second set's output row),
-  // [nseq][Ls] floats, over the bf16 outputs in fp32 (the gated backward's
-  // k_t . dk_t)
+  float* LDrev;
+  // gated, bf16, d = 128 (may be null): row dots [nseq][Ls] over the bf16
+  // outputs in fp32.  launch_fwd_duo, second argument set: rk[n][row] =
+  // (first set's Q row) . (second set's output row) (the gated backward's
+  // k_t . dk_t); launch_fwd_u: (Q2 row) . (output row) (q_t . dq_t)
   float* rk;
   // launches with outputs (may be null): the state at every boundary row
   // y = m * dump_rows (0 < y < Ls) of each sequence, to
@@ -220,9 +224,12 @@ hipError_t launch_gate_anchors(const float* WfT, const float* WrT, const float* 
                                int64_t Ls, int D, hipStream_t s);
 // dG[t] = the in-block suffix sum of r_u = q_u . dq_u - k_u . dk_u plus
 // tot[n][t / GBLK].  With K and dK null, dG must already hold k_t . dk_t per
-// token (the joint dV/dK walk's row dots) and is overwritten in place.
+// token (the joint dV/dK walk's row dots) and is overwritten in place; with
+// rq also given ([nseq][Ls]: q_t . dq_t from the dQ walk), Q and dQ are not
+// read either.
 hipError_t launch_gate_grad(int dtype, int D, const void* Q, const void* dQ, const void* K,
-                            const void* dK, float* dG, float* tot, const float* dSe,
-                            const float* SendT, int64_t nseq, int64_t Ls, hipStream_t s);
+                            const void* dK, const float* rq, float* dG, float* tot,
+                            const float* dSe, const float* SendT, int64_t nseq, int64_t Ls,
+                            hipStream_t s);
 
 }  // namespace la

@@ -164,9 +164,10 @@ struct WalkJob {
   // one walk of four tiles (NSLOT = 4, NH = 1): the keys of its second state
   // U = sum_t lambda^(t - t0) Q2_t Q_t^T (its values are this walk's queries)
   const void* Q2;
-  // NH = 2 with RK, second job (bf16 at d = 128): per position,
-  // rk[row] = (the first walk's query row) . (this walk's output row) over
-  // the bf16 outputs, in fp32; sequence base like the tensors
+  // RK, last job (bf16 at d = 128): per position, rk[row] = (this walk's
+  // output row) . (the first walk's query row when NH = 2, the Q2 row for
+  // one walk of four tiles) over the bf16 outputs, in fp32; sequence base
+  // like the tensors
   float* rk;
   // output walks built with DUMP (may be null): after every chunk that ends on a boundary
   // row y = m * dump_rows (0 < y < Ls) of the sequence, this walk's state
@@ -223,7 +224,7 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob (&jbs)[NH],
   constexpr bool ACCU = NSLOT == 4 && NH == 1;
   static_assert(NSLOT >= 3 || !OUT, "outputs need the Q slot and P");
   static_assert(NH == 1 || (OUT && NSLOT == 4), "two walks form outputs from four tiles");
-  static_assert(!ACCU || (OUT && !GATED), "the second state rides on a fixed-decay output walk");
+  static_assert(!ACCU || OUT, "the second state rides on an output walk");
   const WalkJob& jb = jbs[0];  // positions, direction, decay: shared
   typedef typename LY::TN TN;
   typedef typename LY::TP TP;
@@ -385,9 +386,11 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob (&jbs)[NH],
   // 582.7 -> 564.1 us (plain whole-row stores: no gain).
   constexpr bool OSTAGE = OUT && sizeof(T) == 2 && D == 128;
   T ohold[NH][4][4];
-  // NH = 2: row dots of the first walk's queries with the second's outputs
-  constexpr bool rkw = RK && NH == 2 && OSTAGE;
-  static_assert(!RK || rkw, "row dots: two walks, bf16 at d = 128");
+  // RK: row dots of the last walk's outputs with the first walk's queries
+  // (NH = 2) or with Q2 (one walk of four tiles), per position to the last
+  // job's rk
+  constexpr bool rkw = RK && (NH == 2 || ACCU) && OSTAGE;
+  static_assert(!RK || rkw, "row dots: two walks or four tiles, bf16 at d = 128");
   unsigned ooff0[4];  // element offset (chunk 0) of the lane's outputs in each 16-row block
   const bool und = !GATED && jb.first_undecayed;  // wave-uniform
   // lambda^(i+1) (or lambda^i for a start state that already carries the
@@ -427,6 +430,8 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob (&jbs)[NH],
     }
   }
   float gsum2 = 0.0f;  // total log2-gate of the chunks walked (GATED)
+  float gchunk2 = 0.0f;  // (GATED) the current chunk's total log2-gate
+  float ug0 = 0.0f;      // (GATED, ACCU) log2-gate of the walk's first token
   float dc = GATED ? 0.0f : lamC;  // decay of the state over the current chunk
 
   // GATED, wave NW-1: the factor tables of chunk cc (its gates are in LDS
@@ -452,6 +457,7 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob (&jbs)[NH],
     const float* tab = reinterpret_cast<const float*>(smem + LY::OFF_T + (cc & 1) * 2 * CH * 4);
     const float clast = tab[tab_pos<T>(cl - 1)];
     gsum2 += clast;
+    gchunk2 = clast;
     dc = lcf ? 1.0f : exp2_np(clast);
     // update weights of the lane's contraction slots
     if constexpr (E == 8) {
@@ -544,13 +550,26 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob (&jbs)[NH],
       for (int js = 0; js < NJS; ++js)
         Vop[h][js] = tr_op<T, TN>(stage + vslot(h) * TB, js * KS, col, lane);
 
-    // ---- ACCU: U += Q2^T (diag(lambda^(64 c + j)) Q), 0 past the tail (before
-    // the outputs are staged in the Q tile)
+    // ---- ACCU: U += Q2^T (diag(w_j) Q), 0 past the tail (before the outputs
+    // are staged in the Q tile); w_j = lambda^(64 c + j), gated the product of
+    // the gates of the walk's tokens after its first up to token j:
+    // exp2(c_j + log2-gates of the earlier chunks - log2-gate of the first)
     if constexpr (ACCU) {
       const char* const sQ = stage + qslot(0) * TB;
       const char* const sU = stage + 3 * TB;
       float wu[NJS][E];
-      if (cl == CH) {
+      if constexpr (GATED) {
+        const float* tab = reinterpret_cast<const float*>(smem + LY::OFF_T + (c & 1) * 2 * CH * 4);
+        if (c == 0) ug0 = tab[tab_pos<T>(0)];
+        const float gb = gsum2 - gchunk2 - ug0;
+#pragma unroll
+        for (int js = 0; js < NJS; ++js)
+#pragma unroll
+          for (int x = 0; x < E; ++x) {
+            const float e = exp2_np(gb + tab[16 * g + E * js + x]);  // slot order
+            wu[js][x] = (cl == CH || slot_token<T>(js * KS, g, x) < cl) ? e : 0.0f;
+          }
+      } else if (cl == CH) {
         const float fu = pow_lam(lg, (float)(CH * c));  // lambda^(64 c)
 #pragma unroll
         for (int js = 0; js < NJS; ++js)
@@ -735,10 +754,11 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob (&jbs)[NH],
           const int row = 8 * w + 4 * hh + (lane >> 4);  // 16 lanes per 256-byte row
           const int piece = lane & 15;
           const bool valid = c * CH + row < len;
-          if (rkw && h == 1) {
+          if (rkw && h == NH - 1) {
             const u32x4 val = *reinterpret_cast<const u32x4*>(sO + TN::off(row, 8 * piece));
+            const int dslot = NH == 2 ? qslot(0) : 3;  // the rows dotted with
             const u32x4 kq =
-                *reinterpret_cast<const u32x4*>(stage + qslot(0) * TB + TN::off(row, 8 * piece));
+                *reinterpret_cast<const u32x4*>(stage + dslot * TB + TN::off(row, 8 * piece));
             const T* a8 = reinterpret_cast<const T*>(&kq);
             const T* b8 = reinterpret_cast<const T*>(&val);
             float d = 0.0f;

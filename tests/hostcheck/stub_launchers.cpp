@@ -67,8 +67,10 @@ hipError_t launch_fwd_triple(const FwdArgs& a, const FwdArgs& b, const FwdArgs& 
 hipError_t launch_fwd_u(const FwdArgs& a, int dtype, int, int64_t nitems, hipStream_t) {
   if (nitems <= 0) return hipSuccess;
   check_fwd(a, nitems);
-  expect(dtype == 0 && !a.gated, "U-forming walk is bf16 fixed decay");
-  expect(a.Q && a.O && a.Q2 && a.Uout && a.split > 1, "outputs and U");
+  expect(dtype == 0, "U-forming walk is bf16");
+  expect(a.Q && a.O && a.Q2 && a.Uout, "outputs and U");
+  expect(!a.gated || (a.G && a.LDrev), "gated U: gates and reverse log-gates");
+  expect(!a.rk || a.gated, "row dots: gated");
   ++g_launches;
   return hipSuccess;
 }
@@ -77,6 +79,7 @@ hipError_t launch_fwd_duo(const FwdArgs& a, const FwdArgs& b, int dtype, int D, 
                           hipStream_t) {
   if (nitems <= 0) return hipSuccess;
   expect(!a.rk && (!b.rk || (b.gated && D == 128)), "row dots: gated, d = 128, second set");
+  expect(dtype == 0, "bf16");
   check_fwd(a, nitems);
   check_fwd(b, nitems);
   expect(dtype == 0, "joint dV/dK walk is bf16 only");
@@ -135,10 +138,11 @@ hipError_t launch_gate_anchors(const float* WfT, const float* WrT, const float* 
 }
 
 hipError_t launch_gate_grad(int, int, const void* Q, const void* dQ, const void* K, const void* dK,
-                            float* dG, float* tot, const float*, const float*, int64_t, int64_t,
-                            hipStream_t) {
-  // K, dK null: dG holds k . dk from the joint dV/dK walk
-  expect(Q && dQ && dG && tot && ((K == nullptr) == (dK == nullptr)), "gate gradient");
+                            const float* rq, float* dG, float* tot, const float*, const float*,
+                            int64_t, int64_t, hipStream_t) {
+  // K, dK null: dG holds k . dk from the joint dV/dK walk; rq: q . dq too
+  expect(Q && dQ && dG && tot && ((K == nullptr) == (dK == nullptr)) && (!rq || !K),
+         "gate gradient");
   ++g_launches;
   return hipSuccess;
 }

@@ -230,13 +230,14 @@ def test_gated_backward_workspace_follows_the_1024_token_plan():
     # the same three on the sweeps' own plan (sub-segments of whole 1024-token
     # blocks covering the plan's sub-segment: split 0 or 40 -> 1024 tokens, 4
     # states; split 3 -> 1728 -> 2048 tokens, 2 states; split 1 -> one
-    # sub-segment, none), the log-gates, the shifted gates, S_end and one
-    # anchor per block.
+    # sub-segment, none), the log-gates of both plans, the shifted gates, the
+    # per-token q . dq, S_end and one anchor per block.
     DD4, nseq, Ls = 64 * 64 * 4, 2, 5000
     up = lambda x: -(-x // 256) * 256
     for split, coarse in ((0, 4), (1, 0), (3, 2), (40, 4)):
         want = (2 * up(nseq * DD4) + 3 * up(nseq * 4 * DD4) + 3 * up(nseq * coarse * DD4)
-                + up(nseq * 4 * 4) + up(nseq * Ls * 4) + up(nseq * DD4) + up(nseq * 5 * 4))
+                + up(nseq * 4 * 4) + up(nseq * coarse * 4) + 2 * up(nseq * Ls * 4)
+                + up(nseq * DD4) + up(nseq * 5 * 4))
         assert la.la_bwd_gated_workspace_bytes(_shape(L=Ls, split=split)) == want, split
 
 
