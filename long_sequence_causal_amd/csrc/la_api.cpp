@@ -284,10 +284,14 @@ hipError_t launch_sweeps(const la::FwdArgs& aq, const la::FwdArgs& av, const la:
 struct TangentWs {
   size_t WS = 0, WT = 0, part = 0, total = 0;
 };
+// pieces per sub-segment of the tangent pre-pass: two when they stay whole
+// chunks (the pre-pass runs two workgroups a CU and has twice as many to
+// place)
+int tangent_pre_r(const Plan& p) { return (p.Lp % (2 * kChunk) == 0) ? 2 : 1; }
 TangentWs tangent_ws(const Plan& p) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   TangentWs w;
-  const size_t st = scan_ws_bytes(p);
+  const size_t st = (size_t)tangent_pre_r(p) * scan_ws_bytes(p);
   w.WS = 0;
   w.WT = up(st);
   w.part = w.WT + up(st);
@@ -757,6 +761,7 @@ la_status la_decay_grad(const la_shape* s, const void* Q, const void* K, const v
   ta.split = pl.split;
   ta.Ls = pl.Ls;
   ta.Lp = pl.Lp;
+  ta.pre_r = tangent_pre_r(pl);
   hipError_t e = la::launch_tangent(ta, s->dtype, pl.D, pl.nseq, dlambda,
                                     static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decay gradient launch");

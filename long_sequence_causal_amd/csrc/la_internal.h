@@ -153,7 +153,7 @@ struct TanArgs {
   const float* lam;  // [H]
   const float* S0;   // [nseq][D][D] or null
   const float* dSe;  // [nseq][D][D] or null
-  float* WS;         // [nseq][split-1][D][D]: local, then start states
+  float* WS;         // [nseq][pre_r (split-1)][D][D]: local, then start states
   float* WT;         // the same for the tangent state
   double* part;      // [nseq][split]: each sub-segment's share of the gradient
   int H;
@@ -161,6 +161,11 @@ struct TanArgs {
   int split;
   int64_t Ls;
   int64_t Lp;
+  // the pre-pass walks pre_r pieces of Lp / pre_r tokens per sub-segment
+  // (pre_r = 1 or 2, Lp / pre_r a multiple of 64); WS, WT then hold
+  // pre_r (split - 1) pairs per sequence, and the start pair of sub-segment
+  // p >= 1 is entry pre_r p - 1
+  int pre_r;
 };
 // Pre-pass over sub-segments 0..split-2, the scan of (state, tangent) pairs,
 // the main pass over every sub-segment and the per-head sum into dlam.

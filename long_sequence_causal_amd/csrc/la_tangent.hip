@@ -18,10 +18,13 @@
 // Every term enters the result as it is; no partial sums cancel.  Still,
 // the result is a small difference of many terms (their absolute sum can be
 // hundreds of times larger), and U varies slowly along the sequence, so a
-// per-token rounding feeding U or M would add up coherently: in bf16 every
-// operand that carries a decay factor (the weighted dO of M1, M2 and the
-// weighted V of both updates) goes through the MFMA as hi + lo, and U, S
-// never leave fp32.  (The
+// per-token rounding feeding U or M would add up coherently: in bf16 the
+// decayed operands (the weighted dO of M1 and M2, the weighted V of the S
+// update) go through the MFMA as hi + lo, and U, S never leave fp32.  The
+// weighted V of the U update goes as one rounded bf16: measured at 256K
+// tokens x 16 heads that keeps every head's gradient within 2.6e-3 of its
+// own size (hi + lo there too: 1e-4) for 9 % of the walk's time (16 of its
+// MFMAs and that split per chunk).  (The
 // reverse-mode identity d l / d lambda = (1 / lambda) sum_u u (q_u . dq_u -
 // k_u . dk_u) + ... does cancel: its terms exceed the result by a factor
 // that grows with the sequence length, which bf16 gradients cannot carry.)
@@ -64,6 +67,14 @@ __device__ inline u32x2 split_hi_lo(float x0, float x1) {
   return u32x2{hi, lo};
 }
 
+// round-to-nearest-even bf16 of a pair, packed (element 0 in the low half)
+__device__ inline unsigned round_pair(float x0, float x1) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const f32x2 x = {x0, x1};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(x, bf16x2));
+}
+
 template <typename T, int D, bool MAIN>
 struct TanLayout {
   typedef PadTile<T, CH, D> TN;
@@ -74,7 +85,9 @@ struct TanLayout {
   static constexpr int BYTES = STAGES * STAGE;
   static constexpr int NW = D / 16;  // waves: one per 16 state columns
   static constexpr int NT = 64 * NW;
-  static constexpr int WAVES_PER_EU = sizeof(T) == 2 ? 2 : 1;
+  // bf16 keeps two waves per SIMD; the pre-pass (LDS for two workgroups a
+  // CU, 128 registers) four, since its arithmetic, not HBM, binds it
+  static constexpr int WAVES_PER_EU = sizeof(T) == 2 ? (MAIN ? 2 : 4) : 1;
   static_assert(BYTES <= LDS_MAX, "LDS budget");
   static_assert(TB == TN::G * 1024, "a tile is G loads of 1 KiB");
 };
@@ -114,13 +127,15 @@ k_tangent(TanArgs a) {
   const int g = lane >> 4;
   const int col = 16 * w;
 
-  // ---- work item: sub-segment p of sequence n
-  const int np = MAIN ? a.split : a.split - 1;
+  // ---- work item: sub-segment p of sequence n (pre-pass: piece p of
+  // Lp / pre_r tokens)
+  const int np = MAIN ? a.split : a.pre_r * (a.split - 1);
   const int64_t n = (int64_t)blockIdx.x / np;
   const int p = (int)((int64_t)blockIdx.x % np);
   const int h = (int)((n / a.nseg) % a.H);
-  const int64_t t0 = (int64_t)p * a.Lp;
-  const int64_t t1 = (t0 + a.Lp < a.Ls) ? t0 + a.Lp : a.Ls;
+  const int64_t lp = MAIN ? a.Lp : a.Lp / a.pre_r;
+  const int64_t t0 = (int64_t)p * lp;
+  const int64_t t1 = (t0 + lp < a.Ls) ? t0 + lp : a.Ls;
   const int len = (int)(t1 > t0 ? t1 - t0 : 0);
   const int nch = (len + CH - 1) / CH;
   const float lg = log2f(a.lam[h]);
@@ -136,7 +151,7 @@ k_tangent(TanArgs a) {
       if (p == 0) {
         sp = a.S0 ? a.S0 + n * DD : nullptr;
       } else {
-        const int64_t o = (n * (a.split - 1) + (p - 1)) * DD;
+        const int64_t o = (n * (int64_t)a.pre_r * (a.split - 1) + (a.pre_r * p - 1)) * DD;
         sp = a.WS + o;
         tp = a.WT + o;
       }
@@ -280,9 +295,10 @@ k_tangent(TanArgs a) {
               const float a11 = (float)Dop[x + 1] * tq[8 * js + x + 1];
               const float a20 = a10 * (fB + (float)(1 + slot_token<T>(js * KS, 0, x)));
               const float a21 = a11 * (fB + (float)(1 + slot_token<T>(js * KS, 0, x + 1)));
-              const u32x2 s1 = split_hi_lo(a10, a11), s2 = split_hi_lo(a20, a21);
+              const u32x2 s1 = split_hi_lo(a10, a11);
               h1[x / 2] = s1[0];
               l1[x / 2] = s1[1];
+              const u32x2 s2 = split_hi_lo(a20, a21);
               h2[x / 2] = s2[0];
               l2[x / 2] = s2[1];
             }
@@ -326,31 +342,30 @@ k_tangent(TanArgs a) {
         accT[tk] = dc * accT[tk] + dcu * accS[tk];
         accS[tk] *= dc;
       }
-      // V^T operands of this wave's columns, scaled per token (hi + lo in bf16)
+      // V^T operands of this wave's columns, scaled per token (S update: hi + lo
+      // in bf16; U update: one rounding)
       const float* tw = tabW + 16 * g;
       const float cB = (float)(clf - 1) - fB;  // clf - 1 - slot_token = cB - slot_token(., 0, .)
-      op_t B1[NJS], B1l[NJS], B2[NJS], B2l[NJS];
+      op_t B1[NJS], B1l[NJS], B2[NJS];
 #pragma unroll
       for (int js = 0; js < NJS; ++js) {
         const op_t Vop = tr_op<T, TN>(sV, js * KS, col, lane);
         if constexpr (E == 8) {
-          u32x4 b1, b1l, b2, b2l;
+          u32x4 b1, b1l, b2;
 #pragma unroll
           for (int x = 0; x < 8; x += 2) {
             const float vw0 = (float)Vop[x] * tw[8 * js + x];
             const float vw1 = (float)Vop[x + 1] * tw[8 * js + x + 1];
             const float vu0 = vw0 * (cB - (float)slot_token<T>(js * KS, 0, x));
             const float vu1 = vw1 * (cB - (float)slot_token<T>(js * KS, 0, x + 1));
-            const u32x2 s1 = split_hi_lo(vw0, vw1), s2 = split_hi_lo(vu0, vu1);
+            const u32x2 s1 = split_hi_lo(vw0, vw1);
             b1[x / 2] = s1[0];
             b1l[x / 2] = s1[1];
-            b2[x / 2] = s2[0];
-            b2l[x / 2] = s2[1];
+            b2[x / 2] = round_pair(vu0, vu1);
           }
           B1[js] = __builtin_bit_cast(bf16x8, b1);
           B1l[js] = __builtin_bit_cast(bf16x8, b1l);
           B2[js] = __builtin_bit_cast(bf16x8, b2);
-          B2l[js] = __builtin_bit_cast(bf16x8, b2l);
         } else {
           B1[js] = Vop * tw[js];
           B2[js] = B1[js] * (float)(clf - 1 - slot_token<T>(js * KS, g, 0));
@@ -363,10 +378,7 @@ k_tangent(TanArgs a) {
           const op_t Ak = tr_op<T, TN>(sK, js * KS, 16 * tk, lane);
           accS[tk] = X::mfma(Ak, B1[js], accS[tk]);
           accT[tk] = X::mfma(Ak, B2[js], accT[tk]);
-          if constexpr (E == 8) {
-            accS[tk] = X::mfma(Ak, B1l[js], accS[tk]);
-            accT[tk] = X::mfma(Ak, B2l[js], accT[tk]);
-          }
+          if constexpr (E == 8) accS[tk] = X::mfma(Ak, B1l[js], accS[tk]);
         }
     }
   }
@@ -394,7 +406,7 @@ k_tangent(TanArgs a) {
       a.part[n * a.split + p] = t;
     }
   } else {
-    const int64_t o = (n * (a.split - 1) + p) * DD;
+    const int64_t o = (n * np + p) * DD;
 #pragma unroll
     for (int tk = 0; tk < NKT; ++tk)
 #pragma unroll
@@ -406,9 +418,9 @@ k_tangent(TanArgs a) {
   }
 }
 
-// Chain the local pairs (S, U) of sub-segments 0..split-2 of every sequence
-// from (S0, 0), in place: entry p becomes the start pair of sub-segment p + 1.
-// One thread per (sequence, state element).
+// Chain the local pairs (S, U) of the pre-pass pieces 0..pre_r (split-1) - 1
+// of every sequence from (S0, 0), in place: entry q becomes the start pair of
+// piece q + 1.  One thread per (sequence, state element).
 __global__ __launch_bounds__(256) void k_tangent_scan(TanArgs a, int64_t total, int D) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= total) return;
@@ -416,13 +428,14 @@ __global__ __launch_bounds__(256) void k_tangent_scan(TanArgs a, int64_t total, 
   const int64_t n = idx / DD, e = idx % DD;
   const int h = (int)((n / a.nseg) % a.H);
   const float lg = log2f(a.lam[h]);
-  const float Lp = (float)a.Lp;  // a multiple of 64, at most 2^24: exact
+  const float Lp = (float)(a.Lp / a.pre_r);  // a multiple of 64, at most 2^24: exact
   const float dl = exp2f(Lp * lg);
   const float dw = Lp * dl;
   float x = a.S0 ? a.S0[n * DD + e] : 0.0f;
   float y = 0.0f;
-  for (int p = 0; p < a.split - 1; ++p) {
-    const int64_t o = (n * (a.split - 1) + p) * DD + e;
+  const int nq = a.pre_r * (a.split - 1);
+  for (int p = 0; p < nq; ++p) {
+    const int64_t o = (n * nq + p) * DD + e;
     y = dl * y + dw * x + a.WT[o];
     x = dl * x + a.WS[o];
     a.WS[o] = x;
@@ -457,7 +470,7 @@ template <typename T, int D>
 hipError_t tangent_t(const TanArgs& a, int64_t nseq, float* dlam, hipStream_t s) {
   hipError_t e;
   if (nseq > 0 && a.split > 1) {
-    hipLaunchKernelGGL((k_tangent<T, D, false>), dim3((unsigned)(nseq * (a.split - 1))),
+    hipLaunchKernelGGL((k_tangent<T, D, false>), dim3((unsigned)(nseq * a.pre_r * (a.split - 1))),
                        dim3(TanLayout<T, D, false>::NT), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t total = nseq * (int64_t)D * D;

@@ -156,7 +156,8 @@ def test_automatic_plan_takes_a_second_round_only_for_long_walks():
     assert la.la_bwd_workspace_bytes(s) == 2 * 16 * state + 3 * 16 * 31 * state
     # the decay gradient's tangent walks keep one round: (S, U) starts and one
     # fp64 share per sub-segment
-    assert la.la_decay_grad_workspace_bytes(s) == 2 * 16 * 15 * state + 16 * 16 * 8
+    # (its pre-pass walks each sub-segment as two pieces: two local pairs each)
+    assert la.la_decay_grad_workspace_bytes(s) == 2 * 2 * 16 * 15 * state + 16 * 16 * 8
 
 
 def test_scan_rejects_bad_arguments():
@@ -246,9 +247,10 @@ def test_decay_gradient_validates_on_the_host():
     s = _shape(L=3000, split=4)
     v = lambda x: None if x is None else ctypes.c_void_p(x)
     need = la.la_decay_grad_workspace_bytes(s)
-    # start pairs (S, U) of 3 sub-segments and one fp64 share per sub-segment
+    # start pairs (S, U) of the pre-pass's pieces (3 sub-segments of 768
+    # tokens, two pieces of 384 each) and one fp64 share per sub-segment
     nseq, D = s.B * s.H, s.dk
-    assert need == 2 * nseq * 3 * D * D * 4 + 256
+    assert need == 2 * nseq * 2 * 3 * D * D * 4 + 256
     assert la.la_decay_grad_workspace_bytes(_shape(dk=96, dv=96)) == 0
 
     def call(Q=FAKE, K=FAKE, V=FAKE, lam=FAKE, S0=None, dO=FAKE, dSe=None, out=FAKE,
