@@ -103,4 +103,7 @@ def test_decay_grad_at_full_size_every_head(name, dse):
     log(f"  whole-vector err {e:.3e}; per head on its own scale: "
         + " ".join(f"h{h}={x:.1e}" for h, x in enumerate(own)))
     assert e <= TOL["bf16"]
+    # every head on its own scale as well: the U update's weighted V is one
+    # bf16 rounding, which keeps each head within 2.6e-3 at these sizes
+    assert own.max() <= 1e-2
     del q, k, v, dO
