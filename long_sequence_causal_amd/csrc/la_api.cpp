@@ -133,12 +133,9 @@ size_t scan_ws_bytes(const Plan& p) {
   return (size_t)p.nseq * (size_t)(p.split - 1) * (size_t)p.D * (size_t)p.D * sizeof(float);
 }
 
-// la_chunk_bwd's workspace: two prepared start states per sequence and three
-// sets of sub-segment start states (the dQ, dV and dK sweeps run in one
-// launch, each from its own)
-size_t bwd_ws_bytes(const Plan& p) {
-  return 2 * (size_t)p.nseq * p.D * p.D * sizeof(float) + 3 * scan_ws_bytes(p);
-}
+// la_chunk_bwd's workspace: the sub-segment start states of the dQ sweep and
+// of the dV sweep (the dK sweep reads the dV sweep's transposed)
+size_t bwd_ws_bytes(const Plan& p) { return 2 * scan_ws_bytes(p); }
 
 la_status hip_fail(hipError_t e, const char* what) {
   return fail(LA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -172,7 +169,7 @@ la::FwdArgs flow_args(const Plan& pl, int H, int nseg, const void* Q, const void
 la_status run_states(const Plan& pl, int dtype, int H, int nseg, const void* K, const void* V,
                      const float* lam, const float* start, float* W, int reverse, hipStream_t st,
                      bool gated = false, const float* G = nullptr, float* LDw = nullptr,
-                     bool start_undecayed = false) {
+                     bool start_undecayed = false, bool start_transposed = false) {
   if (pl.nseq == 0 || pl.split <= 1) return LA_OK;
   la::FwdArgs pa = flow_args(pl, H, nseg, nullptr, K, V, lam, reverse);
   pa.gated = gated;  // gated: sub-segment log-gates to LDw for the combine
@@ -205,6 +202,8 @@ la_status run_states(const Plan& pl, int dtype, int H, int nseg, const void* K, 
   sa.reverse = 0;
   sa.inclusive = 1;
   sa.s0_undecayed = start_undecayed;
+  sa.s0_transposed = start_transposed;
+  sa.d = pl.D;
   sa.gated = gated;
   sa.LD = LDw;
   e = la::launch_scan(sa, st);
@@ -478,7 +477,7 @@ bool sweep_slots_valid(const Plan& c, const Plan& f, int64_t step) {
 // sweeps' sub-segment log-gates (reused), shifted gates [nseq][Ls], the final
 // dQ-sweep state [nseq][D][D] and one anchor per 1024-token block
 struct GatedBwdWs {
-  size_t A, A2, W, W2, W3, Wc, W2c, W3c, LD, LDr, Gs, RQ, SE, TOT, total;
+  size_t W, W2, W3, Wc, W2c, LD, LDr, Gs, RQ, SE, TOT, total;
 };
 GatedBwdWs gated_bwd_ws(const Plan& p0) {
   const Plan p = gated_bwd_plan(p0);
@@ -488,14 +487,11 @@ GatedBwdWs gated_bwd_ws(const Plan& p0) {
   auto up = [](size_t b) { return (b + 255) / 256 * 256; };
   const size_t DD4 = (size_t)p.D * p.D * sizeof(float);
   size_t o = 0;
-  w.A = o;  o += up((size_t)p.nseq * DD4);
-  w.A2 = o; o += up((size_t)p.nseq * DD4);
   w.W = o;  o += up(scan_ws_bytes(p));   // 1024-row states (forward)
   w.W2 = o; o += up(scan_ws_bytes(p));
   w.W3 = o; o += up(scan_ws_bytes(p));   // (reverse, transposed)
   w.Wc = o;  o += up(scan_ws_bytes(pc));  // the sweeps' own start states
   w.W2c = o; o += up(scan_ws_bytes(pc));
-  w.W3c = o; o += up(scan_ws_bytes(pc));
   w.LD = o; o += up((size_t)p.nseq * (size_t)(p.split > 1 ? p.split - 1 : 0) * sizeof(float));
   w.LDr = o; o += up((size_t)pc.nseq * (size_t)(pc.split > 1 ? pc.split - 1 : 0) * sizeof(float));
   w.Gs = o; o += up((size_t)p.nseq * (size_t)p.Ls * sizeof(float));
@@ -551,14 +547,11 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
   if (pl.nseq == 0) return LA_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* base = static_cast<char*>(ws);
-  float* A = reinterpret_cast<float*>(base + L.A);    // S0^T (dQ sweep)
-  float* A2 = reinterpret_cast<float*>(base + L.A2);  // dS_end^T (dK sweep)
   float* W = reinterpret_cast<float*>(base + L.W);    // forward sweep: S^T starts
   float* W2 = reinterpret_cast<float*>(base + L.W2);  // dV sweep: G starts
   float* W3 = reinterpret_cast<float*>(base + L.W3);  // dK sweep: G^T starts
   float* Wc = reinterpret_cast<float*>(base + L.Wc);  // the same on the sweeps' plan
   float* W2c = reinterpret_cast<float*>(base + L.W2c);
-  float* W3c = reinterpret_cast<float*>(base + L.W3c);
   float* LDw = reinterpret_cast<float*>(base + L.LD);
   float* LDr = reinterpret_cast<float*>(base + L.LDr);
   float* RQ = reinterpret_cast<float*>(base + L.RQ);
@@ -566,26 +559,11 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
   float* SE = reinterpret_cast<float*>(base + L.SE);
   float* TOT = reinterpret_cast<float*>(base + L.TOT);
   const int H = (int)s->H;
-  la::PrepArgs pa;
-  std::memset(&pa, 0, sizeof(pa));
-  pa.nseq = pl.nseq;
-  pa.D = pl.D;
-  pa.lam = nullptr;
-  pa.H = H;
-  pa.hdiv = s->nseg;
   hipError_t e;
 
   // dq_t = S_t dO_t: the gated forward recurrence of S^T read by dO, from
-  // S0^T; it ends with S_end^T, kept for the log-gate gradient
-  const float* start = nullptr;
-  if (S0) {
-    pa.src = S0;
-    pa.dst = A;
-    pa.transpose = 1;
-    pa.mode = 0;
-    if ((e = la::launch_prep(pa, st)) != hipSuccess) return hip_fail(e, "prep launch");
-    start = A;
-  }
+  // S0^T (S0 read transposed); it ends with S_end^T, kept for the log-gate
+  // gradient
   // The sweeps walk plc (sub-segments of step x 1024 tokens) from start
   // states formed on that plan, and write the 1024-row states the log-gate
   // anchors need (W and W3) themselves as they pass those rows; every such
@@ -598,14 +576,15 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
   const Plan& prf = fine ? plr : plrc;  // and of the reverse ones
   float* const Wf = fine ? W : Wc;
   float* const W2f = fine ? W2 : W2c;
-  float* const W3f = fine ? W3 : W3c;
   const int sstep = fine ? (int)step : 1;
   const bool dumps = dlog_alpha && !fine;
   const bool need_send = dlog_alpha && dS_end;
-  r = run_states(pf, s->dtype, H, s->nseg, V, K, nullptr, start, Wf, 0, st, true, log_alpha, LDw);
+  r = run_states(pf, s->dtype, H, s->nseg, V, K, nullptr, S0, Wf, 0, st, true, log_alpha, LDw,
+                 false, true);
   if (r != LA_OK) return r;
-  la::FwdArgs aq = main_args(plc, H, s->nseg, dO, V, K, nullptr, start, dQ,
+  la::FwdArgs aq = main_args(plc, H, s->nseg, dO, V, K, nullptr, S0, dQ,
                              need_send ? SE : nullptr, Wf, 0, true, log_alpha);
+  aq.s0_transposed = 1;
   aq.sws_nper = pf.split - 1;
   aq.sws_step = sstep;
   if (dumps) {
@@ -660,26 +639,19 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
     r = run_states(prf, s->dtype, H, s->nseg, Q, dO, nullptr, dS_end, W2f, 1, st, true, Gs, LDw);
     if (r != LA_OK) return r;
   }
-  if (prf.split > 1) {
-    e = la::launch_transpose_copy(W2f, W3f, prf.nseq * (prf.split - 1), prf.D, st);
+  // (the 1024-token plan's anchors read the reverse states transposed from W3)
+  if (fine && prf.split > 1) {
+    e = la::launch_transpose_copy(W2f, W3, prf.nseq * (prf.split - 1), prf.D, st);
     if (e != hipSuccess) return hip_fail(e, "transpose launch");
-  }
-  const float* startK = nullptr;
-  if (dS_end) {
-    pa.src = dS_end;
-    pa.dst = A2;
-    pa.transpose = 1;
-    pa.mode = 0;
-    if ((e = la::launch_prep(pa, st)) != hipSuccess) return hip_fail(e, "prep launch");
-    startK = A2;
   }
   {
     // the dV and dK sweeps (with the dQ sweep unless it ran above): the start
     // states are ready, and both plans have plc.split walks per sequence
     la::FwdArgs av = main_args(plrc, H, s->nseg, K, Q, dO, nullptr, dS_end, dV, dS0, W2f, 1,
                                true, Gs);
-    la::FwdArgs ak = main_args(plrc, H, s->nseg, V, dO, Q, nullptr, startK, dK, nullptr, W3f, 1,
+    la::FwdArgs ak = main_args(plrc, H, s->nseg, V, dO, Q, nullptr, dS_end, dK, nullptr, W2f, 1,
                                true, Gs);
+    ak.s0_transposed = ak.sws_transposed = 1;  // dS_end^T, G^T
     av.sws_nper = ak.sws_nper = prf.split - 1;
     av.sws_step = ak.sws_step = sstep;
     if (dumps) {
@@ -912,13 +884,9 @@ static la_status chunk_bwd(const la_shape* s, const void* Q, const void* K, cons
                 ws ? ws_bytes : (size_t)0);
   if (pl.nseq == 0) return LA_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const size_t DDn = (size_t)pl.nseq * pl.D * pl.D;
   const size_t Wn = scan_ws_bytes(pl) / sizeof(float);
-  float* A = static_cast<float*>(ws);  // prepared start state of the dQ sweep (S0^T)
-  float* A2 = A + DDn;                 // prepared start state of the dK sweep (dS_end^T)
-  float* W = A2 + DDn;                 // sub-segment start states: dQ sweep
-  float* Wv = W + Wn;                  // dV sweep
-  float* Wk = Wv + Wn;                 // dK sweep (the dV sweep's, transposed)
+  float* W = static_cast<float*>(ws);  // sub-segment start states: dQ sweep
+  float* Wv = W + Wn;                  // dV sweep (read transposed by the dK sweep)
   const int H = (int)s->H;
   la::PrepArgs pa;
   std::memset(&pa, 0, sizeof(pa));
@@ -930,22 +898,12 @@ static la_status chunk_bwd(const la_shape* s, const void* Q, const void* K, cons
   hipError_t e;
 
   // dq_t = S_t dO_t: the forward recurrence of S^T = sum v k^T read by dO,
-  // started from S0^T; its sub-segment start states from a pre-pass and scan
-  // over (V, K), or the transposes of the ones a forward call left.
-  const float* start = nullptr;
-  if (S0) {
-    pa.src = S0;
-    pa.dst = A;
-    pa.transpose = 1;
-    pa.mode = 0;
-    if ((e = la::launch_prep(pa, st)) != hipSuccess) return hip_fail(e, "prep launch");
-    start = A;
-  }
-  if (from_fwd && pl.split > 1) {
-    e = la::launch_transpose_copy(fwd_starts, W, pl.nseq * (pl.split - 1), pl.D, st);
-    if (e != hipSuccess) return hip_fail(e, "transpose launch");
-  } else {
-    r = run_states(pl, s->dtype, H, s->nseg, V, K, lambda, start, W, 0, st);
+  // started from S0^T (S0 read transposed); its sub-segment start states
+  // from a pre-pass and scan over (V, K), or the ones a forward call left,
+  // read transposed.
+  if (!(from_fwd && pl.split > 1)) {
+    r = run_states(pl, s->dtype, H, s->nseg, V, K, lambda, S0, W, 0, st, false, nullptr, nullptr,
+                   false, true);
     if (r != LA_OK) return r;
   }
 
@@ -957,18 +915,14 @@ static la_status chunk_bwd(const la_shape* s, const void* Q, const void* K, cons
   // sum dO q^T over the same pairs (q_t, dO_t) with the roles swapped, seeded
   // with the transposed seed, so its sub-segment start states are the
   // transposes of the dV sweep's: one set of local states and one scan serve
-  // both.
-  const float* startK = nullptr;
-  if (dS_end) {
-    pa.src = dS_end;
-    pa.dst = A2;
-    pa.transpose = 1;
-    pa.mode = 0;
-    if ((e = la::launch_prep(pa, st)) != hipSuccess) return hip_fail(e, "prep launch");
-    startK = A2;
+  // both (the dK sweep reads them, and dS_end, transposed).
+  la::FwdArgs aq0 = main_args(pl, H, s->nseg, dO, V, K, lambda, S0, dQ, nullptr, W, 0, false,
+                              nullptr);
+  aq0.s0_transposed = 1;
+  if (from_fwd) {
+    aq0.Sws = fwd_starts;
+    aq0.sws_transposed = 1;
   }
-  const la::FwdArgs aq0 = main_args(pl, H, s->nseg, dO, V, K, lambda, start, dQ, nullptr, W, 0,
-                                    false, nullptr);
   if (s->dtype == LA_BF16) {
     // The reverse sweeps cut each sequence at the forward one's rows (the
     // short sub-segment first in reverse time), and the dQ sweep, which
@@ -999,16 +953,15 @@ static la_status chunk_bwd(const la_shape* s, const void* Q, const void* K, cons
       sa.inclusive = 1;
       sa.s0_undecayed = 1;
       if ((e = la::launch_scan(sa, st)) != hipSuccess) return hip_fail(e, "state scan launch");
-      e = la::launch_transpose_copy(Wv, Wk, pl.nseq * (pl.split - 1), pl.D, st);
-      if (e != hipSuccess) return hip_fail(e, "transpose launch");
     } else if ((e = la::launch_fwd(aq0, s->dtype, pl.D, true, pl.nseq, st)) != hipSuccess) {
       return hip_fail(e, "dQ sweep launch");
     }
     la::FwdArgs av = main_args(plr, H, s->nseg, K, Q, dO, lambda, dS_end, dV, dS0, Wv, 1, false,
                                nullptr);
-    la::FwdArgs ak = main_args(plr, H, s->nseg, V, dO, Q, lambda, startK, dK, nullptr, Wk, 1,
+    la::FwdArgs ak = main_args(plr, H, s->nseg, V, dO, Q, lambda, dS_end, dK, nullptr, Wv, 1,
                                false, nullptr);
     av.s0_undecayed = ak.s0_undecayed = 1;
+    ak.s0_transposed = ak.sws_transposed = 1;
     if ((e = la::launch_fwd_duo(av, ak, s->dtype, pl.D, pl.nseq * pl.split, st)) != hipSuccess)
       return hip_fail(e, "dV/dK sweep launch");
   } else {
@@ -1017,15 +970,12 @@ static la_status chunk_bwd(const la_shape* s, const void* Q, const void* K, cons
     r = run_states(pl, s->dtype, H, s->nseg, Q, dO, lambda, dS_end, Wv, 1, st, false, nullptr,
                    nullptr, true);
     if (r != LA_OK) return r;
-    if (pl.split > 1) {
-      e = la::launch_transpose_copy(Wv, Wk, pl.nseq * (pl.split - 1), pl.D, st);
-      if (e != hipSuccess) return hip_fail(e, "transpose launch");
-    }
     la::FwdArgs av = main_args(pl, H, s->nseg, K, Q, dO, lambda, dS_end, dV, dS0, Wv, 1, false,
                                nullptr);
-    la::FwdArgs ak = main_args(pl, H, s->nseg, V, dO, Q, lambda, startK, dK, nullptr, Wk, 1,
+    la::FwdArgs ak = main_args(pl, H, s->nseg, V, dO, Q, lambda, dS_end, dK, nullptr, Wv, 1,
                                false, nullptr);
     av.s0_undecayed = ak.s0_undecayed = 1;
+    ak.s0_transposed = ak.sws_transposed = 1;
     if ((e = launch_sweeps(aq0, av, ak, s->dtype, pl.D, pl.nseq * pl.split, st)) != hipSuccess)
       return hip_fail(e, "sweep launch");
   }

@@ -77,17 +77,32 @@ __device__ __forceinline__ void chunk_item(const FwdArgs& a0, const FwdArgs& a1,
 
     // ---- start state -> accumulators (wave w: columns [16 w, 16 w + 16))
     const float* sp = nullptr;
+    bool tr = false;  // stored transposed (wave-uniform)
     if (x.start_from_state) {
-      if (p == 0)
+      if (p == 0) {
         sp = x.S0 ? x.S0 + n * D * D : nullptr;
-      else
+        tr = x.s0_transposed;
+      } else {
         sp = x.Sws + (n * x.sws_nper + sws_slot(x, p)) * (int64_t)D * D;
+        tr = x.sws_transposed;
+      }
     }
+    if (sp && tr) {
+      // element (row 16 tk + 4 g + r, column col + l16) at [col + l16][row]:
+      // 16 bytes of one stored row per tile
 #pragma unroll
-    for (int tk = 0; tk < NKT; ++tk)
+      for (int tk = 0; tk < NKT; ++tk) {
+        const f32x4 t4 = *reinterpret_cast<const f32x4*>(sp + (col + l16) * D + 16 * tk + 4 * g);
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        accS[u][tk][r] = sp ? sp[(16 * tk + 4 * g + r) * D + col + l16] : 0.0f;
+        for (int r = 0; r < 4; ++r) accS[u][tk][r] = t4[r];
+      }
+    } else {
+#pragma unroll
+      for (int tk = 0; tk < NKT; ++tk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          accS[u][tk][r] = sp ? sp[(16 * tk + 4 * g + r) * D + col + l16] : 0.0f;
+    }
   }
   f32x4 accU[NKT];
   if constexpr (ACCU) {

@@ -71,6 +71,11 @@ struct FwdArgs {
   // The backward's reverse sweeps start from dS_end this way, which spares
   // them a division by lambda.
   int s0_undecayed;
+  // the start states are stored transposed ([col][row]; S0 and Sws
+  // separately): the backward's sweeps read S0^T, dS_end^T and the dV
+  // sweep's start states as the dK sweep's this way, with no transposed copy
+  int s0_transposed;
+  int sws_transposed;
   // state-only launches: walk each sub-segment's chunks last
   // first (the state a sub-segment ends with is the same sum, so only the
   // rounding order changes); a sub-segment with a ragged chunk walks in order
@@ -133,6 +138,9 @@ struct ScanArgs {
   // the first segment decays S0 by lambda^(seg_len - 1) instead of
   // lambda^seg_len (S0 already carries the first token's decay; fixed decay)
   int s0_undecayed;
+  // S0 is stored transposed (E = d * d)
+  int s0_transposed;
+  int d;
   // fixed decay: the first segment in scan order spans first_len tokens
   // (0: seg_len like the others), the short one of a partition cut from the
   // sequence's other end

@@ -27,7 +27,8 @@ __global__ __launch_bounds__(256) void k_state_scan(ScanArgs a) {
   const int64_t len0 = a.first_len > 0 ? a.first_len : a.seg_len;
   float dcur = GATED ? 0.0f
                      : pow_lam(lg, (float)((a.s0_undecayed && len0 > 0) ? len0 - 1 : len0));
-  float x = a.S0 ? a.S0[n * a.E + e] : 0.0f;
+  const int64_t e0 = a.s0_transposed ? (e % a.d) * a.d + e / a.d : e;
+  float x = a.S0 ? a.S0[n * a.E + e0] : 0.0f;
   // Segments go in groups of PF whose inputs are all loaded before any of
   // the group's outputs is stored: Sout may be dS itself, so the compiler
   // cannot move a load above an earlier store, and one segment per memory

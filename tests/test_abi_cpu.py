@@ -153,7 +153,7 @@ def test_automatic_plan_takes_a_second_round_only_for_long_walks():
     # the backward follows the same plan: two prepared states and three sets
     # of starts (dQ, dV and dK sweeps)
     s = la.make_shape(1, 16, 262144, 128, 128, 1, la.LA_BF16, 0)
-    assert la.la_bwd_workspace_bytes(s) == 2 * 16 * state + 3 * 16 * 31 * state
+    assert la.la_bwd_workspace_bytes(s) == 2 * 16 * 31 * state
     # the decay gradient's tangent walks keep one round: (S, U) starts and one
     # fp64 share per sub-segment
     # (its pre-pass walks each sub-segment as two pieces: two local pairs each)
@@ -177,7 +177,7 @@ def test_scan_rejects_bad_arguments():
 def test_bwd_rejects_bad_arguments():
     L = la.lib()
     v = lambda x: None if x is None else ctypes.c_void_p(x)
-    s = _shape()
+    s = _shape(split=2)
 
     def call(**kw):
         a = dict(Q=FAKE, K=FAKE, V=FAKE, lam=FAKE, S0=None, dO=FAKE, dSe=None, dQ=FAKE,
@@ -190,14 +190,13 @@ def test_bwd_rejects_bad_arguments():
     assert call(dO=None) == la.LA_ERR_INVALID_ARG
     assert call(dK=None) == la.LA_ERR_INVALID_ARG
     assert call(dS0=FAKE + 2) == la.LA_ERR_INVALID_ARG
+    # no workspace at split 1 (the sweeps read S0 and dS_end themselves,
+    # transposed where they need it) ...
+    assert la.la_bwd_workspace_bytes(_shape()) == 0
+    # ... and two sets of sub-segment start states otherwise (dQ and dV
+    # sweeps; the dK sweep reads the dV sweep's transposed)
     need = la.la_bwd_workspace_bytes(s)
-    # two prepared start states per sequence (the dV and dK sweeps run
-    # together), no sub-segment states at split 1
-    assert need == 2 * (2 * 64 * 64 * 4)
-    s4 = _shape(split=2)
-    # ... and three sets of sub-segment start states (dQ, dV and dK sweeps,
-    # which run in one launch)
-    assert la.la_bwd_workspace_bytes(s4) == 2 * (2 * 64 * 64 * 4) + 3 * (2 * 1 * 64 * 64 * 4)
+    assert need == 2 * (2 * 1 * 64 * 64 * 4)
     assert call(ws=None) == la.LA_ERR_WORKSPACE
     assert call(ws=FAKE, nb=need - 16) == la.LA_ERR_WORKSPACE
 
@@ -226,17 +225,17 @@ def test_gated_entry_points_validate_on_the_host():
 
 def test_gated_backward_workspace_follows_the_1024_token_plan():
     # L = 5000 -> 79 chunks -> 5 sub-segments of 1024 tokens whatever split asks;
-    # d = 64: a state is 16 KiB.  Blocks (256-byte aligned): two prepared start
-    # states, the 1024-row states (4 each: forward, dV, dV transposed for dK),
-    # the same three on the sweeps' own plan (sub-segments of whole 1024-token
-    # blocks covering the plan's sub-segment: split 0 or 40 -> 1024 tokens, 4
-    # states; split 3 -> 1728 -> 2048 tokens, 2 states; split 1 -> one
-    # sub-segment, none), the log-gates of both plans, the shifted gates, the
-    # per-token q . dq, S_end and one anchor per block.
+    # d = 64: a state is 16 KiB.  Blocks (256-byte aligned): the 1024-row
+    # states (4 each: forward, dV, dV transposed for the anchors), the forward
+    # and dV start states on the sweeps' own plan (sub-segments of whole
+    # 1024-token blocks covering the plan's sub-segment: split 0 or 40 -> 1024
+    # tokens, 4 states; split 3 -> 1728 -> 2048 tokens, 2 states; split 1 ->
+    # one sub-segment, none), the log-gates of both plans, the shifted gates,
+    # the per-token q . dq, S_end and one anchor per block.
     DD4, nseq, Ls = 64 * 64 * 4, 2, 5000
     up = lambda x: -(-x // 256) * 256
     for split, coarse in ((0, 4), (1, 0), (3, 2), (40, 4)):
-        want = (2 * up(nseq * DD4) + 3 * up(nseq * 4 * DD4) + 3 * up(nseq * coarse * DD4)
+        want = (3 * up(nseq * 4 * DD4) + 2 * up(nseq * coarse * DD4)
                 + up(nseq * 4 * 4) + up(nseq * coarse * 4) + 2 * up(nseq * Ls * 4)
                 + up(nseq * DD4) + up(nseq * 5 * 4))
         assert la.la_bwd_gated_workspace_bytes(_shape(L=Ls, split=split)) == want, split
