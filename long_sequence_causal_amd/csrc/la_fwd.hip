@@ -69,7 +69,7 @@ __device__ __forceinline__ void chunk_item(const FwdArgs& a0, const FwdArgs& a1,
     jb[u].rk = (RK && u == NH - 1) ? x.rk + n * a.Ls : nullptr;
     jb[u].dump = nullptr;
     if (DUMP && WITH_O && x.dump) {
-      jb[u].dump_rows = x.dump_rows;
+      jb[u].dump_shift = __builtin_ctz((unsigned)x.dump_rows);  // a power of two (host-checked)
       jb[u].ndump = (int)((a.Ls + x.dump_rows - 1) / x.dump_rows - 1);
       jb[u].dump_rev = x.dump_rev;
       jb[u].dump = x.dump + n * (int64_t)jb[u].ndump * D * D;
@@ -205,6 +205,12 @@ __global__ __launch_bounds__((FwdLayout<T, D, 3, GATED>::NT),
     chunk_item<T, D, true, GATED, 1, false, false, GATED>(c, c, item);
 }
 
+// A dump's row count must be a power of two of at least one chunk (the
+// walks test boundary rows with a mask and a shift).
+static bool bad_dump(const FwdArgs& a) {
+  return a.dump && (a.dump_rows < 64 || (a.dump_rows & (a.dump_rows - 1)) != 0);
+}
+
 template <typename T, int D>
 static hipError_t launch_triple_t(const FwdArgs& a, const FwdArgs& b, const FwdArgs& c,
                                   int64_t nitems, hipStream_t s) {
@@ -222,6 +228,7 @@ hipError_t launch_fwd_triple(const FwdArgs& a, const FwdArgs& b, const FwdArgs& 
                              int D, int64_t nitems, hipStream_t s) {
   if (nitems <= 0) return hipSuccess;
   if (a.gated != b.gated || a.gated != c.gated) return hipErrorInvalidValue;
+  if (bad_dump(a) || bad_dump(b) || bad_dump(c)) return hipErrorInvalidValue;
   if (dtype == 0) {
     if (D == 64) return launch_triple_t<__bf16, 64>(a, b, c, nitems, s);
     if (D == 128) return launch_triple_t<__bf16, 128>(a, b, c, nitems, s);
@@ -273,6 +280,7 @@ hipError_t launch_fwd_duo(const FwdArgs& a, const FwdArgs& b, int dtype, int D, 
     return hipErrorInvalidValue;
   if (dtype != 0) return hipErrorInvalidValue;  // bf16 only
   if (a.rk || (b.rk && D != 128)) return hipErrorInvalidValue;  // row dots: b, d = 128
+  if (bad_dump(a) || bad_dump(b)) return hipErrorInvalidValue;
   if (D == 64) return launch_duo_t<__bf16, 64>(a, b, nitems, s);
   if (D == 128) return launch_duo_t<__bf16, 128>(a, b, nitems, s);
   return hipErrorInvalidValue;
@@ -318,7 +326,7 @@ hipError_t launch_fwd_u(const FwdArgs& a, int dtype, int D, int64_t nitems, hipS
   if (nitems <= 0) return hipSuccess;
   if (!a.Q2 || !a.Uout || !a.O || (a.gated && (!a.G || !a.LDrev)) || (a.rk && !a.gated))
     return hipErrorInvalidValue;
-  if (dtype != 0) return hipErrorInvalidValue;  // bf16 only
+  if (dtype != 0 || bad_dump(a)) return hipErrorInvalidValue;  // bf16 only
   if (D == 64) return launch_u_t<64>(a, nitems, s);
   if (D == 128) return launch_u_t<128>(a, nitems, s);
   return hipErrorInvalidValue;
@@ -327,7 +335,7 @@ hipError_t launch_fwd_u(const FwdArgs& a, int dtype, int D, int64_t nitems, hipS
 template <typename T, int D, bool GATED>
 static hipError_t launch_fwd_t(const FwdArgs& a, bool with_o, int64_t nwg, hipStream_t s) {
   if (a.dump) {
-    if (!GATED || !with_o) return hipErrorInvalidValue;  // (built for the gated dQ sweep only)
+    if (!GATED || !with_o || bad_dump(a)) return hipErrorInvalidValue;  // (gated dQ sweep only)
     hipLaunchKernelGGL((k_chunk_fwd_dump<T, D>), dim3((unsigned)nwg),
                        dim3(FwdLayout<T, D, 3, true>::NT), 0, s, a);
   } else if (with_o)

@@ -96,7 +96,8 @@ struct FwdArgs {
   // k_t . dk_t); launch_fwd_u: (Q2 row) . (output row) (q_t . dq_t)
   float* rk;
   // launches with outputs (may be null): the state at every boundary row
-  // y = m * dump_rows (0 < y < Ls) of each sequence, to
+  // y = m * dump_rows (0 < y < Ls; dump_rows a power of two, at least 64) of
+  // each sequence, to
   // dump[n][m - 1] ([nseq][ceil(Ls / dump_rows) - 1][D][D]), or to
   // dump[n][ceil(Ls / dump_rows) - 1 - m] when dump_rev; written by the walk
   // whose chunk ends there (reverse sweeps: at Ls % 64 == 0 every such row

@@ -170,11 +170,11 @@ struct WalkJob {
   // like the tensors
   float* rk;
   // output walks built with DUMP (may be null): after every chunk that ends on a boundary
-  // row y = m * dump_rows (0 < y < Ls) of the sequence, this walk's state
-  // goes to dump[slot] ([ndump][D][D], the sequence's own), slot y / dump_rows
-  // - 1, or ndump - y / dump_rows when dump_rev (numbered from the end)
+  // row y = m * 2^dump_shift (0 < y < Ls) of the sequence, this walk's state
+  // goes to dump[slot] ([ndump][D][D], the sequence's own), slot m - 1, or
+  // ndump - m when dump_rev (numbered from the end)
   float* dump;
-  int dump_rows, ndump, dump_rev;
+  int dump_shift, ndump, dump_rev;
 };
 
 // Walk the range with the state in accS (wave w: columns [16 w, 16 w + 16),
@@ -820,13 +820,17 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob (&jbs)[NH],
     // (compiled into the walks that may be asked for it only: its mere
     // presence slowed the other walks' chunk loop by a tenth)
     if constexpr (OUT && DUMP) {
-      const int64_t pe = t0 + (int64_t)c * CH + cl;  // position after the chunk
-      const int64_t y = jb.reverse ? jb.Ls - pe : pe;
+      // position after the chunk, counted from the sequence's end when
+      // reverse (a sequence has fewer than 2^31 rows: wave-uniform 32-bit
+      // scalar arithmetic; a 64-bit remainder here cost about 40 vector
+      // instructions per chunk and walk)
+      const int pe = (int)t0 + c * CH + cl;
+      const int y = jb.reverse ? (int)jb.Ls - pe : pe;
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
         const WalkJob& jh = jbs[h];
-        if (jh.dump && y > 0 && y < jb.Ls && y % jh.dump_rows == 0) {
-          const int m = (int)(y / jh.dump_rows);
+        if (jh.dump && y > 0 && y < (int)jb.Ls && (y & ((1 << jh.dump_shift) - 1)) == 0) {
+          const int m = y >> jh.dump_shift;
           float* dst = jh.dump + (int64_t)(jh.dump_rev ? jh.ndump - m : m - 1) * D * D;
           // the lane's element offset, formed here: without the empty asm the
           // compiler hoists all NKT x 4 store addresses out of the chunk loop
