@@ -759,11 +759,18 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob (&jbs)[NH],
             const int dslot = NH == 2 ? qslot(0) : 3;  // the rows dotted with
             const u32x4 kq =
                 *reinterpret_cast<const u32x4*>(stage + dslot * TB + TN::off(row, 8 * piece));
-            const T* a8 = reinterpret_cast<const T*>(&kq);
-            const T* b8 = reinterpret_cast<const T*>(&val);
+            // (bf16 only: two products a step into the fp32 sum, no conversions;
+            // the pairs are copied out of the vectors: a bit cast of a vector
+            // element here compiled to the same element for every step)
             float d = 0.0f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) d += X::to_f(a8[e]) * X::to_f(b8[e]);
+            for (int e = 0; e < 4; ++e) {
+              const unsigned ka = kq[e], vb = val[e];
+              bf16x2 x, y;
+              __builtin_memcpy(&x, &ka, 4);
+              __builtin_memcpy(&y, &vb, 4);
+              d = __builtin_amdgcn_fdot2_f32_bf16(x, y, d, false);
+            }
 #pragma unroll
             for (int m = 8; m >= 1; m >>= 1) d += __shfl_xor(d, m, 16);
             if (valid) {
