@@ -109,8 +109,8 @@ k_tangent(TanArgs a) {
   constexpr int NJS = CH / KS;
   constexpr int S = LY::STAGES;
   constexpr int G = TN::G;
-  constexpr int NBLK = LY::NTEN * G;       // 1 KiB loads per chunk
-  constexpr int NLW = (NBLK + NW - 1) / NW;
+  constexpr int NBW = (G + NW - 1) / NW;   // 1 KiB blocks per tile of the busiest wave
+  static_assert(G > NW, "every wave loads at least one block");
   __shared__ __attribute__((aligned(1024))) char smem[LY::BYTES];
   __shared__ double red[NW];
   // per-token factors of the current chunk in operand slot order (entry
@@ -167,11 +167,14 @@ k_tangent(TanArgs a) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): retire them before the chunk loop
   }
 
-  // ---- chunk loads: load b fills granules 64 (b % G) .. + 63 of tile b / G;
-  // lane l's granule (row, piece) = divmod(64 (b % G) + l, G), the padding
-  // piece of a row loading the row's first piece.  Rows past the end are
-  // clamped to the last token (masked by the factors).  Offsets are 32-bit
-  // bytes from the sequence's first row (the host keeps a sequence below 4 GiB).
+  // ---- chunk loads: block blk (0..G-1) of a tile is granules 64 blk .. + 63;
+  // lane l's granule (row, piece) = divmod(64 blk + l, G), the padding piece
+  // of a row loading the row's first piece.  Wave w takes blocks w, w + NW,
+  // ... and loads each for every tile of the stage (their offsets within a
+  // tile agree), so it keeps one chunk-0 offset per block.  Rows past the end
+  // are clamped to the last token (masked by the factors).  Offsets are
+  // 32-bit bytes from the sequence's first row and wrap modulo 2^32 like the
+  // offsets they stand for (the host keeps a sequence below 4 GiB).
   auto tensor = [&](int ten) -> const T* {
     const void* bp;
     if (MAIN)
@@ -180,20 +183,40 @@ k_tangent(TanArgs a) {
       bp = ten == 0 ? a.K : a.V;
     return reinterpret_cast<const T*>(bp) + seq0;
   };
+  auto piece_of = [&](int blk, int& row) -> int {  // lane's row; piece offset (elements)
+    const int pos = 64 * blk + lane;
+    row = pos / G;
+    const int pc = pos % G;
+    return ((pc == G - 1) ? 0 : pc) * EP;
+  };
+  const int nbw = (G - w + NW - 1) / NW;  // this wave's blocks (wave-uniform)
+  unsigned voff0[NBW];
+#pragma unroll
+  for (int k = 0; k < NBW; ++k) {
+    int row;
+    const int po = piece_of((w + NW * k < G) ? w + NW * k : 0, row);
+    voff0[k] = (unsigned)(((t0 + row) * D + po) * (int64_t)sizeof(T));
+  }
   const unsigned smem_lds = lds_address(smem);
   auto issue = [&](int c, int stage) {
+    const bool full = (c + 1) * CH <= len;
 #pragma unroll
-    for (int q = 0; q < NLW; ++q) {
-      const int b = w + NW * q;
-      if (b < NBLK) {
-        const int ten = b / G, blk = b % G;
-        const int pos = 64 * blk + lane;
-        const int row = pos / G, pc = pos % G;
-        const int piece = (pc == G - 1) ? 0 : pc;
-        const int tt = (c * CH + row < len) ? c * CH + row : len - 1;
-        const unsigned voff = (unsigned)(((t0 + tt) * D + piece * EP) * (int64_t)sizeof(T));
-        dma16(tensor(ten), voff,
-              smem_lds + (unsigned)(stage * LY::STAGE + ten * LY::TB + blk * 1024));
+    for (int k = 0; k < NBW; ++k) {
+      if (k < NBW - 1 || nbw == NBW) {
+        const int blk = w + NW * k;
+        unsigned voff;
+        if (full) {
+          voff = voff0[k] + (unsigned)c * (unsigned)(CH * D * (int)sizeof(T));
+        } else {
+          int row;
+          const int po = piece_of(blk, row);
+          const int tt = (c * CH + row < len) ? c * CH + row : len - 1;
+          voff = (unsigned)(((t0 + tt) * D + po) * (int64_t)sizeof(T));
+        }
+#pragma unroll
+        for (int ten = 0; ten < LY::NTEN; ++ten)
+          dma16(tensor(ten), voff,
+                smem_lds + (unsigned)(stage * LY::STAGE + ten * LY::TB + blk * 1024));
       }
     }
   };
@@ -236,6 +259,12 @@ k_tangent(TanArgs a) {
   if (S > 1 && nch > 0) issue(0, 0);
   for (int c = 0; c < nch; ++c) {
     const int cl = (len - c * CH < CH) ? (len - c * CH) : CH;
+    // fp32 at d = 128: the lane index, opaque to the compiler once per chunk,
+    // so that the transposed-operand addresses are formed in the chunk from
+    // one lane term and immediates instead of being held (and spilled)
+    // across the loop
+    int ln = lane;
+    if constexpr (E == 1 && D == 128) asm volatile("" : "+v"(ln));
     int stg = 0;
     if constexpr (S == 1) {
       lds_barrier();  // every wave is done with the previous chunk
@@ -267,10 +296,11 @@ k_tangent(TanArgs a) {
           score_tile(idx, jb, ib);
           f32x4 aqk = {0.f, 0.f, 0.f, 0.f};
           f32x4 avd = {0.f, 0.f, 0.f, 0.f};
-          const int rk = 16 * jb + perm16<T>(l16), rq = 16 * ib + perm16<T>(l16);
+          const int l16x = ln & 15, gx = ln >> 4;  // (l16, g from the chunk's lane index)
+          const int rk = 16 * jb + perm16<T>(l16x), rq = 16 * ib + perm16<T>(l16x);
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) {
-            const int f = (E == 8) ? 8 * score_granule<D>(ks, g) : ks * KS + g;
+            const int f = (E == 8) ? 8 * score_granule<D>(ks, gx) : ks * KS + gx;
             aqk = X::mfma(lds_op<T>(sK, TN::off(rk, f)), lds_op<T>(sQ, TN::off(rq, f)), aqk);
             avd = X::mfma(lds_op<T>(sV, TN::off(rk, f)), lds_op<T>(sD, TN::off(rq, f)), avd);
           }
@@ -286,7 +316,7 @@ k_tangent(TanArgs a) {
         op_t D1[NJS], D1l[NJS], D2[NJS], D2l[NJS];
 #pragma unroll
         for (int js = 0; js < NJS; ++js) {
-          const op_t Dop = tr_op<T, TN>(sD, js * KS, col, lane);
+          const op_t Dop = tr_op<T, TN>(sD, js * KS, col, ln);
           if constexpr (E == 8) {
             u32x4 h1, l1, h2, l2;
 #pragma unroll
@@ -317,7 +347,7 @@ k_tangent(TanArgs a) {
           f32x4 m2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int js = 0; js < NJS; ++js) {
-            const op_t Aq = tr_op<T, TN>(sQ, js * KS, 16 * tk, lane);
+            const op_t Aq = tr_op<T, TN>(sQ, js * KS, 16 * tk, ln);
             m1 = X::mfma(Aq, D1[js], m1);
             m2 = X::mfma(Aq, D2[js], m2);
             if constexpr (E == 8) {
@@ -349,7 +379,7 @@ k_tangent(TanArgs a) {
       op_t B1[NJS], B1l[NJS], B2[NJS];
 #pragma unroll
       for (int js = 0; js < NJS; ++js) {
-        const op_t Vop = tr_op<T, TN>(sV, js * KS, col, lane);
+        const op_t Vop = tr_op<T, TN>(sV, js * KS, col, ln);
         if constexpr (E == 8) {
           u32x4 b1, b1l, b2;
 #pragma unroll
@@ -372,14 +402,15 @@ k_tangent(TanArgs a) {
         }
       }
 #pragma unroll
-      for (int tk = 0; tk < NKT; ++tk)
+      for (int tk = 0; tk < NKT; ++tk) {
 #pragma unroll
         for (int js = 0; js < NJS; ++js) {
-          const op_t Ak = tr_op<T, TN>(sK, js * KS, 16 * tk, lane);
+          const op_t Ak = tr_op<T, TN>(sK, js * KS, 16 * tk, ln);
           accS[tk] = X::mfma(Ak, B1[js], accS[tk]);
           accT[tk] = X::mfma(Ak, B2[js], accT[tk]);
           if constexpr (E == 8) accS[tk] = X::mfma(Ak, B1l[js], accS[tk]);
         }
+      }
     }
   }
 
@@ -387,11 +418,16 @@ k_tangent(TanArgs a) {
     // the state term <dS_end, U_end>, on the sequence's last sub-segment
     if (p == a.split - 1 && a.dSe) {
       const float* ds = a.dSe + n * DD;
+      // the lane's element offset, formed here: otherwise the compiler shares
+      // the 32 addresses with the start-state loads and keeps them across the
+      // chunk loop
+      unsigned lo = (unsigned)(4 * g * D + col + l16);
+      asm volatile("" : "+v"(lo));
       float e = 0.0f;
 #pragma unroll
       for (int tk = 0; tk < NKT; ++tk)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) e += ds[(16 * tk + 4 * g + r) * D + col + l16] * accT[tk][r];
+        for (int r = 0; r < 4; ++r) e += ds[lo + (unsigned)((16 * tk + r) * D)] * accT[tk][r];
       dsum += (double)e;
     }
     // workgroup sum in a fixed order

@@ -23,6 +23,7 @@ CASES = [
     # dtype, D, B, H, L, nseg, split, S0 std, dS_end std, decay
     ("fp32", 64, 2, 2, 200, 1, 0, 0.5, 0.5, True),
     ("fp32", 128, 1, 2, 64 * 6, 2, 3, 0.5, 0.5, True),
+    ("fp32", 128, 1, 2, 64 * 5 + 23, 1, 2, 0.5, 0.5, True),  # ragged, no scratch spills
     ("fp32", 64, 1, 3, 1000, 1, 1, 0.0, 0.0, True),
     ("fp32", 64, 1, 2, 300, 1, 0, 0.5, 0.5, False),
     ("bf16", 128, 2, 3, 337, 1, 0, 0.5, 0.5, True),
