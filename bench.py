@@ -90,7 +90,7 @@ def measured_traffic():
     return rec["traffic_bytes"]
 
 
-def backward_leg(torch, la, workload_inputs, WORKLOADS, dev, iters):
+def backward_leg(torch, la, workload_inputs, WORKLOADS, dev, iters, ramp_ms):
     """la_chunk_bwd at the training workload (B=1, H=16, L=262144, d=128,
     bf16; dO ~ N(0,1), S0 = dS_end = 0): time per call with events, against
     the backward's algorithmic bytes (Q, K, V, dO read and dQ, dK, dV written
@@ -108,14 +108,13 @@ def backward_leg(torch, la, workload_inputs, WORKLOADS, dev, iters):
     def call():
         la.la_chunk_bwd(q, k, v, lam, dO, S0=S0, dS_end=dSe, out=out, workspace=ws)
 
-    for _ in range(2):
-        call()
-    torch.cuda.synchronize()
+    ramp(call, ramp_ms)
     ms = time_events(call, iters, torch.cuda.current_stream())
     nbytes = B * H * L * 7 * d * 2 + B * H * d * d * 4 * (1 + int(S0 is not None) + int(dSe is not None))
     flops = B * H * L * 205440
     t = ms / 1e3
-    rec = {"workload": w.name, "B": B, "H": H, "L": L, "d": d, "us_per_call": ms * 1e3,
+    rec = {"workload": w.name, "B": B, "H": H, "L": L, "d": d, "ramp_ms_each": ramp_ms,
+           "us_per_call": ms * 1e3,
            "tokens_per_s": B * L / t, "alg_bytes": nbytes, "achieved_GBs": nbytes / t / 1e9,
            "frac_hbm": nbytes / t / 1e9 / HBM_PEAK_GBS, "tflops_alg": flops / t / 1e12}
     # the same backward taking the start states a forward call just left in
@@ -127,9 +126,7 @@ def backward_leg(torch, la, workload_inputs, WORKLOADS, dev, iters):
         la.la_chunk_bwd(q, k, v, lam, dO, S0=S0, dS_end=dSe, out=out, workspace=ws,
                         fwd_workspace=fws)
 
-    for _ in range(2):
-        fcall()
-    torch.cuda.synchronize()
+    ramp(fcall, ramp_ms)
     fms = time_events(fcall, iters, torch.cuda.current_stream())
     ft = fms / 1e3
     rec["from_fwd_states"] = {"us_per_call": fms * 1e3, "tokens_per_s": B * L / ft,
@@ -146,9 +143,7 @@ def backward_leg(torch, la, workload_inputs, WORKLOADS, dev, iters):
     def gcall():
         la.la_chunk_bwd_gated(q, k, v, G, dO, S0=S0, dS_end=dSe, out=gout, workspace=gws)
 
-    for _ in range(2):
-        gcall()
-    torch.cuda.synchronize()
+    ramp(gcall, ramp_ms)
     gms = time_events(gcall, iters, torch.cuda.current_stream())
     gbytes = nbytes + B * H * L * 8
     gt = gms / 1e3
@@ -162,9 +157,7 @@ def backward_leg(torch, la, workload_inputs, WORKLOADS, dev, iters):
     def tcall():
         la.la_decay_grad(q, k, v, lam, dO, S0=S0, dS_end=dSe, out=dlam, workspace=tws)
 
-    for _ in range(2):
-        tcall()
-    torch.cuda.synchronize()
+    ramp(tcall, ramp_ms)
     tms = time_events(tcall, iters, torch.cuda.current_stream())
     tbytes = B * H * L * 4 * d * 2
     tt = tms / 1e3
@@ -175,7 +168,7 @@ def backward_leg(torch, la, workload_inputs, WORKLOADS, dev, iters):
     return rec
 
 
-def gated_leg(torch, la, inp, dev, iters, gate_logs):
+def gated_leg(torch, la, inp, dev, iters, gate_logs, ramp_ms):
     """la_chunk_fwd_gated on the same 64K x 32 inputs with seeded per-token
     log-gates (on average each head's fixed decay): time per call, against
     the forward's algorithmic bytes plus the gates read once (4 B per
@@ -191,18 +184,16 @@ def gated_leg(torch, la, inp, dev, iters, gate_logs):
     def call():
         la.la_chunk_fwd_gated(q, k, v, G, S0=S0, out=O, S_end_out=S_end, workspace=ws)
 
-    for _ in range(3):
-        call()
-    torch.cuda.synchronize()
+    ramp(call, ramp_ms)
     ms = time_events(call, iters, torch.cuda.current_stream())
     nbytes = alg_bytes(B, H, L, d) + B * H * L * 4
     t = ms / 1e3
-    return {"workload": "segment_64k with per-token gates", "us_per_call": ms * 1e3,
+    return {"workload": "segment_64k with per-token gates", "ramp_ms": ramp_ms, "us_per_call": ms * 1e3,
             "tokens_per_s": B * L / t, "alg_bytes": nbytes, "achieved_GBs": nbytes / t / 1e9,
             "frac_hbm": nbytes / t / 1e9 / HBM_PEAK_GBS}
 
 
-def decode_leg(torch, la, dev, iters, name="decode_b64"):
+def decode_leg(torch, la, dev, iters, name="decode_b64", ramp_ms=0.0):
     """la_step on a decode batch (decode_b64: 64 sequences x 32 heads, d = 128,
     bf16, state updated in place; decode_b512: 512 sequences, whose 1 GiB of
     state cannot stay in the last-level cache between steps): the median of
@@ -218,15 +209,13 @@ def decode_leg(torch, la, dev, iters, name="decode_b64"):
     def call():
         la.la_step(q, k, v, lam, S, out=o, S_out=S)
 
-    for _ in range(5):
-        call()
-    torch.cuda.synchronize()
+    ramp(call, ramp_ms)
     each = sorted(time_each(call, iters, torch.cuda.current_stream()))
     ms = each[len(each) // 2]  # median: a step is short enough for one stall to swamp a mean
     nbytes = B * H * (2 * d * d * 4 + 4 * d * 2)
     t = ms / 1e3
     del inp, q, k, v, S, o
-    return {"workload": name, "B": B, "H": H, "d": d, "dtype": w["dtype"],
+    return {"workload": name, "B": B, "H": H, "d": d, "dtype": w["dtype"], "ramp_ms": ramp_ms,
             "us_per_call": ms * 1e3, "us_min": each[0] * 1e3, "us_max": each[-1] * 1e3,
             "calls": iters, "tokens_per_s": B / t, "alg_bytes": nbytes,
             "achieved_GBs": nbytes / t / 1e9, "frac_hbm": nbytes / t / 1e9 / HBM_PEAK_GBS}
@@ -362,6 +351,9 @@ def main():
     ap.add_argument("--ramp-ms", type=float, default=500.0,
                     help="untimed calls for at least this long before the warm-up steps, so "
                          "that the GPU clock has settled whatever --warmup is")
+    ap.add_argument("--leg-ramp-ms", type=float, default=200.0,
+                    help="untimed calls before each further leg (the clock drops while the host "
+                         "prepares a leg)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--split", type=int, default=0, help="internal split (0 = library choice)")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward leg")
@@ -500,24 +492,25 @@ def main():
     }
     if not args.no_gated:
         from long_sequence_causal_amd.inputs import gate_logs
-        gl = gated_leg(torch, la, inp, dev, args.steps, gate_logs)
+        gl = gated_leg(torch, la, inp, dev, args.steps, gate_logs, args.leg_ramp_ms)
         eprint(f"[bench] gated forward: {gl['us_per_call']:.1f} us/call, "
                f"{gl['achieved_GBs']:.0f} GB/s algorithmic")
         rec["gated"] = gl
     if not args.no_bwd:
         del O, ws
-        bw = backward_leg(torch, la, workload_inputs, WORKLOADS, dev, max(3, args.steps // 5))
+        bw = backward_leg(torch, la, workload_inputs, WORKLOADS, dev, max(3, args.steps // 5),
+                          args.leg_ramp_ms)
         eprint(f"[bench] backward ({bw['workload']}): {bw['us_per_call']:.1f} us/call, "
                f"{bw['achieved_GBs']:.0f} GB/s algorithmic; from the forward's states "
                f"{bw['from_fwd_states']['us_per_call']:.1f} us/call; gated {bw['gated']['us_per_call']:.1f} us/call; "
                f"decay gradient {bw['decay_grad']['us_per_call']:.1f} us/call")
         rec["backward"] = bw
     if not args.no_decode:
-        dl = decode_leg(torch, la, dev, max(200, args.steps))
+        dl = decode_leg(torch, la, dev, max(200, args.steps), ramp_ms=args.leg_ramp_ms)
         eprint(f"[bench] decode step ({dl['workload']}): {dl['us_per_call']:.1f} us/call median "
                f"(min {dl['us_min']:.1f}, max {dl['us_max']:.1f} over {dl['calls']}), "
                f"{dl['achieved_GBs']:.0f} GB/s algorithmic")
-        dx = decode_leg(torch, la, dev, 50, "decode_b512")
+        dx = decode_leg(torch, la, dev, 50, "decode_b512", ramp_ms=args.leg_ramp_ms)
         eprint(f"[bench] decode step ({dx['workload']}, state beyond the last-level cache): "
                f"{dx['us_per_call']:.1f} us/call median, {dx['achieved_GBs']:.0f} GB/s algorithmic")
         dl["beyond_cache"] = dx
