@@ -14,10 +14,11 @@
 //     which scale q_u by exp(c_u), k_u by exp(-c_u) and S_end by exp(c_L)).
 //     The suffix sums run only inside blocks of 1024 tokens
 //     (k_gate_grad_blocks forms r_u = q_u . dq_u - k_u . dk_u and its reverse
-//     cumulative sum there); the value at the first token of the next block
-//     is taken exactly from the first form, with S and G the fp32 start states
-//     the two sweeps already hold at that row (k_gate_anchors), and
-//     k_gate_grad_finish adds it.  Summing r over a whole long segment
+//     cumulative sum there, k_gate_grad_rows when the walks formed both row
+//     dots); the value at the first token of the next block is taken exactly
+//     from the first form, with S and G the fp32 start states the two sweeps
+//     already hold at that row (k_gate_anchors), and k_gate_grad_finish adds
+//     it (k_gate_grad_rows adds it itself).  Summing r over a whole long segment
 //     instead would carry the rounding of dq and dk (and of the sweeps'
 //     bf16 operands) over every token: about 15 % at 256K tokens.
 #include "la_device.h"
@@ -59,13 +60,11 @@ __device__ inline float dot8(const T* a, const T* b) {
 // shuffles, then the block's reverse cumulative sum is taken in LDS:
 // dG[t] = sum_{u >= t in block} r_u, and the block total goes to tot[n][b]
 // (when tot is not null).  MODE 1: k_u . dk_u comes from dG itself (formed
-// by the joint dV/dK walk), read before the block's values are written;
-// MODE 2: q_u . dq_u comes from rq too (formed by the dQ walk), so no
-// token tensor is read.
+// by the joint dV/dK walk), read before the block's values are written.
 template <typename T, int D, int MODE>
 __global__ __launch_bounds__(256) void k_gate_grad_blocks(const T* Q, const T* dQ, const T* K,
-                                                          const T* dK, const float* rq, float* dG,
-                                                          float* tot, int64_t Ls, int64_t nb) {
+                                                          const T* dK, float* dG, float* tot,
+                                                          int64_t Ls, int64_t nb) {
   static_assert(D / 8 <= 16, "16 lanes of 8 features cover a row");
   __shared__ float r[GBLK];
   const int64_t n = blockIdx.x / nb;
@@ -76,17 +75,13 @@ __global__ __launch_bounds__(256) void k_gate_grad_blocks(const T* Q, const T* d
   const int tok = threadIdx.x >> 4;   // 16 tokens per pass
   for (int i = tok; i < GBLK; i += 16) {
     float s = 0.0f;
-    if constexpr (MODE == 2) {
-      if (sub == 0 && i < len) s = rq[n * Ls + t0 + i] - dG[n * Ls + t0 + i];
-    } else {
-      if (i < len && sub < D / 8) {
-        const int64_t row = (n * Ls + t0 + i) * D + 8 * sub;
-        s = MODE == 1 ? dot8(Q + row, dQ + row) : dot8(Q + row, dQ + row) - dot8(K + row, dK + row);
-      }
-#pragma unroll
-      for (int m = 8; m >= 1; m >>= 1) s += __shfl_xor(s, m, 16);
-      if (MODE == 1 && i < len) s -= dG[n * Ls + t0 + i];
+    if (i < len && sub < D / 8) {
+      const int64_t row = (n * Ls + t0 + i) * D + 8 * sub;
+      s = MODE == 1 ? dot8(Q + row, dQ + row) : dot8(Q + row, dQ + row) - dot8(K + row, dK + row);
     }
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) s += __shfl_xor(s, m, 16);
+    if (MODE == 1 && i < len) s -= dG[n * Ls + t0 + i];
     if (sub == 0) r[i] = s;  // tokens past the end hold 0
   }
   __syncthreads();
@@ -106,6 +101,49 @@ __global__ __launch_bounds__(256) void k_gate_grad_blocks(const T* Q, const T* d
   }
   for (int i = threadIdx.x; i < len; i += 256) dG[n * Ls + t0 + i] = r[i];
   if (threadIdx.x == 0 && tot) tot[n * nb + b] = r[0];
+}
+
+// The same when both row dots come from the walks (q_u . dq_u in rq, k_u .
+// dk_u in dG), with the anchors already in tot: one workgroup of 256 lanes
+// per (sequence, block of GBLK tokens), lane j taking tokens 4 j .. 4 j + 3.
+// Each lane sums its four from the end, the lanes' totals are summed from
+// the end across each wave by shuffles and across the four waves in LDS, and
+// dG[t] = sum_{u >= t in block} r_u + tot[n][block] is written in place.
+__global__ __launch_bounds__(256) void k_gate_grad_rows(const float* rq, float* dG,
+                                                        const float* tot, int64_t Ls, int64_t nb) {
+  static_assert(GBLK == 4 * 256, "four tokens a lane");
+  __shared__ float wsum[4];
+  const int64_t n = blockIdx.x / nb;
+  const int64_t b = blockIdx.x % nb;
+  const int64_t base = n * Ls + b * GBLK;
+  const int len = (int)((b * GBLK + GBLK < Ls) ? GBLK : Ls - b * GBLK);
+  const int j = threadIdx.x, lane = j & 63, w = j >> 6;
+  float s[4];
+  float acc = 0.0f;
+#pragma unroll
+  for (int e = 3; e >= 0; --e) {  // tokens past the end add 0
+    const int i = 4 * j + e;
+    const float r = (i < len) ? rq[base + i] - dG[base + i] : 0.0f;
+    acc += r;
+    s[e] = acc;
+  }
+  // inclusive suffix sum of the lanes' totals within the wave
+  float x = acc;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float y = __shfl_down(x, off, 64);
+    if (lane + off < 64) x += y;
+  }
+  if (lane == 0) wsum[w] = x;
+  __syncthreads();
+  float later = x - acc;  // lanes after this one in the wave
+  for (int ww = w + 1; ww < 4; ++ww) later += wsum[ww];
+  const float anchor = tot[n * nb + b];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int i = 4 * j + e;
+    if (i < len) dG[base + i] = (s[e] + later) + anchor;
+  }
 }
 
 // One workgroup per (sequence n, block b): tot[n][b] = the gate gradient at
@@ -193,15 +231,16 @@ static hipError_t gate_grad_t(const void* Q, const void* dQ, const void* K, cons
   const int64_t nb = gate_grad_blocks(Ls);
   const dim3 grid((unsigned)(nseq * nb));
   // the block totals are not needed: tot already holds the anchors
-  if (rq)
-    hipLaunchKernelGGL((k_gate_grad_blocks<T, D, 2>), grid, dim3(256), 0, s, nullptr, nullptr,
-                       nullptr, nullptr, rq, dG, nullptr, Ls, nb);
-  else if (K && dK)
+  if (rq) {  // both row dots from the walks: one pass, anchors included
+    hipLaunchKernelGGL(k_gate_grad_rows, grid, dim3(256), 0, s, rq, dG, tot, Ls, nb);
+    return hipGetLastError();
+  }
+  if (K && dK)
     hipLaunchKernelGGL((k_gate_grad_blocks<T, D, 0>), grid, dim3(256), 0, s, (const T*)Q,
-                       (const T*)dQ, (const T*)K, (const T*)dK, nullptr, dG, nullptr, Ls, nb);
+                       (const T*)dQ, (const T*)K, (const T*)dK, dG, nullptr, Ls, nb);
   else
     hipLaunchKernelGGL((k_gate_grad_blocks<T, D, 1>), grid, dim3(256), 0, s, (const T*)Q,
-                       (const T*)dQ, nullptr, nullptr, nullptr, dG, nullptr, Ls, nb);
+                       (const T*)dQ, nullptr, nullptr, dG, nullptr, Ls, nb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t all = nseq * Ls;
