@@ -150,6 +150,15 @@ __device__ inline float wave_prefix_sum(float x) {
   x += dpp_or_zero<0x143, 0xC>(x);  // row_bcast:31 -> rows 2, 3
   return x;
 }
+// sum of x over each row of 16 lanes, in every lane of the row (rotations
+// within the row: row_ror 8, 4, 2, 1; no LDS permutes)
+__device__ inline float row16_sum(float x) {
+  x += dpp_or_zero<0x128, 0xF>(x);
+  x += dpp_or_zero<0x124, 0xF>(x);
+  x += dpp_or_zero<0x122, 0xF>(x);
+  x += dpp_or_zero<0x121, 0xF>(x);
+  return x;
+}
 __device__ inline float lane_value(float x, int lane) {  // x of a wave-uniform lane
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
 }

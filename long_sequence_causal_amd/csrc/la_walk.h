@@ -771,8 +771,7 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob (&jbs)[NH],
               __builtin_memcpy(&y, &vb, 4);
               d = __builtin_amdgcn_fdot2_f32_bf16(x, y, d, false);
             }
-#pragma unroll
-            for (int m = 8; m >= 1; m >>= 1) d += __shfl_xor(d, m, 16);
+            d = row16_sum(d);  // the row's 16 lanes are one DPP row
             if (valid) {
               if (piece == 0) jbs[NH - 1].rk[relrow(c * CH + row)] = d;
               T* orow = Oseq[h] + (unsigned)((relrow(c * CH + row)) * D + 8 * piece);
