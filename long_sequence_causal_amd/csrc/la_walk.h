@@ -383,8 +383,12 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob (&jbs)[NH],
   // K, V lines the state pre-pass left in the last-level cache); storing each
   // lane's 8-byte piece directly sends every 128-byte line to L2 in four
   // pieces from four waves.  Measured at 64K tokens x 32 heads: whole call
-  // 582.7 -> 564.1 us (plain whole-row stores: no gain).
-  constexpr bool OSTAGE = OUT && sizeof(T) == 2 && D == 128;
+  // 582.7 -> 564.1 us (plain whole-row stores: no gain).  Not so for two
+  // walks without row dots (the backward's joint dV/dK walk): there the
+  // staging's two barriers per chunk cost more than the merged lines save,
+  // and its outputs go straight out in 8-byte pieces (plain stores; as
+  // non-temporal pieces the walk took half as long again).
+  constexpr bool OSTAGE = OUT && sizeof(T) == 2 && D == 128 && !(NH == 2 && !RK);
   T ohold[NH][4][4];
   // RK: row dots of the last walk's outputs with the first walk's queries
   // (NH = 2) or with Q2 (one walk of four tiles), per position to the last
