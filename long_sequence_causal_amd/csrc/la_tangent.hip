@@ -34,7 +34,10 @@
 //   U <- lambda^n (U + n S) + dU,   S <- lambda^n S + dS
 // (the Jordan block of the derivative of lambda^n) with (dS, dU) the
 // sub-segment's local pair from zero.  The pre-pass forms
-// the local pairs (K, V only), the scan chains them from (S0, 0), the main
+// the local pairs (K, V only; last chunk first, each chunk's weights
+// carrying the decay of the m tokens after it: lambda^(m + cl-1-j) and
+// (m + cl-1-j) lambda^(m + cl-1-j), so the pair is never rescaled), the scan
+// chains them from (S0, 0), the main
 // pass walks every sub-segment from its start pair and sums its share, and
 // the last kernel adds each head's shares in a fixed order.
 //
@@ -198,7 +201,12 @@ k_tangent(TanArgs a) {
     voff0[k] = (unsigned)(((t0 + row) * D + po) * (int64_t)sizeof(T));
   }
   const unsigned smem_lds = lds_address(smem);
-  auto issue = [&](int c, int stage) {
+  // pre-pass over whole chunks: walked last chunk first (step c takes chunk
+  // nch - 1 - c), the decay of the chunks after it carried by the update
+  // weights instead of scaling the pair every chunk
+  const bool lcf = !MAIN && len % CH == 0;
+  auto issue = [&](int cs, int stage) {
+    const int c = lcf ? nch - 1 - cs : cs;
     const bool full = (c + 1) * CH <= len;
 #pragma unroll
     for (int k = 0; k < NBW; ++k) {
@@ -366,16 +374,23 @@ k_tangent(TanArgs a) {
     // ---- updates: U = lambda^cl (U + cl S) + K^T diag((cl-1-j) lambda^(cl-1-j)) V,
     //               S = lambda^cl S + K^T diag(lambda^(cl-1-j)) V
     {
-      const float dcu = dc * (float)clf;
+      // last chunk first: the m = 64 c tokens after this chunk decay its
+      // contribution (weights lambda^(m + cl-1-j), (m + cl-1-j) lambda^(m + cl-1-j));
+      // otherwise the pair moves over the chunk first
+      const float fk = lcf ? pow_lam(lg, (float)(CH * c)) : 1.0f;
+      if (!lcf) {
+        const float dcu = dc * (float)clf;
 #pragma unroll
-      for (int tk = 0; tk < NKT; ++tk) {
-        accT[tk] = dc * accT[tk] + dcu * accS[tk];
-        accS[tk] *= dc;
+        for (int tk = 0; tk < NKT; ++tk) {
+          accT[tk] = dc * accT[tk] + dcu * accS[tk];
+          accS[tk] *= dc;
+        }
       }
       // V^T operands of this wave's columns, scaled per token (S update: hi + lo
       // in bf16; U update: one rounding)
       const float* tw = tabW + 16 * g;
-      const float cB = (float)(clf - 1) - fB;  // clf - 1 - slot_token = cB - slot_token(., 0, .)
+      // m + clf - 1 - slot_token = cB - slot_token(., 0, .) (small integers, exact)
+      const float cB = (float)(clf - 1) - fB + (lcf ? (float)(CH * c) : 0.0f);
       op_t B1[NJS], B1l[NJS], B2[NJS];
 #pragma unroll
       for (int js = 0; js < NJS; ++js) {
@@ -384,8 +399,8 @@ k_tangent(TanArgs a) {
           u32x4 b1, b1l, b2;
 #pragma unroll
           for (int x = 0; x < 8; x += 2) {
-            const float vw0 = (float)Vop[x] * tw[8 * js + x];
-            const float vw1 = (float)Vop[x + 1] * tw[8 * js + x + 1];
+            const float vw0 = (float)Vop[x] * (tw[8 * js + x] * fk);
+            const float vw1 = (float)Vop[x + 1] * (tw[8 * js + x + 1] * fk);
             const float vu0 = vw0 * (cB - (float)slot_token<T>(js * KS, 0, x));
             const float vu1 = vw1 * (cB - (float)slot_token<T>(js * KS, 0, x + 1));
             const u32x2 s1 = split_hi_lo(vw0, vw1);
@@ -397,8 +412,8 @@ k_tangent(TanArgs a) {
           B1l[js] = __builtin_bit_cast(bf16x8, b1l);
           B2[js] = __builtin_bit_cast(bf16x8, b2);
         } else {
-          B1[js] = Vop * tw[js];
-          B2[js] = B1[js] * (float)(clf - 1 - slot_token<T>(js * KS, g, 0));
+          B1[js] = Vop * (tw[js] * fk);
+          B2[js] = B1[js] * (cB + fB - (float)slot_token<T>(js * KS, g, 0));
         }
       }
 #pragma unroll
