@@ -36,33 +36,31 @@ __global__ __launch_bounds__(256) void k_state_scan(ScanArgs a) {
   // written only after its own input was read, so in place stays correct.
   constexpr int PF = 16;
   auto seg = [&](int it) { return a.reverse ? (a.P - 1 - it) : it; };
-  int it = 0;
-  for (; it + PF <= a.P; it += PF) {
+  for (int it = 0; it < a.P; it += PF) {
+    // (the last group may be partial: the same count for every thread)
+    const int cnt = (a.P - it < PF) ? a.P - it : PF;
     float d[PF], f[PF];
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
-      const int s = seg(it + j);
-      d[j] = a.dS[(n * a.P + s) * a.E + e];
-      f[j] = GATED ? a.LD[n * a.P + s] : 0.0f;
+      d[j] = 0.0f;
+      f[j] = 0.0f;
+      if (j < cnt) {
+        const int s = seg(it + j);
+        d[j] = a.dS[(n * a.P + s) * a.E + e];
+        if (GATED) f[j] = a.LD[n * a.P + s];
+      }
     }
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
-      const int64_t idx = (n * a.P + seg(it + j)) * a.E + e;
-      if (!a.inclusive) a.Sout[idx] = x;
-      // gated: the segment's own product of gates, exp(LD)
-      x = (GATED ? expf(f[j]) : dcur) * x + d[j];
-      dcur = dec;
-      if (a.inclusive) a.Sout[idx] = x;
+      if (j < cnt) {
+        const int64_t idx = (n * a.P + seg(it + j)) * a.E + e;
+        if (!a.inclusive) a.Sout[idx] = x;
+        // gated: the segment's own product of gates, exp(LD)
+        x = (GATED ? expf(f[j]) : dcur) * x + d[j];
+        dcur = dec;
+        if (a.inclusive) a.Sout[idx] = x;
+      }
     }
-  }
-  for (; it < a.P; ++it) {
-    const int s = seg(it);
-    const int64_t idx = (n * a.P + s) * a.E + e;
-    const float d = a.dS[idx];
-    if (!a.inclusive) a.Sout[idx] = x;
-    x = (GATED ? expf(a.LD[n * a.P + s]) : dcur) * x + d;
-    dcur = dec;
-    if (a.inclusive) a.Sout[idx] = x;
   }
   if (a.Send) a.Send[n * a.E + e] = x;
 }
