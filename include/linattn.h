@@ -241,9 +241,11 @@ la_status la_state_scan_gated(int64_t B, int64_t H, int32_t P, int32_t dk, int32
                               const float* dS, const float* log_decay, const float* S0,
                               float* S_start, float* S_end, int32_t reverse, void* stream);
 
-/* Workspace bytes la_chunk_bwd_gated needs for `shape`: about
- * 3 * ceil(L/nseg / 1024) fp32 d x d states per sequence (the start states of
- * the sweeps, 192 B per token-head at d = 128) plus the shifted gates. */
+/* Workspace bytes la_chunk_bwd_gated needs for `shape`: about 3.4 (segments
+ * of whole 64-token chunks) to 4.5 (ragged ones) times ceil(L/nseg / 1024)
+ * fp32 d x d states per sequence (the sweeps' start states and the states at
+ * every 1024th row, about 220 B per token-head at d = 128) plus the shifted
+ * gates and per-token sums. */
 size_t la_bwd_gated_workspace_bytes(const la_shape* shape);
 
 /*
