@@ -531,6 +531,12 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob (&jbs)[NH],
         if (gwave) write_tables(0);
         lds_barrier();
       }
+      // the next chunk's tables, now: its gates came with this chunk's tiles,
+      // its buffer was last read in the previous chunk, and the gate wave
+      // (one score tile fewer than the busiest waves) has time for them
+      // before the scores' barrier, where at the chunk's end every wave
+      // waited for it at the next barrier
+      if (gwave && c + 1 < nch) write_tables(c + 1);
       read_factors(c);
     } else {
       if (cl != CH) {
@@ -853,12 +859,6 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob (&jbs)[NH],
             for (int r = 0; r < 4; ++r) dst[lo + (unsigned)((16 * tk + r) * D)] = accS[h][tk][r];
         }
       }
-    }
-    // GATED: the next chunk's tables (its gates came with this chunk's
-    // tiles), while the update runs on the matrix cores; the next barrier
-    // publishes them
-    if constexpr (GATED) {
-      if (gwave && c + 1 < nch) write_tables(c + 1);
     }
   }
 
