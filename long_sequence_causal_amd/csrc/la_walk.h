@@ -739,14 +739,17 @@ __device__ __forceinline__ float walk(char* smem, const WalkJob (&jbs)[NH],
 
     // ---- the chunk's O tile through LDS: each wave writes its 16 columns of
     // every token, then stores 8 whole rows, 16 bytes per lane.  One walk:
-    // through its Q tile, right after the outputs.  Two walks (NH = 2): after
+    // through its V tile, right after the outputs (one barrier: nothing reads
+    // that tile after the chunk's V operands).  Two walks (NH = 2): after
     // the state updates, through the tiles no longer read then (the first
     // walk's keys, the second walk's queries), so that the first walk's
     // queries stay in place; RK dots them with the second walk's output rows
     // on the way out.
     auto flush_o = [&]() {
-      auto oslot = [](int h) { return NH == 2 ? (h == 0 ? 2 : 1) : 0; };
-      lds_barrier();  // every wave is done reading the tiles written below
+      // one walk: its V tile, read only into registers at the chunk's start
+      // (so every wave is done with it since the scores' barrier)
+      auto oslot = [&](int h) { return NH == 2 ? (h == 0 ? 2 : 1) : vslot(0); };
+      if constexpr (NH == 2) lds_barrier();  // every wave is done reading the tiles written below
 #pragma unroll
       for (int h = 0; h < NH; ++h) {
         char* const sO = const_cast<char*>(stage + oslot(h) * TB);
