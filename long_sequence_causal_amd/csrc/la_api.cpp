@@ -673,13 +673,16 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
 
   // d l / d log(alpha_t) = sum_{u >= t} (q_u . dq_u - k_u . dk_u) + <dS_end, S_end>, the sum
   // anchored at every sub-segment boundary y by its exact value alpha_y <G_y, S_{y-1}>
-  if (dlog_alpha) {
+  if (dlog_alpha && rq_from_walk) {
+    e = la::launch_gate_grad_rows(RQ, dlog_alpha, W, W3, log_alpha, dS_end,
+                                  need_send ? SE : nullptr, pl.nseq, pl.Ls, pl.D, st);
+    if (e != hipSuccess) return hip_fail(e, "gate gradient launch");
+  } else if (dlog_alpha) {
     e = la::launch_gate_anchors(W, W3, log_alpha, dS_end, need_send ? SE : nullptr, TOT, pl.nseq,
                                 pl.Ls, pl.D, st);
     if (e != hipSuccess) return hip_fail(e, "gate anchor launch");
     e = la::launch_gate_grad(s->dtype, pl.D, Q, dQ, rk_from_walk ? nullptr : K,
-                             rk_from_walk ? nullptr : dK, rq_from_walk ? RQ : nullptr, dlog_alpha,
-                             TOT, dS_end, need_send ? SE : nullptr, pl.nseq, pl.Ls, st);
+                             rk_from_walk ? nullptr : dK, dlog_alpha, TOT, pl.nseq, pl.Ls, st);
     if (e != hipSuccess) return hip_fail(e, "gate gradient launch");
   }
   return LA_OK;

@@ -17,8 +17,8 @@
 //     cumulative sum there, k_gate_grad_rows when the walks formed both row
 //     dots); the value at the first token of the next block is taken exactly
 //     from the first form, with S and G the fp32 start states the two sweeps
-//     already hold at that row (k_gate_anchors), and k_gate_grad_finish adds
-//     it (k_gate_grad_rows adds it itself).  Summing r over a whole long segment
+//     already hold at that row (block_anchor: k_gate_anchors, then
+//     k_gate_grad_finish adds it; k_gate_grad_rows forms and adds it itself).  Summing r over a whole long segment
 //     instead would carry the rounding of dq and dk (and of the sweeps'
 //     bf16 operands) over every token: about 15 % at 256K tokens.
 #include "la_device.h"
@@ -105,26 +105,96 @@ __global__ __launch_bounds__(256) void k_gate_grad_blocks(const T* Q, const T* d
 
 // The same when both row dots come from the walks (q_u . dq_u in rq, k_u .
 // dk_u in dG), with the anchors already in tot: one workgroup of 256 lanes
-// per (sequence, block of GBLK tokens), lane j taking tokens 4 j .. 4 j + 3.
-// Each lane sums its four from the end, the lanes' totals are summed from
-// the end across each wave by shuffles and across the four waves in LDS, and
-// dG[t] = sum_{u >= t in block} r_u + tot[n][block] is written in place.
+// Elementwise dot of two fp32 arrays of n4 four-float vectors by one
+// workgroup of 256 lanes: each lane takes vectors j, j + 256, ..., four loads
+// of each operand in flight, products and the lane's partial sum in fp32;
+// the lanes' partials are returned to the caller's fp64 sum.
+__device__ inline float block_dot(const f32x4* x, const f32x4* y, int64_t n4, int j) {
+  constexpr int U = 4;
+  float e = 0.0f;
+  for (int64_t i0 = j; i0 < n4; i0 += 256 * U) {
+    f32x4 a[U], c[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = i0 + 256 * u;
+      a[u] = (i < n4) ? x[i] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      c[u] = (i < n4) ? y[i] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const f32x4 p = a[u] * c[u];
+      e += (p[0] + p[1]) + (p[2] + p[3]);
+    }
+  }
+  return e;
+}
+
+// The gate gradient at the first token y = (b+1) GBLK of block b + 1 of
+// sequence n, alpha_y <G_y, S_{y-1}>: an elementwise dot of S^T (the forward
+// sweep's start state of sub-segment b + 1) and G^T (the reverse sweep's
+// start state at row y, transposed; the reverse sweep numbers its
+// sub-segments from the end); for the last block <dS_end, S_end> (S_end
+// given transposed; either null: 0).  Products in fp32, the 256 lanes'
+// partials summed in fp64 in a fixed order (by waves, then the four waves in
+// order); the result is returned to every lane.
+__device__ inline float block_anchor(const float* WfT, const float* WrT, const float* G,
+                                     const float* dSe, const float* SendT, int64_t n, int64_t b,
+                                     int64_t Ls, int64_t nb, int D, double* wred) {
+  const int j = threadIdx.x, lane = j & 63, w = j >> 6;
+  const int64_t DD = (int64_t)D * D;
+  float e = 0.0f;
+  double scale = 1.0;
+  if (b < nb - 1) {
+    e = block_dot(reinterpret_cast<const f32x4*>(WfT + (n * (nb - 1) + b) * DD),
+                  reinterpret_cast<const f32x4*>(WrT + (n * (nb - 1) + (nb - 2 - b)) * DD),
+                  DD / 4, j);
+    scale = exp((double)G[n * Ls + (b + 1) * GBLK]);
+  } else if (dSe && SendT) {
+    for (int64_t i = j; i < DD; i += 256) {
+      const int64_t kk = i / D, vv = i % D;
+      e += dSe[n * DD + i] * SendT[n * DD + vv * D + kk];
+    }
+  }
+  double x = (double)e;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_down(x, off, 64);
+  if (lane == 0) wred[w] = x;
+  __syncthreads();
+  const double t = ((wred[0] + wred[1]) + (wred[2] + wred[3])) * scale;
+  return (float)t;
+}
+
+// One workgroup per (sequence, block of GBLK tokens): the block's anchor
+// (block_anchor), then dG[t] = sum_{u >= t in block} r_u + anchor with
+// r_u = rq[u] - dG[u] (q.dq from the dQ walk, k.dk already in dG from the
+// joint dV/dK walk), written in place.  Lane j takes tokens 4 j .. 4 j + 3:
+// each lane sums its four from the end, the lanes' totals are summed from
+// the end across each wave by shuffles and across the four waves in LDS.
 __global__ __launch_bounds__(256) void k_gate_grad_rows(const float* rq, float* dG,
-                                                        const float* tot, int64_t Ls, int64_t nb) {
+                                                        const float* WfT, const float* WrT,
+                                                        const float* G, const float* dSe,
+                                                        const float* SendT, int64_t Ls,
+                                                        int64_t nb, int D) {
   static_assert(GBLK == 4 * 256, "four tokens a lane");
   __shared__ float wsum[4];
+  __shared__ double wred[4];
   const int64_t n = blockIdx.x / nb;
   const int64_t b = blockIdx.x % nb;
   const int64_t base = n * Ls + b * GBLK;
   const int len = (int)((b * GBLK + GBLK < Ls) ? GBLK : Ls - b * GBLK);
   const int j = threadIdx.x, lane = j & 63, w = j >> 6;
+  float r[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {  // tokens past the end add 0
+    const int i = 4 * j + e;
+    r[e] = (i < len) ? rq[base + i] - dG[base + i] : 0.0f;
+  }
+  const float anchor = block_anchor(WfT, WrT, G, dSe, SendT, n, b, Ls, nb, D, wred);
   float s[4];
   float acc = 0.0f;
 #pragma unroll
-  for (int e = 3; e >= 0; --e) {  // tokens past the end add 0
-    const int i = 4 * j + e;
-    const float r = (i < len) ? rq[base + i] - dG[base + i] : 0.0f;
-    acc += r;
+  for (int e = 3; e >= 0; --e) {
+    acc += r[e];
     s[e] = acc;
   }
   // inclusive suffix sum of the lanes' totals within the wave
@@ -138,7 +208,6 @@ __global__ __launch_bounds__(256) void k_gate_grad_rows(const float* rq, float* 
   __syncthreads();
   float later = x - acc;  // lanes after this one in the wave
   for (int ww = w + 1; ww < 4; ++ww) later += wsum[ww];
-  const float anchor = tot[n * nb + b];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int i = 4 * j + e;
@@ -146,45 +215,16 @@ __global__ __launch_bounds__(256) void k_gate_grad_rows(const float* rq, float* 
   }
 }
 
-// One workgroup per (sequence n, block b): tot[n][b] = the gate gradient at
-// the first token y = (b+1) GBLK of the next block, alpha_y <G_y, S_{y-1}>,
-// an elementwise dot of S^T (the forward sweep's start state of sub-segment
-// b + 1) and G^T (the reverse sweep's start state at row y, transposed; the
-// reverse sweep numbers its sub-segments from the end), or for the last block
-// <dS_end, S_end> (S_end given transposed; either null: 0).  Products in
-// fp32, sums in fp64 in a fixed order.
+// One workgroup per (sequence n, block b): tot[n][b] = block_anchor.
 __global__ __launch_bounds__(256) void k_gate_anchors(const float* WfT, const float* WrT,
                                                       const float* G, const float* dSe,
                                                       const float* SendT, float* tot, int64_t Ls,
                                                       int64_t nb, int D) {
-  __shared__ double red[256];
+  __shared__ double wred[4];
   const int64_t n = (int64_t)blockIdx.x / nb;
   const int64_t b = (int64_t)blockIdx.x % nb;
-  const int j = threadIdx.x;
-  const int64_t DD = (int64_t)D * D;
-  float e = 0.0f;
-  double scale = 1.0;
-  if (b < nb - 1) {
-    const f32x4* x = reinterpret_cast<const f32x4*>(WfT + (n * (nb - 1) + b) * DD);
-    const f32x4* y = reinterpret_cast<const f32x4*>(WrT + (n * (nb - 1) + (nb - 2 - b)) * DD);
-    for (int64_t i = j; i < DD / 4; i += 256) {
-      const f32x4 p = x[i] * y[i];
-      e += (p[0] + p[1]) + (p[2] + p[3]);
-    }
-    scale = exp((double)G[n * Ls + (b + 1) * GBLK]);
-  } else if (dSe && SendT) {
-    for (int64_t i = j; i < DD; i += 256) {
-      const int64_t kk = i / D, vv = i % D;
-      e += dSe[n * DD + i] * SendT[n * DD + vv * D + kk];
-    }
-  }
-  red[j] = (double)e;
-  __syncthreads();
-  for (int s2 = 128; s2 > 0; s2 >>= 1) {
-    if (j < s2) red[j] += red[j + s2];
-    __syncthreads();
-  }
-  if (j == 0) tot[n * nb + b] = (float)(red[0] * scale);
+  const float t = block_anchor(WfT, WrT, G, dSe, SendT, n, b, Ls, nb, D, wred);
+  if (threadIdx.x == 0) tot[n * nb + b] = t;
 }
 
 __global__ __launch_bounds__(256) void k_gate_grad_finish(float* dG, const float* tot, int64_t nseq,
@@ -222,19 +262,23 @@ hipError_t launch_gate_anchors(const float* WfT, const float* WrT, const float* 
   return hipGetLastError();
 }
 
+hipError_t launch_gate_grad_rows(const float* rq, float* dG, const float* WfT, const float* WrT,
+                                 const float* G, const float* dSe, const float* SendT,
+                                 int64_t nseq, int64_t Ls, int D, hipStream_t s) {
+  const int64_t nb = gate_grad_blocks(Ls);
+  if (nseq <= 0 || nb <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_gate_grad_rows, dim3((unsigned)(nseq * nb)), dim3(256), 0, s, rq, dG, WfT,
+                     WrT, G, dSe, SendT, Ls, nb, D);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 static hipError_t gate_grad_t(const void* Q, const void* dQ, const void* K, const void* dK,
-                              const float* rq, float* dG, float* tot, const float* dSe,
-                              const float* SendT, int64_t nseq, int64_t Ls, hipStream_t s) {
-  (void)dSe;
-  (void)SendT;
+                              float* dG, const float* tot, int64_t nseq, int64_t Ls,
+                              hipStream_t s) {
   const int64_t nb = gate_grad_blocks(Ls);
   const dim3 grid((unsigned)(nseq * nb));
   // the block totals are not needed: tot already holds the anchors
-  if (rq) {  // both row dots from the walks: one pass, anchors included
-    hipLaunchKernelGGL(k_gate_grad_rows, grid, dim3(256), 0, s, rq, dG, tot, Ls, nb);
-    return hipGetLastError();
-  }
   if (K && dK)
     hipLaunchKernelGGL((k_gate_grad_blocks<T, D, 0>), grid, dim3(256), 0, s, (const T*)Q,
                        (const T*)dQ, (const T*)K, (const T*)dK, dG, nullptr, Ls, nb);
@@ -250,16 +294,15 @@ static hipError_t gate_grad_t(const void* Q, const void* dQ, const void* K, cons
 }
 
 hipError_t launch_gate_grad(int dtype, int D, const void* Q, const void* dQ, const void* K,
-                            const void* dK, const float* rq, float* dG, float* tot,
-                            const float* dSe, const float* SendT, int64_t nseq, int64_t Ls,
+                            const void* dK, float* dG, const float* tot, int64_t nseq, int64_t Ls,
                             hipStream_t s) {
   if (nseq <= 0 || Ls <= 0) return hipSuccess;
   if (dtype == 0) {
-    if (D == 64) return gate_grad_t<__bf16, 64>(Q, dQ, K, dK, rq, dG, tot, dSe, SendT, nseq, Ls, s);
-    if (D == 128) return gate_grad_t<__bf16, 128>(Q, dQ, K, dK, rq, dG, tot, dSe, SendT, nseq, Ls, s);
+    if (D == 64) return gate_grad_t<__bf16, 64>(Q, dQ, K, dK, dG, tot, nseq, Ls, s);
+    if (D == 128) return gate_grad_t<__bf16, 128>(Q, dQ, K, dK, dG, tot, nseq, Ls, s);
   } else {
-    if (D == 64) return gate_grad_t<float, 64>(Q, dQ, K, dK, rq, dG, tot, dSe, SendT, nseq, Ls, s);
-    if (D == 128) return gate_grad_t<float, 128>(Q, dQ, K, dK, rq, dG, tot, dSe, SendT, nseq, Ls, s);
+    if (D == 64) return gate_grad_t<float, 64>(Q, dQ, K, dK, dG, tot, nseq, Ls, s);
+    if (D == 128) return gate_grad_t<float, 128>(Q, dQ, K, dK, dG, tot, nseq, Ls, s);
   }
   return hipErrorInvalidValue;
 }

@@ -238,12 +238,16 @@ hipError_t launch_gate_anchors(const float* WfT, const float* WrT, const float* 
                                int64_t Ls, int D, hipStream_t s);
 // dG[t] = the in-block suffix sum of r_u = q_u . dq_u - k_u . dk_u plus
 // tot[n][t / GBLK].  With K and dK null, dG must already hold k_t . dk_t per
-// token (the joint dV/dK walk's row dots) and is overwritten in place; with
-// rq also given ([nseq][Ls]: q_t . dq_t from the dQ walk), Q and dQ are not
-// read either.
+// token (the joint dV/dK walk's row dots) and is overwritten in place.
 hipError_t launch_gate_grad(int dtype, int D, const void* Q, const void* dQ, const void* K,
-                            const void* dK, const float* rq, float* dG, float* tot,
-                            const float* dSe, const float* SendT, int64_t nseq, int64_t Ls,
+                            const void* dK, float* dG, const float* tot, int64_t nseq, int64_t Ls,
                             hipStream_t s);
+// Both row dots from the walks (rq [nseq][Ls]: q_t . dq_t from the dQ walk;
+// dG: k_t . dk_t from the joint dV/dK walk): one pass that forms each block's
+// anchor as launch_gate_anchors does (same arguments) and writes dG[t] = the
+// in-block suffix sum of rq - dG plus the anchor, in place.
+hipError_t launch_gate_grad_rows(const float* rq, float* dG, const float* WfT, const float* WrT,
+                                 const float* G, const float* dSe, const float* SendT,
+                                 int64_t nseq, int64_t Ls, int D, hipStream_t s);
 
 }  // namespace la
