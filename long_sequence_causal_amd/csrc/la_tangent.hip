@@ -95,7 +95,7 @@ struct TanLayout {
   static_assert(TB == TN::G * 1024, "a tile is G loads of 1 KiB");
 };
 
-template <typename T, int D, bool MAIN>
+template <typename T, int D, bool MAIN, bool LAZY>
 __global__ __launch_bounds__((TanLayout<T, D, MAIN>::NT), (TanLayout<T, D, MAIN>::WAVES_PER_EU)) void
 k_tangent(TanArgs a) {
   typedef TanLayout<T, D, MAIN> LY;
@@ -142,6 +142,10 @@ k_tangent(TanArgs a) {
   const int len = (int)(t1 > t0 ? t1 - t0 : 0);
   const int nch = (len + CH - 1) / CH;
   const float lg = log2f(a.lam[h]);
+  // the main pass runs as two launches, eager (lambda < 1/2) and lazy
+  // (lambda >= 1/2, below); each sub-segment is walked by the one that fits
+  // its head, the other's workgroup ending here
+  if (MAIN && (fabsf(lg) <= 1.0f) != LAZY) return;
   const int64_t DD = (int64_t)D * D;
   const int64_t seq0 = n * a.Ls * D;  // element offset of the sequence's first row
 
@@ -260,12 +264,26 @@ k_tangent(TanArgs a) {
   set_factors(CH);  // tabW is complete at the loop's first barrier
 
   double dsum = 0.0;  // this lane's share of lambda * gradient (main pass)
+  // Lazy main pass (lambda >= 1/2): the accumulators hold the pair divided
+  // by lambda^ntok, ntok the tokens since they last held it as it is, so
+  // that a chunk adds its update with weights divided by lambda^ntok (ntok
+  // counting the chunk) instead of scaling both accumulators by lambda^cl;
+  // its inter-chunk inner products <U, M1> + <S, M2> are multiplied by
+  // lambda^ntok (ntok before the chunk) instead.  Periods of R chunks keep those divisors within 2^64; the
+  // accumulators are scaled back at the end of each.  Below 1/2 one chunk's
+  // divisor could leave fp32's range: the eager pass scales the pair every
+  // chunk.
+  const float alg = fabsf(lg);
+  const int R = !LAZY ? (1 << 30) : (alg * (float)nch <= 1.0f ? nch : (int)(1.0f / alg));
+  int ntok = 0;
   // The token of a contraction slot is a lane-group term plus a
   // compile-time one (slot_token(j0, g, x) = slot_token(j0, 0, x) + fB);
   // small integers, so the factors below are exact in fp32 either way.
   const float fB = (float)slot_token<T>(0, g, 0);
   if (S > 1 && nch > 0) issue(0, 0);
-  for (int c = 0; c < nch; ++c) {
+  for (int c0 = 0; c0 < nch; c0 += R) {
+  const int c1 = (nch - c0 > R) ? c0 + R : nch;
+  for (int c = c0; c < c1; ++c) {
     const int cl = (len - c * CH < CH) ? (len - c * CH) : CH;
     // fp32 at d = 128: the lane index, opaque to the compiler once per chunk,
     // so that the transposed-operand addresses are formed in the chunk from
@@ -295,6 +313,7 @@ k_tangent(TanArgs a) {
 
     if constexpr (MAIN) {
       float part = 0.0f;
+      float pin = 0.0f;  // lazy: the inter term, in the accumulators' scale
       // ---- intra: sum_{j<i} (i-j) lambda^(i-j) (q_i . k_j)(dO_i . v_j), wave's tiles
 #pragma unroll
       for (int st = 0; st < NST; ++st) {
@@ -364,10 +383,15 @@ k_tangent(TanArgs a) {
             }
           }
 #pragma unroll
-          for (int r = 0; r < 4; ++r) part += accT[tk][r] * m1[r] + accS[tk][r] * m2[r];
+          for (int r = 0; r < 4; ++r) {
+            if constexpr (LAZY)
+              pin += accT[tk][r] * m1[r] + accS[tk][r] * m2[r];
+            else
+              part += accT[tk][r] * m1[r] + accS[tk][r] * m2[r];
+          }
         }
       }
-      dsum += (double)part;
+      dsum += LAZY ? (double)(part + pin * pow_lam(lg, (float)ntok)) : (double)part;
     }
 
     __builtin_amdgcn_sched_barrier(0);
@@ -377,8 +401,13 @@ k_tangent(TanArgs a) {
       // last chunk first: the m = 64 c tokens after this chunk decay its
       // contribution (weights lambda^(m + cl-1-j), (m + cl-1-j) lambda^(m + cl-1-j));
       // otherwise the pair moves over the chunk first
-      const float fk = lcf ? pow_lam(lg, (float)(CH * c)) : 1.0f;
-      if (!lcf) {
+      float fk = lcf ? pow_lam(lg, (float)(CH * c)) : 1.0f;
+      if constexpr (LAZY) {
+        ntok += clf;
+        fk = exp2f(-(float)ntok * lg);  // lambda^-ntok <= 2^64
+#pragma unroll
+        for (int tk = 0; tk < NKT; ++tk) accT[tk] += (float)clf * accS[tk];
+      } else if (!lcf) {
         const float dcu = dc * (float)clf;
 #pragma unroll
         for (int tk = 0; tk < NKT; ++tk) {
@@ -399,8 +428,10 @@ k_tangent(TanArgs a) {
           u32x4 b1, b1l, b2;
 #pragma unroll
           for (int x = 0; x < 8; x += 2) {
-            const float vw0 = (float)Vop[x] * (tw[8 * js + x] * fk);
-            const float vw1 = (float)Vop[x + 1] * (tw[8 * js + x + 1] * fk);
+            const float vw0 = LAZY ? ((float)Vop[x] * tw[8 * js + x]) * fk
+                                   : (float)Vop[x] * (tw[8 * js + x] * fk);
+            const float vw1 = LAZY ? ((float)Vop[x + 1] * tw[8 * js + x + 1]) * fk
+                                   : (float)Vop[x + 1] * (tw[8 * js + x + 1] * fk);
             const float vu0 = vw0 * (cB - (float)slot_token<T>(js * KS, 0, x));
             const float vu1 = vw1 * (cB - (float)slot_token<T>(js * KS, 0, x + 1));
             const u32x2 s1 = split_hi_lo(vw0, vw1);
@@ -427,6 +458,16 @@ k_tangent(TanArgs a) {
         }
       }
     }
+  }
+  if constexpr (LAZY) {  // back to the pair as it is
+    const float sg = pow_lam(lg, (float)ntok);
+#pragma unroll
+    for (int tk = 0; tk < NKT; ++tk) {
+      accS[tk] *= sg;
+      accT[tk] *= sg;
+    }
+    ntok = 0;
+  }
   }
 
   if constexpr (MAIN) {
@@ -521,7 +562,7 @@ template <typename T, int D>
 hipError_t tangent_t(const TanArgs& a, int64_t nseq, float* dlam, hipStream_t s) {
   hipError_t e;
   if (nseq > 0 && a.split > 1) {
-    hipLaunchKernelGGL((k_tangent<T, D, false>), dim3((unsigned)(nseq * a.pre_r * (a.split - 1))),
+    hipLaunchKernelGGL((k_tangent<T, D, false, false>), dim3((unsigned)(nseq * a.pre_r * (a.split - 1))),
                        dim3(TanLayout<T, D, false>::NT), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t total = nseq * (int64_t)D * D;
@@ -530,7 +571,10 @@ hipError_t tangent_t(const TanArgs& a, int64_t nseq, float* dlam, hipStream_t s)
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (nseq > 0) {
-    hipLaunchKernelGGL((k_tangent<T, D, true>), dim3((unsigned)(nseq * a.split)),
+    hipLaunchKernelGGL((k_tangent<T, D, true, false>), dim3((unsigned)(nseq * a.split)),
+                       dim3(TanLayout<T, D, true>::NT), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((k_tangent<T, D, true, true>), dim3((unsigned)(nseq * a.split)),
                        dim3(TanLayout<T, D, true>::NT), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

@@ -68,6 +68,29 @@ def test_decay_grad_is_deterministic_and_split_independent():
     assert e <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("dtype,D,split", [("bf16", 128, 1), ("bf16", 128, 2), ("fp32", 64, 2),
+                                           ("bf16", 64, 3), ("fp32", 128, 1)])
+def test_decay_grad_for_decays_on_both_sides_of_one_half(dtype, D, split):
+    """Heads with lambda below 1/2 (the walk scales its pair every chunk), at
+    1/2 and above (the pair is kept divided by a power of lambda and scaled
+    back every few chunks, the period the shorter the faster the decay: one
+    chunk at 1/2 and 0.6, three at 0.8, the whole walk at 0.97 and 1), over
+    eleven chunks and a ragged tail: each head against the oracle on its own
+    scale."""
+    lam = torch.tensor([0.3, 0.5, 0.6, 0.8, 0.97, 1.0], dtype=torch.float32)
+    B, H, L = 1, lam.numel(), 64 * 11 + 9
+    log(f"decay grad across one half: dtype={dtype} D={D} split={split} lambda={lam.tolist()}")
+    inp = make_inputs(B, H, L, D, D, dtype=dtype, s0_std=0.5, nseg=1, need_dO=True,
+                      dS_end_std=0.5, seed=4400 + D + split, device="cuda", lam=lam)
+    q, k, v, lam_d, S0, dO, dSe = (inp[x] for x in ("q", "k", "v", "lam", "S0", "dO", "dS_end"))
+    got = f64(la.la_decay_grad(q, k, v, lam_d, dO, S0=S0, dS_end=dSe, split=split))
+    torch.cuda.synchronize()
+    ref = lao.dlambda(f64(q), f64(k), f64(v), f64(lam_d), f64(dO), S0=f64(S0), dS_end=f64(dSe))
+    own = np.abs(got - ref) / np.abs(ref)
+    log("  per head on its own scale: " + " ".join(f"{x:.1e}" for x in own))
+    assert own.max() <= TOL[dtype]
+
+
 @pytest.mark.parametrize("B,L", [(1, 0), (0, 128)])
 def test_decay_grad_of_empty_problem_is_zero(B, L):
     H, D = 3, 64
