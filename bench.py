@@ -149,6 +149,22 @@ def backward_leg(torch, la, workload_inputs, WORKLOADS, dev, iters, ramp_ms):
     gt = gms / 1e3
     rec["gated"] = {"us_per_call": gms * 1e3, "tokens_per_s": B * L / gt, "alg_bytes": gbytes,
                     "achieved_GBs": gbytes / gt / 1e9, "frac_hbm": gbytes / gt / 1e9 / HBM_PEAK_GBS}
+    # and from the start states a gated forward call just left in its
+    # workspace (la_chunk_bwd_gated_from_fwd)
+    gfws = torch.empty(max(la.la_fwd_gated_workspace_bytes(shape), 1), dtype=torch.uint8,
+                       device=dev)
+    la.la_chunk_fwd_gated(q, k, v, G, S0=S0, need_O=False, workspace=gfws)
+
+    def gfcall():
+        la.la_chunk_bwd_gated(q, k, v, G, dO, S0=S0, dS_end=dSe, out=gout, workspace=gws,
+                              fwd_workspace=gfws)
+
+    ramp(gfcall, ramp_ms)
+    gfms = time_events(gfcall, iters, torch.cuda.current_stream())
+    gft = gfms / 1e3
+    rec["gated"]["from_fwd_states"] = {"us_per_call": gfms * 1e3, "tokens_per_s": B * L / gft,
+                                       "achieved_GBs": gbytes / gft / 1e9,
+                                       "frac_hbm": gbytes / gft / 1e9 / HBM_PEAK_GBS}
     # the decay gradient (forward-mode tangent walk) on the same inputs: reads
     # Q, K, V, dO once (4 d elements per token-head)
     dlam = torch.empty((H,), dtype=torch.float32, device=dev)
@@ -164,7 +180,7 @@ def backward_leg(torch, la, workload_inputs, WORKLOADS, dev, iters, ramp_ms):
     rec["decay_grad"] = {"us_per_call": tms * 1e3, "tokens_per_s": B * L / tt, "alg_bytes": tbytes,
                          "achieved_GBs": tbytes / tt / 1e9,
                          "frac_hbm": tbytes / tt / 1e9 / HBM_PEAK_GBS}
-    del inp, q, k, v, dO, out, ws, G, dG, gout, gws, dlam, tws, fws
+    del inp, q, k, v, dO, out, ws, G, dG, gout, gws, gfws, dlam, tws, fws
     return rec
 
 
@@ -502,7 +518,8 @@ def main():
                           args.leg_ramp_ms)
         eprint(f"[bench] backward ({bw['workload']}): {bw['us_per_call']:.1f} us/call, "
                f"{bw['achieved_GBs']:.0f} GB/s algorithmic; from the forward's states "
-               f"{bw['from_fwd_states']['us_per_call']:.1f} us/call; gated {bw['gated']['us_per_call']:.1f} us/call; "
+               f"{bw['from_fwd_states']['us_per_call']:.1f} us/call; gated {bw['gated']['us_per_call']:.1f} us/call "
+               f"(from the gated forward's states {bw['gated']['from_fwd_states']['us_per_call']:.1f}); "
                f"decay gradient {bw['decay_grad']['us_per_call']:.1f} us/call")
         rec["backward"] = bw
     if not args.no_decode:

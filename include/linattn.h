@@ -280,6 +280,33 @@ la_status la_chunk_bwd_gated(const la_shape* shape, const void* Q, const void* K
                              void* dV, float* dS0, float* dlog_alpha, void* ws,
                              size_t ws_bytes, void* stream);
 
+/*
+ * la_chunk_bwd_gated for a training step that has just run la_chunk_fwd_gated
+ * on the same inputs, as la_chunk_bwd_from_fwd is for la_chunk_bwd: when the
+ * backward's sweeps walk the forward's own sub-segments (the forward's plan
+ * cuts each segment into whole 1024-token blocks, e.g. 8192-token
+ * sub-segments, and the segments are whole 64-token chunks or dlog_alpha is
+ * NULL), the dQ sweep takes the start states that forward call left in its
+ * workspace instead of a gated state pre-pass over K and V and a scan (about
+ * one ninth of the gated backward's time at 256K tokens x 16 heads).  Any
+ * other shape forms them itself and does not read fwd_ws.
+ *   fwd_ws   the workspace of a la_chunk_fwd_gated call with the same shape
+ *            (split included), Q, K, V, log_alpha and S0, not written since;
+ *            read only.  Required when la_fwd_gated_workspace_bytes(shape) > 0,
+ *            else ignored.
+ *   other arguments and the workspace as for la_chunk_bwd_gated.
+ * Results agree with la_chunk_bwd_gated up to fp32 rounding (the forward
+ * forms the same states with K and V in the other operand roles).  Errors as
+ * la_chunk_bwd_gated; a stale or foreign fwd_ws gives wrong numbers, not an
+ * error.
+ */
+la_status la_chunk_bwd_gated_from_fwd(const la_shape* shape, const void* Q, const void* K,
+                                      const void* V, const float* log_alpha, const float* S0,
+                                      const void* dO, const float* dS_end, const void* fwd_ws,
+                                      void* dQ, void* dK, void* dV, float* dS0,
+                                      float* dlog_alpha, void* ws, size_t ws_bytes,
+                                      void* stream);
+
 /* Workspace bytes la_decay_grad needs for `shape`; 0 for an invalid shape. */
 size_t la_decay_grad_workspace_bytes(const la_shape* shape);
 

@@ -512,10 +512,15 @@ size_t la_bwd_gated_workspace_bytes(const la_shape* shape) {
   return gated_bwd_ws(pl).total;
 }
 
-la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, const void* V,
-                             const float* log_alpha, const float* S0, const void* dO,
-                             const float* dS_end, void* dQ, void* dK, void* dV, float* dS0,
-                             float* dlog_alpha, void* ws, size_t ws_bytes, void* stream) {
+// The backward of la_chunk_fwd_gated; with from_fwd, fwd_starts holds the
+// start states S [nseq][split-1][D][D] a la_chunk_fwd_gated call of the same
+// shape left in its workspace, which the dQ sweep reads transposed when it
+// walks that call's sub-segments.
+static la_status chunk_bwd_gated(const la_shape* s, const void* Q, const void* K,
+                                 const void* V, const float* log_alpha, const float* S0,
+                                 const void* dO, const float* dS_end, const float* fwd_starts,
+                                 bool from_fwd, void* dQ, void* dK, void* dV, float* dS0,
+                                 float* dlog_alpha, void* ws, size_t ws_bytes, void* stream) {
   Plan pl0;
   la_status r = check_shape(s, &pl0);
   if (r != LA_OK) return r;
@@ -537,7 +542,10 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
   const bool has_tokens = pl.nseq > 0 && pl.Ls > 0;
   if (has_tokens && (!Q || !K || !V || !log_alpha || !dO || !dQ || !dK || !dV))
     return fail(LA_ERR_INVALID_ARG, "Q, K, V, log_alpha, dO, dQ, dK and dV are required");
-  const void* ptrs[] = {Q, K, V, log_alpha, S0, dO, dS_end, dQ, dK, dV, dS0, dlog_alpha, ws};
+  if (from_fwd && pl0.nseq > 0 && pl0.split > 1 && !fwd_starts)
+    return fail(LA_ERR_INVALID_ARG, "fwd_ws is required (this shape splits sequences)");
+  const void* ptrs[] = {Q, K, V, log_alpha, S0, dO, dS_end, dQ, dK, dV, dS0, dlog_alpha, ws,
+                        fwd_starts};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return fail(LA_ERR_INVALID_ARG, "pointer %p is not 16-byte aligned", p);
   const GatedBwdWs L = gated_bwd_ws(pl0);
@@ -579,14 +587,23 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
   const int sstep = fine ? (int)step : 1;
   const bool dumps = dlog_alpha && !fine;
   const bool need_send = dlog_alpha && dS_end;
-  r = run_states(pf, s->dtype, H, s->nseg, V, K, nullptr, S0, Wf, 0, st, true, log_alpha, LDw,
-                 false, true);
-  if (r != LA_OK) return r;
+  // the forward's start states serve when the sweeps walk its own sub-segments
+  const bool reuse = from_fwd && !fine && pf.split > 1 && pf.Lp == pl0.Lp &&
+                     pf.split == pl0.split && pf.ragged_first == pl0.ragged_first;
+  if (!reuse) {
+    r = run_states(pf, s->dtype, H, s->nseg, V, K, nullptr, S0, Wf, 0, st, true, log_alpha, LDw,
+                   false, true);
+    if (r != LA_OK) return r;
+  }
   la::FwdArgs aq = main_args(plc, H, s->nseg, dO, V, K, nullptr, S0, dQ,
                              need_send ? SE : nullptr, Wf, 0, true, log_alpha);
   aq.s0_transposed = 1;
   aq.sws_nper = pf.split - 1;
   aq.sws_step = sstep;
+  if (reuse) {
+    aq.Sws = fwd_starts;
+    aq.sws_transposed = 1;
+  }
   if (dumps) {
     aq.dump = W;
     aq.dump_rows = (int)kGateBlock;
@@ -686,6 +703,24 @@ la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, co
     if (e != hipSuccess) return hip_fail(e, "gate gradient launch");
   }
   return LA_OK;
+}
+
+la_status la_chunk_bwd_gated(const la_shape* s, const void* Q, const void* K, const void* V,
+                             const float* log_alpha, const float* S0, const void* dO,
+                             const float* dS_end, void* dQ, void* dK, void* dV, float* dS0,
+                             float* dlog_alpha, void* ws, size_t ws_bytes, void* stream) {
+  return chunk_bwd_gated(s, Q, K, V, log_alpha, S0, dO, dS_end, nullptr, false, dQ, dK, dV, dS0,
+                         dlog_alpha, ws, ws_bytes, stream);
+}
+
+la_status la_chunk_bwd_gated_from_fwd(const la_shape* s, const void* Q, const void* K,
+                                      const void* V, const float* log_alpha, const float* S0,
+                                      const void* dO, const float* dS_end, const void* fwd_ws,
+                                      void* dQ, void* dK, void* dV, float* dS0,
+                                      float* dlog_alpha, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  return chunk_bwd_gated(s, Q, K, V, log_alpha, S0, dO, dS_end, static_cast<const float*>(fwd_ws),
+                         true, dQ, dK, dV, dS0, dlog_alpha, ws, ws_bytes, stream);
 }
 
 size_t la_decay_grad_workspace_bytes(const la_shape* shape) {

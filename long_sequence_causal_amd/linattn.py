@@ -25,7 +25,7 @@ EXPORTS = ("la_version", "la_status_str", "la_last_error", "la_fwd_workspace_byt
            "la_fwd_gated_workspace_bytes", "la_chunk_fwd_gated", "la_state_scan_gated",
            "la_bwd_gated_workspace_bytes", "la_chunk_bwd_gated",
            "la_decay_grad_workspace_bytes", "la_decay_grad", "la_step", "la_chunk_bwd_from_fwd",
-           "la_chunk_fwd_noalloc")
+           "la_chunk_bwd_gated_from_fwd", "la_chunk_fwd_noalloc")
 
 
 class LinAttnError(RuntimeError):
@@ -79,6 +79,8 @@ def lib():
     L.la_bwd_gated_workspace_bytes.argtypes = [sp]
     L.la_chunk_bwd_gated.restype = ctypes.c_int
     L.la_chunk_bwd_gated.argtypes = [sp] + [vp] * 13 + [sz, vp]
+    L.la_chunk_bwd_gated_from_fwd.restype = ctypes.c_int
+    L.la_chunk_bwd_gated_from_fwd.argtypes = [sp] + [vp] * 14 + [sz, vp]
     L.la_state_scan_gated.restype = ctypes.c_int
     L.la_state_scan_gated.argtypes = [i64, i64, i32, i32, i32, vp, vp, vp, vp, vp, i32, vp]
     L.la_chunk_bwd_from_fwd.restype = ctypes.c_int
@@ -372,10 +374,12 @@ def la_bwd_gated_workspace_bytes(shape: la_shape) -> int:
 
 def la_chunk_bwd_gated(q, k, v, log_alpha, dO, S0=None, dS_end=None, nseg: int = 1,
                        need_dS0: bool = True, need_dlog_alpha: bool = True, split: int = 0,
-                       workspace=None, out=None):
+                       workspace=None, out=None, fwd_workspace=None):
     """Backward of the gated forward.  Returns (dQ, dK, dV, dS0 or None,
     dlog_alpha or None); `out` may give all five preallocated (None entries
-    are not returned)."""
+    are not returned).  With `fwd_workspace` (the workspace tensor a
+    la_chunk_fwd_gated call with the same shape and inputs just used) the call
+    goes to la_chunk_bwd_gated_from_fwd."""
     B, H, L, dk = q.shape
     dv = v.shape[-1]
     dt = _dtype_code(q.dtype)
@@ -401,10 +405,21 @@ def la_chunk_bwd_gated(q, k, v, log_alpha, dO, S0=None, dS_end=None, nseg: int =
         dG = torch.empty((B, H, L), dtype=torch.float32, device=q.device) if need_dlog_alpha else None
     nbytes = la_bwd_gated_workspace_bytes(shape)
     ws = workspace if workspace is not None else _workspace(nbytes, q.device)
-    _check(lib().la_chunk_bwd_gated(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
-                                    _ptr(S0), _ptr(dO), _ptr(dS_end), _ptr(dQ), _ptr(dK), _ptr(dV),
-                                    _ptr(dS0), _ptr(dG), _ptr(ws), ws.numel() if ws is not None else 0,
-                                    _stream()))
+    nws = ws.numel() if ws is not None else 0
+    if fwd_workspace is not None:
+        need = la_fwd_gated_workspace_bytes(shape)
+        if fwd_workspace.numel() * fwd_workspace.element_size() < need:
+            raise ValueError(f"fwd_workspace holds fewer than the {need} bytes of this shape's plan")
+        _need(fwd_workspace, "fwd_workspace")
+        _check(lib().la_chunk_bwd_gated_from_fwd(
+            ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(S0), _ptr(dO),
+            _ptr(dS_end), _ptr(fwd_workspace), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dS0), _ptr(dG),
+            _ptr(ws), nws, _stream()))
+    else:
+        _check(lib().la_chunk_bwd_gated(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
+                                        _ptr(log_alpha), _ptr(S0), _ptr(dO), _ptr(dS_end),
+                                        _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dS0), _ptr(dG),
+                                        _ptr(ws), nws, _stream()))
     return dQ, dK, dV, dS0, dG
 
 

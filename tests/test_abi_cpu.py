@@ -221,6 +221,13 @@ def test_gated_entry_points_validate_on_the_host():
     assert scan(None, FAKE, FAKE) == la.LA_ERR_INVALID_ARG
     assert scan(FAKE, FAKE + 8, FAKE) == la.LA_ERR_INVALID_ARG
     assert scan(FAKE, FAKE, FAKE, P=-1) == la.LA_ERR_INVALID_ARG
+    # the backward from the forward's states: split 4 needs the forward's workspace
+    bneed = la.la_bwd_gated_workspace_bytes(s)
+    bwd = lambda fws: L.la_chunk_bwd_gated_from_fwd(
+        ctypes.byref(s), v(FAKE), v(FAKE), v(FAKE), v(FAKE), None, v(FAKE), None, v(fws),
+        v(FAKE), v(FAKE), v(FAKE), None, None, v(FAKE), bneed, None)
+    assert bwd(None) == la.LA_ERR_INVALID_ARG
+    assert bwd(FAKE + 8) == la.LA_ERR_INVALID_ARG
 
 
 def test_gated_backward_workspace_follows_the_1024_token_plan():

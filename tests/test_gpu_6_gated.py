@@ -219,6 +219,50 @@ def test_gated_bwd_matches_oracle(dtype, D, B, H, L, nseg, split, s0, dse):
     assert errs[4] <= (TOL[dtype] if H > 1 or dtype == "fp32" else 2.5e-2)
 
 
+FROM_FWD_CASES = [
+    # dtype, D, B, H, L, nseg, split, whether the forward's states serve
+    ("bf16", 128, 1, 2, 4096 * 3, 1, 3, True),   # 4096-token sub-segments
+    ("bf16", 64, 2, 2, 1024 * 5, 1, 5, True),    # 1024-token sub-segments
+    ("bf16", 128, 1, 2, 2 * 3072, 2, 3, True),   # two segments of 3 x 1024 tokens
+    ("fp32", 64, 1, 2, 2048, 1, 2, True),        # the fp32 sweeps
+    ("bf16", 128, 1, 2, 5000, 1, 3, False),      # 1728-token sub-segments
+    ("bf16", 128, 1, 2, 4096 + 17, 1, 2, False),  # a ragged segment: the 1024-token plan
+]
+
+
+@pytest.mark.parametrize("dtype,D,B,H,L,nseg,split,reuse", FROM_FWD_CASES)
+def test_gated_bwd_from_the_forwards_states(dtype, D, B, H, L, nseg, split, reuse):
+    """la_chunk_bwd_gated_from_fwd right after la_chunk_fwd_gated on the same
+    inputs: the oracle's gradients; la_chunk_bwd_gated's up to the rounding
+    of the start states where the dQ sweep reads the forward's, bitwise where
+    the plans differ and it forms its own."""
+    log(f"gated bwd from fwd dtype={dtype} D={D} B={B} H={H} L={L} nseg={nseg} split={split}")
+    inp = make_inputs(B, H, L, D, D, dtype=dtype, s0_std=0.5, nseg=nseg, need_dO=True,
+                      dS_end_std=0.5, seed=4300 + L + D, device="cuda")
+    G = gate_logs(decay_schedule(H, True), B, L, 4300 + L, device="cuda")
+    q, k, v, S0, dO, dSe = (inp[x] for x in ("q", "k", "v", "S0", "dO", "dS_end"))
+    shape = la.make_shape(B, H, L, D, D, nseg, la.LA_BF16 if dtype == "bf16" else la.LA_FP32,
+                          split)
+    fws = torch.empty(max(la.la_fwd_gated_workspace_bytes(shape), 16), dtype=torch.uint8,
+                      device="cuda")
+    la.la_chunk_fwd_gated(q, k, v, G, S0=S0, nseg=nseg, split=split, workspace=fws)
+    got = la.la_chunk_bwd_gated(q, k, v, G, dO, S0=S0, dS_end=dSe, nseg=nseg, split=split,
+                                fwd_workspace=fws)
+    own = la.la_chunk_bwd_gated(q, k, v, G, dO, S0=S0, dS_end=dSe, nseg=nseg, split=split)
+    torch.cuda.synchronize()
+    ref = lao.bwd_gated(f64(q), f64(k), f64(v), f64(G), f64(dO), S0=f64(S0), dS_end=f64(dSe),
+                        nseg=nseg)
+    errs = [rel_err(f64(x), r) for x, r in zip(got, ref)]
+    diffs = [rel_err(f64(x), f64(y)) for x, y in zip(got, own)]
+    log("  err dQ={:.3e} dK={:.3e} dV={:.3e} dS0={:.3e} dlogalpha={:.3e}".format(*errs))
+    log("  vs la_chunk_bwd_gated: " + " ".join(f"{d:.1e}" for d in diffs))
+    assert max(errs) <= TOL[dtype]
+    if reuse:
+        assert max(diffs) <= TOL[dtype]
+    else:
+        assert all(torch.equal(x, y) for x, y in zip(got, own))
+
+
 def test_gated_bwd_optional_outputs():
     """dS0 and the log-gate gradient may be skipped; the other gradients do
     not change."""

@@ -91,6 +91,8 @@ def test_forward_backward_scan_stay_inside_their_buffers(dtype, D, B, H, L, nseg
     la.la_chunk_bwd(q, k, v, lam, dO, S0=S0, dS_end=dSe, nseg=nseg, split=split, out=outs,
                     workspace=bws)
     g.check("la_chunk_bwd", list(zip(("dQ", "dK", "dV", "dS0"), outs)))
+    for t in outs:
+        t.fill_(float("nan"))
     la.la_chunk_bwd(q, k, v, lam, dO, S0=S0, dS_end=dSe, nseg=nseg, split=split, out=outs,
                     workspace=bws, fwd_workspace=ws)
     g.check("la_chunk_bwd_from_fwd", list(zip(("dQ", "dK", "dV", "dS0"), outs)))
@@ -113,6 +115,12 @@ def test_forward_backward_scan_stay_inside_their_buffers(dtype, D, B, H, L, nseg
     la.la_chunk_bwd_gated(q, k, v, G, dO, S0=S0, dS_end=dSe, nseg=nseg, split=split, out=gouts,
                           workspace=gbws)
     g.check("la_chunk_bwd_gated", list(zip(("dQ", "dK", "dV", "dS0", "dlog_alpha"), gouts)))
+    for t in gouts:
+        t.fill_(float("nan"))
+    la.la_chunk_bwd_gated(q, k, v, G, dO, S0=S0, dS_end=dSe, nseg=nseg, split=split, out=gouts,
+                          workspace=gbws, fwd_workspace=gws)
+    g.check("la_chunk_bwd_gated_from_fwd",
+            list(zip(("dQ", "dK", "dV", "dS0", "dlog_alpha"), gouts)))
     # decay gradient
     dl = g.new((H,), torch.float32)
     tws = g.workspace(la.la_decay_grad_workspace_bytes(shape))
