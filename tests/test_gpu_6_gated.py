@@ -220,18 +220,19 @@ def test_gated_bwd_matches_oracle(dtype, D, B, H, L, nseg, split, s0, dse):
 
 
 FROM_FWD_CASES = [
-    # dtype, D, B, H, L, nseg, split, whether the forward's states serve
-    ("bf16", 128, 1, 2, 4096 * 3, 1, 3, True),   # 4096-token sub-segments
-    ("bf16", 64, 2, 2, 1024 * 5, 1, 5, True),    # 1024-token sub-segments
-    ("bf16", 128, 1, 2, 2 * 3072, 2, 3, True),   # two segments of 3 x 1024 tokens
-    ("fp32", 64, 1, 2, 2048, 1, 2, True),        # the fp32 sweeps
-    ("bf16", 128, 1, 2, 5000, 1, 3, False),      # 1728-token sub-segments
-    ("bf16", 128, 1, 2, 4096 + 17, 1, 2, False),  # a ragged segment: the 1024-token plan
+    # dtype, D, B, H, L, nseg, split, log-gate gradient, whether the forward's states serve
+    ("bf16", 128, 1, 2, 4096 * 3, 1, 3, True, True),    # 4096-token sub-segments
+    ("bf16", 64, 2, 2, 1024 * 5, 1, 5, True, True),     # 1024-token sub-segments
+    ("bf16", 128, 1, 2, 2 * 3072, 2, 3, True, True),    # two segments of 3 x 1024 tokens
+    ("fp32", 64, 1, 2, 2048, 1, 2, True, True),         # the fp32 sweeps
+    ("bf16", 128, 1, 2, 3 * 1024 - 5, 1, 3, False, True),  # ragged, no log-gate gradient
+    ("bf16", 128, 1, 2, 5000, 1, 3, True, False),       # 1728-token sub-segments
+    ("bf16", 128, 1, 2, 4096 + 17, 1, 2, True, False),  # ragged: the 1024-token plan
 ]
 
 
-@pytest.mark.parametrize("dtype,D,B,H,L,nseg,split,reuse", FROM_FWD_CASES)
-def test_gated_bwd_from_the_forwards_states(dtype, D, B, H, L, nseg, split, reuse):
+@pytest.mark.parametrize("dtype,D,B,H,L,nseg,split,dla,reuse", FROM_FWD_CASES)
+def test_gated_bwd_from_the_forwards_states(dtype, D, B, H, L, nseg, split, dla, reuse):
     """la_chunk_bwd_gated_from_fwd right after la_chunk_fwd_gated on the same
     inputs: the oracle's gradients; la_chunk_bwd_gated's up to the rounding
     of the start states where the dQ sweep reads the forward's, bitwise where
@@ -247,14 +248,17 @@ def test_gated_bwd_from_the_forwards_states(dtype, D, B, H, L, nseg, split, reus
                       device="cuda")
     la.la_chunk_fwd_gated(q, k, v, G, S0=S0, nseg=nseg, split=split, workspace=fws)
     got = la.la_chunk_bwd_gated(q, k, v, G, dO, S0=S0, dS_end=dSe, nseg=nseg, split=split,
-                                fwd_workspace=fws)
-    own = la.la_chunk_bwd_gated(q, k, v, G, dO, S0=S0, dS_end=dSe, nseg=nseg, split=split)
+                                need_dlog_alpha=dla, fwd_workspace=fws)
+    own = la.la_chunk_bwd_gated(q, k, v, G, dO, S0=S0, dS_end=dSe, nseg=nseg, split=split,
+                                need_dlog_alpha=dla)
     torch.cuda.synchronize()
     ref = lao.bwd_gated(f64(q), f64(k), f64(v), f64(G), f64(dO), S0=f64(S0), dS_end=f64(dSe),
                         nseg=nseg)
+    n = 5 if dla else 4
+    got, own, ref = got[:n], own[:n], ref[:n]
     errs = [rel_err(f64(x), r) for x, r in zip(got, ref)]
     diffs = [rel_err(f64(x), f64(y)) for x, y in zip(got, own)]
-    log("  err dQ={:.3e} dK={:.3e} dV={:.3e} dS0={:.3e} dlogalpha={:.3e}".format(*errs))
+    log("  err dQ, dK, dV, dS0[, dlogalpha]: " + " ".join(f"{e:.3e}" for e in errs))
     log("  vs la_chunk_bwd_gated: " + " ".join(f"{d:.1e}" for d in diffs))
     assert max(errs) <= TOL[dtype]
     if reuse:
