@@ -4,8 +4,9 @@ backward's sweeps write the 1024-row states for the anchors themselves and the
 row sums run in one pass), and towards the backward taking the forward's
 workspace: per drawn configuration (dtype, d, batch, heads, segment length,
 segments, internal split, S0, dS_end) one of the forward with the backward
-from its workspace, the backward on its own, the gated backward or the decay
-gradient, against the CPU oracle.  The draws are fixed by the seed, so a
+from its workspace, the backward on its own, the gated backward (every other
+one after the gated forward, from its workspace) or the decay gradient,
+against the CPU oracle.  The draws are fixed by the seed, so a
 failure names a reproducible case.  Needs a gfx950 GPU."""
 import random
 
@@ -80,14 +81,27 @@ def test_random_shape_matches_oracle(i, what, dtype, D, B, H, L, nseg, split, s0
         bounds = [tol] * len(errs)
     elif what == "gated_bwd":
         G = gate_logs(decay_schedule(H, True), B, L, 10000 + i, device="cuda")
-        got = la.la_chunk_bwd_gated(q, k, v, G, dO, S0=S0, dS_end=dSe, nseg=nseg, split=split)
+        errs = []
+        fws = None
+        if i % 8 == 6:  # every other one after the gated forward, from its workspace
+            shape = la.make_shape(B, H, L, D, D, nseg,
+                                  la.LA_BF16 if dtype == "bf16" else la.LA_FP32, split)
+            fws = torch.empty(max(la.la_fwd_gated_workspace_bytes(shape), 16), dtype=torch.uint8,
+                              device="cuda")
+            O, S_end = la.la_chunk_fwd_gated(q, k, v, G, S0=S0, nseg=nseg, split=split,
+                                             workspace=fws)
+            torch.cuda.synchronize()
+            ref_f = lao.fwd_gated(f64(q), f64(k), f64(v), f64(G), S0=f64(S0), nseg=nseg)
+            errs = [rel_err(f64(O), ref_f[0]), rel_err(f64(S_end), ref_f[1])]
+        got = la.la_chunk_bwd_gated(q, k, v, G, dO, S0=S0, dS_end=dSe, nseg=nseg, split=split,
+                                    fwd_workspace=fws)
         torch.cuda.synchronize()
         ref = lao.bwd_gated(f64(q), f64(k), f64(v), f64(G), f64(dO), S0=f64(S0), dS_end=f64(dSe),
                             nseg=nseg)
-        errs = [rel_err(f64(x), r) for x, r in zip(got, ref)]
+        errs += [rel_err(f64(x), r) for x, r in zip(got, ref)]
         # the log-gate gradient of a single short-window head on its own
         # scale, as in the gated tests: 2.5 %
-        bounds = [tol] * 4 + [tol if (H > 1 or dtype == "fp32") else 2.5e-2]
+        bounds = [tol] * (len(errs) - 1) + [tol if (H > 1 or dtype == "fp32") else 2.5e-2]
     else:
         got = la.la_decay_grad(q, k, v, lam, dO, S0=S0, dS_end=dSe, nseg=nseg, split=split)
         torch.cuda.synchronize()
