@@ -425,8 +425,9 @@ la_status la_chunk_fwd_gated(const la_shape* s, const void* Q, const void* K, co
 
 // The gated backward forms the sweeps' states on sub-segments of exactly 1024
 // tokens (whatever `split` asks for): the start states at their boundaries
-// anchor the log-gate gradient (k_gate_anchors), so that its suffix sums never
-// run over more than 1024 tokens.  The reverse sweeps take the short
+// anchor the log-gate gradient (launch_gate_anchors, or inside
+// launch_gate_grad_rows), so that its suffix sums never run over more than
+// 1024 tokens.  The reverse sweeps take the short
 // sub-segment first, which puts their boundaries on the same rows.
 constexpr int64_t kGateBlock = 1024;
 Plan gated_bwd_plan(const Plan& p) {
