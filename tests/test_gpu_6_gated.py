@@ -298,17 +298,26 @@ def test_gated_bwd_at_the_training_workload_every_head():
     G = gate_logs(lam, w.B, w.L, w.seed, device="cuda")
     log(f"gated bwd full size: {w.name} B={w.B} H={w.H} L={w.L}")
     got = la.la_chunk_bwd_gated(q, k, v, G, dO)
+    # and from the gated forward's workspace, as a training step calls it
+    shape = la.make_shape(w.B, w.H, w.L, w.d, w.d, 1, la.LA_BF16, 0)
+    fws = torch.empty(max(la.la_fwd_gated_workspace_bytes(shape), 16), dtype=torch.uint8,
+                      device="cuda")
+    la.la_chunk_fwd_gated(q, k, v, G, need_O=False, workspace=fws)
+    got_f = la.la_chunk_bwd_gated(q, k, v, G, dO, fwd_workspace=fws)
     torch.cuda.synchronize()
     names = ("dQ", "dK", "dV", "dS0", "dlogalpha")
-    acc = WholeTensorErr()
+    acc, acc_f = WholeTensorErr(), WholeTensorErr()
     for h0 in range(0, w.H, 8):
         hs = list(range(h0, min(w.H, h0 + 8)))
         sl = lambda t: f64(t[:, hs[0]:hs[-1] + 1])
         log(f"  oracle heads {hs}")
         ref = lao.bwd_gated(sl(q), sl(k), sl(v), sl(G), sl(dO))
-        for n, x, r in zip(names, got, ref):
+        for n, x, xf, r in zip(names, got, got_f, ref):
             acc.add(n, sl(x), r, hs)
+            acc_f.add(n, sl(xf), r, hs)
         del ref
     errs = acc.report("gated train_256k")
+    errs_f = acc_f.report("gated train_256k from the forward's states")
     assert max(errs.values()) <= TOL["bf16"]
-    del q, k, v, dO, got
+    assert max(errs_f.values()) <= TOL["bf16"]
+    del q, k, v, dO, got, got_f, fws
