@@ -359,6 +359,21 @@ la_status la_step(int64_t B, int64_t H, int32_t dk, int32_t dv, int32_t dtype,
                   const float* S, float* S_out, void* o, void* stream);
 
 /*
+ * One decode step of the gated recurrence (la_chunk_fwd_gated) for a batch
+ * of B * H sequences, the token's own gate in place of lambda_h:
+ *     S_out = alpha S + k v^T          o = q^T S_out
+ *   log_alpha [B,H] fp32   log of the token's gate per sequence and head,
+ *                          log(alpha) <= 0; required.  alpha is formed in
+ *                          fp32 as 2^(log_alpha * log2 e).
+ *   other arguments, checks and errors as la_step.
+ * Stepping a sequence token by token from S0 gives la_chunk_fwd_gated's
+ * outputs and final state over those tokens, up to rounding.
+ */
+la_status la_step_gated(int64_t B, int64_t H, int32_t dk, int32_t dv, int32_t dtype,
+                        const void* q, const void* k, const void* v, const float* log_alpha,
+                        const float* S, float* S_out, void* o, void* stream);
+
+/*
  * la_chunk_fwd without a workspace, for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc.  Same arguments, results and checks as la_chunk_fwd (the

@@ -779,9 +779,11 @@ la_status la_decay_grad(const la_shape* s, const void* Q, const void* K, const v
   return LA_OK;
 }
 
-la_status la_step(int64_t B, int64_t H, int32_t dk, int32_t dv, int32_t dtype, const void* q,
-                  const void* k, const void* v, const float* lambda, const float* S,
-                  float* S_out, void* o, void* stream) {
+// One decode step, with the per-head decay lambda or (gated, lambda null) the
+// token's log-gate per sequence.
+static la_status step(int64_t B, int64_t H, int32_t dk, int32_t dv, int32_t dtype, const void* q,
+                      const void* k, const void* v, const float* lambda, const float* log_alpha,
+                      const float* S, float* S_out, void* o, void* stream) {
   if (B < 0 || H < 0) return fail(LA_ERR_INVALID_ARG, "negative size (B=%lld H=%lld)",
                                   (long long)B, (long long)H);
   if (dk <= 0 || dv <= 0) return fail(LA_ERR_INVALID_ARG, "dk and dv must be positive");
@@ -793,9 +795,10 @@ la_status la_step(int64_t B, int64_t H, int32_t dk, int32_t dv, int32_t dtype, c
     return fail(LA_ERR_UNSUPPORTED, "too many sequences for one launch");
   const int64_t nseq = B * H;
   if (nseq == 0) return LA_OK;
-  if (!q || !k || !v || !lambda || !S_out)
-    return fail(LA_ERR_INVALID_ARG, "q, k, v, lambda and S_out are required");
-  const void* ptrs[] = {q, k, v, lambda, S, S_out, o};
+  if (!q || !k || !v || !S_out || (!lambda && !log_alpha))
+    return fail(LA_ERR_INVALID_ARG, "q, k, v, %s and S_out are required",
+                log_alpha || !lambda ? "log_alpha" : "lambda");
+  const void* ptrs[] = {q, k, v, lambda, log_alpha, S, S_out, o};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return fail(LA_ERR_INVALID_ARG, "pointer %p is not 16-byte aligned", p);
   const size_t sbytes = (size_t)nseq * (size_t)dk * (size_t)dv * sizeof(float);
@@ -811,6 +814,7 @@ la_status la_step(int64_t B, int64_t H, int32_t dk, int32_t dv, int32_t dtype, c
   sa.k = k;
   sa.v = v;
   sa.lam = lambda;
+  sa.loga = log_alpha;
   sa.S = S;
   sa.Sout = S_out;
   sa.o = o;
@@ -818,6 +822,20 @@ la_status la_step(int64_t B, int64_t H, int32_t dk, int32_t dv, int32_t dtype, c
   hipError_t e = la::launch_step(sa, dtype, dk, nseq, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode step launch");
   return LA_OK;
+}
+
+la_status la_step(int64_t B, int64_t H, int32_t dk, int32_t dv, int32_t dtype, const void* q,
+                  const void* k, const void* v, const float* lambda, const float* S,
+                  float* S_out, void* o, void* stream) {
+  if (!lambda && B > 0 && H > 0) return fail(LA_ERR_INVALID_ARG, "lambda is required");
+  return step(B, H, dk, dv, dtype, q, k, v, lambda, nullptr, S, S_out, o, stream);
+}
+
+la_status la_step_gated(int64_t B, int64_t H, int32_t dk, int32_t dv, int32_t dtype,
+                        const void* q, const void* k, const void* v, const float* log_alpha,
+                        const float* S, float* S_out, void* o, void* stream) {
+  if (!log_alpha && B > 0 && H > 0) return fail(LA_ERR_INVALID_ARG, "log_alpha is required");
+  return step(B, H, dk, dv, dtype, q, k, v, nullptr, log_alpha, S, S_out, o, stream);
 }
 
 la_status la_state_scan_gated(int64_t B, int64_t H, int32_t P, int32_t dk, int32_t dv,

@@ -188,6 +188,7 @@ struct StepArgs {
   const void* k;     // [nseq][D]
   const void* v;     // [nseq][D]
   const float* lam;  // [H]
+  const float* loga; // [nseq] or null: the token's log-gate per sequence, in place of lam
   const float* S;    // [nseq][D][D] or null (zero)
   float* Sout;       // [nseq][D][D], may equal S
   void* o;           // [nseq][D] or null

@@ -1,7 +1,10 @@
 // la_step.hip -- one recurrent decode step for a batch of sequences:
 //   S' = lambda_h S + k v^T,   o = q^T S'
 // for every (b, h): the token recurrence itself, the constant-memory
-// inference form named in the LASP-2 page's abstract.  The work is a
+// inference form named in the LASP-2 page's abstract; gated, the decay is
+// the token's own gate alpha = exp(log alpha) of the sequence (the per-token
+// gates of the Gated Linear Attention entry of that page's related-paper
+// list).  The work is a
 // rank-one update of the fp32 state and a matrix-vector product: a few
 // flops per state element, so the step is bound by HBM, reading the state
 // once and writing it once.
@@ -37,7 +40,9 @@ __global__ __launch_bounds__(256) void k_step(StepArgs a) {
   const int rr = tid >> 3;
   const int c4 = (tid & 7) * 4;
   const int64_t DD = (int64_t)D * D;
-  const float lam = a.lam[h];
+  // gated: alpha = 2^(log alpha * log2 e), as the chunk walks form their
+  // gate factors
+  const float lam = a.loga ? exp2f(a.loga[n] * 1.4426950408889634f) : a.lam[h];
 
   const float* S = a.S ? a.S + n * DD : nullptr;
   float* So = a.Sout + n * DD;

@@ -25,7 +25,7 @@ EXPORTS = ("la_version", "la_status_str", "la_last_error", "la_fwd_workspace_byt
            "la_fwd_gated_workspace_bytes", "la_chunk_fwd_gated", "la_state_scan_gated",
            "la_bwd_gated_workspace_bytes", "la_chunk_bwd_gated",
            "la_decay_grad_workspace_bytes", "la_decay_grad", "la_step", "la_chunk_bwd_from_fwd",
-           "la_chunk_bwd_gated_from_fwd", "la_chunk_fwd_noalloc")
+           "la_chunk_bwd_gated_from_fwd", "la_step_gated", "la_chunk_fwd_noalloc")
 
 
 class LinAttnError(RuntimeError):
@@ -87,6 +87,8 @@ def lib():
     L.la_chunk_bwd_from_fwd.argtypes = [sp] + [vp] * 13 + [sz, vp]
     L.la_step.restype = ctypes.c_int
     L.la_step.argtypes = [i64, i64, i32, i32, i32] + [vp] * 7 + [vp]
+    L.la_step_gated.restype = ctypes.c_int
+    L.la_step_gated.argtypes = [i64, i64, i32, i32, i32] + [vp] * 7 + [vp]
     L.la_decay_grad_workspace_bytes.restype = sz
     L.la_decay_grad_workspace_bytes.argtypes = [sp]
     L.la_decay_grad.restype = ctypes.c_int
@@ -478,4 +480,31 @@ def la_step(q, k, v, lam, S=None, out=None, S_out=None, need_o: bool = True):
         torch.empty((B, H, dv), dtype=q.dtype, device=q.device) if need_o else None)
     _check(lib().la_step(B, H, dk, dv, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(lam), _ptr(S),
                          _ptr(S_out), _ptr(o), _stream()))
+    return o, S_out
+
+
+def la_step_gated(q, k, v, log_alpha, S=None, out=None, S_out=None, need_o: bool = True):
+    """One gated decode step: S' = exp(log_alpha) S + k v^T, o = q^T S' for
+    q, k [B,H,dk], v [B,H,dv], log_alpha [B,H] fp32 (the token's log-gate per
+    sequence and head) and S [B,H,dk,dv] fp32 (None = zero).  S_out may be S
+    (in place).  Returns (o or None, S')."""
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dt = _dtype_code(q.dtype)
+    dev = q.device
+    _expect_all(
+        dev,
+        (q, "q", (B, H, dk), q.dtype),
+        (k, "k", (B, H, dk), q.dtype),
+        (v, "v", (B, H, dv), q.dtype),
+        (log_alpha, "log_alpha", (B, H), torch.float32),
+        (S, "S", (B, H, dk, dv), torch.float32),
+        (S_out, "S_out", (B, H, dk, dv), torch.float32),
+        (out, "out", (B, H, dv), q.dtype))
+    if S_out is None:
+        S_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    o = out if out is not None else (
+        torch.empty((B, H, dv), dtype=q.dtype, device=q.device) if need_o else None)
+    _check(lib().la_step_gated(B, H, dk, dv, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                               _ptr(S), _ptr(S_out), _ptr(o), _stream()))
     return o, S_out

@@ -163,7 +163,9 @@ hipError_t launch_tangent(const TanArgs& a, int, int D, int64_t nseq, float* dla
 }
 
 hipError_t launch_step(const StepArgs& a, int, int D, int64_t nseq, hipStream_t) {
-  expect(nseq > 0 && a.q && a.k && a.v && a.lam && a.Sout && (D == 64 || D == 128), "step");
+  expect(nseq > 0 && a.q && a.k && a.v && (a.lam != nullptr) != (a.loga != nullptr) && a.Sout &&
+             (D == 64 || D == 128),
+         "step");
   ++g_launches;
   return hipSuccess;
 }

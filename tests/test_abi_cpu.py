@@ -289,6 +289,17 @@ def test_decode_step_validates_on_the_host():
     assert call(k=FAKE + 4) == la.LA_ERR_INVALID_ARG
     # S_out overlapping S without being S
     assert call(S=FAKE + (1 << 24), So=FAKE + (1 << 24) + 4096) == la.LA_ERR_INVALID_ARG
+    assert call(lam=None) == la.LA_ERR_INVALID_ARG
+
+    def gcall(B=2, H=3, G=FAKE, S=None, So=FAKE + (1 << 24), dk=64):
+        return L.la_step_gated(B, H, dk, dk, la.LA_BF16, v(FAKE), v(FAKE), v(FAKE), v(G), v(S),
+                               v(So), v(FAKE), None)
+    assert gcall(B=0, G=None, So=None) == la.LA_OK  # no-op
+    assert gcall(G=None) == la.LA_ERR_INVALID_ARG      # log_alpha required
+    assert gcall(G=FAKE + 4) == la.LA_ERR_INVALID_ARG  # misaligned
+    assert gcall(So=None) == la.LA_ERR_INVALID_ARG
+    assert gcall(dk=96) == la.LA_ERR_UNSUPPORTED
+    assert gcall(S=FAKE + (1 << 24), So=FAKE + (1 << 24) + 4096) == la.LA_ERR_INVALID_ARG
 
 
 def test_empty_problem_is_a_no_op():

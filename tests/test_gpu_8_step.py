@@ -1,14 +1,15 @@
 """Parity of the recurrent decode step (la_step) with the CPU oracle
 (lao.step, pinned against the forward pass) and with the chunked forward
-of the HIP path over the same tokens, through the C ABI.  Needs a gfx950
-GPU."""
+of the HIP path over the same tokens, through the C ABI; the gated step
+(la_step_gated) against the oracle's gated forward over one token and the
+chunked gated forward over a chain of tokens.  Needs a gfx950 GPU."""
 import numpy as np
 import pytest
 import torch
 
 from gpu_helpers import TOL, f64, log, rel_err, require_gpu
 from long_sequence_causal_amd import linattn as la
-from long_sequence_causal_amd.inputs import decode_inputs, decay_schedule, make_inputs
+from long_sequence_causal_amd.inputs import decode_inputs, decay_schedule, gate_logs, make_inputs
 from oracle import lao
 
 pytestmark = pytest.mark.gpu
@@ -84,6 +85,62 @@ def test_a_chain_of_steps_matches_the_chunked_forward(dtype, D):
     e = [rel_err(f64(Os), O_r), rel_err(f64(S), S_r[:, :, 0]), rel_err(f64(Os), f64(O)),
          rel_err(f64(S), f64(S_end)[:, :, 0])]
     log("  chain err vs oracle o={:.3e} S={:.3e}; vs chunked forward o={:.3e} S={:.3e}".format(*e))
+    assert max(e) <= TOL[dtype]
+
+
+GATED_CASES = [
+    # dtype, D, B, H, S std
+    ("fp32", 64, 2, 3, 0.5),
+    ("fp32", 128, 1, 4, 0.0),
+    ("bf16", 128, 4, 8, 0.5),
+    ("bf16", 64, 3, 2, 0.5),
+]
+
+
+@pytest.mark.parametrize("dtype,D,B,H,s_std", GATED_CASES)
+def test_gated_step_matches_the_oracle(dtype, D, B, H, s_std):
+    """One gated step is the oracle's gated forward over that one token from
+    S; the gates span (-2, 0], with the extremes 0 (no decay) and -80 (the
+    state all but forgotten) in the first sequence."""
+    log(f"gated step dtype={dtype} D={D} B={B} H={H} S_std={s_std}")
+    q, k, v, _, S = _draw(B, H, D, dtype, s_std, 600 + D + B + H)
+    g = torch.Generator(device="cuda").manual_seed(601 + D)
+    G = -(torch.rand((B, H), generator=g, device="cuda") * 2.0)
+    G[0, 0] = 0.0
+    if H > 1:
+        G[0, 1] = -80.0
+    o, S1 = la.la_step_gated(q, k, v, G, S)
+    torch.cuda.synchronize()
+    S0 = None if S is None else f64(S)[:, :, None]
+    O_r, Se_r = lao.fwd_gated(f64(q)[:, :, None], f64(k)[:, :, None], f64(v)[:, :, None],
+                              f64(G)[:, :, None], S0=S0)
+    eo, es = rel_err(f64(o), O_r[:, :, 0]), rel_err(f64(S1), Se_r[:, :, 0])
+    log(f"  err o={eo:.3e} S'={es:.3e}")
+    assert eo <= TOL[dtype] and es <= TOL["fp32"]
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp32", 64)])
+def test_a_chain_of_gated_steps_matches_the_chunked_gated_forward(dtype, D):
+    """T gated decode steps from S0 (in place) give the outputs and final
+    state of the chunked gated forward over the same T tokens and gates."""
+    B, H, T = 2, 3, 70
+    inp = make_inputs(B, H, T, D, D, dtype=dtype, s0_std=0.5, seed=89, device="cuda")
+    q, k, v, lam, S0 = inp["q"], inp["k"], inp["v"], inp["lam"], inp["S0"]
+    G = gate_logs(lam, B, T, 89, device="cuda")
+    O, S_end = la.la_chunk_fwd_gated(q, k, v, G, S0=S0)
+    S = S0[:, :, 0].clone()
+    outs = []
+    for t in range(T):
+        o, S = la.la_step_gated(q[:, :, t].contiguous(), k[:, :, t].contiguous(),
+                                v[:, :, t].contiguous(), G[:, :, t].contiguous(), S, S_out=S)
+        outs.append(o)
+    torch.cuda.synchronize()
+    Os = torch.stack(outs, dim=2)
+    O_r, S_r = lao.fwd_gated(f64(q), f64(k), f64(v), f64(G), S0=f64(S0))
+    e = [rel_err(f64(Os), O_r), rel_err(f64(S), S_r[:, :, 0]), rel_err(f64(Os), f64(O)),
+         rel_err(f64(S), f64(S_end)[:, :, 0])]
+    log("  gated chain err vs oracle o={:.3e} S={:.3e}; vs chunked gated forward o={:.3e} "
+        "S={:.3e}".format(*e))
     assert max(e) <= TOL[dtype]
 
 

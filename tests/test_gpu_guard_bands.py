@@ -144,3 +144,8 @@ def test_decode_step_stays_inside_its_buffers(dtype, D):
     g.check("la_step", [("o", o), ("S_out", So)])
     la.la_step(q, k, v, lam, So, out=o, S_out=So)  # in place
     g.check("la_step in place", [("o", o), ("S_out", So)])
+    G = -torch.rand((B, H), generator=gen, device="cuda")
+    o.fill_(float("nan"))
+    So.fill_(float("nan"))
+    la.la_step_gated(q, k, v, G, S, out=o, S_out=So)
+    g.check("la_step_gated", [("o", o), ("S_out", So)])
