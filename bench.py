@@ -230,11 +230,30 @@ def decode_leg(torch, la, dev, iters, name="decode_b64", ramp_ms=0.0):
     ms = each[len(each) // 2]  # median: a step is short enough for one stall to swamp a mean
     nbytes = B * H * (2 * d * d * 4 + 4 * d * 2)
     t = ms / 1e3
+    rec = {"workload": name, "B": B, "H": H, "d": d, "dtype": w["dtype"], "ramp_ms": ramp_ms,
+           "us_per_call": ms * 1e3, "us_min": each[0] * 1e3, "us_max": each[-1] * 1e3,
+           "calls": iters, "tokens_per_s": B / t, "alg_bytes": nbytes,
+           "achieved_GBs": nbytes / t / 1e9, "frac_hbm": nbytes / t / 1e9 / HBM_PEAK_GBS}
+    if name == "decode_b64":
+        # the gated step on the same batch, each sequence's gate for the token
+        # drawn around its head's decay (one fp32 log-gate per sequence more)
+        G = torch.log(lam).view(1, H) * (2.0 * torch.rand((B, H), device=dev,
+                                                           generator=torch.Generator(device=dev).manual_seed(5)))
+
+        def gcall():
+            la.la_step_gated(q, k, v, G, S, out=o, S_out=S)
+
+        ramp(gcall, ramp_ms)
+        geach = sorted(time_each(gcall, iters, torch.cuda.current_stream()))
+        gms = geach[len(geach) // 2]
+        gbytes = nbytes + B * H * 4
+        gt = gms / 1e3
+        rec["gated"] = {"us_per_call": gms * 1e3, "tokens_per_s": B / gt, "alg_bytes": gbytes,
+                        "achieved_GBs": gbytes / gt / 1e9,
+                        "frac_hbm": gbytes / gt / 1e9 / HBM_PEAK_GBS}
+        del G
     del inp, q, k, v, S, o
-    return {"workload": name, "B": B, "H": H, "d": d, "dtype": w["dtype"], "ramp_ms": ramp_ms,
-            "us_per_call": ms * 1e3, "us_min": each[0] * 1e3, "us_max": each[-1] * 1e3,
-            "calls": iters, "tokens_per_s": B / t, "alg_bytes": nbytes,
-            "achieved_GBs": nbytes / t / 1e9, "frac_hbm": nbytes / t / 1e9 / HBM_PEAK_GBS}
+    return rec
 
 
 def ramp(fn, min_ms):
@@ -526,7 +545,7 @@ def main():
         dl = decode_leg(torch, la, dev, max(200, args.steps), ramp_ms=args.leg_ramp_ms)
         eprint(f"[bench] decode step ({dl['workload']}): {dl['us_per_call']:.1f} us/call median "
                f"(min {dl['us_min']:.1f}, max {dl['us_max']:.1f} over {dl['calls']}), "
-               f"{dl['achieved_GBs']:.0f} GB/s algorithmic")
+               f"{dl['achieved_GBs']:.0f} GB/s algorithmic; gated {dl['gated']['us_per_call']:.1f} us/call")
         dx = decode_leg(torch, la, dev, 50, "decode_b512", ramp_ms=args.leg_ramp_ms)
         eprint(f"[bench] decode step ({dx['workload']}, state beyond the last-level cache): "
                f"{dx['us_per_call']:.1f} us/call median, {dx['achieved_GBs']:.0f} GB/s algorithmic")
