@@ -19,12 +19,12 @@
 // the result is a small difference of many terms (their absolute sum can be
 // hundreds of times larger), and U varies slowly along the sequence, so a
 // per-token rounding feeding U or M would add up coherently: in bf16 the
-// decayed operands (the weighted dO of M1 and M2, the weighted V of the S
-// update) go through the MFMA as hi + lo, and U, S never leave fp32.  The
-// weighted V of the U update goes as one rounded bf16: measured at 256K
-// tokens x 16 heads that keeps every head's gradient within 2.6e-3 of its
-// own size (hi + lo there too: 1e-4) for 9 % of the walk's time (16 of its
-// MFMAs and that split per chunk).  (The
+// decayed operands (the weighted dO of M1 and M2, the weighted V of both
+// updates) go through the MFMA as hi + lo, and U, S never leave fp32.  (The
+// weighted V of the U update as one rounded bf16 saves about 9 % of the
+// walk's time and keeps the benchmark's heads within 2.6e-3 of their own
+// size, but a single head whose gradient is small next to its terms, e.g.
+// 72.7 at 2176 tokens, came out 8.5 % off; hi + lo: 1e-5.)  (The
 // reverse-mode identity d l / d lambda = (1 / lambda) sum_u u (q_u . dq_u -
 // k_u . dk_u) + ... does cancel: its terms exceed the result by a factor
 // that grows with the sequence length, which bf16 gradients cannot carry.)
@@ -68,14 +68,6 @@ __device__ inline u32x2 split_hi_lo(float x0, float x1) {
   const f32x2 h = {__builtin_bit_cast(float, hi << 16), __builtin_bit_cast(float, hi & 0xffff0000u)};
   const unsigned lo = __builtin_bit_cast(unsigned, __builtin_convertvector(x - h, bf16x2));
   return u32x2{hi, lo};
-}
-
-// round-to-nearest-even bf16 of a pair, packed (element 0 in the low half)
-__device__ inline unsigned round_pair(float x0, float x1) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const f32x2 x = {x0, x1};
-  return __builtin_bit_cast(unsigned, __builtin_convertvector(x, bf16x2));
 }
 
 template <typename T, int D, bool MAIN>
@@ -415,17 +407,16 @@ k_tangent(TanArgs a) {
           accS[tk] *= dc;
         }
       }
-      // V^T operands of this wave's columns, scaled per token (S update: hi + lo
-      // in bf16; U update: one rounding)
+      // V^T operands of this wave's columns, scaled per token (hi + lo in bf16)
       const float* tw = tabW + 16 * g;
       // m + clf - 1 - slot_token = cB - slot_token(., 0, .) (small integers, exact)
       const float cB = (float)(clf - 1) - fB + (lcf ? (float)(CH * c) : 0.0f);
-      op_t B1[NJS], B1l[NJS], B2[NJS];
+      op_t B1[NJS], B1l[NJS], B2[NJS], B2l[NJS];
 #pragma unroll
       for (int js = 0; js < NJS; ++js) {
         const op_t Vop = tr_op<T, TN>(sV, js * KS, col, ln);
         if constexpr (E == 8) {
-          u32x4 b1, b1l, b2;
+          u32x4 b1, b1l, b2, b2l;
 #pragma unroll
           for (int x = 0; x < 8; x += 2) {
             const float vw0 = LAZY ? ((float)Vop[x] * tw[8 * js + x]) * fk
@@ -437,11 +428,14 @@ k_tangent(TanArgs a) {
             const u32x2 s1 = split_hi_lo(vw0, vw1);
             b1[x / 2] = s1[0];
             b1l[x / 2] = s1[1];
-            b2[x / 2] = round_pair(vu0, vu1);
+            const u32x2 s2 = split_hi_lo(vu0, vu1);
+            b2[x / 2] = s2[0];
+            b2l[x / 2] = s2[1];
           }
           B1[js] = __builtin_bit_cast(bf16x8, b1);
           B1l[js] = __builtin_bit_cast(bf16x8, b1l);
           B2[js] = __builtin_bit_cast(bf16x8, b2);
+          B2l[js] = __builtin_bit_cast(bf16x8, b2l);
         } else {
           B1[js] = Vop * (tw[js] * fk);
           B2[js] = B1[js] * (cB + fB - (float)slot_token<T>(js * KS, g, 0));
@@ -454,6 +448,7 @@ k_tangent(TanArgs a) {
           const op_t Ak = tr_op<T, TN>(sK, js * KS, 16 * tk, ln);
           accS[tk] = X::mfma(Ak, B1[js], accS[tk]);
           accT[tk] = X::mfma(Ak, B2[js], accT[tk]);
+          if constexpr (E == 8) accT[tk] = X::mfma(Ak, B2l[js], accT[tk]);
           if constexpr (E == 8) accS[tk] = X::mfma(Ak, B1l[js], accS[tk]);
         }
       }

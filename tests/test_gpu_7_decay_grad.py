@@ -91,6 +91,29 @@ def test_decay_grad_for_decays_on_both_sides_of_one_half(dtype, D, split):
     assert own.max() <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype,D,B,H,L,nseg,split,s0,dse,decay,seed", [
+    ("bf16", 128, 2, 1, 2176, 1, 0, 0.5, 0.0, True, 10011),
+    ("bf16", 128, 1, 1, 1372, 2, 2, 0.0, 0.0, False, 9085),
+])
+def test_decay_grad_of_a_single_head_whose_gradient_is_small(dtype, D, B, H, L, nseg, split, s0,
+                                                             dse, decay, seed):
+    """Two single-head cases whose gradient is small next to its terms (72.7
+    and -6381): with the U update's weighted V as one bf16 rounding they came
+    out 8.5 % and 2.6 % off; as hi + lo, like every decayed operand, within
+    1e-4."""
+    inp = make_inputs(B, H, L, D, D, dtype=dtype, decay=decay, s0_std=s0, nseg=nseg,
+                      need_dO=True, dS_end_std=dse, seed=seed, device="cuda")
+    q, k, v, lam, S0, dO, dSe = (inp[x] for x in ("q", "k", "v", "lam", "S0", "dO", "dS_end"))
+    ref = lao.dlambda(f64(q), f64(k), f64(v), f64(lam), f64(dO), S0=f64(S0), dS_end=f64(dSe),
+                      nseg=nseg)
+    for sp in (split, 1):
+        got = la.la_decay_grad(q, k, v, lam, dO, S0=S0, dS_end=dSe, nseg=nseg, split=sp)
+        torch.cuda.synchronize()
+        e = rel_err(f64(got), ref)
+        log(f"  split {sp}: dlambda {f64(got)} ref {ref} err {e:.3e}")
+        assert e <= 1e-3
+
+
 @pytest.mark.parametrize("B,L", [(1, 0), (0, 128)])
 def test_decay_grad_of_empty_problem_is_zero(B, L):
     H, D = 3, 64
@@ -127,7 +150,6 @@ def test_decay_grad_at_full_size_every_head(name, dse):
     log(f"  whole-vector err {e:.3e}; per head on its own scale: "
         + " ".join(f"h{h}={x:.1e}" for h, x in enumerate(own)))
     assert e <= TOL["bf16"]
-    # every head on its own scale as well: the U update's weighted V is one
-    # bf16 rounding, which keeps each head within 2.6e-3 at these sizes
+    # every head on its own scale as well
     assert own.max() <= 1e-2
     del q, k, v, dO
