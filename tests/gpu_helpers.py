@@ -27,6 +27,30 @@ def rel_err(x, ref):
     return num / den if den > 0 else num
 
 
+def gate_grad_err(got, ref, q, k, dq_ref, dk_ref, nseg=1):
+    """The measure of the log-gate gradient (bf16 paths): its value at t is an
+    in-block suffix sum of q_u . dq_u - k_u . dk_u over 1024-token blocks of
+    each segment, terms that cancel, so its attainable accuracy is set by the
+    terms' magnitude T = max_t sum_{u >= t in t's block} (|q_u . dq_u| +
+    |k_u . dk_u|) (from the oracle's dq, dk), not by max|ref| alone.  Returns
+    max|got - ref| / max(max|ref|, T / 10): at most 1e-2 means an error below
+    1e-2 of the largest value or below 1e-3 of T (half a bf16 unit roundoff
+    of the terms), whichever is larger."""
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    q, k = np.asarray(q, np.float64), np.asarray(k, np.float64)
+    B, H, L, _ = q.shape
+    a = np.abs((q * np.asarray(dq_ref)).sum(-1)) + np.abs((k * np.asarray(dk_ref)).sum(-1))
+    Ls = L // nseg
+    nb = -(-Ls // 1024)
+    pad = np.zeros((B, H, nseg, nb * 1024))
+    pad[..., :Ls] = a.reshape(B, H, nseg, Ls)
+    blk = pad.reshape(B, H, nseg, nb, 1024)
+    T = float(np.flip(np.cumsum(np.flip(blk, -1), -1), -1).max()) if L else 0.0
+    den = max(float(np.abs(ref).max()) if ref.size else 0.0, T / 10.0)
+    num = float(np.abs(got - ref).max()) if ref.size else 0.0
+    return num / den if den > 0 else num
+
+
 class WholeTensorErr:
     """The graded measure max |X - X_ref| / max |X_ref| over whole tensors that
     are compared a slice of heads at a time: running maxima of the numerator

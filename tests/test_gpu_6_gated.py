@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import TOL, WholeTensorErr, f64, log, rel_err, require_gpu
+from gpu_helpers import gate_grad_err, TOL, WholeTensorErr, f64, log, rel_err, require_gpu
 from long_sequence_causal_amd import linattn as la
 from long_sequence_causal_amd.inputs import decay_schedule, gate_logs, make_inputs, workload_inputs
 from oracle import lao
@@ -211,12 +211,14 @@ def test_gated_bwd_matches_oracle(dtype, D, B, H, L, nseg, split, s0, dse):
     ref = lao.bwd_gated(f64(q), f64(k), f64(v), f64(G), f64(dO), S0=f64(S0), dS_end=f64(dSe),
                         nseg=nseg)
     errs = [rel_err(f64(x), r) for x, r in zip(got, ref)]
-    log("  err dQ={:.3e} dK={:.3e} dV={:.3e} dS0={:.3e} dlogalpha={:.3e}".format(*errs))
+    eg = gate_grad_err(f64(got[4]), ref[4], f64(q), f64(k), ref[0], ref[1], nseg)
+    log("  err dQ={:.3e} dK={:.3e} dV={:.3e} dS0={:.3e} dlogalpha={:.3e} "
+        "(against its terms' scale: {:.3e})".format(*errs, eg))
     assert max(errs[:4]) <= TOL[dtype]
-    # dlog_alpha: with one head the measure is that head's own scale; for a
-    # short-window head (fast gates) the bf16 rounding of dq and dk inside the
-    # anchored 1024-token suffix sums reaches about 1.7 % of it (bound 2.5 %)
-    assert errs[4] <= (TOL[dtype] if H > 1 or dtype == "fp32" else 2.5e-2)
+    # dlog_alpha: fp32 on the plain measure; bf16 on the measure of a sum of
+    # cancelling terms (gate_grad_err): a short-window head's gradient can be
+    # a few hundred times smaller than its terms
+    assert (errs[4] if dtype == "fp32" else eg) <= TOL[dtype]
 
 
 FROM_FWD_CASES = [
@@ -257,6 +259,8 @@ def test_gated_bwd_from_the_forwards_states(dtype, D, B, H, L, nseg, split, dla,
     n = 5 if dla else 4
     got, own, ref = got[:n], own[:n], ref[:n]
     errs = [rel_err(f64(x), r) for x, r in zip(got, ref)]
+    if dla and dtype == "bf16":  # a sum of cancelling terms: gate_grad_err
+        errs[4] = gate_grad_err(f64(got[4]), ref[4], f64(q), f64(k), ref[0], ref[1], nseg)
     diffs = [rel_err(f64(x), f64(y)) for x, y in zip(got, own)]
     log("  err dQ, dK, dV, dS0[, dlogalpha]: " + " ".join(f"{e:.3e}" for e in errs))
     log("  vs la_chunk_bwd_gated: " + " ".join(f"{d:.1e}" for d in diffs))

@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import TOL, f64, log, rel_err, require_gpu
+from gpu_helpers import TOL, f64, gate_grad_err, log, rel_err, require_gpu
 from long_sequence_causal_amd import linattn as la
 from long_sequence_causal_amd.inputs import gate_logs, make_inputs
 from oracle import lao
@@ -82,6 +82,8 @@ def test_random_shape_gated(i, dtype, D, B, H, L, nseg, split, s0, dse, decay):
     g_r = lao.bwd_gated(a[0], a[1], a[2], a[3], a[4], S0=f64(S0), dS_end=f64(dSe), nseg=nseg)
     errs = [rel_err(f64(O), O_r), rel_err(f64(Se), Se_r)] + [rel_err(f64(x), r) for x, r in zip(got, g_r)]
     log("  err O={:.2e} S_end={:.2e} dQ={:.2e} dK={:.2e} dV={:.2e} dS0={:.2e} dlogalpha={:.2e}".format(*errs))
+    if dtype == "bf16":  # the log-gate gradient, a sum of cancelling terms: gate_grad_err
+        errs[-1] = gate_grad_err(f64(got[4]), g_r[4], a[0], a[1], g_r[0], g_r[1], nseg)
     assert max(errs) <= TOL[dtype]
 
 
