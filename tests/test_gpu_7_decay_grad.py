@@ -114,6 +114,39 @@ def test_decay_grad_of_a_single_head_whose_gradient_is_small(dtype, D, B, H, L, 
         assert e <= 1e-3
 
 
+def _random_lambda_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        out.append((i, "bf16" if i % 3 else "fp32", int(rng.choice([64, 128])),
+                    int(rng.choice([1, 2])), int(rng.choice([1, 2])), int(rng.integers(50, 3000)),
+                    int(rng.choice([1, 2])), int(rng.choice([0, 1, 2, 3])),
+                    [float(x) for x in rng.uniform(0.3, 1.0, 2)],
+                    float(rng.choice([0.0, 0.5])), float(rng.choice([0.0, 0.5]))))
+    return out
+
+
+@pytest.mark.parametrize("i,dtype,D,B,H,Ls,nseg,split,lams,s0,dse", _random_lambda_cases(16, 4242))
+def test_decay_grad_at_random_lambda_every_head_on_its_own_scale(i, dtype, D, B, H, Ls, nseg, split,
+                                                                 lams, s0, dse):
+    """Seeded random configurations with one or two heads at lambda drawn
+    from [0.3, 1] (the eager and the lazy walk, periods of every length):
+    each head's gradient against the oracle on its own scale, where a small
+    gradient next to its terms shows any rounding that adds up."""
+    lam = torch.tensor(lams[:H], dtype=torch.float32)
+    inp = make_inputs(B, H, Ls * nseg, D, D, dtype=dtype, s0_std=s0, nseg=nseg, need_dO=True,
+                      dS_end_std=dse, seed=30000 + i, device="cuda", lam=lam)
+    q, k, v, lm, S0, dO, dSe = (inp[x] for x in ("q", "k", "v", "lam", "S0", "dO", "dS_end"))
+    got = f64(la.la_decay_grad(q, k, v, lm, dO, S0=S0, dS_end=dSe, nseg=nseg, split=split))
+    torch.cuda.synchronize()
+    ref = lao.dlambda(f64(q), f64(k), f64(v), f64(lm), f64(dO), S0=f64(S0), dS_end=f64(dSe),
+                      nseg=nseg)
+    own = np.abs(got - ref) / np.abs(ref)
+    log(f"case {i} {dtype} D={D} B={B} H={H} L={Ls * nseg} nseg={nseg} split={split} "
+        f"lambda={lam.tolist()}: own-scale err " + " ".join(f"{x:.1e}" for x in own))
+    assert own.max() <= TOL[dtype]
+
+
 @pytest.mark.parametrize("B,L", [(1, 0), (0, 128)])
 def test_decay_grad_of_empty_problem_is_zero(B, L):
     H, D = 3, 64
